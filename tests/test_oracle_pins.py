@@ -1,0 +1,397 @@
+"""Pins for the CPU oracle, against facts that do not come from the oracle.
+
+Each test states what it pins and where the fact comes from: the collision law
+and the angular-sector picture of the Reformer explainer page
+(akshathtiwari.co.in/blog/reformer), closed forms worked by hand, exact
+invariants, and brute force on tiny inputs.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+
+def _unit(v):
+    return v / np.linalg.norm(v)
+
+
+# ---------------------------------------------------------------- hashing --
+
+@pytest.mark.parametrize("theta", [math.pi / 12, math.pi / 6, math.pi / 3, math.pi / 2, 2 * math.pi / 3])
+def test_collision_law_two_buckets(theta):
+    """Explainer page, angular-LSH passage: P[h(x) = h(y)] = 1 - theta/pi.
+    With two buckets the hash is one random hyperplane, where the law is exact."""
+    rng = np.random.default_rng(11)
+    D, N = 64, 20000
+    q, _ = np.linalg.qr(rng.standard_normal((D, 2)))
+    x = q[:, 0]
+    y = math.cos(theta) * q[:, 0] + math.sin(theta) * q[:, 1]
+    rot = rng.standard_normal((N, D, 1))
+    b, _ = O.hash_buckets(np.stack([x, y]), rot, 2)
+    freq = np.mean(b[:, 0] == b[:, 1])
+    p = 1 - theta / math.pi
+    assert abs(freq - p) < 5 * math.sqrt(p * (1 - p) / N) + 1e-12
+
+
+@pytest.mark.parametrize("k", [1, 2, 4, 8])
+def test_two_dimensional_sectors_closed_form(k):
+    """Explainer page, angular sectors after a rotation.  In two dimensions,
+    with the n_b/2 = k projection directions at angles phi + j*pi/k, the entry
+    m of [p ; -p] is |x| cos(alpha - phi - m*pi/k), so the bucket is the
+    sector round((alpha - phi) * k / pi) mod 2k.  Pins the [+p ; -p] index
+    layout and the argmax."""
+    rng = np.random.default_rng(100 + k)
+    D = 64
+    phi = rng.uniform(0, 2 * math.pi)
+    rot = np.zeros((1, D, k))
+    for j in range(k):
+        rot[0, 0, j] = math.cos(phi + j * math.pi / k)
+        rot[0, 1, j] = math.sin(phi + j * math.pi / k)
+    x = rng.standard_normal((3000, D))
+    alpha = np.arctan2(x[:, 1], x[:, 0])
+    t = (alpha - phi) * k / math.pi
+    keep = np.abs((t - np.floor(t)) - 0.5) > 1e-6
+    expect = np.mod(np.round(t[keep]).astype(np.int64), 2 * k)
+    b, _ = O.hash_buckets(x[keep], rot, 2 * k)
+    np.testing.assert_array_equal(b[0], expect)
+
+
+def test_two_dimensional_sector_collision_rate():
+    """Same construction with phi uniform: P_coll = max(0, 1 - k theta / pi)."""
+    rng = np.random.default_rng(7)
+    k, theta, N, D = 2, math.pi / 6, 20000, 64
+    x = np.zeros((2, D))
+    x[0, 0] = 1.0
+    x[1, 0], x[1, 1] = math.cos(theta), math.sin(theta)
+    phis = rng.uniform(0, 2 * math.pi, size=N)
+    rot = np.zeros((N, D, k))
+    for j in range(k):
+        rot[:, 0, j] = np.cos(phis + j * math.pi / k)
+        rot[:, 1, j] = np.sin(phis + j * math.pi / k)
+    b, _ = O.hash_buckets(x, rot, 2 * k)
+    p = max(0.0, 1 - k * theta / math.pi)
+    assert abs(np.mean(b[:, 0] == b[:, 1]) - p) < 5 * math.sqrt(p * (1 - p) / N)
+
+
+def test_hash_negation_and_scaling_invariants():
+    """Negating x swaps every entry of [p ; -p] with its partner n_b/2 away, so
+    h(-x) = (h(x) + n_b/2) mod n_b; scaling by a power of two is exact and
+    leaves the argmax alone."""
+    rng = np.random.default_rng(3)
+    for n_b in (2, 8, 64, 1024):
+        x = rng.standard_normal((200, 64)).astype(np.float32).astype(np.float64)
+        rot = rng.standard_normal((3, 64, n_b // 2)).astype(np.float32).astype(np.float64)
+        b, _ = O.hash_buckets(x, rot, n_b)
+        bn, _ = O.hash_buckets(-x, rot, n_b)
+        np.testing.assert_array_equal(bn, (b + n_b // 2) % n_b)
+        for s in (0.125, 4.0):
+            bs, _ = O.hash_buckets(s * x, rot, n_b)
+            np.testing.assert_array_equal(bs, b)
+
+
+def test_hash_exact_ties_take_lowest_index():
+    """Ties in [p ; -p] go to the lowest index (duplicate or negated rotation
+    columns make exact ties); x = 0 and n_b = 1 give bucket 0."""
+    rng = np.random.default_rng(5)
+    D, half = 64, 16
+    rot = rng.standard_normal((1, D, half))
+    dup = rot.copy()
+    dup[0, :, 9] = dup[0, :, 2]
+    b, _ = O.hash_buckets(dup[0, :, 2][None, :], dup, 2 * half)
+    assert b[0, 0] == 2
+    neg = rot.copy()
+    neg[0, :, 9] = -neg[0, :, 2]
+    b, _ = O.hash_buckets(neg[0, :, 2][None, :], neg, 2 * half)       # +p_2 ties -p_9
+    assert b[0, 0] == 2
+    b, _ = O.hash_buckets(-neg[0, :, 2][None, :], neg, 2 * half)      # +p_9 ties -p_2
+    assert b[0, 0] == 9
+    b, _ = O.hash_buckets(np.zeros((1, D)), rot, 2 * half)
+    assert b[0, 0] == 0
+    b, _ = O.hash_buckets(rng.standard_normal((5, D)), None, 1)
+    assert not b.any()
+
+
+def test_hash_decides_below_float64_resolution():
+    """Exact p_9 = 1 + 2^-70 beats p_2 = 1, a difference float64 sums cannot
+    see (they return a tie, which the lowest-index rule would give to 2).
+    Pins that near-ties are decided in exact arithmetic."""
+    D, half = 64, 16
+    rot = np.zeros((1, D, half))
+    rot[0, 0, 2] = 1.0
+    rot[0, 0, 9], rot[0, 1, 9] = 1.0, 2.0 ** -70
+    x = np.zeros((1, D))
+    x[0, 0], x[0, 1] = 1.0, 1.0
+    b, _ = O.hash_buckets(x, rot, 2 * half)
+    assert b[0, 0] == 9
+    b, _ = O.hash_buckets(-x, rot, 2 * half)
+    assert b[0, 0] == half + 9
+
+
+def test_hash_matches_exact_arithmetic_on_tiny_inputs():
+    """Brute force in exact rational arithmetic on every token of a tiny case."""
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((6, 8)).astype(np.float32).astype(np.float64)
+    rot = rng.standard_normal((2, 8, 4)).astype(np.float32).astype(np.float64)
+    b, _ = O.hash_buckets(x, rot, 8)
+    for r in range(2):
+        for i in range(6):
+            assert b[r, i] == O.lsh_oracle._exact_bucket(x[i], rot[r])
+
+
+# ------------------------------------------------------------------- sort --
+
+def test_sort_counting_rank_closed_form():
+    """Stable sort by (round, bucket, position): position i of round r lands in
+    slot r*L + #{j : b_j < b_i} + #{j < i : b_j = b_i}; also a permutation per
+    round with non-decreasing buckets, and undo . sorted = identity."""
+    rng = np.random.default_rng(1)
+    n_h, L, n_b = 3, 200, 7
+    bk = rng.integers(0, n_b, size=(n_h, L))
+    s, u = O.sort_by_bucket(bk)
+    for r in range(n_h):
+        seg = s[r * L:(r + 1) * L]
+        assert sorted(seg.tolist()) == list(range(L))
+        assert np.all(np.diff(bk[r, seg]) >= 0)
+        for i in range(L):
+            rank = sum(1 for j in range(L) if bk[r, j] < bk[r, i]) + \
+                   sum(1 for j in range(i) if bk[r, j] == bk[r, i])
+            assert s[r * L + rank] == i
+            assert u[r, i] == r * L + rank
+    assert np.array_equal(s[u.reshape(-1)], np.tile(np.arange(L), n_h))
+
+
+# -------------------------------------------------------------- attention --
+
+def _problem(seed, L, n_b, n_h, D=64):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((L, D))
+    v = rng.standard_normal((L, D))
+    rot = None if n_b == 1 else rng.standard_normal((n_h, D, n_b // 2))
+    return x, v, rot
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_weights_sum_to_one(causal):
+    """Every round's attention weights sum to 1: V = 1 gives o_r = 1 and out = 1.
+    (A self-only round has lse near -1e5, where float64 differences of lse
+    values carry about 1e5 * 2^-53 of absolute error, hence the combined bound.)"""
+    x, _, rot = _problem(2, 48, 4, 3)
+    r = O.forward_problem(x, np.ones((48, 64)), rot, 4, 3, 8, causal)
+    np.testing.assert_allclose(r["o_sorted"], 1.0, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(r["out"], 1.0, rtol=0, atol=1e-10)
+
+
+def test_causal_first_position_is_self_only():
+    """Causal: position 0 has no earlier key, so it attends only to itself
+    (every round exactly; the combine of rounds whose lse is -1e5 carries
+    float64 rounding of order 1e5 * 2^-53)."""
+    x, v, rot = _problem(4, 64, 8, 3)
+    r = O.forward_problem(x, v, rot, 8, 3, 8, True)
+    np.testing.assert_allclose(r["out"][0], v[0], rtol=0, atol=1e-10)
+    for rr in range(3):
+        np.testing.assert_array_equal(r["o_sorted"][r["undo_idx"][rr, 0]], v[0])
+
+
+def _brute_force(x, v, causal):
+    """Textbook dense attention written as loops: logit x_i . x_j / |x_j| / sqrt(D),
+    self at -1e5, causal excludes j > i."""
+    L, D = x.shape
+    out = np.zeros_like(v)
+    lse = np.zeros(L)
+    for i in range(L):
+        logits = []
+        for j in range(L):
+            if causal and j > i:
+                continue
+            s = -1e5 if j == i else float(x[i] @ x[j]) / math.sqrt(float(x[j] @ x[j])) / math.sqrt(D)
+            logits.append((j, s))
+        m = max(s for _, s in logits)
+        z = sum(math.exp(s - m) for _, s in logits)
+        for j, s in logits:
+            out[i] += math.exp(s - m) / z * v[j]
+        lse[i] = m + math.log(z)
+    return out, lse
+
+
+@pytest.mark.parametrize("n_h", [1, 2, 3])
+@pytest.mark.parametrize("causal", [False, True])
+def test_one_bucket_one_chunk_is_full_attention(n_h, causal):
+    """n_b = 1 and chunk_len = L: every window holds all tokens (twice), so the
+    result is dense attention; duplicates scale every weight alike."""
+    L = 12
+    x, v, _ = _problem(20 + n_h, L, 1, n_h)
+    r = O.forward_problem(x, v, None, 1, n_h, L, causal)
+    out, lse = _brute_force(x, v, causal)
+    np.testing.assert_allclose(r["out"], out, rtol=0, atol=1e-10)
+    # each token appears twice per round and once per round in n_h rounds
+    np.testing.assert_allclose(r["lse"], lse + math.log(2 * n_h), rtol=1e-14, atol=1e-12)
+    fo, fl = O.full_attention(x, v, causal)
+    np.testing.assert_allclose(fo, out, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(fl, lse, rtol=0, atol=1e-12)
+
+
+def test_hand_worked_logits_scale_and_key_normalisation():
+    """Four tokens, one bucket, one chunk (the window is the chunk twice).
+    Keys are normalised, queries are not, the scale is 1/sqrt(64) = 1/8:
+      x0 = 2 e0, x1 = 3 e0 + 4 e1 (|x1| = 5), x2 = -e1, x3 = e2 / 2.
+    Logits worked by hand (self excluded):
+      q0: k1 = 2*3/5/8 = 0.15, k2 = 0, k3 = 0
+      q1: k0 = 3/8, k2 = -4/8, k3 = 0
+      q2: k0 = 0, k1 = -0.8/8, k3 = 0
+      q3: all 0.
+    With one-hot values, out_i is the weight vector."""
+    D = 64
+    x = np.zeros((4, D))
+    x[0, 0] = 2
+    x[1, 0], x[1, 1] = 3, 4
+    x[2, 1] = -1
+    x[3, 2] = 0.5
+    v = np.eye(4, D)
+    e = math.exp
+    expect = np.zeros((4, D))
+    w = [[0, e(0.15), 1, 1], [e(0.375), 0, e(-0.5), 1], [1, e(-0.1), 0, 1], [1, 1, 1, 0]]
+    for i in range(4):
+        expect[i, :4] = np.array(w[i]) / sum(w[i])
+    r = O.forward_problem(x, v, None, 1, 1, 4, False)
+    np.testing.assert_allclose(r["out"], expect, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(r["lse"], [math.log(2 * sum(wi)) for wi in w], rtol=0, atol=1e-14)
+
+
+# Two buckets, two rounds, x_i = +e0 for even i and -e0 for odd i; round 0's
+# single rotation column is +e0 and round 1's is -e0.  Round 0 therefore sorts
+# the even positions (bucket 0) before the odd ones, round 1 the reverse.
+# Chunks of 4 over the 32 round-major slots, worked by hand:
+#   ch0 [0,2,4,6]    ch1 [8,10,12,14]  ch2 [1,3,5,7]   ch3 [9,11,13,15]
+#   ch4 [1,3,5,7]    ch5 [9,11,13,15]  ch6 [0,2,4,6]   ch7 [8,10,12,14]
+# and the window of chunk c is chunk c-1 (cyclic over all 8) plus chunk c:
+HAND_WINDOWS = {
+    0: {8, 10, 12, 14, 0, 2, 4, 6},
+    1: {0, 2, 4, 6, 8, 10, 12, 14},
+    2: {8, 10, 12, 14, 1, 3, 5, 7},
+    3: {1, 3, 5, 7, 9, 11, 13, 15},
+    4: {9, 11, 13, 15, 1, 3, 5, 7},
+    5: {1, 3, 5, 7, 9, 11, 13, 15},
+    6: {9, 11, 13, 15, 0, 2, 4, 6},
+    7: {0, 2, 4, 6, 8, 10, 12, 14},
+}
+HAND_CHUNK_OF = {  # (round, position) -> chunk
+    **{(0, p): c for c, ps in {0: [0, 2, 4, 6], 1: [8, 10, 12, 14], 2: [1, 3, 5, 7], 3: [9, 11, 13, 15]}.items() for p in ps},
+    **{(1, p): c for c, ps in {4: [1, 3, 5, 7], 5: [9, 11, 13, 15], 6: [0, 2, 4, 6], 7: [8, 10, 12, 14]}.items() for p in ps},
+}
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_hand_enumerated_windows(causal):
+    """Pins the look-back to the previous chunk, its wrap across rounds, the
+    hash sign layout and the stable sort: with one-hot values each round's
+    output is its weight vector, whose support must be the hand-enumerated
+    window minus the token itself (keys after it dropped when causal; the
+    token alone when nothing else is left)."""
+    L, D = 16, 64
+    x = np.zeros((L, D))
+    x[:, 0] = [1.0 if i % 2 == 0 else -1.0 for i in range(L)]
+    rot = np.zeros((2, D, 1))
+    rot[0, 0, 0], rot[1, 0, 0] = 1.0, -1.0
+    v = np.eye(L, D)
+    r = O.forward_problem(x, v, rot, 2, 2, 4, causal)
+    for rr in range(2):
+        for i in range(L):
+            win = HAND_WINDOWS[HAND_CHUNK_OF[(rr, i)]] - {i}
+            if causal:
+                win = {j for j in win if j < i}
+            expect = win if win else {i}
+            o = r["o_sorted"][r["undo_idx"][rr, i]]
+            assert set(np.nonzero(o > 0)[0].tolist()) == expect, (rr, i)
+
+
+def test_uniform_logits_window_means():
+    """All keys in one direction: every non-self logit is 1/8, so each round's
+    output is the plain mean of the window's values without the token itself.
+    One bucket, L = 16, chunks of 4, two rounds with the identity order, so the
+    windows are {12..15, 0..3}, {0..7}, {4..11}, {8..15} for tokens in 0..3,
+    4..7, 8..11, 12..15.  With v_j = j the outputs are (60 - i)/7,
+    (28 - i)/7, (60 - i)/7, (92 - i)/7 and every LSE is 1/8 + log 14."""
+    L, D = 16, 64
+    x = np.zeros((L, D))
+    x[:, 0] = 1.0
+    v = np.repeat(np.arange(L, dtype=np.float64)[:, None], D, axis=1)
+    r = O.forward_problem(x, v, None, 1, 2, 4, False)
+    sums = [60, 28, 60, 92]
+    expect = np.array([(sums[i // 4] - i) / 7 for i in range(L)])
+    np.testing.assert_allclose(r["out"][:, 0], expect, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(r["lse"], 0.125 + math.log(14), rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------- combine --
+
+def test_single_round_combine_is_identity():
+    x, v, rot = _problem(6, 64, 8, 1)
+    r = O.forward_problem(x, v, rot, 8, 1, 16, False)
+    np.testing.assert_array_equal(r["out"], r["o_sorted"][r["undo_idx"][0]])
+    np.testing.assert_allclose(r["lse"], r["lse_sorted"][r["undo_idx"][0]], rtol=0, atol=1e-14)
+
+
+def test_identical_rounds_equal_one_round():
+    """Repeating the same rotation gives identical windows in every round
+    (the wrap joins identical chunks), so the combined output equals one round."""
+    x, v, rot = _problem(8, 64, 8, 1)
+    one = O.forward_problem(x, v, rot, 8, 1, 16, True)
+    three = O.forward_problem(x, v, np.repeat(rot, 3, axis=0), 8, 3, 16, True)
+    np.testing.assert_allclose(three["out"], one["out"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(three["lse"], one["lse"] + math.log(3), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_combine_equals_softmax_over_the_multiset_union(causal):
+    """The log-sum-exp combine equals one softmax over the concatenation of all
+    rounds' windows (duplicates kept), computed here with plain loops."""
+    L, C, n_h, n_b = 32, 8, 3, 4
+    x, v, rot = _problem(12, L, n_b, n_h)
+    r = O.forward_problem(x, v, rot, n_b, n_h, C, causal)
+    s_idx, u = r["sorted_idx"], r["undo_idx"]
+    n_slots = n_h * L
+    for i in range(L):
+        pairs = []
+        for rr in range(n_h):
+            c = u[rr, i] // C
+            for g in list(range(((c - 1) % (n_slots // C)) * C, ((c - 1) % (n_slots // C)) * C + C)) + \
+                    list(range(c * C, c * C + C)):
+                j = int(s_idx[g])
+                if causal and j > i:
+                    continue
+                s = -1e5 if j == i else float(x[i] @ x[j]) / float(np.linalg.norm(x[j])) / 8.0
+                pairs.append((j, s))
+        m = max(s for _, s in pairs)
+        z = sum(math.exp(s - m) for _, s in pairs)
+        out = sum(math.exp(s - m) / z * v[j] for j, s in pairs)
+        np.testing.assert_allclose(r["out"][i], out, rtol=0, atol=1e-12)
+        assert abs(r["lse"][i] - (m + math.log(z))) < 1e-12
+
+
+# ----------------------------------------------------------------- recall --
+
+def test_recall_is_one_when_every_key_is_in_the_window():
+    x, _, _ = _problem(14, 32, 1, 1)
+    s, u = O.sort_by_bucket(np.zeros((1, 32), dtype=np.int64))
+    assert O.recall_at_k(x, s, u, 32, range(32), 5) == 1.0
+    assert abs(O.attention_mass_recall(x, s, u, 32, range(32)) - 1.0) < 1e-12
+
+
+def test_more_rounds_raise_recall_on_clustered_keys():
+    """Explainer page, multi-round passage: more independent rounds raise
+    recall.  The 8-round run shares its first two rotations with the 2-round
+    run, so its windows include the 2-round ones except at the wrap of the
+    first chunk."""
+    from lsh_attention_amd import inputs as I
+    inp = I.make_inputs("peaked_vmf_16k", n_hashes=8, B=1, H=1, L=2048)
+    x = inp.qk.values[0, 0].astype(np.float64)
+    rot = inp.rot.values.astype(np.float64)[:, :, :16]     # 32 buckets: mean occupancy 64
+    q = range(0, 2048, 16)
+    rec = {}
+    for n_h in (2, 8):
+        b, _ = O.hash_buckets(x, rot[:n_h], 32)
+        s, u = O.sort_by_bucket(b)
+        rec[n_h] = O.recall_at_k(x, s, u, 64, q, 16)
+    assert rec[8] > rec[2]
