@@ -1,0 +1,184 @@
+"""Benchmark of the fused shared-QK LSH-attention forward pass on one MI355X.
+
+A step is one call of reformer_lsh_attn_fwd over one batch of synthetic input
+(hash -> sort -> chunked attention -> unsort/combine, all heads).  Inputs,
+workspace and outputs are resident in HBM before timing starts.  Prints one
+JSON line on stdout; diagnostics go to stderr.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_seq_64k]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "LSH-attn fwd tokens/sec at L=64K, 8 hashes; % HBM / MFMA roofline"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 MFMA / packed vector
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(B, H, L, D, n_b, n_h, es):
+    """Per-launch algorithmic bytes and flops of each kernel (see the design
+    notes): what the method must read and write, not what a kernel happens to."""
+    th = B * H * L            # token-heads
+    tr = th * n_h             # token-rounds
+    half = n_b // 2
+    return {
+        "prep": {"bytes": 2 * n_h * D * half * es, "flops": 0},
+        "hash": {"bytes": th * (D * es + 4 * n_h), "flops": 2 * th * D * half * n_h},
+        "fixup": {"bytes": 0, "flops": 0},
+        "sort_hist": {"bytes": tr * 4, "flops": 0},
+        "sort_scan": {"bytes": 0, "flops": 0},
+        "sort_scatter": {"bytes": tr * 12, "flops": 0},
+        # index + one output row + lse per token-round, QK and V rows read once per token-head
+        "chunk_attn": {"bytes": tr * (4 + D * es + 4) + th * 2 * D * es, "flops": tr * 4 * D * 128},
+        # per token-head: n_h rows + lse + undo index, one output row
+        "combine": {"bytes": th * (n_h * (D * es + 8) + D * es), "flops": 0},
+    }
+
+
+def cpu_baseline(inp, max_seconds: float = 30.0):
+    """The oracle, untouched, on a bounded sample: one (batch, head) problem of
+    the same workload at full length; tokens/s scaled to the whole batch."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+    w = inp.workload
+    B, H, L, _ = inp.qk.values.shape
+    x = inp.qk.values[0, 0].astype(np.float64)
+    v = inp.v.values[0, 0].astype(np.float64)
+    rot = None if inp.rot is None else inp.rot.values.astype(np.float64)
+    t0 = time.perf_counter()
+    O.forward_problem(x, v, rot, w.n_buckets, inp.n_hashes, w.chunk_len, w.causal)
+    t = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(B * L / (B * H * t), 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"1 of {B * H} (batch, head) problems at full L={L}, all {inp.n_hashes} rounds, "
+                      f"float64 numpy, {t:.2f} s; tokens/s = B*L / (B*H*t)",
+            "seconds": round(t, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_seq_64k")
+    ap.add_argument("--n-hashes", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the forward pass is not sharded across GPUs in this build "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from lsh_attention_amd import binding as bd
+    from lsh_attention_amd import inputs as I
+
+    inp = I.make_inputs(args.workload, n_hashes=args.n_hashes)
+    w = inp.workload
+    B, H, L, D = inp.qk.values.shape
+    n_h, n_b = inp.n_hashes, w.n_buckets
+    es = 2 if w.dtype == "bf16" else 4
+    log(f"workload {w.name}: B{B} H{H} L{L} D{D} n_b{n_b} n_h{n_h} causal={w.causal} {w.dtype}; "
+        f"sha256(qk)={inp.meta['qk_sha256'][:16]}")
+
+    def dev(t):
+        if t is None:
+            return None
+        if t.bits is not None:
+            return torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(t.values)).cuda()
+
+    qk, v, rot = dev(inp.qk), dev(inp.v), dev(inp.rot)
+    dt = bd.LSH_BF16 if w.dtype == "bf16" else bd.LSH_F32
+    ws = torch.empty(bd.fwd_workspace_bytes(B, H, L, D, n_b, n_h, 64, dt), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(qk)
+    lse = torch.empty((B, H, L), dtype=torch.float32, device="cuda")
+
+    def step(events=None):
+        bd.reformer_lsh_attn_fwd(qk, v, rot, n_b, n_h, 64, w.causal, out=out, lse=lse, workspace=ws,
+                                 stage_events=events)
+
+    for _ in range(args.warmup):
+        step()
+    events = [bd.EventSet() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per_kernel = np.array([e.durations_ms() for e in events])  # [steps, kernels]
+    gpu_ms = float(np.mean([e.elapsed_ms(0, bd.N_EVENTS - 1) for e in events]))
+    for e in events:
+        e.close()
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens = B * L
+    value = tokens / (elapsed / args.steps)
+    log(f"{args.steps} steps: {ms_per_step:.4f} ms/step wall, {gpu_ms:.4f} ms/step between first and last event")
+
+    work = algorithmic_work(B, H, L, D, n_b, n_h, es)
+    peak_flops = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+    kernels = {}
+    for i, name in enumerate(bd.KERNEL_NAMES):
+        us = float(np.mean(per_kernel[:, i])) * 1e3
+        wk = work[name]
+        ent = {"us": round(us, 2)}
+        if us > 0 and wk["bytes"]:
+            ent["GBps"] = round(wk["bytes"] / (us * 1e-6) / 1e9, 1)
+            ent["hbm_frac"] = round(ent["GBps"] / HBM_PEAK_GBS, 4)
+        if us > 0 and wk["flops"]:
+            ent["TFLOPs"] = round(wk["flops"] / (us * 1e-6) / 1e12, 1)
+            ent["mfma_frac"] = round(ent["TFLOPs"] / peak_flops, 4)
+        kernels[name] = ent
+        log(f"  {name:13s} {us:9.2f} us  {json.dumps({k: x for k, x in ent.items() if k != 'us'})}")
+    dom = max(kernels, key=lambda k: kernels[k]["us"])
+    d_us = kernels[dom]["us"]
+    wk = work[dom]
+    # The binding roofline of the dominant kernel: compute if its flops take longer
+    # at peak than its bytes at peak bandwidth.
+    if wk["flops"] / (peak_flops * 1e12) > wk["bytes"] / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": round(wk["flops"] / (d_us * 1e-6) / 1e12, 2), "peak": peak_flops,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(wk["bytes"] / (d_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["kernel"] = dom
+    roof["traffic"] = None
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": L, "d_head": D, "n_buckets": n_b,
+                   "n_hashes": n_h, "chunk_len": 64, "causal": w.causal},
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (cpu_baseline leg)")
+        result["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,144 @@
+/*
+ * lsh_attn.h - C ABI of the gfx950 (MI355X) shared-QK angular-LSH attention
+ * forward pass (Reformer).
+ *
+ * The method (Reformer explainer, akshathtiwari.co.in/blog/reformer, and the
+ * Reformer abstract, "Reformer: The Efficient Transformer"):
+ *   1. hash   - each token's shared query/key x is put in the angular sector
+ *               it falls in after a random rotation: bucket = argmax of
+ *               [x R_r ; -x R_r], one rotation R_r per hash round;
+ *   2. sort   - tokens are sorted by (round, bucket, position);
+ *   3. chunk attention - the sorted sequence is cut into equal chunks; each
+ *               chunk attends to itself and the previous chunk;
+ *   4. unsort - per-round results are put back in token order;
+ *   5. combine - rounds are merged with weights softmax_r(lse_r), the union
+ *               of the rounds' buckets.
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees, synchronises or prints.  It is stateless.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     work is enqueued asynchronously on it; device faults surface at the
+ *     caller's next synchronisation.
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     invalid call returns a negative status and enqueues nothing.
+ *   - Layouts are contiguous, row-major.  B = batch, H = heads, L = sequence
+ *     length, D = head dim (64), n_b = buckets, n_h = hash rounds,
+ *     C = chunk length (64).  "BH" = B*H independent problems.
+ *   - qk, v, out, rot, o_sorted use the element type `dt` (fp32 or bf16);
+ *     lse arrays are fp32; index arrays are int32.
+ *   - Limits: D == 64, C == 64, L % C == 0, n_b == 1 or even in [2, 4096],
+ *     1 <= n_h <= 16, B*H*n_h*L <= 2^31 - 1.
+ *   - Outputs must not overlap inputs (LSH_ERR_ALIAS).
+ */
+#ifndef LSH_ATTN_H
+#define LSH_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { LSH_F32 = 0, LSH_BF16 = 1 } lsh_dtype;
+
+enum {
+  LSH_OK = 0,
+  LSH_ERR_NULL = -1,        /* a required pointer is NULL */
+  LSH_ERR_SHAPE = -2,       /* a dimension <= 0, L % C != 0, or an index overflows int32 */
+  LSH_ERR_BUCKETS = -3,     /* n_b < 1, odd n_b > 1, or n_b > 4096 */
+  LSH_ERR_UNSUPPORTED = -4, /* D != 64, C != 64, n_h > 16, or unknown dtype */
+  LSH_ERR_WORKSPACE = -5,   /* workspace pointer NULL or smaller than required */
+  LSH_ERR_ALIAS = -6,       /* an output overlaps an input */
+  LSH_ERR_HIP = -7          /* a kernel launch or event record failed */
+};
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* lsh_status_string(int status);
+
+/* Step 1, hashing (explainer page: angular LSH after a random rotation, several
+ * independent rounds).
+ *   qk      [B, H, L, D]      shared query/key vectors, element type dt.
+ *   rot     [n_h, D, n_b/2]   rotations, element type dt, shared by all (b, h);
+ *                             may be NULL when n_b == 1.
+ *   buckets [B, H, n_h, L]    out: bucket of token i in round r, in [0, n_b):
+ *                             the index of the largest entry of
+ *                             [x R_r ; -x R_r], lowest index on exact ties.
+ *   ws      workspace of at least lsh_hash_workspace_bytes(...) bytes.
+ * The decision is exact: fp32 MFMA scores are certified against a rigorous
+ * rounding bound, and any token whose top two scores are closer than that
+ * bound is re-decided from float64 sums. */
+int lsh_hash_workspace_bytes(int B, int H, int L, int D, int n_b, int n_h, lsh_dtype dt,
+                             size_t* bytes);
+int lsh_hash(const void* qk, const void* rot, int32_t* buckets, int B, int H, int L, int D,
+             int n_b, int n_h, lsh_dtype dt, void* ws, size_t ws_bytes, void* stream);
+
+/* Step 2, sort by (round, bucket, position) (explainer page: sort by bucket).
+ *   buckets    [B, H, n_h, L]  input, values in [0, n_b) (not checked on device).
+ *   sorted_idx [B, H, n_h*L]   out: slot g = r*L + k holds the original position
+ *                              of the k-th token of round r's stable order.
+ *   undo_idx   [B, H, n_h, L]  out: the slot g of position i in round r.
+ *   ws         workspace of at least lsh_sort_workspace_bytes(...) bytes. */
+int lsh_sort_workspace_bytes(int B, int H, int L, int n_b, int n_h, size_t* bytes);
+int lsh_sort(const int32_t* buckets, int32_t* sorted_idx, int32_t* undo_idx, int B, int H, int L,
+             int n_b, int n_h, void* ws, size_t ws_bytes, void* stream);
+
+/* Step 3, chunked attention (explainer page: equal chunks of the sorted order).
+ * Slots g in [0, n_h*L) are cut into chunks of C; chunk c attends to chunks
+ * (c-1) mod (n_h*L/C) and c (2C keys).  For query i = sorted_idx[g] and key j:
+ * logit = (x_i . x_j / max(|x_j|, 1e-12)) / sqrt(D); j == i gets -1e5 (so a token
+ * sees itself only when nothing else is left); causal != 0 drops j > i.
+ *   qk, v      [B, H, L, D]       element type dt.
+ *   sorted_idx [B, H, n_h*L]      from lsh_sort.
+ *   o_sorted   [B, H, n_h*L, D]   out: softmax-weighted sum of V per slot (dt).
+ *   lse_sorted [B, H, n_h*L]      out: log-sum-exp of the slot's logits (fp32). */
+int lsh_chunk_attn(const void* qk, const void* v, const int32_t* sorted_idx, void* o_sorted,
+                   float* lse_sorted, int B, int H, int L, int D, int n_h, int C, int causal,
+                   lsh_dtype dt, void* stream);
+
+/* Steps 4-5, unsort and combine (explainer page: union of the rounds).
+ * LSE_i = logsumexp_r lse_r(i), out_i = sum_r exp(lse_r(i) - LSE_i) o_r(i), with
+ * o_r(i) = o_sorted[undo_idx[r][i]].
+ *   out     [B, H, L, D]   out, element type dt.
+ *   lse_out [B, H, L]      optional out (NULL to skip), fp32. */
+int lsh_unsort_combine(const void* o_sorted, const float* lse_sorted, const int32_t* undo_idx,
+                       void* out, float* lse_out, int B, int H, int L, int D, int n_h,
+                       lsh_dtype dt, void* stream);
+
+/* The whole forward pass, steps 1-5, with all intermediates in the workspace.
+ * Arguments as above.  `stage_events` is optional: NULL, or an array of
+ * LSH_FWD_N_EVENTS hipEvent_t (as void*) that are recorded on `stream` before
+ * the first and after every kernel launch, in the order of the
+ * LSH_FWD_KERNEL_* list, for per-kernel timing. */
+#define LSH_FWD_KERNEL_PREP 0      /* rotation transpose + norms */
+#define LSH_FWD_KERNEL_HASH 1      /* MFMA projection + certified argmax */
+#define LSH_FWD_KERNEL_FIXUP 2     /* float64 re-decision of uncertified tokens */
+#define LSH_FWD_KERNEL_HIST 3      /* per-tile bucket histograms */
+#define LSH_FWD_KERNEL_SCAN 4      /* exclusive scan of the histograms */
+#define LSH_FWD_KERNEL_SCATTER 5   /* stable in-tile ranking + scatter */
+#define LSH_FWD_KERNEL_ATTN 6      /* chunked attention */
+#define LSH_FWD_KERNEL_COMBINE 7   /* unsort + combine */
+#define LSH_FWD_N_KERNELS 8
+#define LSH_FWD_N_EVENTS (LSH_FWD_N_KERNELS + 1)
+
+int lsh_fwd_workspace_bytes(int B, int H, int L, int D, int n_b, int n_h, int C, lsh_dtype dt,
+                            size_t* bytes);
+int reformer_lsh_attn_fwd(const void* qk, const void* v, const void* rot, int n_buckets,
+                          int n_hashes, int chunk_len, int causal, int B, int H, int L, int D,
+                          lsh_dtype dt, void* out, float* lse_out, void* ws, size_t ws_bytes,
+                          void* stream, void* const* stage_events);
+
+/* Timing helpers for callers that have no HIP runtime binding of their own:
+ * create/destroy a hipEvent_t (returned as void*), and the elapsed time in
+ * milliseconds between two recorded events (synchronises on `end`). */
+int lsh_event_create(void** event);
+int lsh_event_destroy(void* event);
+int lsh_event_record(void* event, void* stream);
+int lsh_event_elapsed_ms(void* start, void* end, float* ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSH_ATTN_H */

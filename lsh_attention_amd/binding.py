@@ -1,0 +1,256 @@
+"""Thin ctypes binding of the C ABI in include/lsh_attn.h.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, outputs and workspaces are allocated with torch (device memory
+plumbing), and the C entry point of the same name is called on torch's
+current HIP stream.  Every step of the method runs in the library's gfx950
+kernels; there is no fallback, and a missing library or GPU raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblsh_attn.so")
+_HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "lsh_attn.h")
+_lib = None
+
+LSH_F32, LSH_BF16 = 0, 1
+N_KERNELS = 8
+N_EVENTS = N_KERNELS + 1
+KERNEL_NAMES = ["prep", "hash", "fixup", "sort_hist", "sort_scan", "sort_scatter", "chunk_attn", "combine"]
+
+_c_int, _c_size, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+_SIGS = {
+    "lsh_status_string": (ctypes.c_char_p, [_c_int]),
+    "lsh_hash_workspace_bytes": (_c_int, [_c_int] * 7 + [ctypes.POINTER(_c_size)]),
+    "lsh_hash": (_c_int, [_vp, _vp, _vp] + [_c_int] * 7 + [_vp, _c_size, _vp]),
+    "lsh_sort_workspace_bytes": (_c_int, [_c_int] * 5 + [ctypes.POINTER(_c_size)]),
+    "lsh_sort": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [_vp, _c_size, _vp]),
+    "lsh_chunk_attn": (_c_int, [_vp] * 5 + [_c_int] * 8 + [_vp]),
+    "lsh_unsort_combine": (_c_int, [_vp] * 5 + [_c_int] * 6 + [_vp]),
+    "lsh_fwd_workspace_bytes": (_c_int, [_c_int] * 8 + [ctypes.POINTER(_c_size)]),
+    "reformer_lsh_attn_fwd": (_c_int, [_vp] * 3 + [_c_int] * 9 + [_vp, _vp, _vp, _c_size, _vp, _vp]),
+    "lsh_event_create": (_c_int, [ctypes.POINTER(_vp)]),
+    "lsh_event_destroy": (_c_int, [_vp]),
+    "lsh_event_record": (_c_int, [_vp, _vp]),
+    "lsh_event_elapsed_ms": (_c_int, [_vp, _vp, ctypes.POINTER(ctypes.c_float)]),
+}
+
+
+class LshError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = lib().lsh_status_string(status).decode()
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def header_functions() -> list:
+    """Names of the functions declared in include/lsh_attn.h."""
+    text = open(_HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\*|int)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C-ABI library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built: run `python -m lsh_attention_amd.build`")
+        h = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(h, name)
+            f.restype, f.argtypes = res, args
+        _lib = h
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise LshError(fn, status)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return LSH_BF16
+    if t.dtype == torch.float32:
+        return LSH_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU (the HIP path has no CPU fallback)")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def hash_workspace_bytes(B, H, L, D, n_buckets, n_hashes, dtype_code) -> int:
+    n = _c_size()
+    _check("lsh_hash_workspace_bytes", lib().lsh_hash_workspace_bytes(B, H, L, D, n_buckets, n_hashes, dtype_code,
+                                                                     ctypes.byref(n)))
+    return n.value
+
+
+def sort_workspace_bytes(B, H, L, n_buckets, n_hashes) -> int:
+    n = _c_size()
+    _check("lsh_sort_workspace_bytes", lib().lsh_sort_workspace_bytes(B, H, L, n_buckets, n_hashes, ctypes.byref(n)))
+    return n.value
+
+
+def fwd_workspace_bytes(B, H, L, D, n_buckets, n_hashes, chunk_len, dtype_code) -> int:
+    n = _c_size()
+    _check("lsh_fwd_workspace_bytes", lib().lsh_fwd_workspace_bytes(B, H, L, D, n_buckets, n_hashes, chunk_len,
+                                                                   dtype_code, ctypes.byref(n)))
+    return n.value
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def lsh_hash(qk: torch.Tensor, rot: torch.Tensor | None, n_buckets: int, n_hashes: int,
+             buckets: torch.Tensor | None = None) -> torch.Tensor:
+    """qk [B,H,L,D], rot [n_h,D,n_b/2] (or None when n_b == 1) -> buckets int32 [B,H,n_h,L]."""
+    _dev(qk, rot, buckets)
+    B, H, L, D = qk.shape
+    dt = _dtype_code(qk)
+    if rot is not None and rot.dtype != qk.dtype:
+        raise TypeError("rot must have the dtype of qk")
+    if buckets is None:
+        buckets = torch.empty((B, H, n_hashes, L), dtype=torch.int32, device=qk.device)
+    ws = _workspace(hash_workspace_bytes(B, H, L, D, n_buckets, n_hashes, dt), qk.device)
+    _check("lsh_hash", lib().lsh_hash(qk.data_ptr(), _ptr(rot), buckets.data_ptr(), B, H, L, D, n_buckets, n_hashes,
+                                      dt, ws.data_ptr(), ws.numel(), _stream(qk.device)))
+    return buckets
+
+
+def lsh_sort(buckets: torch.Tensor, n_buckets: int):
+    """buckets int32 [B,H,n_h,L] -> (sorted_idx int32 [B,H,n_h*L], undo_idx int32 [B,H,n_h,L])."""
+    _dev(buckets)
+    if buckets.dtype != torch.int32:
+        raise TypeError("buckets must be int32")
+    B, H, n_h, L = buckets.shape
+    sorted_idx = torch.empty((B, H, n_h * L), dtype=torch.int32, device=buckets.device)
+    undo_idx = torch.empty((B, H, n_h, L), dtype=torch.int32, device=buckets.device)
+    ws = _workspace(sort_workspace_bytes(B, H, L, n_buckets, n_h), buckets.device)
+    _check("lsh_sort", lib().lsh_sort(buckets.data_ptr(), sorted_idx.data_ptr(), undo_idx.data_ptr(), B, H, L,
+                                      n_buckets, n_h, ws.data_ptr(), ws.numel(), _stream(buckets.device)))
+    return sorted_idx, undo_idx
+
+
+def lsh_chunk_attn(qk: torch.Tensor, v: torch.Tensor, sorted_idx: torch.Tensor, n_hashes: int, chunk_len: int,
+                   causal: bool):
+    """-> (o_sorted [B,H,n_h*L,D] in qk's dtype, lse_sorted float32 [B,H,n_h*L])."""
+    _dev(qk, v, sorted_idx)
+    B, H, L, D = qk.shape
+    dt = _dtype_code(qk)
+    if v.shape != qk.shape or v.dtype != qk.dtype:
+        raise ValueError("v must match qk in shape and dtype")
+    if sorted_idx.dtype != torch.int32 or sorted_idx.shape != (B, H, n_hashes * L):
+        raise ValueError("sorted_idx must be int32 [B,H,n_h*L]")
+    o_sorted = torch.empty((B, H, n_hashes * L, D), dtype=qk.dtype, device=qk.device)
+    lse_sorted = torch.empty((B, H, n_hashes * L), dtype=torch.float32, device=qk.device)
+    _check("lsh_chunk_attn", lib().lsh_chunk_attn(qk.data_ptr(), v.data_ptr(), sorted_idx.data_ptr(),
+                                                  o_sorted.data_ptr(), lse_sorted.data_ptr(), B, H, L, D, n_hashes,
+                                                  chunk_len, int(bool(causal)), dt, _stream(qk.device)))
+    return o_sorted, lse_sorted
+
+
+def lsh_unsort_combine(o_sorted: torch.Tensor, lse_sorted: torch.Tensor, undo_idx: torch.Tensor,
+                       want_lse: bool = True):
+    """-> (out [B,H,L,D] in o_sorted's dtype, lse float32 [B,H,L] or None)."""
+    _dev(o_sorted, lse_sorted, undo_idx)
+    B, H, n_h, L = undo_idx.shape
+    D = o_sorted.shape[-1]
+    dt = _dtype_code(o_sorted)
+    out = torch.empty((B, H, L, D), dtype=o_sorted.dtype, device=o_sorted.device)
+    lse = torch.empty((B, H, L), dtype=torch.float32, device=o_sorted.device) if want_lse else None
+    _check("lsh_unsort_combine", lib().lsh_unsort_combine(o_sorted.data_ptr(), lse_sorted.data_ptr(),
+                                                          undo_idx.data_ptr(), out.data_ptr(), _ptr(lse), B, H, L,
+                                                          D, n_h, dt, _stream(o_sorted.device)))
+    return out, lse
+
+
+def reformer_lsh_attn_fwd(qk: torch.Tensor, v: torch.Tensor, rot: torch.Tensor | None, n_buckets: int,
+                          n_hashes: int, chunk_len: int = 64, causal: bool = False, want_lse: bool = True,
+                          out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                          workspace: torch.Tensor | None = None, stage_events=None):
+    """The fused forward pass.  Returns (out [B,H,L,D], lse float32 [B,H,L] or None).
+    `workspace` (uint8, at least fwd_workspace_bytes) and `out`/`lse` may be passed
+    in to avoid allocation; `stage_events` is an EventSet for per-kernel timing."""
+    _dev(qk, v, rot, out, lse, workspace)
+    B, H, L, D = qk.shape
+    dt = _dtype_code(qk)
+    if v.shape != qk.shape or v.dtype != qk.dtype:
+        raise ValueError("v must match qk in shape and dtype")
+    if rot is not None and rot.dtype != qk.dtype:
+        raise TypeError("rot must have the dtype of qk")
+    if out is None:
+        out = torch.empty_like(qk)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=qk.device)
+    if workspace is None:
+        workspace = _workspace(fwd_workspace_bytes(B, H, L, D, n_buckets, n_hashes, chunk_len, dt), qk.device)
+    ev = None if stage_events is None else stage_events.array()
+    _check("reformer_lsh_attn_fwd", lib().reformer_lsh_attn_fwd(
+        qk.data_ptr(), v.data_ptr(), _ptr(rot), n_buckets, n_hashes, chunk_len, int(bool(causal)), B, H, L, D, dt,
+        out.data_ptr(), _ptr(lse), workspace.data_ptr(), workspace.numel(), _stream(qk.device), ev))
+    return out, lse
+
+
+class EventSet:
+    """N_EVENTS hipEvents created by the library, recorded by the fused call
+    around each kernel; `durations_ms()` gives the per-kernel times."""
+
+    def __init__(self, n: int = N_EVENTS):
+        self._ev = (_vp * n)()
+        for i in range(n):
+            h = _vp()
+            _check("lsh_event_create", lib().lsh_event_create(ctypes.byref(h)))
+            self._ev[i] = h
+        self.n = n
+
+    def array(self):
+        return ctypes.cast(self._ev, _vp)
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        ms = ctypes.c_float()
+        _check("lsh_event_elapsed_ms", lib().lsh_event_elapsed_ms(self._ev[i], self._ev[j], ctypes.byref(ms)))
+        return ms.value
+
+    def durations_ms(self) -> list:
+        return [self.elapsed_ms(i, i + 1) for i in range(self.n - 1)]
+
+    def record(self, i: int, device=None):
+        _check("lsh_event_record", lib().lsh_event_record(self._ev[i], _stream(device)))
+
+    def close(self):
+        for i in range(self.n):
+            if self._ev[i]:
+                lib().lsh_event_destroy(self._ev[i])
+                self._ev[i] = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

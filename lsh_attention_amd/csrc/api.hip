@@ -1,0 +1,338 @@
+// C ABI of the shared-QK LSH attention forward pass: argument validation,
+// workspace carving and the stream-ordered launch sequence.  Validation runs
+// entirely on the host and returns before anything is enqueued.
+#include <string.h>
+
+#include "lsh_internal.h"
+
+using namespace lsh;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t elem_size(lsh_dtype dt) { return dt == LSH_BF16 ? 2 : 4; }
+
+bool dtype_ok(lsh_dtype dt) { return dt == LSH_F32 || dt == LSH_BF16; }
+
+int check_problem(int B, int H, int L, int D, int n_h) {
+  if (B <= 0 || H <= 0 || L <= 0 || D <= 0 || n_h <= 0) return LSH_ERR_SHAPE;
+  if (D != kD) return LSH_ERR_UNSUPPORTED;
+  if (n_h > kMaxHashes) return LSH_ERR_UNSUPPORTED;
+  if (L % kChunk != 0) return LSH_ERR_SHAPE;
+  const uint64_t slots = (uint64_t)B * (uint64_t)H * (uint64_t)n_h * (uint64_t)L;
+  if (slots > 0x7FFFFFFFull) return LSH_ERR_SHAPE;
+  return LSH_OK;
+}
+
+int check_buckets(int n_b, int L) {
+  if (n_b < 1 || n_b > kMaxBuckets) return LSH_ERR_BUCKETS;
+  if (n_b > 1 && (n_b % 2) != 0) return LSH_ERR_BUCKETS;
+  if ((uint64_t)n_b * (uint64_t)sort_tiles(L) > 0x7FFFFFFFull) return LSH_ERR_SHAPE;
+  return LSH_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Sequential carving of a workspace into 256-byte aligned regions.
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, kAlign);
+    return o;
+  }
+};
+
+struct HashWs {
+  size_t rot_t, rho, fix_count, fix_queue, total;
+};
+HashWs hash_ws(int BH, int L, int n_b, int n_h, lsh_dtype dt) {
+  Carver c;
+  HashWs w;
+  w.rot_t = c.take((size_t)n_h * padded_half(n_b) * kD * elem_size(dt));
+  w.rho = c.take((size_t)n_h * sizeof(float));
+  w.fix_count = c.take(sizeof(int));
+  w.fix_queue = c.take((size_t)BH * n_h * L * sizeof(int));
+  w.total = c.off;
+  return w;
+}
+
+size_t sort_ws_bytes(int BH, int L, int n_b, int n_h) {
+  return align_up((size_t)BH * n_h * n_b * sort_tiles(L) * sizeof(int), kAlign);
+}
+
+struct FwdWs {
+  HashWs hash;
+  size_t hash_base, sort_base, buckets, sorted_idx, undo_idx, o_sorted, lse_sorted, total;
+};
+FwdWs fwd_ws(int BH, int L, int n_b, int n_h, lsh_dtype dt) {
+  Carver c;
+  FwdWs w;
+  const size_t slots = (size_t)BH * n_h * L;
+  w.hash = hash_ws(BH, L, n_b, n_h, dt);
+  w.hash_base = c.take(w.hash.total);
+  w.sort_base = c.take(sort_ws_bytes(BH, L, n_b, n_h));
+  w.buckets = c.take(slots * sizeof(int32_t));
+  w.sorted_idx = c.take(slots * sizeof(int32_t));
+  w.undo_idx = c.take(slots * sizeof(int32_t));
+  w.o_sorted = c.take(slots * kD * elem_size(dt));
+  w.lse_sorted = c.take(slots * sizeof(float));
+  w.total = c.off;
+  return w;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LSH_OK : LSH_ERR_HIP; }
+
+// Enqueue hashing (prep, MFMA hash, fixup) into the given scratch regions.
+hipError_t enqueue_hash(const void* qk, const void* rot, int32_t* buckets, char* ws, const HashWs& w, int BH,
+                        int L, int n_b, int n_h, lsh_dtype dt, hipStream_t s, void* const* ev, int* k) {
+  auto mark = [&](void) -> hipError_t {
+    if (ev == nullptr) return hipSuccess;
+    ++*k;
+    return hipEventRecord((hipEvent_t)ev[*k], s);
+  };
+  hipError_t e;
+  if (n_b == 1) {
+    if ((e = launch_fill_zero(buckets, (size_t)BH * n_h * L, s)) != hipSuccess) return e;
+    if ((e = mark()) != hipSuccess) return e;
+    if ((e = mark()) != hipSuccess) return e;
+    return mark();
+  }
+  float* rho = (float*)(ws + w.rho);
+  int* count = (int*)(ws + w.fix_count);
+  int* queue = (int*)(ws + w.fix_queue);
+  void* rot_t = ws + w.rot_t;
+  if ((e = launch_prep(rot, rot_t, rho, count, n_h, n_b, dt, s)) != hipSuccess) return e;
+  if ((e = mark()) != hipSuccess) return e;
+  if ((e = launch_hash(qk, rot_t, rho, buckets, queue, count, BH, L, n_b, n_h, dt, s)) != hipSuccess) return e;
+  if ((e = mark()) != hipSuccess) return e;
+  if ((e = launch_fixup(qk, rot, buckets, queue, count, L, n_b, n_h, dt, s)) != hipSuccess) return e;
+  return mark();
+}
+
+hipError_t enqueue_sort(const int32_t* buckets, int32_t* sorted_idx, int32_t* undo_idx, int* hist, int BH, int L,
+                        int n_b, int n_h, hipStream_t s, void* const* ev, int* k) {
+  auto mark = [&](void) -> hipError_t {
+    if (ev == nullptr) return hipSuccess;
+    ++*k;
+    return hipEventRecord((hipEvent_t)ev[*k], s);
+  };
+  const int BHR = BH * n_h;
+  hipError_t e;
+  if ((e = launch_sort_hist(buckets, hist, BHR, L, n_b, s)) != hipSuccess) return e;
+  if ((e = mark()) != hipSuccess) return e;
+  if ((e = launch_sort_scan(hist, BHR, L, n_b, s)) != hipSuccess) return e;
+  if ((e = mark()) != hipSuccess) return e;
+  if ((e = launch_sort_scatter(buckets, hist, sorted_idx, undo_idx, BHR, L, n_b, n_h, s)) != hipSuccess) return e;
+  return mark();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lsh_status_string(int status) {
+  switch (status) {
+    case LSH_OK: return "ok";
+    case LSH_ERR_NULL: return "a required pointer is NULL";
+    case LSH_ERR_SHAPE: return "invalid shape (dimension <= 0, L not a multiple of 64, or int32 index overflow)";
+    case LSH_ERR_BUCKETS: return "invalid bucket count (must be 1 or even, at most 4096)";
+    case LSH_ERR_UNSUPPORTED: return "unsupported configuration (D and chunk_len must be 64, n_hashes <= 16, dtype f32 or bf16)";
+    case LSH_ERR_WORKSPACE: return "workspace missing or too small";
+    case LSH_ERR_ALIAS: return "an output overlaps an input";
+    case LSH_ERR_HIP: return "HIP launch or event error";
+    default: return "unknown status";
+  }
+}
+
+int lsh_hash_workspace_bytes(int B, int H, int L, int D, int n_b, int n_h, lsh_dtype dt, size_t* bytes) {
+  if (bytes == nullptr) return LSH_ERR_NULL;
+  int st = check_problem(B, H, L, D, n_h);
+  if (st == LSH_OK) st = check_buckets(n_b, L);
+  if (st == LSH_OK && !dtype_ok(dt)) st = LSH_ERR_UNSUPPORTED;
+  if (st != LSH_OK) return st;
+  *bytes = hash_ws(B * H, L, n_b, n_h, dt).total;
+  return LSH_OK;
+}
+
+int lsh_hash(const void* qk, const void* rot, int32_t* buckets, int B, int H, int L, int D, int n_b, int n_h,
+             lsh_dtype dt, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_problem(B, H, L, D, n_h);
+  if (st == LSH_OK) st = check_buckets(n_b, L);
+  if (st == LSH_OK && !dtype_ok(dt)) st = LSH_ERR_UNSUPPORTED;
+  if (st != LSH_OK) return st;
+  if (qk == nullptr || buckets == nullptr || (n_b > 1 && rot == nullptr)) return LSH_ERR_NULL;
+  const int BH = B * H;
+  const HashWs w = hash_ws(BH, L, n_b, n_h, dt);
+  if (n_b > 1 && (ws == nullptr || ws_bytes < w.total)) return LSH_ERR_WORKSPACE;
+  const size_t es = elem_size(dt);
+  const size_t nb_bytes = (size_t)BH * n_h * L * sizeof(int32_t);
+  if (overlaps(buckets, nb_bytes, qk, (size_t)BH * L * kD * es) ||
+      overlaps(buckets, nb_bytes, rot, n_b > 1 ? (size_t)n_h * kD * (n_b / 2) * es : 0) ||
+      overlaps(buckets, nb_bytes, ws, n_b > 1 ? ws_bytes : 0))
+    return LSH_ERR_ALIAS;
+  int k = 0;
+  return hip_status(enqueue_hash(qk, rot, buckets, (char*)ws, w, BH, L, n_b, n_h, dt, (hipStream_t)stream,
+                                 nullptr, &k));
+}
+
+int lsh_sort_workspace_bytes(int B, int H, int L, int n_b, int n_h, size_t* bytes) {
+  if (bytes == nullptr) return LSH_ERR_NULL;
+  int st = check_problem(B, H, L, kD, n_h);
+  if (st == LSH_OK) st = check_buckets(n_b, L);
+  if (st != LSH_OK) return st;
+  *bytes = sort_ws_bytes(B * H, L, n_b, n_h);
+  return LSH_OK;
+}
+
+int lsh_sort(const int32_t* buckets, int32_t* sorted_idx, int32_t* undo_idx, int B, int H, int L, int n_b,
+             int n_h, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_problem(B, H, L, kD, n_h);
+  if (st == LSH_OK) st = check_buckets(n_b, L);
+  if (st != LSH_OK) return st;
+  if (buckets == nullptr || sorted_idx == nullptr || undo_idx == nullptr) return LSH_ERR_NULL;
+  const int BH = B * H;
+  const size_t need = sort_ws_bytes(BH, L, n_b, n_h);
+  if (ws == nullptr || ws_bytes < need) return LSH_ERR_WORKSPACE;
+  const size_t nb = (size_t)BH * n_h * L * sizeof(int32_t);
+  if (overlaps(sorted_idx, nb, buckets, nb) || overlaps(undo_idx, nb, buckets, nb) ||
+      overlaps(sorted_idx, nb, undo_idx, nb) || overlaps(sorted_idx, nb, ws, ws_bytes) ||
+      overlaps(undo_idx, nb, ws, ws_bytes) || overlaps(buckets, nb, ws, ws_bytes))
+    return LSH_ERR_ALIAS;
+  int k = 0;
+  return hip_status(enqueue_sort(buckets, sorted_idx, undo_idx, (int*)ws, BH, L, n_b, n_h, (hipStream_t)stream,
+                                 nullptr, &k));
+}
+
+int lsh_chunk_attn(const void* qk, const void* v, const int32_t* sorted_idx, void* o_sorted, float* lse_sorted,
+                   int B, int H, int L, int D, int n_h, int C, int causal, lsh_dtype dt, void* stream) {
+  int st = check_problem(B, H, L, D, n_h);
+  if (st != LSH_OK) return st;
+  if (C != kChunk) return C <= 0 ? LSH_ERR_SHAPE : LSH_ERR_UNSUPPORTED;
+  if (!dtype_ok(dt)) return LSH_ERR_UNSUPPORTED;
+  if (qk == nullptr || v == nullptr || sorted_idx == nullptr || o_sorted == nullptr || lse_sorted == nullptr)
+    return LSH_ERR_NULL;
+  const int BH = B * H;
+  const size_t es = elem_size(dt);
+  const size_t slots = (size_t)BH * n_h * L;
+  const size_t in_bytes = (size_t)BH * L * kD * es;
+  const size_t o_bytes = slots * kD * es, l_bytes = slots * sizeof(float), i_bytes = slots * sizeof(int32_t);
+  const void* ins[3] = {qk, v, sorted_idx};
+  const size_t in_n[3] = {in_bytes, in_bytes, i_bytes};
+  for (int a = 0; a < 3; ++a)
+    if (overlaps(o_sorted, o_bytes, ins[a], in_n[a]) || overlaps(lse_sorted, l_bytes, ins[a], in_n[a]))
+      return LSH_ERR_ALIAS;
+  if (overlaps(o_sorted, o_bytes, lse_sorted, l_bytes)) return LSH_ERR_ALIAS;
+  return hip_status(launch_chunk_attn(qk, v, sorted_idx, o_sorted, lse_sorted, BH, L, n_h, causal, dt,
+                                      (hipStream_t)stream));
+}
+
+int lsh_unsort_combine(const void* o_sorted, const float* lse_sorted, const int32_t* undo_idx, void* out,
+                       float* lse_out, int B, int H, int L, int D, int n_h, lsh_dtype dt, void* stream) {
+  int st = check_problem(B, H, L, D, n_h);
+  if (st != LSH_OK) return st;
+  if (!dtype_ok(dt)) return LSH_ERR_UNSUPPORTED;
+  if (o_sorted == nullptr || lse_sorted == nullptr || undo_idx == nullptr || out == nullptr) return LSH_ERR_NULL;
+  const int BH = B * H;
+  const size_t es = elem_size(dt);
+  const size_t slots = (size_t)BH * n_h * L;
+  const size_t out_bytes = (size_t)BH * L * kD * es, lo_bytes = (size_t)BH * L * sizeof(float);
+  const void* ins[3] = {o_sorted, lse_sorted, undo_idx};
+  const size_t in_n[3] = {slots * kD * es, slots * sizeof(float), slots * sizeof(int32_t)};
+  for (int a = 0; a < 3; ++a)
+    if (overlaps(out, out_bytes, ins[a], in_n[a]) || overlaps(lse_out, lo_bytes, ins[a], in_n[a]))
+      return LSH_ERR_ALIAS;
+  if (overlaps(out, out_bytes, lse_out, lo_bytes)) return LSH_ERR_ALIAS;
+  return hip_status(launch_combine(o_sorted, lse_sorted, undo_idx, out, lse_out, BH, L, n_h, dt,
+                                   (hipStream_t)stream));
+}
+
+int lsh_fwd_workspace_bytes(int B, int H, int L, int D, int n_b, int n_h, int C, lsh_dtype dt, size_t* bytes) {
+  if (bytes == nullptr) return LSH_ERR_NULL;
+  int st = check_problem(B, H, L, D, n_h);
+  if (st == LSH_OK) st = check_buckets(n_b, L);
+  if (st != LSH_OK) return st;
+  if (C != kChunk) return C <= 0 ? LSH_ERR_SHAPE : LSH_ERR_UNSUPPORTED;
+  if (!dtype_ok(dt)) return LSH_ERR_UNSUPPORTED;
+  *bytes = fwd_ws(B * H, L, n_b, n_h, dt).total;
+  return LSH_OK;
+}
+
+int reformer_lsh_attn_fwd(const void* qk, const void* v, const void* rot, int n_buckets, int n_hashes, int chunk_len,
+                          int causal, int B, int H, int L, int D, lsh_dtype dt, void* out, float* lse_out, void* ws,
+                          size_t ws_bytes, void* stream, void* const* stage_events) {
+  int st = check_problem(B, H, L, D, n_hashes);
+  if (st == LSH_OK) st = check_buckets(n_buckets, L);
+  if (st != LSH_OK) return st;
+  if (chunk_len != kChunk) return chunk_len <= 0 ? LSH_ERR_SHAPE : LSH_ERR_UNSUPPORTED;
+  if (!dtype_ok(dt)) return LSH_ERR_UNSUPPORTED;
+  if (qk == nullptr || v == nullptr || out == nullptr || (n_buckets > 1 && rot == nullptr)) return LSH_ERR_NULL;
+  const int BH = B * H, n_h = n_hashes, n_b = n_buckets;
+  const FwdWs w = fwd_ws(BH, L, n_b, n_h, dt);
+  if (ws == nullptr || ws_bytes < w.total) return LSH_ERR_WORKSPACE;
+  const size_t es = elem_size(dt);
+  const size_t in_bytes = (size_t)BH * L * kD * es;
+  const size_t rot_bytes = n_b > 1 ? (size_t)n_h * kD * (n_b / 2) * es : 0;
+  const size_t lo_bytes = (size_t)BH * L * sizeof(float);
+  const void* ins[4] = {qk, v, rot, ws};
+  const size_t in_n[4] = {in_bytes, in_bytes, rot_bytes, ws_bytes};
+  for (int a = 0; a < 4; ++a)
+    if (overlaps(out, in_bytes, ins[a], in_n[a]) || overlaps(lse_out, lo_bytes, ins[a], in_n[a]))
+      return LSH_ERR_ALIAS;
+  if (overlaps(out, in_bytes, lse_out, lo_bytes)) return LSH_ERR_ALIAS;
+  if (overlaps(ws, ws_bytes, qk, in_bytes) || overlaps(ws, ws_bytes, v, in_bytes) ||
+      overlaps(ws, ws_bytes, rot, rot_bytes))
+    return LSH_ERR_ALIAS;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)ws;
+  int32_t* buckets = (int32_t*)(base + w.buckets);
+  int32_t* sorted_idx = (int32_t*)(base + w.sorted_idx);
+  int32_t* undo_idx = (int32_t*)(base + w.undo_idx);
+  void* o_sorted = base + w.o_sorted;
+  float* lse_sorted = (float*)(base + w.lse_sorted);
+  int k = 0;
+  hipError_t e = hipSuccess;
+  if (stage_events != nullptr) e = hipEventRecord((hipEvent_t)stage_events[0], s);
+  if (e == hipSuccess)
+    e = enqueue_hash(qk, rot, buckets, base + w.hash_base, w.hash, BH, L, n_b, n_h, dt, s, stage_events, &k);
+  if (e == hipSuccess)
+    e = enqueue_sort(buckets, sorted_idx, undo_idx, (int*)(base + w.sort_base), BH, L, n_b, n_h, s, stage_events,
+                     &k);
+  if (e == hipSuccess) e = launch_chunk_attn(qk, v, sorted_idx, o_sorted, lse_sorted, BH, L, n_h, causal, dt, s);
+  if (e == hipSuccess && stage_events != nullptr) e = hipEventRecord((hipEvent_t)stage_events[++k], s);
+  if (e == hipSuccess) e = launch_combine(o_sorted, lse_sorted, undo_idx, out, lse_out, BH, L, n_h, dt, s);
+  if (e == hipSuccess && stage_events != nullptr) e = hipEventRecord((hipEvent_t)stage_events[++k], s);
+  return hip_status(e);
+}
+
+int lsh_event_create(void** event) {
+  if (event == nullptr) return LSH_ERR_NULL;
+  hipEvent_t e;
+  if (hipEventCreate(&e) != hipSuccess) return LSH_ERR_HIP;
+  *event = (void*)e;
+  return LSH_OK;
+}
+
+int lsh_event_destroy(void* event) {
+  if (event == nullptr) return LSH_ERR_NULL;
+  return hip_status(hipEventDestroy((hipEvent_t)event));
+}
+
+int lsh_event_record(void* event, void* stream) {
+  if (event == nullptr) return LSH_ERR_NULL;
+  return hip_status(hipEventRecord((hipEvent_t)event, (hipStream_t)stream));
+}
+
+int lsh_event_elapsed_ms(void* start, void* end, float* ms) {
+  if (start == nullptr || end == nullptr || ms == nullptr) return LSH_ERR_NULL;
+  if (hipEventSynchronize((hipEvent_t)end) != hipSuccess) return LSH_ERR_HIP;
+  return hip_status(hipEventElapsedTime(ms, (hipEvent_t)start, (hipEvent_t)end));
+}
+
+}  // extern "C"

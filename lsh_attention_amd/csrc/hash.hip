@@ -1,0 +1,393 @@
+// Step 1 of the shared-QK LSH attention forward pass: angular LSH.
+//
+// Reformer explainer (akshathtiwari.co.in/blog/reformer), angular-LSH
+// passage: a token's bucket is the angular sector its vector falls in after a
+// random rotation, one independent rotation per hash round.  Concretely the
+// bucket is the index of the largest entry of [x R_r ; -x R_r], lowest index
+// on exact ties, with R_r of shape [D, n_b/2].
+//
+// gfx950 design:
+//  * The projection x R_r is a dense contraction (K = 64), done on MFMA with
+//    the rotation as the A operand (rotation columns = MFMA rows) and the
+//    tokens as the B operand (tokens = MFMA columns), so each lane's
+//    accumulators hold one token's scores for 16 rotation columns.
+//  * The argmax is fused into the MFMA epilogue.  Each score becomes a sort
+//    key: |score| with its low mantissa bits replaced by a column code; the
+//    running top-2 keys are kept per lane with max3/med3 (2.5 VALU ops per
+//    score).  The winner's index comes from its code; its sign from one dot
+//    product.
+//  * The decision is certified: an fp32 sum of 64 exact bf16 products (or
+//    rounded fp32 products) is within eps = 65 * 2^-23 * |x| * max_j |r_j| of
+//    the exact value, and the key truncation adds at most one key-grid step
+//    delta.  If the top-2 gap is not above 2 eps + delta the token is queued and
+//    re-decided from float64 sums by `fixup_kernel`, so the result equals the
+//    exact-arithmetic argmax.
+//  * The rotation is shared by every (batch, head): it is transposed once per
+//    call into [n_h][n_b/2 padded to 32][D] so a workgroup stages it into LDS
+//    with 16-byte row loads, and read by all four waves from there.
+#include "lsh_internal.h"
+
+namespace lsh {
+
+namespace {
+
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ inline double to_f64(uint16_t b) { return (double)bf16_to_f32(b); }
+__device__ inline double to_f64(float f) { return (double)f; }
+
+__device__ inline uint32_t umax3(uint32_t a, uint32_t b, uint32_t c) {
+  return max(max(a, b), c);
+}
+__device__ inline uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Rotation transpose + per-round largest column norm + queue reset.
+// One block per round.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ rot, T* __restrict__ rot_t,
+                                                   float* __restrict__ rho, int* __restrict__ fix_count,
+                                                   int half, int halfp) {
+  const int r = blockIdx.x;
+  const T* R = rot + (size_t)r * kD * half;
+  T* RT = rot_t + (size_t)r * halfp * kD;
+  double best = 0.0;
+  for (int j = threadIdx.x; j < halfp; j += blockDim.x) {
+    double nrm = 0.0;
+    for (int d = 0; d < kD; ++d) {
+      T val = j < half ? R[(size_t)d * half + j] : T(0);
+      RT[(size_t)j * kD + d] = val;
+      double f = to_f64(val);
+      nrm = fma(f, f, nrm);
+    }
+    best = fmax(best, nrm);
+  }
+  for (int off = 32; off >= 1; off >>= 1) best = fmax(best, __shfl_xor(best, off));
+  __shared__ double red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double m = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+    // Round the norm up so that it bounds every column norm.
+    rho[r] = (float)(sqrt(m) * (1.0 + 1e-6));
+    if (r == 0) *fix_count = 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Hash kernel.  Block = 4 waves, 64 tokens per wave (two 32-token MFMA column
+// groups), 256 tokens per block; grid = (ceil(L / 256), B*H).
+// ---------------------------------------------------------------------------
+constexpr int kHashTok = 256;
+constexpr int kHashCB = 128;  // rotation columns staged in LDS per pass
+
+template <bool BF16>
+struct HashTraits;
+template <>
+struct HashTraits<true> {
+  using T = uint16_t;
+  static constexpr int kRow = 72;  // LDS row stride in elements (144 B, conflict-free b128 reads)
+};
+template <>
+struct HashTraits<false> {
+  using T = float;
+  static constexpr int kRow = 68;  // 272 B
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void hash_kernel(const typename HashTraits<BF16>::T* __restrict__ qk,
+                                                   const typename HashTraits<BF16>::T* __restrict__ rot_t,
+                                                   const float* __restrict__ rho,
+                                                   int32_t* __restrict__ buckets, int* __restrict__ fix_queue,
+                                                   int* __restrict__ fix_count, int L, int n_h, int half,
+                                                   int halfp, uint32_t lowmask, int ibits) {
+  using T = typename HashTraits<BF16>::T;
+  constexpr int kRow = HashTraits<BF16>::kRow;
+  __shared__ __attribute__((aligned(16))) T sR[kHashCB * kRow];
+
+  const int blocks_per_bh = (L + kHashTok - 1) / kHashTok;
+  const int bh = blockIdx.x / blocks_per_bh;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n = lane & 31;    // token column within a 32-token group / rotation row within a tile
+  const int hb = lane >> 5;   // which half of the K slice this lane feeds
+  const int tok_base = (blockIdx.x % blocks_per_bh) * kHashTok + wave * 64;
+  const bool wave_valid = tok_base < L;  // L % 64 == 0: a wave is all-valid or all-invalid
+  const uint32_t kmask = 0x7FFFFFFFu & ~lowmask;
+  // The key mask lives in a VGPR so that key = (score & mask) | code is a single
+  // v_and_or_b32 with the (wave-uniform) code as its one scalar operand.
+  uint32_t kmask_v;
+  asm("v_mov_b32 %0, %1" : "=v"(kmask_v) : "s"(kmask));
+
+  // B operand (tokens), kept in registers for every round.
+  //  bf16: k-step s covers dims 16s..16s+15; this lane holds dims 16s + 8hb + 0..7.
+  //  fp32: k-step s covers dims {s, s+32}; this lane holds dim s + 32hb.
+  constexpr int kSteps = BF16 ? 4 : 32;
+  bf16x8 bq16[2][4];
+  float bq32[2][BF16 ? 1 : 32];
+  float nrm2[2];
+  for (int q = 0; q < 2; ++q) {
+    const int tok = tok_base + 32 * q + n;
+    const T* xr = qk + ((size_t)bh * L + (wave_valid ? tok : 0)) * kD;
+    float acc = 0.f;
+    if constexpr (BF16) {
+      for (int s = 0; s < 4; ++s) {
+        uint4 raw = wave_valid ? *(const uint4*)(xr + 16 * s + 8 * hb) : make_uint4(0, 0, 0, 0);
+        bq16[q][s] = __builtin_bit_cast(bf16x8, raw);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+        for (int e = 0; e < 4; ++e) {
+          float lo = __uint_as_float(w[e] << 16), hi = __uint_as_float(w[e] & 0xFFFF0000u);
+          acc = fmaf(lo, lo, acc);
+          acc = fmaf(hi, hi, acc);
+        }
+      }
+    } else {
+      for (int s4 = 0; s4 < 8; ++s4) {
+        float4 raw = wave_valid ? *(const float4*)(xr + 32 * hb + 4 * s4) : make_float4(0, 0, 0, 0);
+        bq32[q][4 * s4 + 0] = raw.x;
+        bq32[q][4 * s4 + 1] = raw.y;
+        bq32[q][4 * s4 + 2] = raw.z;
+        bq32[q][4 * s4 + 3] = raw.w;
+        acc = fmaf(raw.x, raw.x, acc);
+        acc = fmaf(raw.y, raw.y, acc);
+        acc = fmaf(raw.z, raw.z, acc);
+        acc = fmaf(raw.w, raw.w, acc);
+      }
+    }
+    nrm2[q] = acc + __shfl_xor(acc, 32);
+  }
+  (void)kSteps;
+
+  for (int r = 0; r < n_h; ++r) {
+    uint32_t m1[2] = {0u, 0u}, m2[2] = {0u, 0u};
+    const T* src_round = rot_t + (size_t)r * halfp * kD;
+    for (int cb = 0; cb < halfp; cb += kHashCB) {
+      const int ncols = min(kHashCB, halfp - cb);
+      __syncthreads();
+      {
+        constexpr int kPieces = BF16 ? 8 : 16;  // 16-byte pieces per 64-element row
+        constexpr int kPer = BF16 ? 8 : 4;      // elements per piece
+        const T* src = src_round + (size_t)cb * kD;
+        for (int c = threadIdx.x; c < ncols * kPieces; c += 256) {
+          const int row = c / kPieces, piece = c % kPieces;
+          *(uint4*)(sR + row * kRow + piece * kPer) = *(const uint4*)(src + row * kD + piece * kPer);
+        }
+      }
+      __syncthreads();
+      for (int t = 0; t < ncols / 32; ++t) {
+        f32x16 acc0 = {}, acc1 = {};
+        const T* arow = sR + (32 * t + n) * kRow;
+        if constexpr (BF16) {
+          for (int s = 0; s < 4; ++s) {
+            bf16x8 a = *(const bf16x8*)(arow + 16 * s + 8 * hb);
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq16[0][s], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq16[1][s], acc1, 0, 0, 0);
+          }
+        } else {
+          for (int s4 = 0; s4 < 8; ++s4) {
+            float4 a4 = *(const float4*)(arow + 32 * hb + 4 * s4);
+            const float a[4] = {a4.x, a4.y, a4.z, a4.w};
+            for (int e = 0; e < 4; ++e) {
+              acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], bq32[0][4 * s4 + e], acc0, 0, 0, 0);
+              acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], bq32[1][4 * s4 + e], acc1, 0, 0, 0);
+            }
+          }
+        }
+        // Column code of accumulator e of tile tg: lowmask - (16 tg + e).
+        const uint32_t tg = (uint32_t)((cb >> 5) + t);
+        const uint32_t cbase = lowmask - 16u * tg;
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          uint32_t a0 = (__float_as_uint(acc0[e]) & kmask_v) | (cbase - e);
+          uint32_t b0 = (__float_as_uint(acc0[e + 1]) & kmask_v) | (cbase - e - 1);
+          uint32_t hi0 = umax3(m1[0], a0, b0);
+          m2[0] = max(m2[0], umed3(m1[0], a0, b0));
+          m1[0] = hi0;
+          uint32_t a1 = (__float_as_uint(acc1[e]) & kmask_v) | (cbase - e);
+          uint32_t b1 = (__float_as_uint(acc1[e + 1]) & kmask_v) | (cbase - e - 1);
+          uint32_t hi1 = umax3(m1[1], a1, b1);
+          m2[1] = max(m2[1], umed3(m1[1], a1, b1));
+          m1[1] = hi1;
+        }
+      }
+    }
+
+    // Merge with the partner lane (same tokens, the other 16 rows of each tile),
+    // decode the winner, recompute its signed score, certify.
+    const float eps_scale = 65.0f * 0x1p-23f * rho[r];
+    int32_t result[2];
+    bool certified[2];
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t pm1 = __shfl_xor(m1[q], 32), pm2 = __shfl_xor(m2[q], 32);
+      const uint32_t M1 = max(m1[q], pm1);
+      const uint32_t M2 = max(min(m1[q], pm1), max(m2[q], pm2));
+      // Half of the tile the winner's row lies in (ties of identical keys are
+      // equal-value ties, which are never certified, so any choice works).
+      const int win_h = m1[q] > pm1 ? hb : (m1[q] < pm1 ? (hb ^ 1) : 0);
+      const uint32_t u = lowmask - (M1 & lowmask);  // 16 tg + e
+      const int tg = (int)(u >> 4), e = (int)(u & 15);
+      const int jstar = 32 * tg + 8 * (e >> 2) + 4 * win_h + (e & 3);  // < halfp
+      const float t1 = __uint_as_float(M1 & kmask), t2 = __uint_as_float(M2 & kmask);
+      const float eps = eps_scale * (sqrtf(nrm2[q]) * 1.000001f);
+      const int ebits = (int)((M1 >> 23) & 0xFFu) - 23 + ibits;
+      const float delta = ebits >= 1 ? __uint_as_float((uint32_t)ebits << 23) : 0x1p-126f;
+      certified[q] = (t1 - t2) > 2.0f * eps + delta;
+      // Signed score of the winner: this lane's half of the dot product plus the partner's.
+      const T* rr = rot_t + ((size_t)r * halfp + jstar) * kD;
+      float dp = 0.f;
+      if constexpr (BF16) {
+        for (int s = 0; s < 4; ++s) {
+          uint4 raw = *(const uint4*)(rr + 16 * s + 8 * hb);
+          const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+          const uint4 xb = __builtin_bit_cast(uint4, bq16[q][s]);
+          const uint32_t xw[4] = {xb.x, xb.y, xb.z, xb.w};
+          for (int k = 0; k < 4; ++k) {
+            dp = fmaf(__uint_as_float(w[k] << 16), __uint_as_float(xw[k] << 16), dp);
+            dp = fmaf(__uint_as_float(w[k] & 0xFFFF0000u), __uint_as_float(xw[k] & 0xFFFF0000u), dp);
+          }
+        }
+      } else {
+        for (int s4 = 0; s4 < 8; ++s4) {
+          float4 a4 = *(const float4*)(rr + 32 * hb + 4 * s4);
+          dp = fmaf(a4.x, bq32[q][4 * s4 + 0], dp);
+          dp = fmaf(a4.y, bq32[q][4 * s4 + 1], dp);
+          dp = fmaf(a4.z, bq32[q][4 * s4 + 2], dp);
+          dp = fmaf(a4.w, bq32[q][4 * s4 + 3], dp);
+        }
+      }
+      dp += __shfl_xor(dp, 32);
+      result[q] = dp > 0.f ? jstar : jstar + half;
+    }
+    if (wave_valid) {
+      // Lanes 0-31 store group 0, lanes 32-63 group 1: 64 consecutive tokens.
+      const int q = hb;
+      const int tok = tok_base + 32 * q + n;
+      const size_t idx = ((size_t)bh * n_h + r) * L + tok;
+      if (certified[q]) {
+        buckets[idx] = result[q];
+      } else {
+        buckets[idx] = -1;
+        const int slot = atomicAdd(fix_count, 1);
+        fix_queue[slot] = (int)idx;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Float64 re-decision of queued tokens: one wave per token-round, every
+// column's score as a float64 sum of exact products, argmax with the lowest
+// index on ties.  Grid-stride over the queue.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void fixup_kernel(const T* __restrict__ qk, const T* __restrict__ rot,
+                                                    int32_t* __restrict__ buckets,
+                                                    const int* __restrict__ fix_queue,
+                                                    const int* __restrict__ fix_count, int L, int n_h,
+                                                    int half) {
+  const int lane = threadIdx.x & 63;
+  const int gw = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int nw = (gridDim.x * blockDim.x) >> 6;
+  const int count = *fix_count;
+  for (int it = gw; it < count; it += nw) {
+    const int idx = fix_queue[it];
+    const int tok = idx % L;
+    const int br = idx / L;
+    const int r = br % n_h;
+    const int bh = br / n_h;
+    const T* x = qk + ((size_t)bh * L + tok) * kD;
+    const T* R = rot + (size_t)r * kD * half;
+    double best_v = -1.0;
+    int best_i = 0x7FFFFFFF;
+    for (int j0 = 0; j0 < half; j0 += 64 * 8) {
+      double acc[8];
+      for (int k = 0; k < 8; ++k) acc[k] = 0.0;
+      for (int d = 0; d < kD; ++d) {
+        const double xd = to_f64(x[d]);
+        for (int k = 0; k < 8; ++k) {
+          const int j = j0 + lane + 64 * k;
+          if (j < half) acc[k] = fma(xd, to_f64(R[(size_t)d * half + j]), acc[k]);
+        }
+      }
+      for (int k = 0; k < 8; ++k) {
+        const int j = j0 + lane + 64 * k;
+        if (j < half) {
+          const double p = acc[k];
+          const double v = fabs(p);
+          const int i = p < 0.0 ? j + half : j;  // the larger of +p (index j) and -p (index j + half)
+          if (v > best_v || (v == best_v && i < best_i)) {
+            best_v = v;
+            best_i = i;
+          }
+        }
+      }
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double ov = __shfl_xor(best_v, off);
+      const int oi = __shfl_xor(best_i, off);
+      if (ov > best_v || (ov == best_v && oi < best_i)) {
+        best_v = ov;
+        best_i = oi;
+      }
+    }
+    if (lane == 0) buckets[idx] = best_i;
+  }
+}
+
+__global__ void fill_zero_kernel(int32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_prep(const void* rot, void* rot_t, float* rho, int* fix_count, int n_h, int n_b,
+                       lsh_dtype dt, hipStream_t s) {
+  const int half = n_b / 2, halfp = padded_half(n_b);
+  if (dt == LSH_BF16)
+    prep_kernel<uint16_t><<<n_h, 256, 0, s>>>((const uint16_t*)rot, (uint16_t*)rot_t, rho, fix_count, half, halfp);
+  else
+    prep_kernel<float><<<n_h, 256, 0, s>>>((const float*)rot, (float*)rot_t, rho, fix_count, half, halfp);
+  return hipGetLastError();
+}
+
+hipError_t launch_hash(const void* qk, const void* rot_t, const float* rho, int32_t* buckets,
+                       int* fix_queue, int* fix_count, int BH, int L, int n_b, int n_h,
+                       lsh_dtype dt, hipStream_t s) {
+  const int half = n_b / 2, halfp = padded_half(n_b);
+  // Codes 16 tg + e < halfp / 2 must fit in the low bits of the key.
+  int ibits = 0;
+  while ((1 << ibits) < halfp / 2) ++ibits;
+  const uint32_t lowmask = (1u << ibits) - 1u;
+  const unsigned grid = (unsigned)((L + kHashTok - 1) / kHashTok) * (unsigned)BH;
+  if (dt == LSH_BF16)
+    hash_kernel<true><<<grid, 256, 0, s>>>((const uint16_t*)qk, (const uint16_t*)rot_t, rho, buckets, fix_queue,
+                                           fix_count, L, n_h, half, halfp, lowmask, ibits);
+  else
+    hash_kernel<false><<<grid, 256, 0, s>>>((const float*)qk, (const float*)rot_t, rho, buckets, fix_queue,
+                                            fix_count, L, n_h, half, halfp, lowmask, ibits);
+  return hipGetLastError();
+}
+
+hipError_t launch_fixup(const void* qk, const void* rot, int32_t* buckets, const int* fix_queue,
+                        const int* fix_count, int L, int n_b, int n_h, lsh_dtype dt, hipStream_t s) {
+  const int half = n_b / 2;
+  if (dt == LSH_BF16)
+    fixup_kernel<uint16_t><<<256, 256, 0, s>>>((const uint16_t*)qk, (const uint16_t*)rot, buckets, fix_queue,
+                                               fix_count, L, n_h, half);
+  else
+    fixup_kernel<float><<<256, 256, 0, s>>>((const float*)qk, (const float*)rot, buckets, fix_queue, fix_count,
+                                            L, n_h, half);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(int32_t* p, size_t n, hipStream_t s) {
+  fill_zero_kernel<<<1024, 256, 0, s>>>(p, n);
+  return hipGetLastError();
+}
+
+}  // namespace lsh

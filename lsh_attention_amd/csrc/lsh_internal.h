@@ -1,0 +1,56 @@
+// Internal declarations shared by the gfx950 kernels and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "lsh_attn.h"
+
+namespace lsh {
+
+constexpr int kD = 64;          // head dimension handled by the kernels
+constexpr int kChunk = 64;      // chunk length handled by the attention kernel
+constexpr int kMaxHashes = 16;  // upper bound on hash rounds
+constexpr int kMaxBuckets = 4096;
+constexpr int kSortTile = 2048; // tokens per sort workgroup
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+__host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Columns of the transposed rotation, padded to whole 32-column MFMA tiles.
+inline int padded_half(int n_b) { return n_b == 1 ? 0 : (int)align_up((size_t)(n_b / 2), 32); }
+inline int sort_tiles(int L) { return (L + kSortTile - 1) / kSortTile; }
+
+// ---- launchers (stream-ordered, no synchronisation) ----
+// Rotation transpose [n_h][D][half] -> [n_h][halfp][D] with zero padding, the
+// per-round largest column norm, and the reset of the uncertified-token count.
+hipError_t launch_prep(const void* rot, void* rot_t, float* rho, int* fix_count, int n_h, int n_b,
+                       lsh_dtype dt, hipStream_t s);
+hipError_t launch_hash(const void* qk, const void* rot_t, const float* rho, int32_t* buckets,
+                       int* fix_queue, int* fix_count, int BH, int L, int n_b, int n_h,
+                       lsh_dtype dt, hipStream_t s);
+hipError_t launch_fixup(const void* qk, const void* rot, int32_t* buckets, const int* fix_queue,
+                        const int* fix_count, int L, int n_b, int n_h, lsh_dtype dt,
+                        hipStream_t s);
+hipError_t launch_fill_zero(int32_t* p, size_t n, hipStream_t s);
+
+hipError_t launch_sort_hist(const int32_t* buckets, int* hist, int BHR, int L, int n_b,
+                            hipStream_t s);
+hipError_t launch_sort_scan(int* hist, int BHR, int L, int n_b, hipStream_t s);
+hipError_t launch_sort_scatter(const int32_t* buckets, const int* hist, int32_t* sorted_idx,
+                               int32_t* undo_idx, int BHR, int L, int n_b, int n_h,
+                               hipStream_t s);
+
+hipError_t launch_chunk_attn(const void* qk, const void* v, const int32_t* sorted_idx,
+                             void* o_sorted, float* lse_sorted, int BH, int L, int n_h,
+                             int causal, lsh_dtype dt, hipStream_t s);
+
+hipError_t launch_combine(const void* o_sorted, const float* lse_sorted, const int32_t* undo_idx,
+                          void* out, float* lse_out, int BH, int L, int n_h, lsh_dtype dt,
+                          hipStream_t s);
+
+}  // namespace lsh

@@ -1,0 +1,159 @@
+// Step 2 of the shared-QK LSH attention forward pass: sort tokens by bucket.
+//
+// Reformer explainer (akshathtiwari.co.in/blog/reformer): tokens are sorted by
+// bucket so bucket-mates become contiguous.  The key here is (round, bucket,
+// position): a stable sort of each round's positions by bucket.  Since the key
+// is unique the permutation is fully determined.
+//
+// With at most 4096 buckets this is a counting sort, O(n) rather than the
+// explainer's O(n log n) comparison sort, in three launches per call:
+//   hist    - per (problem, round, tile of kSortTile tokens) bucket histogram
+//             in LDS, stored bucket-major: hist[bhr][bucket][tile];
+//   scan    - exclusive prefix sum of that array per (problem, round), which
+//             gives every (bucket, tile) its first output slot;
+//   scatter - each wave of a tile ranks its sub-tile's tokens in order: the
+//             lanes holding the same bucket are found with one ballot per key
+//             bit, their rank is a popcount below the lane, and a per-wave LDS
+//             counter per bucket carries the running offset.
+// Bucket values outside [0, n_b) are clamped to n_b - 1 (callers must not
+// pass them; clamping only keeps every write in bounds).
+#include "lsh_internal.h"
+
+namespace lsh {
+
+namespace {
+
+__device__ inline int clamp_bucket(int32_t b, int n_b) { return (int)min((uint32_t)b, (uint32_t)(n_b - 1)); }
+
+__global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t* __restrict__ buckets,
+                                                        int* __restrict__ hist, int L, int n_b,
+                                                        int n_tiles) {
+  extern __shared__ int sh[];  // n_b counters
+  const int bhr = blockIdx.x / n_tiles, tile = blockIdx.x % n_tiles;
+  for (int b = threadIdx.x; b < n_b; b += blockDim.x) sh[b] = 0;
+  __syncthreads();
+  const int t0 = tile * kSortTile, t1 = min(L, t0 + kSortTile);
+  const int32_t* bk = buckets + (size_t)bhr * L;
+  for (int i = t0 + (int)threadIdx.x; i < t1; i += blockDim.x) atomicAdd(&sh[clamp_bucket(bk[i], n_b)], 1);
+  __syncthreads();
+  int* out = hist + (size_t)bhr * n_b * n_tiles;
+  for (int b = threadIdx.x; b < n_b; b += blockDim.x) out[(size_t)b * n_tiles + tile] = sh[b];
+}
+
+// One block per (problem, round): exclusive scan of n = n_b * n_tiles counts.
+__global__ __launch_bounds__(256) void sort_scan_kernel(int* __restrict__ hist, int n) {
+  int* h = hist + (size_t)blockIdx.x * n;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ int wsum[4];
+  int carry = 0;
+  constexpr int kPer = 8;
+  for (int base = 0; base < n; base += 256 * kPer) {
+    const int i0 = base + (int)threadIdx.x * kPer;
+    int v[kPer];
+    int s = 0;
+    for (int k = 0; k < kPer; ++k) {
+      v[k] = (i0 + k < n) ? h[i0 + k] : 0;
+      s += v[k];
+    }
+    int incl = s;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int woff = 0, total = 0;
+    for (int w = 0; w < 4; ++w) {
+      if (w < wave) woff += wsum[w];
+      total += wsum[w];
+    }
+    int run = carry + woff + incl - s;
+    for (int k = 0; k < kPer; ++k) {
+      if (i0 + k < n) h[i0 + k] = run;
+      run += v[k];
+    }
+    carry += total;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __restrict__ buckets,
+                                                           const int* __restrict__ hist,
+                                                           int32_t* __restrict__ sorted_idx,
+                                                           int32_t* __restrict__ undo_idx, int L, int n_b,
+                                                           int n_h, int n_tiles, int nbits) {
+  extern __shared__ int sh[];  // 4 waves x n_b running offsets
+  const int bhr = blockIdx.x / n_tiles, tile = blockIdx.x % n_tiles;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = tile * kSortTile, t1 = min(L, t0 + kSortTile);
+  constexpr int kPerWave = kSortTile / 4;
+  const int w0 = t0 + wave * kPerWave, w1 = min(t1, w0 + kPerWave);
+  int* cnt = sh + wave * n_b;
+  for (int b = threadIdx.x; b < 4 * n_b; b += blockDim.x) sh[b] = 0;
+  __syncthreads();
+  const int32_t* bk = buckets + (size_t)bhr * L;
+  // 1. per-wave counts of its sub-tile
+  for (int i = w0 + lane; i < w1; i += 64) atomicAdd(&cnt[clamp_bucket(bk[i], n_b)], 1);
+  __syncthreads();
+  // 2. first slot of (bucket, wave): the scanned (bucket, tile) offset plus the
+  //    counts of the earlier waves of this tile.
+  const int* hs = hist + (size_t)bhr * n_b * n_tiles;
+  for (int b = threadIdx.x; b < n_b; b += blockDim.x) {
+    int run = hs[(size_t)b * n_tiles + tile];
+    for (int w = 0; w < 4; ++w) {
+      const int c = sh[w * n_b + b];
+      sh[w * n_b + b] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  // 3. ordered walk, 64 tokens at a time.
+  const int r = bhr % n_h, bh = bhr / n_h;
+  int32_t* sidx = sorted_idx + (size_t)bh * n_h * L;
+  int32_t* uidx = undo_idx + (size_t)bhr * L;
+  for (int i0 = w0; i0 < w1; i0 += 64) {
+    const int i = i0 + lane;
+    const bool act = i < w1;
+    const int b = act ? clamp_bucket(bk[i], n_b) : 0;
+    uint64_t match = __ballot(act);
+    for (int k = 0; k < nbits; ++k) {
+      const bool bit = (b >> k) & 1;
+      const uint64_t bal = __ballot(bit);
+      match &= bit ? bal : ~bal;
+    }
+    const uint64_t below = match & ((1ull << lane) - 1ull);
+    const int rank = __popcll(below);
+    const int first = act ? cnt[b] : 0;
+    if (act && below == 0ull) cnt[b] = first + __popcll(match);
+    if (act) {
+      const int g = r * L + first + rank;
+      sidx[g] = i;
+      uidx[i] = g;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_sort_hist(const int32_t* buckets, int* hist, int BHR, int L, int n_b, hipStream_t s) {
+  const int nt = sort_tiles(L);
+  sort_hist_kernel<<<nt * BHR, 256, n_b * sizeof(int), s>>>(buckets, hist, L, n_b, nt);
+  return hipGetLastError();
+}
+
+hipError_t launch_sort_scan(int* hist, int BHR, int L, int n_b, hipStream_t s) {
+  sort_scan_kernel<<<BHR, 256, 0, s>>>(hist, n_b * sort_tiles(L));
+  return hipGetLastError();
+}
+
+hipError_t launch_sort_scatter(const int32_t* buckets, const int* hist, int32_t* sorted_idx,
+                               int32_t* undo_idx, int BHR, int L, int n_b, int n_h, hipStream_t s) {
+  const int nt = sort_tiles(L);
+  int nbits = 0;
+  while ((1 << nbits) < n_b) ++nbits;
+  sort_scatter_kernel<<<nt * BHR, 256, 4 * n_b * sizeof(int), s>>>(buckets, hist, sorted_idx, undo_idx, L,
+                                                                        n_b, n_h, nt, nbits);
+  return hipGetLastError();
+}
+
+}  // namespace lsh

@@ -48,17 +48,34 @@ KEY_NORM_FLOOR = 1e-12
 # Step 1: angular LSH (explainer page: random rotation, angular sector)
 # --------------------------------------------------------------------------
 
-def _exact_bucket(x_row: np.ndarray, rot_r: np.ndarray) -> int:
-    """Argmax of [x R ; -x R] in exact rational arithmetic (inputs are binary
-    floating-point numbers, hence exact rationals); lowest index on ties."""
+def _exact_value(x_row: np.ndarray, col: np.ndarray) -> Fraction:
+    """x . col in exact rational arithmetic (binary floating-point inputs are
+    dyadic rationals n / 2^k; the sum is formed over a common power of two)."""
+    terms = []
+    for a, r in zip(x_row.tolist(), col.tolist()):
+        if a == 0.0 or r == 0.0:
+            continue
+        na, da = float(a).as_integer_ratio()
+        nr, dr = float(r).as_integer_ratio()
+        terms.append((na * nr, (da.bit_length() - 1) + (dr.bit_length() - 1)))
+    if not terms:
+        return Fraction(0)
+    K = max(k for _, k in terms)
+    return Fraction(sum(n << (K - k) for n, k in terms), 1 << K)
+
+
+def _exact_bucket(x_row: np.ndarray, rot_r: np.ndarray, candidates=None) -> int:
+    """Argmax of [x R ; -x R] in exact arithmetic, lowest index on ties, over the
+    given entry indices (all 2 * n_b/2 entries when None)."""
     half = rot_r.shape[1]
-    xs = [Fraction(float(a)) for a in x_row]
+    idxs = range(2 * half) if candidates is None else sorted(int(c) for c in candidates)
+    cols = {}
     best_val, best_idx = None, 0
-    cols = []
-    for j in range(half):
-        cols.append(sum(xs[d] * Fraction(float(rot_r[d, j])) for d in range(len(xs))))
-    for idx in range(2 * half):
-        val = cols[idx] if idx < half else -cols[idx - half]
+    for idx in idxs:
+        j = idx % half
+        if j not in cols:
+            cols[j] = _exact_value(x_row, rot_r[:, j])
+        val = cols[j] if idx < half else -cols[j]
         if best_val is None or val > best_val:
             best_val, best_idx = val, idx
     return best_idx
@@ -94,10 +111,13 @@ def hash_buckets(x: np.ndarray, rot: np.ndarray | None, n_buckets: int):
         with np.errstate(divide="ignore", invalid="ignore"):
             margin[r] = np.where(xnorm > 0, gap / xnorm, 0.0)
         # float64 rounding of a D-term dot product is below D * 2^-53 * |x||r_j|;
-        # any gap under a far larger band is re-decided in exact arithmetic.
+        # any gap under a far larger band is re-decided in exact arithmetic,
+        # among the entries within twice the band of the float64 maximum (a
+        # superset of the exact maximisers).
         band = 1e-9 * xnorm * np.max(np.linalg.norm(rot[r], axis=0))
         for i in np.nonzero(gap <= band)[0]:
-            b[i] = _exact_bucket(x[i], rot[r])
+            cand = np.nonzero(c[i] >= c[i, b[i]] - 2.0 * band[i])[0]
+            b[i] = _exact_bucket(x[i], rot[r], cand)
         buckets[r] = b
     return buckets, margin
 

@@ -1,0 +1,123 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects invalid
+arguments on the host before touching the GPU (no compute is launched here)."""
+import ctypes
+import os
+
+import pytest
+
+from lsh_attention_amd import binding as bd
+
+OK, NULL, SHAPE, BUCKETS, UNSUPPORTED, WORKSPACE, ALIAS, HIPERR = 0, -1, -2, -3, -4, -5, -6, -7
+F32, BF16 = 0, 1
+# Distinct fake device addresses: validation must reject the call before any
+# pointer is dereferenced or any HIP call is made.
+P1, P2, P3, P4, P5 = (0x10000000 * k for k in range(1, 6))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bd.library_path()):
+        pytest.fail("liblsh_attn.so is not built; run `python -m lsh_attention_amd.build`")
+    return bd.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = bd.header_functions()
+    assert "reformer_lsh_attn_fwd" in names and len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(bd._SIGS) == set(names)
+
+
+def test_status_strings(L):
+    for s in (OK, NULL, SHAPE, BUCKETS, UNSUPPORTED, WORKSPACE, ALIAS, HIPERR, 99):
+        assert isinstance(L.lsh_status_string(s), bytes) and L.lsh_status_string(s)
+
+
+def _ws(fn, *args):
+    n = ctypes.c_size_t()
+    st = getattr(bd.lib(), fn)(*args, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_sizes(L):
+    st, n1 = _ws("lsh_fwd_workspace_bytes", 1, 8, 65536, 64, 1024, 8, 64, BF16)
+    assert st == OK
+    # buckets, sorted, undo (int32) + o_sorted (bf16) + lse (fp32) per slot at least
+    assert n1 >= 8 * 8 * 65536 * (3 * 4 + 64 * 2 + 4)
+    st, n2 = _ws("lsh_fwd_workspace_bytes", 1, 8, 65536, 64, 1024, 8, 64, F32)
+    assert st == OK and n2 > n1
+    st, h = _ws("lsh_hash_workspace_bytes", 1, 8, 65536, 64, 1024, 8, BF16)
+    assert st == OK and h >= 8 * 512 * 64 * 2
+    st, s = _ws("lsh_sort_workspace_bytes", 1, 8, 65536, 1024, 8)
+    assert st == OK and s >= 8 * 8 * 1024 * 32 * 4
+    assert L.lsh_fwd_workspace_bytes(1, 1, 64, 64, 2, 1, 64, BF16, None) == NULL
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((0, 1, 64, 64, 2, 1, 64, BF16), SHAPE),
+    ((1, 1, 100, 64, 2, 1, 64, BF16), SHAPE),       # L not a multiple of 64
+    ((1, 1, 64, 32, 2, 1, 64, BF16), UNSUPPORTED),  # D != 64
+    ((1, 1, 64, 64, 2, 1, 32, BF16), UNSUPPORTED),  # chunk_len != 64
+    ((1, 1, 64, 64, 2, 1, 0, BF16), SHAPE),
+    ((1, 1, 64, 64, 3, 1, 64, BF16), BUCKETS),      # odd n_b
+    ((1, 1, 64, 64, 0, 1, 64, BF16), BUCKETS),
+    ((1, 1, 64, 64, 8192, 1, 64, BF16), BUCKETS),
+    ((1, 1, 64, 64, 2, 17, 64, BF16), UNSUPPORTED), # n_h > 16
+    ((1, 1, 64, 64, 2, 0, 64, BF16), SHAPE),
+    ((1, 1, 64, 64, 2, 1, 64, 7), UNSUPPORTED),     # dtype
+    ((1024, 1024, 4096, 64, 2, 1, 64, BF16), SHAPE),  # B*H*n_h*L overflows int32
+    ((1, 1, 64, 64, 1, 1, 64, F32), OK),
+    ((1, 1, 64, 64, 4096, 16, 64, BF16), OK),
+])
+def test_shape_validation(L, args, expect):
+    st, _ = _ws("lsh_fwd_workspace_bytes", *args)
+    assert st == expect
+
+
+def test_fused_call_rejects_before_launch(L):
+    st, need = _ws("lsh_fwd_workspace_bytes", 1, 2, 128, 64, 8, 2, 64, BF16)
+    assert st == OK
+    f = L.reformer_lsh_attn_fwd
+    # NULL inputs
+    assert f(None, P2, P3, 8, 2, 64, 0, 1, 2, 128, 64, BF16, P4, None, P5, need, None, None) == NULL
+    assert f(P1, P2, None, 8, 2, 64, 0, 1, 2, 128, 64, BF16, P4, None, P5, need, None, None) == NULL
+    assert f(P1, P2, P3, 8, 2, 64, 0, 1, 2, 128, 64, BF16, None, None, P5, need, None, None) == NULL
+    # rot may be NULL with one bucket only
+    assert f(P1, P2, None, 1, 2, 64, 0, 1, 2, 128, 64, BF16, P4, None, None, 0, None, None) == WORKSPACE
+    # workspace
+    assert f(P1, P2, P3, 8, 2, 64, 0, 1, 2, 128, 64, BF16, P4, None, None, need, None, None) == WORKSPACE
+    assert f(P1, P2, P3, 8, 2, 64, 0, 1, 2, 128, 64, BF16, P4, None, P5, need - 1, None, None) == WORKSPACE
+    # aliasing: out == qk, out inside the workspace, lse on top of v
+    assert f(P1, P2, P3, 8, 2, 64, 0, 1, 2, 128, 64, BF16, P1, None, P5, need, None, None) == ALIAS
+    assert f(P1, P2, P3, 8, 2, 64, 0, 1, 2, 128, 64, BF16, P5 + 256, None, P5, need, None, None) == ALIAS
+    assert f(P1, P2, P3, 8, 2, 64, 0, 1, 2, 128, 64, BF16, P4, P2, P5, need, None, None) == ALIAS
+    # shape errors win over pointer errors
+    assert f(None, None, None, 8, 2, 64, 0, 1, 2, 100, 64, BF16, None, None, None, 0, None, None) == SHAPE
+
+
+def test_stage_calls_reject_before_launch(L):
+    st, hws = _ws("lsh_hash_workspace_bytes", 1, 1, 256, 64, 16, 2, BF16)
+    assert L.lsh_hash(P1, P2, None, 1, 1, 256, 64, 16, 2, BF16, P4, hws, None) == NULL
+    assert L.lsh_hash(P1, P2, P3, 1, 1, 256, 64, 16, 2, BF16, P4, hws - 1, None) == WORKSPACE
+    assert L.lsh_hash(P1, P2, P1, 1, 1, 256, 64, 16, 2, BF16, P4, hws, None) == ALIAS
+    assert L.lsh_hash(P1, P2, P3, 1, 1, 256, 64, 15, 2, BF16, P4, hws, None) == BUCKETS
+    st, sws = _ws("lsh_sort_workspace_bytes", 1, 1, 256, 16, 2)
+    assert L.lsh_sort(P1, P2, P3, 1, 1, 256, 16, 2, P4, sws - 4, None) == WORKSPACE
+    assert L.lsh_sort(P1, P1, P3, 1, 1, 256, 16, 2, P4, sws, None) == ALIAS
+    assert L.lsh_sort(P1, P2, P2, 1, 1, 256, 16, 2, P4, sws, None) == ALIAS
+    assert L.lsh_chunk_attn(P1, P2, P3, P4, None, 1, 1, 256, 64, 2, 64, 0, BF16, None) == NULL
+    assert L.lsh_chunk_attn(P1, P2, P3, P1, P5, 1, 1, 256, 64, 2, 64, 0, BF16, None) == ALIAS
+    assert L.lsh_chunk_attn(P1, P2, P3, P4, P5, 1, 1, 256, 64, 2, 128, 0, BF16, None) == UNSUPPORTED
+    assert L.lsh_unsort_combine(P1, P2, P3, None, None, 1, 1, 256, 64, 2, BF16, None) == NULL
+    assert L.lsh_unsort_combine(P1, P2, P3, P1, None, 1, 1, 256, 64, 2, BF16, None) == ALIAS
+    assert L.lsh_unsort_combine(P1, P2, P3, P4, P4, 1, 1, 256, 64, 2, BF16, None) == ALIAS
+    assert L.lsh_event_create(None) == NULL
+    assert L.lsh_event_elapsed_ms(None, None, None) == NULL
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        bd.reformer_lsh_attn_fwd(x, x, None, 1, 1)

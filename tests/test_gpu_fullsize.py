@@ -1,0 +1,78 @@
+"""Parity at the workloads' full sizes, in the launch configuration the
+benchmark times (the fused call), checked where the oracle can afford it:
+whole problems for the hash and every problem for the sort (bit-exact), and
+sampled chunks and tokens for the floating-point stages."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from _helpers import TOL, f64, lse_check, rel_check, upload
+from lsh_attention_amd import binding as bd
+from lsh_attention_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+FULL = [("single_head_fp32", 1), ("mlm_small_512", 4), ("causal_lm_4k", 4), ("long_seq_64k", 8),
+        ("peaked_vmf_16k", 2), ("peaked_vmf_16k", 8)]
+
+
+def say(*a):
+    print("[gpu-fullsize]", *a, flush=True)
+
+
+@pytest.mark.parametrize("name,n_h", FULL, ids=[f"{n}-h{h}" for n, h in FULL])
+def test_full_size(gpu_lib, name, n_h):
+    inp = I.make_inputs(name, n_hashes=n_h)
+    w = inp.workload
+    B, H, L, D = inp.qk.values.shape
+    n_b, causal, tol = w.n_buckets, w.causal, TOL[w.dtype]
+    say(f"case {name} B{B} H{H} L{L} n_b{n_b} n_h{n_h} causal={causal} {w.dtype} sha(qk)={inp.meta['qk_sha256'][:12]}")
+    qk, v, rot = upload(inp)
+    out_f, lse_f = bd.reformer_lsh_attn_fwd(qk, v, rot, n_b, n_h, 64, causal)
+    buckets = bd.lsh_hash(qk, rot, n_b, n_h)
+    sidx, undo = bd.lsh_sort(buckets, n_b)
+    o_s, l_s = bd.lsh_chunk_attn(qk, v, sidx, n_h, 64, causal)
+    out, lse = bd.lsh_unsort_combine(o_s, l_s, undo)
+    torch.cuda.synchronize()
+    assert torch.equal(out_f, out) and torch.equal(lse_f, lse)
+    del out_f, lse_f
+    say("  fused == staged")
+
+    gb, gs, gu = buckets.cpu().numpy(), sidx.cpu().numpy(), undo.cpu().numpy()
+    rng = np.random.default_rng(2024)
+    problems = [(int(b), int(h)) for b, h in zip(rng.integers(0, B, 2), rng.integers(0, H, 2))]
+    rot64 = None if inp.rot is None else inp.rot.values.astype(np.float64)
+    near = 0
+    for b, h in problems:
+        ob, margin = O.hash_buckets(inp.qk.values[b, h].astype(np.float64), rot64, n_b)
+        near += int(np.sum(margin < 1e-6))
+        np.testing.assert_array_equal(gb[b, h], ob, err_msg=f"buckets b{b} h{h}")
+    say(f"  hash bit-exact on problems {problems}; oracle near-ties {near}")
+
+    for b in range(B):
+        for h in range(H):
+            os_, ou = O.sort_by_bucket(gb[b, h].astype(np.int64))
+            if not (np.array_equal(gs[b, h], os_) and np.array_equal(gu[b, h], ou)):
+                raise AssertionError(f"permutation mismatch at b{b} h{h}")
+    say("  sort bit-exact on every problem")
+
+    n_chunks = n_h * L // 64
+    for b, h in problems:
+        x = inp.qk.values[b, h].astype(np.float64)
+        vv = inp.v.values[b, h].astype(np.float64)
+        chunks = sorted(set(rng.integers(0, n_chunks, 24).tolist()) | {0, n_chunks - 1})
+        oo, ol = O.chunk_attention(x, vv, gs[b, h].astype(np.int64), 64, causal, chunks=chunks)
+        rows = np.concatenate([np.arange(c * 64, c * 64 + 64) for c in chunks])
+        rel_check(f64(o_s[b, h, torch.as_tensor(rows, device="cuda")]), oo[rows], tol, f"o_sorted b{b} h{h}")
+        lse_check(f64(l_s[b, h, torch.as_tensor(rows, device="cuda")]), ol[rows], f"lse_sorted b{b} h{h}")
+        toks = sorted(set(rng.integers(0, L, 48).tolist()) | {0, L - 1})
+        ref_o = np.empty((len(toks), D))
+        ref_l = np.empty(len(toks))
+        for k, i in enumerate(toks):
+            ref_o[k], ref_l[k] = O.token_output(x, vv, gs[b, h].astype(np.int64), gu[b, h].astype(np.int64), 64,
+                                                causal, i)
+        ti = torch.as_tensor(toks, device="cuda")
+        rel_check(f64(out[b, h, ti]), ref_o, tol, f"out b{b} h{h}")
+        lse_check(f64(lse[b, h, ti]), ref_l, f"lse b{b} h{h}")
+    say("  sampled chunks and tokens within tolerance")

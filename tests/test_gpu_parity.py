@@ -1,0 +1,189 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI.
+
+Integer results (buckets, permutations) must match bit for bit; the hash is
+decided exactly on both sides, and oracle near-ties (margin < 1e-6 on the unit
+vector) are counted and printed.  Each floating-point stage is fed the GPU's
+own upstream results, so a stage is judged on its own; the fused call is also
+checked end to end against the oracle's own forward pass.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from _helpers import TOL, f64, lse_check, rel_check, to_device, upload
+from lsh_attention_amd import binding as bd
+from lsh_attention_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu-parity]", *a, flush=True)
+
+
+def run_stages(qk, v, rot, n_b, n_h, causal):
+    buckets = bd.lsh_hash(qk, rot, n_b, n_h)
+    sorted_idx, undo_idx = bd.lsh_sort(buckets, n_b)
+    o_sorted, lse_sorted = bd.lsh_chunk_attn(qk, v, sorted_idx, n_h, 64, causal)
+    out, lse = bd.lsh_unsort_combine(o_sorted, lse_sorted, undo_idx)
+    torch.cuda.synchronize()
+    return buckets, sorted_idx, undo_idx, o_sorted, lse_sorted, out, lse
+
+
+REDUCED = [
+    ("single_head_fp32", dict(), 1),
+    ("mlm_small_512", dict(B=4, H=2), 4),
+    ("causal_lm_4k", dict(B=1, H=2), 4),
+    ("long_seq_64k", dict(B=1, H=2, L=4160), 8),   # 3 sort tiles, ragged hash block
+    ("peaked_vmf_16k", dict(B=1, H=2), 2),
+    ("peaked_vmf_16k", dict(B=1, H=2), 8),
+]
+
+
+@pytest.mark.parametrize("name,shape,n_h", REDUCED, ids=[f"{n}-h{h}" for n, _, h in REDUCED])
+def test_all_stages_match_oracle(gpu_lib, name, shape, n_h):
+    inp = I.make_inputs(name, n_hashes=n_h, **shape)
+    w = inp.workload
+    B, H, L, _ = inp.qk.values.shape
+    say(f"case {name} B{B} H{H} L{L} n_b{w.n_buckets} n_h{n_h} causal={w.causal} {w.dtype}")
+    qk, v, rot = upload(inp)
+    buckets, sidx, undo, o_s, l_s, out, lse = run_stages(qk, v, rot, w.n_buckets, n_h, w.causal)
+    out_f, lse_f = bd.reformer_lsh_attn_fwd(qk, v, rot, w.n_buckets, n_h, 64, w.causal)
+    torch.cuda.synchronize()
+    # The fused call runs the same kernels: identical bits.
+    assert torch.equal(out_f, out) and torch.equal(lse_f, lse)
+    tol = TOL[w.dtype]
+    gb, gs, gu = buckets.cpu().numpy(), sidx.cpu().numpy(), undo.cpu().numpy()
+    go, gl, gout, glse = f64(o_s), f64(l_s), f64(out), f64(lse)
+    rot64 = None if inp.rot is None else inp.rot.values.astype(np.float64)
+    near = 0
+    for b in range(B):
+        for h in range(H):
+            x = inp.qk.values[b, h].astype(np.float64)
+            vv = inp.v.values[b, h].astype(np.float64)
+            ob, margin = O.hash_buckets(x, rot64, w.n_buckets)
+            near += int(np.sum(margin < 1e-6))
+            np.testing.assert_array_equal(gb[b, h], ob, err_msg=f"buckets b{b} h{h}")
+            os_, ou = O.sort_by_bucket(gb[b, h].astype(np.int64))
+            np.testing.assert_array_equal(gs[b, h], os_, err_msg=f"sorted_idx b{b} h{h}")
+            np.testing.assert_array_equal(gu[b, h], ou, err_msg=f"undo_idx b{b} h{h}")
+            oo, ol = O.chunk_attention(x, vv, gs[b, h].astype(np.int64), 64, w.causal)
+            rel_check(go[b, h], oo, tol, f"o_sorted b{b} h{h}")
+            lse_check(gl[b, h], ol, f"lse_sorted b{b} h{h}")
+            co, cl = O.unsort_combine(go[b, h], gl[b, h], gu[b, h].astype(np.int64))
+            rel_check(gout[b, h], co, tol, f"combine b{b} h{h}")
+            lse_check(glse[b, h], cl, f"combine lse b{b} h{h}")
+            ref = O.forward_problem(x, vv, rot64, w.n_buckets, n_h, 64, w.causal)
+            rel_check(gout[b, h], ref["out"], tol, f"end-to-end b{b} h{h}")
+            lse_check(glse[b, h], ref["lse"], f"end-to-end lse b{b} h{h}")
+    say(f"  ok; oracle near-ties (margin < 1e-6): {near} of {B * H * n_h * L} token-rounds")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n_h", [1, 3])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_one_bucket_one_chunk_equals_full_attention(gpu_lib, dtype, n_h, causal):
+    """n_b = 1 and L = chunk_len = 64: the fused pass is dense attention."""
+    say(f"case brute-force {dtype} n_h{n_h} causal={causal}")
+    qk_t = I.gaussian(77, (1, 2, 64, 64), dtype)
+    v_t = I.gaussian(78, (1, 2, 64, 64), dtype)
+    out, lse = bd.reformer_lsh_attn_fwd(to_device(qk_t), to_device(v_t), None, 1, n_h, 64, causal)
+    torch.cuda.synchronize()
+    for h in range(2):
+        fo, fl = O.full_attention(qk_t.values[0, h].astype(np.float64), v_t.values[0, h].astype(np.float64), causal)
+        rel_check(f64(out)[0, h], fo, TOL[dtype], f"brute force h{h}")
+        lse_check(f64(lse)[0, h], fl + np.log(2 * n_h), f"brute force lse h{h}")
+
+
+def _tie_inputs(dtype, L=320):
+    """Rotations with duplicated and negated columns and tokens placed on them,
+    plus zero rows: every kind of exact tie of [p ; -p]."""
+    rng = np.random.default_rng(5)
+    n_h, half = 2, 16
+    rot = rng.standard_normal((n_h, 64, half)).astype(np.float32)
+    rot[:, :, 9] = rot[:, :, 2]
+    rot[:, :, 11] = -rot[:, :, 4]
+    rot[:, :, 15] = rot[:, :, 15] * 0
+    x = rng.standard_normal((1, 1, L, 64)).astype(np.float32)
+    x[0, 0, 0::5] = rot[0, :, 2]
+    x[0, 0, 1::5] = -rot[0, :, 4]
+    x[0, 0, 2::5] = 0.0
+    x[0, 0, 3::5] = rot[1, :, 11]
+    if dtype == "bf16":
+        rt = I.Tensor(I.f32_from_bf16_bits(I.bf16_bits_from_f32(rot)), I.bf16_bits_from_f32(rot))
+        xt = I.Tensor(I.f32_from_bf16_bits(I.bf16_bits_from_f32(x)), I.bf16_bits_from_f32(x))
+    else:
+        rt, xt = I.Tensor(rot), I.Tensor(x)
+    return xt, rt, 2 * half, n_h
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_exact_ties_take_lowest_index(gpu_lib, dtype):
+    xt, rt, n_b, n_h = _tie_inputs(dtype)
+    say(f"case exact ties {dtype}")
+    got = bd.lsh_hash(to_device(xt), to_device(rt), n_b, n_h).cpu().numpy()
+    ref, _ = O.hash_buckets(xt.values[0, 0].astype(np.float64), rt.values.astype(np.float64), n_b)
+    np.testing.assert_array_equal(got[0, 0], ref)
+    assert np.all(got[0, 0, 0, 0::5] == 2)           # +p_2 ties +p_9
+    assert np.all(got[0, 0, :, 2::5] == 0)           # zero vector
+
+
+def test_every_token_needs_the_exact_path(gpu_lib):
+    """All rotation columns come in identical pairs, so every token's top two
+    scores tie and every token-round goes through the float64 re-decision."""
+    say("case all-tied fixup queue")
+    rng = np.random.default_rng(8)
+    half, n_h = 64, 2
+    base = rng.standard_normal((n_h, 64, half // 2)).astype(np.float32)
+    rot = np.repeat(base, 2, axis=2)
+    rt = I.Tensor(I.f32_from_bf16_bits(I.bf16_bits_from_f32(rot)), I.bf16_bits_from_f32(rot))
+    xt = I.gaussian(9, (2, 2, 576, 64), "bf16")
+    got = bd.lsh_hash(to_device(xt), to_device(rt), 2 * half, n_h).cpu().numpy()
+    for b in range(2):
+        for h in range(2):
+            ref, _ = O.hash_buckets(xt.values[b, h].astype(np.float64), rt.values.astype(np.float64), 2 * half)
+            np.testing.assert_array_equal(got[b, h], ref)
+    assert np.all(got % 2 == 0)  # the lower index of each identical pair
+
+
+@pytest.mark.parametrize("n_b,n_h,L", [(2, 1, 64), (4096, 2, 4096), (8, 16, 128), (64, 1, 64)])
+def test_extreme_bucket_and_round_counts(gpu_lib, n_b, n_h, L):
+    say(f"case extremes n_b{n_b} n_h{n_h} L{L}")
+    qk_t = I.gaussian(31, (1, 2, L, 64), "bf16")
+    v_t = I.gaussian(32, (1, 2, L, 64), "bf16")
+    rot_t = I.rotations(33, n_h, 64, n_b, "bf16")
+    qk, v, rot = to_device(qk_t), to_device(v_t), to_device(rot_t)
+    for causal in (False, True):
+        out, lse = bd.reformer_lsh_attn_fwd(qk, v, rot, n_b, n_h, 64, causal)
+        torch.cuda.synchronize()
+        for h in range(2):
+            ref = O.forward_problem(qk_t.values[0, h].astype(np.float64), v_t.values[0, h].astype(np.float64),
+                                    rot_t.values.astype(np.float64), n_b, n_h, 64, causal)
+            rel_check(f64(out)[0, h], ref["out"], TOL["bf16"], f"out h{h} causal={causal}")
+            lse_check(f64(lse)[0, h], ref["lse"], f"lse h{h}")
+
+
+def test_repeatable_bits(gpu_lib):
+    inp = I.make_inputs("causal_lm_4k", B=2, H=2, L=1024)
+    say("case determinism")
+    qk, v, rot = upload(inp)
+    a = bd.reformer_lsh_attn_fwd(qk, v, rot, 64, 4, 64, True)
+    b = bd.reformer_lsh_attn_fwd(qk, v, rot, 64, 4, 64, True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_caller_stream_and_workspace_reuse(gpu_lib):
+    """Work runs on the caller's stream; one workspace serves repeated calls."""
+    inp = I.make_inputs("mlm_small_512", B=2, H=2)
+    say("case side stream")
+    qk, v, rot = upload(inp)
+    ws = torch.empty(bd.fwd_workspace_bytes(2, 2, 512, 64, 8, 4, 64, bd.LSH_BF16), dtype=torch.uint8, device="cuda")
+    ref = bd.reformer_lsh_attn_fwd(qk, v, rot, 8, 4, workspace=ws)[0].clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        got = bd.reformer_lsh_attn_fwd(qk, v, rot, 8, 4, workspace=ws)[0]
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
