@@ -49,6 +49,20 @@ def algorithmic_work(B, H, L, D, n_b, n_h, es):
     }
 
 
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE record (profiles/traffic_<workload>.json), or None when there is
+    no record or the kernel's source has changed since it was taken."""
+    from lsh_attention_amd.prof_summary import source_sha256
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get("kernels", {}).get(kernel)
+    if rec is None or rec.get("source_sha256") != source_sha256(kernel):
+        return None
+    return rec["traffic_bytes"]
+
+
 def cpu_baseline(inp, max_seconds: float = 30.0):
     """The oracle, untouched, on a bounded sample: one (batch, head) problem of
     the same workload at full length; tokens/s scaled to the whole batch."""
@@ -80,6 +94,9 @@ def main():
     ap.add_argument("--workload", default="long_seq_64k")
     ap.add_argument("--n-hashes", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, run one plain device-to-device copy of this many MiB "
+                         "(a reference kernel of known traffic for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the forward pass is not sharded across GPUs in this build "
@@ -135,6 +152,13 @@ def main():
     value = tokens / (elapsed / args.steps)
     log(f"{args.steps} steps: {ms_per_step:.4f} ms/step wall, {gpu_ms:.4f} ms/step between first and last event")
 
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     work = algorithmic_work(B, H, L, D, n_b, n_h, es)
     peak_flops = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
     kernels = {}
@@ -163,7 +187,7 @@ def main():
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["kernel"] = dom
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(w.name, dom)
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

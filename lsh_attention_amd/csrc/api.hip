@@ -49,13 +49,13 @@ struct Carver {
 };
 
 struct HashWs {
-  size_t rot_t, rho, fix_count, fix_queue, total;
+  size_t rot_t, colmax, fix_count, fix_queue, total;
 };
 HashWs hash_ws(int BH, int L, int n_b, int n_h, lsh_dtype dt) {
   Carver c;
   HashWs w;
   w.rot_t = c.take((size_t)n_h * padded_half(n_b) * kD * elem_size(dt));
-  w.rho = c.take((size_t)n_h * sizeof(float));
+  w.colmax = c.take((size_t)n_h * colmax_blocks(n_b) * sizeof(float));
   w.fix_count = c.take(sizeof(int));
   w.fix_queue = c.take((size_t)BH * n_h * L * sizeof(int));
   w.total = c.off;
@@ -103,15 +103,15 @@ hipError_t enqueue_hash(const void* qk, const void* rot, int32_t* buckets, char*
     if ((e = mark()) != hipSuccess) return e;
     return mark();
   }
-  float* rho = (float*)(ws + w.rho);
+  float* colmax = (float*)(ws + w.colmax);
   int* count = (int*)(ws + w.fix_count);
   int* queue = (int*)(ws + w.fix_queue);
   void* rot_t = ws + w.rot_t;
-  if ((e = launch_prep(rot, rot_t, rho, count, n_h, n_b, dt, s)) != hipSuccess) return e;
+  if ((e = launch_prep(rot, rot_t, colmax, count, n_h, n_b, dt, s)) != hipSuccess) return e;
   if ((e = mark()) != hipSuccess) return e;
-  if ((e = launch_hash(qk, rot_t, rho, buckets, queue, count, BH, L, n_b, n_h, dt, s)) != hipSuccess) return e;
+  if ((e = launch_hash(qk, rot_t, colmax, buckets, queue, count, BH, L, n_b, n_h, dt, s)) != hipSuccess) return e;
   if ((e = mark()) != hipSuccess) return e;
-  if ((e = launch_fixup(qk, rot, buckets, queue, count, L, n_b, n_h, dt, s)) != hipSuccess) return e;
+  if ((e = launch_fixup(qk, rot_t, buckets, queue, count, L, n_b, n_h, dt, s)) != hipSuccess) return e;
   return mark();
 }
 

@@ -13,28 +13,38 @@
 // log-sum-exp.
 //
 // gfx950 design (one block of 4 waves walks a run of consecutive chunks of one
-// (batch, head)):
-//  * The 64 rows of x and v of each chunk are gathered once (128-byte rows,
-//    addressed through sorted_idx) into LDS; the previous chunk's rows stay
-//    resident from the previous iteration (two-slot ring), so each chunk is
-//    read from HBM/L2 once per block instead of twice.
+// (batch, head); wave w owns queries 16w..16w+15 of the current chunk):
+//  * Gathers are software-pipelined: the 64 x rows and 64 v rows of chunk c+1
+//    (128-byte rows addressed through sorted_idx) are loaded into registers
+//    while chunk c is computed, then written to LDS.  The previous chunk's
+//    rows stay resident (two-slot ring), so each row is gathered once per
+//    block.  The block's slice of sorted_idx is staged in LDS up front.
+//  * V is stored transposed in LDS for the P.V product.  Each thread gathers
+//    one 4-byte word (two dims) from each of 8 rows and writes two 16-byte
+//    rows of V^T, so the transpose costs 2 LDS writes per thread per chunk.
 //  * S^T = K Q^T on MFMA (keys are MFMA rows, queries MFMA columns), so each
-//    lane holds one query's logits for 4 consecutive keys per 16-key tile; the
-//    softmax reductions are two cross-lane steps.
-//  * O^T = V^T P^T on MFMA: the P^T operand is exactly the lane's own logits
-//    (the K index is permuted to match), V is kept transposed in LDS.
-//  * Key norms are applied to the fp32 logits (raw bf16 keys feed the MFMA),
-//    so no rounded normalised keys enter the product.
-//  * The softmax runs in base 2 on v_exp_f32.
+//    lane holds one query's logits for 4 consecutive keys per 16-key tile.
+//  * O^T = V^T P^T on MFMA: the P^T operand is exactly the lane's own
+//    probabilities (the K index is permuted to match).
+//  * Softmax offset: keys are unit-normalised, so every logit is at most
+//    M_i = |x_i| / sqrt(64) (Cauchy-Schwarz).  Offsetting by M_i instead of the
+//    row maximum gives the same softmax and lse, needs no max reduction, and
+//    the self / causal masks become one compare that zeroes the probability.
+//    If a row's sum falls below 2^-60 (only a self-only row, or keys far from
+//    the query's direction at huge norms), the wave recomputes that chunk with
+//    the row maximum and the explicit -1e5 self logit.
 #include "lsh_internal.h"
 
 namespace lsh {
 
 namespace {
 
-constexpr int kChunksPerBlock = 8;
+constexpr int kChunksPerBlock = 16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kScale2 = 0.125f * kLog2e;        // 1/sqrt(64), base 2
+constexpr float kSelf2 = -1.0e5f * kLog2e;        // self logit, base 2
+constexpr float kMinSum = 0x1p-60f;               // fast-path validity threshold
 
 template <bool BF16>
 struct AttnTraits;
@@ -43,19 +53,19 @@ struct AttnTraits<true> {
   using T = uint16_t;
   static constexpr int kXRow = 72;   // x rows in LDS: 64 dims + 8 pad (144 B)
   static constexpr int kVRow = 136;  // V^T rows in LDS: 128 keys + 8 pad (272 B)
-  static constexpr int kPer16 = 8;   // elements per 16-byte load
+  static constexpr int kXLoads = 2;  // 16-byte loads per thread for its 16 dims of an x row
+  static constexpr int kVWords = 8;  // 4-byte V words per thread (2 dims x 8 rows)
 };
 template <>
 struct AttnTraits<false> {
   using T = float;
   static constexpr int kXRow = 68;
   static constexpr int kVRow = 132;
-  static constexpr int kPer16 = 4;
+  static constexpr int kXLoads = 4;
+  static constexpr int kVWords = 16;  // 1 dim x 16 rows
 };
 
-__device__ inline uint16_t f32_to_bf16_bits(float f) {
-  return __builtin_bit_cast(uint16_t, (__bf16)f);
-}
+__device__ inline uint16_t f32_to_bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 template <bool BF16, bool CAUSAL>
 __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTraits<BF16>::T* __restrict__ qk,
@@ -67,77 +77,123 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
   using T = typename AttnTraits<BF16>::T;
   constexpr int kXRow = AttnTraits<BF16>::kXRow;
   constexpr int kVRow = AttnTraits<BF16>::kVRow;
-  constexpr int kPer16 = AttnTraits<BF16>::kPer16;
+  constexpr int kXLoads = AttnTraits<BF16>::kXLoads;
+  constexpr int kVWords = AttnTraits<BF16>::kVWords;
   __shared__ __attribute__((aligned(16))) T sX[2][64 * kXRow];
   __shared__ __attribute__((aligned(16))) T sVT[64 * kVRow];  // [dim][64 * slot + key]
-  __shared__ __attribute__((aligned(16))) float sInv[2][64];
-  __shared__ __attribute__((aligned(16))) int sPos[2][64];
+  __shared__ __attribute__((aligned(16))) float sKs[2][64];   // key scale: log2(e) / (8 |x_j|)
+  __shared__ __attribute__((aligned(16))) float sM[2][64];    // query bound: log2(e) |x_i| / 8
+  __shared__ __attribute__((aligned(16))) int sPos[kChunksPerBlock + 1][64];
 
   const int bh = blockIdx.x / blocks_per_bh;
   const int c0 = (blockIdx.x % blocks_per_bh) * kChunksPerBlock;
   const int c1 = min(n_chunks, c0 + kChunksPerBlock);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15;  // query (column) of the MFMA tiles
   const int grp = lane >> 4;  // 4-key group within a 16-key tile
 
   const T* xq = qk + (size_t)bh * L * kD;
   const T* vq = v + (size_t)bh * L * kD;
   const int32_t* sidx = sorted_idx + (size_t)bh * n_slots;
+  T* obase = o_sorted + (size_t)bh * n_slots * kD;
+  float* lbase = lse_sorted + (size_t)bh * n_slots;
 
-  // Gather chunk c into ring slot `slot`: thread t loads 16 dims of row t/4.
-  auto load_chunk = [&](int c, int slot) {
-    const int row = threadIdx.x >> 2, quarter = threadIdx.x & 3;
-    // Positions come from a permutation of [0, L); the clamp only keeps a
-    // malformed index array from reading out of bounds.
-    const int pos = (int)min((uint32_t)sidx[(size_t)c * kChunk + row], (uint32_t)(L - 1));
-    const T* xr = xq + (size_t)pos * kD + 16 * quarter;
-    const T* vr = vq + (size_t)pos * kD + 16 * quarter;
-    float ss = 0.f;
-    constexpr int kLoads = 16 / kPer16;
-    uint4 xv[kLoads], vv[kLoads];
-    for (int k = 0; k < kLoads; ++k) {
-      xv[k] = *(const uint4*)(xr + k * kPer16);
-      vv[k] = *(const uint4*)(vr + k * kPer16);
+  // Positions of the previous chunk of c0 and of chunks c0..c1-1 (entry k <-> chunk c0-1+k).
+  // Positions come from a permutation of [0, L); the clamp only keeps a
+  // malformed index array from reading out of bounds.
+  for (int e = tid; e < (c1 - c0 + 1) * 64; e += 256) {
+    const int k = e >> 6, r = e & 63;
+    const int c = (k == 0) ? (c0 - 1 + n_chunks) % n_chunks : c0 - 1 + k;
+    sPos[k][r] = (int)min((uint32_t)sidx[(size_t)c * kChunk + r], (uint32_t)(L - 1));
+  }
+  __syncthreads();
+
+  // ---- gather of one chunk into registers, and from registers into LDS ----
+  // x: thread t holds 16 dims (quarter t&3) of row t>>2.
+  // v: bf16: dims 2p, 2p+1 (p = t&31) of rows 8(t>>5)..+7; fp32: dim t&63 of rows 16(t>>6)..+15.
+  uint4 xr[kXLoads];
+  uint32_t vw[kVWords];
+  const int xrow = tid >> 2, xq4 = tid & 3;
+  auto gather = [&](int k) {
+    const int* pos = sPos[k];
+    const T* xs = xq + (size_t)pos[xrow] * kD + 16 * xq4;
+#pragma unroll
+    for (int i = 0; i < kXLoads; ++i) xr[i] = *(const uint4*)(xs + i * (16 / kXLoads));
+    if constexpr (BF16) {
+      const int p = tid & 31, r0 = 8 * (tid >> 5);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vw[i] = *(const uint32_t*)(vq + (size_t)pos[r0 + i] * kD + 2 * p);
+    } else {
+      const int p = tid & 63, r0 = 16 * (tid >> 6);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) vw[i] = __float_as_uint(vq[(size_t)pos[r0 + i] * kD + p]);
     }
-    for (int k = 0; k < kLoads; ++k) {
-      *(uint4*)(&sX[slot][row * kXRow + 16 * quarter + k * kPer16]) = xv[k];
-      const uint32_t xw[4] = {xv[k].x, xv[k].y, xv[k].z, xv[k].w};
-      const uint32_t vw[4] = {vv[k].x, vv[k].y, vv[k].z, vv[k].w};
-      if constexpr (BF16) {
-        for (int e = 0; e < 4; ++e) {
-          const float lo = __uint_as_float(xw[e] << 16), hi = __uint_as_float(xw[e] & 0xFFFF0000u);
+  };
+  auto commit = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < kXLoads; ++i)
+      *(uint4*)(&sX[slot][xrow * kXRow + 16 * xq4 + i * (16 / kXLoads)]) = xr[i];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < kXLoads; ++i) {
+      const uint32_t w4[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (BF16) {
+          const float lo = __uint_as_float(w4[e] << 16), hi = __uint_as_float(w4[e] & 0xFFFF0000u);
           ss = fmaf(lo, lo, ss);
           ss = fmaf(hi, hi, ss);
-          const int d = 16 * quarter + k * 8 + 2 * e;
-          sVT[d * kVRow + 64 * slot + row] = (uint16_t)(vw[e] & 0xFFFFu);
-          sVT[(d + 1) * kVRow + 64 * slot + row] = (uint16_t)(vw[e] >> 16);
-        }
-      } else {
-        for (int e = 0; e < 4; ++e) {
-          const float f = __uint_as_float(xw[e]);
+        } else {
+          const float f = __uint_as_float(w4[e]);
           ss = fmaf(f, f, ss);
-          const int d = 16 * quarter + k * 4 + e;
-          sVT[d * kVRow + 64 * slot + row] = __uint_as_float(vw[e]);
         }
       }
     }
     ss += __shfl_xor(ss, 1);
     ss += __shfl_xor(ss, 2);
-    if (quarter == 0) {
-      sInv[slot][row] = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
-      sPos[slot][row] = pos;
+    if (xq4 == 0) {
+      const float nrm = sqrtf(ss);
+      sKs[slot][xrow] = kScale2 / fmaxf(nrm, 1e-12f);
+      sM[slot][xrow] = kScale2 * nrm;
+    }
+    if constexpr (BF16) {
+      const int p = tid & 31, r0 = 8 * (tid >> 5);
+      // low halves = dim 2p, high halves = dim 2p+1, of rows r0..r0+7
+      uint4 lo, hi;
+      lo.x = __builtin_amdgcn_perm(vw[1], vw[0], 0x05040100u);
+      lo.y = __builtin_amdgcn_perm(vw[3], vw[2], 0x05040100u);
+      lo.z = __builtin_amdgcn_perm(vw[5], vw[4], 0x05040100u);
+      lo.w = __builtin_amdgcn_perm(vw[7], vw[6], 0x05040100u);
+      hi.x = __builtin_amdgcn_perm(vw[1], vw[0], 0x07060302u);
+      hi.y = __builtin_amdgcn_perm(vw[3], vw[2], 0x07060302u);
+      hi.z = __builtin_amdgcn_perm(vw[5], vw[4], 0x07060302u);
+      hi.w = __builtin_amdgcn_perm(vw[7], vw[6], 0x07060302u);
+      *(uint4*)(&sVT[(2 * p) * kVRow + 64 * slot + r0]) = lo;
+      *(uint4*)(&sVT[(2 * p + 1) * kVRow + 64 * slot + r0]) = hi;
+    } else {
+      const int p = tid & 63, r0 = 16 * (tid >> 6);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *(uint4*)(&sVT[p * kVRow + 64 * slot + r0 + 4 * i]) =
+            make_uint4(vw[4 * i], vw[4 * i + 1], vw[4 * i + 2], vw[4 * i + 3]);
     }
   };
 
-  load_chunk((c0 - 1 + n_chunks) % n_chunks, (c0 + 1) & 1);
+  gather(0);
+  commit((c0 + 1) & 1);
+  gather(1);
+  commit(c0 & 1);
+  __syncthreads();
 
   for (int c = c0; c < c1; ++c) {
     const int cur = c & 1, prv = cur ^ 1;
-    load_chunk(c, cur);
-    __syncthreads();
+    const int kc = c - c0 + 1;  // sPos entry of chunk c
+    if (c + 1 < c1) gather(kc + 1);
 
     const int qrow = 16 * wave + col;  // this lane's query row in the current chunk
-    const int qpos = sPos[cur][qrow];
+    const int qpos = sPos[kc][qrow];
+    const float M2 = sM[cur][qrow];
 
     // ---- S^T = K Q^T : 8 key tiles of 16 (tiles 0-3 previous chunk, 4-7 current) ----
     f32x4 acc[8];
@@ -156,14 +212,19 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
     } else {
       // k-step s of 4 dims: lane group g feeds dim 16g + s.
       float bq[16];
+#pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
         const float4 t = *(const float4*)(&sX[cur][qrow * kXRow + 16 * grp + 4 * s4]);
-        bq[4 * s4] = t.x; bq[4 * s4 + 1] = t.y; bq[4 * s4 + 2] = t.z; bq[4 * s4 + 3] = t.w;
+        bq[4 * s4] = t.x;
+        bq[4 * s4 + 1] = t.y;
+        bq[4 * s4 + 2] = t.z;
+        bq[4 * s4 + 3] = t.w;
       }
 #pragma unroll
       for (int kt = 0; kt < 8; ++kt) {
         const T* kr = &sX[kt < 4 ? prv : cur][(16 * (kt & 3) + col) * kXRow + 16 * grp];
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
           const float4 t = *(const float4*)(kr + 4 * s4);
           z = __builtin_amdgcn_mfma_f32_16x16x4f32(t.x, bq[4 * s4 + 0], z, 0, 0, 0);
@@ -175,43 +236,67 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
       }
     }
 
-    // ---- logits in base 2, masks, row max ----
-    constexpr float kScale = 0.125f * kLog2e;         // 1/sqrt(64), base 2
-    constexpr float kSelf = -1.0e5f * kLog2e;          // self logit, base 2
-    float mx = -INFINITY;
+    // ---- probabilities, offset by the a-priori bound M2 ----
+    float p[8][4];
+    float sum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
       const int slot = kt < 4 ? prv : cur;
       const int kr0 = 16 * (kt & 3) + 4 * grp;
-      const float4 inv = *(const float4*)(&sInv[slot][kr0]);
-      const int4 kp = *(const int4*)(&sPos[slot][kr0]);
-      const float iv[4] = {inv.x, inv.y, inv.z, inv.w};
+      const float4 ks = *(const float4*)(&sKs[slot][kr0]);
+      const int4 kp = *(const int4*)(&sPos[kt < 4 ? kc - 1 : kc][kr0]);
+      const float ksv[4] = {ks.x, ks.y, ks.z, ks.w};
       const int kpos[4] = {kp.x, kp.y, kp.z, kp.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float s = acc[kt][e] * (iv[e] * kScale);
-        if (kpos[e] == qpos) s = kSelf;
-        if (CAUSAL && kpos[e] > qpos) s = -INFINITY;
-        acc[kt][e] = s;
-        mx = fmaxf(mx, s);
+        const float q = __builtin_amdgcn_exp2f(fmaf(acc[kt][e], ksv[e], -M2));
+        const bool drop = CAUSAL ? (kpos[e] >= qpos) : (kpos[e] == qpos);
+        p[kt][e] = drop ? 0.f : q;
+        sum += p[kt][e];
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    float sum = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 8; ++kt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p = __builtin_amdgcn_exp2f(acc[kt][e] - mx);
-        acc[kt][e] = p;
-        sum += p;
-      }
     sum += __shfl_xor(sum, 16);
     sum += __shfl_xor(sum, 32);
+    float off = M2;
+    const bool slow = !(sum >= kMinSum);
+    if (__ballot(slow) != 0ull) {
+      // Exact path for the wave: logits with the -1e5 self value, row maximum.
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 8; ++kt) {
+        const int slot = kt < 4 ? prv : cur;
+        const int kr0 = 16 * (kt & 3) + 4 * grp;
+        const float4 ks = *(const float4*)(&sKs[slot][kr0]);
+        const int4 kp = *(const int4*)(&sPos[kt < 4 ? kc - 1 : kc][kr0]);
+        const float ksv[4] = {ks.x, ks.y, ks.z, ks.w};
+        const int kpos[4] = {kp.x, kp.y, kp.z, kp.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float s = acc[kt][e] * ksv[e];
+          if (kpos[e] == qpos) s = kSelf2;
+          if (CAUSAL && kpos[e] > qpos) s = -INFINITY;
+          p[kt][e] = s;
+          mx = fmaxf(mx, s);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      sum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[kt][e] = __builtin_amdgcn_exp2f(p[kt][e] - mx);
+          sum += p[kt][e];
+        }
+      sum += __shfl_xor(sum, 16);
+      sum += __shfl_xor(sum, 32);
+      off = mx;
+    }
 
     // ---- O^T = V^T P^T ----
     f32x4 oacc[4];
+#pragma unroll
     for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (BF16) {
 #pragma unroll
@@ -220,8 +305,8 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
         bf16x8 bp;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          bp[e] = (__bf16)acc[2 * ks][e];
-          bp[4 + e] = (__bf16)acc[2 * ks + 1][e];
+          bp[e] = (__bf16)p[2 * ks][e];
+          bp[4 + e] = (__bf16)p[2 * ks + 1][e];
         }
         const int slot = ks < 2 ? prv : cur;
         const int kc0 = 64 * slot + 16 * ((2 * ks) & 3) + 4 * grp;
@@ -239,14 +324,14 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
 #pragma unroll
       for (int kt = 0; kt < 8; ++kt) {
         const int slot = kt < 4 ? prv : cur;
-        const int kc = 64 * slot + 16 * (kt & 3) + 4 * grp;
+        const int kcol = 64 * slot + 16 * (kt & 3) + 4 * grp;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const float4 a = *(const float4*)(&sVT[(16 * dt + col) * kVRow + kc]);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, acc[kt][0], oacc[dt], 0, 0, 0);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, acc[kt][1], oacc[dt], 0, 0, 0);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, acc[kt][2], oacc[dt], 0, 0, 0);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, acc[kt][3], oacc[dt], 0, 0, 0);
+          const float4 a = *(const float4*)(&sVT[(16 * dt + col) * kVRow + kcol]);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, p[kt][0], oacc[dt], 0, 0, 0);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, p[kt][1], oacc[dt], 0, 0, 0);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, p[kt][2], oacc[dt], 0, 0, 0);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, p[kt][3], oacc[dt], 0, 0, 0);
         }
       }
     }
@@ -254,7 +339,7 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
     // ---- normalise and store: lane holds dims 16 dt + 4 grp + 0..3 of its query ----
     const float rs = 1.0f / sum;
     const size_t slot_g = (size_t)c * kChunk + qrow;
-    T* orow = o_sorted + ((size_t)bh * n_slots + slot_g) * kD;
+    T* orow = obase + slot_g * kD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       const float o0 = oacc[dt][0] * rs, o1 = oacc[dt][1] * rs, o2 = oacc[dt][2] * rs, o3 = oacc[dt][3] * rs;
@@ -266,8 +351,13 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
         *(float4*)(orow + 16 * dt + 4 * grp) = make_float4(o0, o1, o2, o3);
       }
     }
-    if (grp == 0) lse_sorted[(size_t)bh * n_slots + slot_g] = (mx + __log2f(sum)) * kLn2;
-    __syncthreads();
+    if (grp == 0) lbase[slot_g] = (off + __log2f(sum)) * kLn2;
+
+    __syncthreads();  // every wave is done with slot prv
+    if (c + 1 < c1) {
+      commit(prv);
+      __syncthreads();
+    }
   }
 }
 

@@ -45,36 +45,41 @@ __device__ inline uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
 }
 
 // ---------------------------------------------------------------------------
-// Rotation transpose + per-round largest column norm + queue reset.
-// One block per round.
+// Rotation transpose [n_h][D][half] -> [n_h][halfp][D] (zero padded), the
+// largest column norm of each 64-column block, and the reset of the
+// uncertified-token count.  Block = (round, 64-column block).
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ rot, T* __restrict__ rot_t,
-                                                   float* __restrict__ rho, int* __restrict__ fix_count,
-                                                   int half, int halfp) {
-  const int r = blockIdx.x;
+                                                   float* __restrict__ colmax, int* __restrict__ fix_count,
+                                                   int half, int halfp, int nblk) {
+  __shared__ T tile[kD][65];
+  __shared__ double red[4];
+  const int r = blockIdx.x / nblk, blk = blockIdx.x % nblk, j0 = blk * 64;
   const T* R = rot + (size_t)r * kD * half;
-  T* RT = rot_t + (size_t)r * halfp * kD;
-  double best = 0.0;
-  for (int j = threadIdx.x; j < halfp; j += blockDim.x) {
-    double nrm = 0.0;
+  for (int idx = threadIdx.x; idx < kD * 64; idx += blockDim.x) {
+    const int d = idx >> 6, jj = idx & 63;
+    tile[d][jj] = (j0 + jj < half) ? R[(size_t)d * half + j0 + jj] : T(0);
+  }
+  __syncthreads();
+  T* RT = rot_t + ((size_t)r * halfp + j0) * kD;
+  for (int idx = threadIdx.x; idx < kD * 64; idx += blockDim.x) {
+    const int jj = idx >> 6, d = idx & 63;
+    if (j0 + jj < halfp) RT[(size_t)jj * kD + d] = tile[d][jj];
+  }
+  double nrm = 0.0;
+  if (threadIdx.x < 64)
     for (int d = 0; d < kD; ++d) {
-      T val = j < half ? R[(size_t)d * half + j] : T(0);
-      RT[(size_t)j * kD + d] = val;
-      double f = to_f64(val);
+      const double f = to_f64(tile[d][threadIdx.x]);
       nrm = fma(f, f, nrm);
     }
-    best = fmax(best, nrm);
-  }
-  for (int off = 32; off >= 1; off >>= 1) best = fmax(best, __shfl_xor(best, off));
-  __shared__ double red[4];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
+  for (int off = 32; off >= 1; off >>= 1) nrm = fmax(nrm, __shfl_xor(nrm, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = nrm;
   __syncthreads();
   if (threadIdx.x == 0) {
-    double m = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
-    // Round the norm up so that it bounds every column norm.
-    rho[r] = (float)(sqrt(m) * (1.0 + 1e-6));
-    if (r == 0) *fix_count = 0;
+    // Rounded up, so it bounds every column norm of the block.
+    colmax[blockIdx.x] = (float)(sqrt(fmax(fmax(red[0], red[1]), fmax(red[2], red[3]))) * (1.0 + 1e-6));
+    if (blockIdx.x == 0) *fix_count = 0;
   }
 }
 
@@ -101,7 +106,7 @@ struct HashTraits<false> {
 template <bool BF16>
 __global__ __launch_bounds__(256) void hash_kernel(const typename HashTraits<BF16>::T* __restrict__ qk,
                                                    const typename HashTraits<BF16>::T* __restrict__ rot_t,
-                                                   const float* __restrict__ rho,
+                                                   const float* __restrict__ colmax,
                                                    int32_t* __restrict__ buckets, int* __restrict__ fix_queue,
                                                    int* __restrict__ fix_count, int L, int n_h, int half,
                                                    int halfp, uint32_t lowmask, int ibits) {
@@ -218,7 +223,11 @@ __global__ __launch_bounds__(256) void hash_kernel(const typename HashTraits<BF1
 
     // Merge with the partner lane (same tokens, the other 16 rows of each tile),
     // decode the winner, recompute its signed score, certify.
-    const float eps_scale = 65.0f * 0x1p-23f * rho[r];
+    // Largest column norm of this round's rotation.
+    const int nblk = (halfp + 63) / 64;
+    float rho = 0.f;
+    for (int k = 0; k < nblk; ++k) rho = fmaxf(rho, colmax[r * nblk + k]);
+    const float eps_scale = 65.0f * 0x1p-23f * rho;
     int32_t result[2];
     bool certified[2];
     for (int q = 0; q < 2; ++q) {
@@ -279,16 +288,19 @@ __global__ __launch_bounds__(256) void hash_kernel(const typename HashTraits<BF1
 }
 
 // ---------------------------------------------------------------------------
-// Float64 re-decision of queued tokens: one wave per token-round, every
-// column's score as a float64 sum of exact products, argmax with the lowest
-// index on ties.  Grid-stride over the queue.
+// Float64 re-decision of queued tokens: one wave per token-round, lane l scores
+// the rotation columns l, l + 64, ... as float64 sums of exact products (from
+// the transposed rotation, one contiguous row per column), then a wave argmax
+// with the lowest index on ties.  Grid-stride over the queue.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void fixup_kernel(const T* __restrict__ qk, const T* __restrict__ rot,
+__global__ __launch_bounds__(256) void fixup_kernel(const T* __restrict__ qk, const T* __restrict__ rot_t,
                                                     int32_t* __restrict__ buckets,
                                                     const int* __restrict__ fix_queue,
                                                     const int* __restrict__ fix_count, int L, int n_h,
-                                                    int half) {
+                                                    int half, int halfp) {
+  constexpr int kPer = 16 / sizeof(T);   // elements per 16-byte load
+  constexpr int kLoads = kD / kPer;      // 16-byte loads per 64-element row
   const int lane = threadIdx.x & 63;
   const int gw = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int nw = (gridDim.x * blockDim.x) >> 6;
@@ -300,30 +312,23 @@ __global__ __launch_bounds__(256) void fixup_kernel(const T* __restrict__ qk, co
     const int r = br % n_h;
     const int bh = br / n_h;
     const T* x = qk + ((size_t)bh * L + tok) * kD;
-    const T* R = rot + (size_t)r * kD * half;
+    uint4 xr[kLoads];
+    for (int k = 0; k < kLoads; ++k) xr[k] = *(const uint4*)(x + k * kPer);
+    const T* xe = (const T*)xr;
     double best_v = -1.0;
     int best_i = 0x7FFFFFFF;
-    for (int j0 = 0; j0 < half; j0 += 64 * 8) {
-      double acc[8];
-      for (int k = 0; k < 8; ++k) acc[k] = 0.0;
-      for (int d = 0; d < kD; ++d) {
-        const double xd = to_f64(x[d]);
-        for (int k = 0; k < 8; ++k) {
-          const int j = j0 + lane + 64 * k;
-          if (j < half) acc[k] = fma(xd, to_f64(R[(size_t)d * half + j]), acc[k]);
-        }
-      }
-      for (int k = 0; k < 8; ++k) {
-        const int j = j0 + lane + 64 * k;
-        if (j < half) {
-          const double p = acc[k];
-          const double v = fabs(p);
-          const int i = p < 0.0 ? j + half : j;  // the larger of +p (index j) and -p (index j + half)
-          if (v > best_v || (v == best_v && i < best_i)) {
-            best_v = v;
-            best_i = i;
-          }
-        }
+    for (int j = lane; j < half; j += 64) {
+      const T* rr = rot_t + ((size_t)r * halfp + j) * kD;
+      uint4 rw[kLoads];
+      for (int k = 0; k < kLoads; ++k) rw[k] = *(const uint4*)(rr + k * kPer);
+      const T* re = (const T*)rw;
+      double p = 0.0;
+      for (int d = 0; d < kD; ++d) p = fma(to_f64(xe[d]), to_f64(re[d]), p);
+      const double v = fabs(p);
+      const int i = p < 0.0 ? j + half : j;  // the larger of +p (index j) and -p (index j + half)
+      if (v > best_v || (v == best_v && i < best_i)) {
+        best_v = v;
+        best_i = i;
       }
     }
     for (int off = 32; off >= 1; off >>= 1) {
@@ -345,17 +350,19 @@ __global__ void fill_zero_kernel(int32_t* p, size_t n) {
 
 }  // namespace
 
-hipError_t launch_prep(const void* rot, void* rot_t, float* rho, int* fix_count, int n_h, int n_b,
+hipError_t launch_prep(const void* rot, void* rot_t, float* colmax, int* fix_count, int n_h, int n_b,
                        lsh_dtype dt, hipStream_t s) {
-  const int half = n_b / 2, halfp = padded_half(n_b);
+  const int half = n_b / 2, halfp = padded_half(n_b), nblk = (halfp + 63) / 64;
   if (dt == LSH_BF16)
-    prep_kernel<uint16_t><<<n_h, 256, 0, s>>>((const uint16_t*)rot, (uint16_t*)rot_t, rho, fix_count, half, halfp);
+    prep_kernel<uint16_t><<<n_h * nblk, 256, 0, s>>>((const uint16_t*)rot, (uint16_t*)rot_t, colmax, fix_count,
+                                                     half, halfp, nblk);
   else
-    prep_kernel<float><<<n_h, 256, 0, s>>>((const float*)rot, (float*)rot_t, rho, fix_count, half, halfp);
+    prep_kernel<float><<<n_h * nblk, 256, 0, s>>>((const float*)rot, (float*)rot_t, colmax, fix_count, half,
+                                                  halfp, nblk);
   return hipGetLastError();
 }
 
-hipError_t launch_hash(const void* qk, const void* rot_t, const float* rho, int32_t* buckets,
+hipError_t launch_hash(const void* qk, const void* rot_t, const float* colmax, int32_t* buckets,
                        int* fix_queue, int* fix_count, int BH, int L, int n_b, int n_h,
                        lsh_dtype dt, hipStream_t s) {
   const int half = n_b / 2, halfp = padded_half(n_b);
@@ -365,23 +372,23 @@ hipError_t launch_hash(const void* qk, const void* rot_t, const float* rho, int3
   const uint32_t lowmask = (1u << ibits) - 1u;
   const unsigned grid = (unsigned)((L + kHashTok - 1) / kHashTok) * (unsigned)BH;
   if (dt == LSH_BF16)
-    hash_kernel<true><<<grid, 256, 0, s>>>((const uint16_t*)qk, (const uint16_t*)rot_t, rho, buckets, fix_queue,
+    hash_kernel<true><<<grid, 256, 0, s>>>((const uint16_t*)qk, (const uint16_t*)rot_t, colmax, buckets, fix_queue,
                                            fix_count, L, n_h, half, halfp, lowmask, ibits);
   else
-    hash_kernel<false><<<grid, 256, 0, s>>>((const float*)qk, (const float*)rot_t, rho, buckets, fix_queue,
+    hash_kernel<false><<<grid, 256, 0, s>>>((const float*)qk, (const float*)rot_t, colmax, buckets, fix_queue,
                                             fix_count, L, n_h, half, halfp, lowmask, ibits);
   return hipGetLastError();
 }
 
-hipError_t launch_fixup(const void* qk, const void* rot, int32_t* buckets, const int* fix_queue,
+hipError_t launch_fixup(const void* qk, const void* rot_t, int32_t* buckets, const int* fix_queue,
                         const int* fix_count, int L, int n_b, int n_h, lsh_dtype dt, hipStream_t s) {
-  const int half = n_b / 2;
+  const int half = n_b / 2, halfp = padded_half(n_b);
   if (dt == LSH_BF16)
-    fixup_kernel<uint16_t><<<256, 256, 0, s>>>((const uint16_t*)qk, (const uint16_t*)rot, buckets, fix_queue,
-                                               fix_count, L, n_h, half);
+    fixup_kernel<uint16_t><<<512, 256, 0, s>>>((const uint16_t*)qk, (const uint16_t*)rot_t, buckets, fix_queue,
+                                               fix_count, L, n_h, half, halfp);
   else
-    fixup_kernel<float><<<256, 256, 0, s>>>((const float*)qk, (const float*)rot, buckets, fix_queue, fix_count,
-                                            L, n_h, half);
+    fixup_kernel<float><<<512, 256, 0, s>>>((const float*)qk, (const float*)rot_t, buckets, fix_queue, fix_count,
+                                            L, n_h, half, halfp);
   return hipGetLastError();
 }
 

@@ -27,13 +27,15 @@ inline int sort_tiles(int L) { return (L + kSortTile - 1) / kSortTile; }
 
 // ---- launchers (stream-ordered, no synchronisation) ----
 // Rotation transpose [n_h][D][half] -> [n_h][halfp][D] with zero padding, the
-// per-round largest column norm, and the reset of the uncertified-token count.
-hipError_t launch_prep(const void* rot, void* rot_t, float* rho, int* fix_count, int n_h, int n_b,
+// largest column norm per 64-column block (colmax: n_h * ceil(halfp/64)
+// floats), and the reset of the uncertified-token count.
+inline int colmax_blocks(int n_b) { return (padded_half(n_b) + 63) / 64; }
+hipError_t launch_prep(const void* rot, void* rot_t, float* colmax, int* fix_count, int n_h, int n_b,
                        lsh_dtype dt, hipStream_t s);
-hipError_t launch_hash(const void* qk, const void* rot_t, const float* rho, int32_t* buckets,
+hipError_t launch_hash(const void* qk, const void* rot_t, const float* colmax, int32_t* buckets,
                        int* fix_queue, int* fix_count, int BH, int L, int n_b, int n_h,
                        lsh_dtype dt, hipStream_t s);
-hipError_t launch_fixup(const void* qk, const void* rot, int32_t* buckets, const int* fix_queue,
+hipError_t launch_fixup(const void* qk, const void* rot_t, int32_t* buckets, const int* fix_queue,
                         const int* fix_count, int L, int n_b, int n_h, lsh_dtype dt,
                         hipStream_t s);
 hipError_t launch_fill_zero(int32_t* p, size_t n, hipStream_t s);

@@ -8,9 +8,10 @@
 // With at most 4096 buckets this is a counting sort, O(n) rather than the
 // explainer's O(n log n) comparison sort, in three launches per call:
 //   hist    - per (problem, round, tile of kSortTile tokens) bucket histogram
-//             in LDS, stored bucket-major: hist[bhr][bucket][tile];
-//   scan    - exclusive prefix sum of that array per (problem, round), which
-//             gives every (bucket, tile) its first output slot;
+//             in LDS, stored hist[bhr][tile][bucket] (coalesced rows);
+//   scan    - per (problem, round): bucket totals over tiles, an exclusive
+//             scan over buckets, then the running sum down the tiles, which
+//             gives every (tile, bucket) its first output slot;
 //   scatter - each wave of a tile ranks its sub-tile's tokens in order: the
 //             lanes holding the same bucket are found with one ballot per key
 //             bit, their rank is a popcount below the lane, and a per-wave LDS
@@ -36,43 +37,45 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t* __restric
   const int32_t* bk = buckets + (size_t)bhr * L;
   for (int i = t0 + (int)threadIdx.x; i < t1; i += blockDim.x) atomicAdd(&sh[clamp_bucket(bk[i], n_b)], 1);
   __syncthreads();
-  int* out = hist + (size_t)bhr * n_b * n_tiles;
-  for (int b = threadIdx.x; b < n_b; b += blockDim.x) out[(size_t)b * n_tiles + tile] = sh[b];
+  int* out = hist + ((size_t)bhr * n_tiles + tile) * n_b;
+  for (int b = threadIdx.x; b < n_b; b += blockDim.x) out[b] = sh[b];
 }
 
-// One block per (problem, round): exclusive scan of n = n_b * n_tiles counts.
-__global__ __launch_bounds__(256) void sort_scan_kernel(int* __restrict__ hist, int n) {
-  int* h = hist + (size_t)blockIdx.x * n;
+// One block of 1024 threads per (problem, round).  Offsets in the order
+// (bucket, tile): slot(b, t) = sum_{b' < b} total(b') + sum_{t' < t} count(b', t).
+constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kScanThreads) void sort_scan_kernel(int* __restrict__ hist, int n_b, int n_tiles) {
+  int* h = hist + (size_t)blockIdx.x * n_tiles * n_b;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __shared__ int wsum[4];
+  constexpr int kWaves = kScanThreads / 64;
+  __shared__ int wsum[kWaves];
   int carry = 0;
-  constexpr int kPer = 8;
-  for (int base = 0; base < n; base += 256 * kPer) {
-    const int i0 = base + (int)threadIdx.x * kPer;
-    int v[kPer];
-    int s = 0;
-    for (int k = 0; k < kPer; ++k) {
-      v[k] = (i0 + k < n) ? h[i0 + k] : 0;
-      s += v[k];
-    }
-    int incl = s;
+  for (int b0 = 0; b0 < n_b; b0 += kScanThreads) {
+    const int b = b0 + (int)threadIdx.x;
+    int tot = 0;
+    if (b < n_b)
+      for (int t = 0; t < n_tiles; ++t) tot += h[(size_t)t * n_b + b];
+    int incl = tot;
     for (int off = 1; off < 64; off <<= 1) {
       const int y = __shfl_up(incl, off);
       if (lane >= off) incl += y;
     }
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
-    int woff = 0, total = 0;
-    for (int w = 0; w < 4; ++w) {
+    int woff = 0, all = 0;
+    for (int w = 0; w < kWaves; ++w) {
       if (w < wave) woff += wsum[w];
-      total += wsum[w];
+      all += wsum[w];
     }
-    int run = carry + woff + incl - s;
-    for (int k = 0; k < kPer; ++k) {
-      if (i0 + k < n) h[i0 + k] = run;
-      run += v[k];
+    if (b < n_b) {
+      int run = carry + woff + incl - tot;
+      for (int t = 0; t < n_tiles; ++t) {
+        const int c = h[(size_t)t * n_b + b];
+        h[(size_t)t * n_b + b] = run;
+        run += c;
+      }
     }
-    carry += total;
+    carry += all;
     __syncthreads();
   }
 }
@@ -97,9 +100,9 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
   __syncthreads();
   // 2. first slot of (bucket, wave): the scanned (bucket, tile) offset plus the
   //    counts of the earlier waves of this tile.
-  const int* hs = hist + (size_t)bhr * n_b * n_tiles;
+  const int* hs = hist + ((size_t)bhr * n_tiles + tile) * n_b;
   for (int b = threadIdx.x; b < n_b; b += blockDim.x) {
-    int run = hs[(size_t)b * n_tiles + tile];
+    int run = hs[b];
     for (int w = 0; w < 4; ++w) {
       const int c = sh[w * n_b + b];
       sh[w * n_b + b] = run;
@@ -142,7 +145,7 @@ hipError_t launch_sort_hist(const int32_t* buckets, int* hist, int BHR, int L, i
 }
 
 hipError_t launch_sort_scan(int* hist, int BHR, int L, int n_b, hipStream_t s) {
-  sort_scan_kernel<<<BHR, 256, 0, s>>>(hist, n_b * sort_tiles(L));
+  sort_scan_kernel<<<BHR, kScanThreads, 0, s>>>(hist, n_b, sort_tiles(L));
   return hipGetLastError();
 }
 

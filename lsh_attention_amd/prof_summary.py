@@ -1,0 +1,96 @@
+"""Summaries of rocprofv3 output for the fused LSH-attention forward pass.
+
+  python -m lsh_attention_amd.prof_summary stats <rocprofv3 output dir>
+      Markdown table of the --kernel-trace --stats run (average duration per
+      kernel, per launch).
+  python -m lsh_attention_amd.prof_summary traffic <pmc dir> <workload> <out.json>
+      From --pmc runs of FETCH_SIZE and WRITE_SIZE (one sub-directory per
+      pass, each holding *_counter_collection.csv) over a benchmark run that
+      ends with one plain device copy of known size (bench.py
+      --copy-probe-mib N): per-kernel HBM bytes per launch, with each counter
+      scaled by (copy bytes / counter reading of the copy).  Each entry keeps
+      the sha256 of the kernel's source so a later change invalidates it.
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+KERNEL_SOURCES = {
+    "prep": ["hash.hip"], "hash": ["hash.hip"], "fixup": ["hash.hip"],
+    "sort_hist": ["sort.hip"], "sort_scan": ["sort.hip"], "sort_scatter": ["sort.hip"],
+    "chunk_attn": ["chunk_attn.hip"], "combine": ["combine.hip"],
+}
+
+
+def kernel_key(name: str) -> str:
+    m = re.search(r"(\w+)_kernel\b", name)
+    if m:
+        return m.group(1)
+    return "copy" if "copy" in name.lower() else name[:40]
+
+
+def source_sha256(key: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(key, []) + ["lsh_internal.h"]:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()
+
+
+def stats_table(d: str) -> str:
+    f = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)[0]
+    rows = list(csv.DictReader(open(f)))
+    out = ["| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
+           "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| {kernel_key(r['Name'])} (`{r['Name'][:70]}`) | {r['Calls']} | "
+                   f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                   f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} % |")
+    return "\n".join(out)
+
+
+def counters(d: str):
+    """{kernel: {counter: mean over dispatches of the per-dispatch value}} plus the copy kernel's bytes."""
+    per = collections.defaultdict(lambda: collections.defaultdict(lambda: collections.defaultdict(float)))
+    copy_bytes = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            k = kernel_key(r["Kernel_Name"])
+            per[k][r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    out = {k: {c: sum(v.values()) / len(v) for c, v in cs.items()} for k, cs in per.items()}
+    return out
+
+
+def traffic(d: str, workload: str, out_json: str, copy_mib: int = 256):
+    c = counters(d)
+    cp = c["copy"]
+    copy_kib = copy_mib * 1024.0
+    f_fac = copy_kib / cp["FETCH_SIZE"]
+    w_fac = copy_kib / cp["WRITE_SIZE"]
+    res = {"workload": workload, "copy_probe_bytes": copy_mib << 20,
+           "fetch_scale": round(f_fac, 4), "write_scale": round(w_fac, 4), "kernels": {}}
+    for k, v in c.items():
+        if k == "copy" or "FETCH_SIZE" not in v:
+            continue
+        fetch = v["FETCH_SIZE"] * 1024 * f_fac
+        write = v.get("WRITE_SIZE", 0.0) * 1024 * w_fac
+        res["kernels"][k] = {"fetch_bytes": round(fetch), "write_bytes": round(write),
+                             "traffic_bytes": round(fetch + write), "source_sha256": source_sha256(k)}
+    json.dump(res, open(out_json, "w"), indent=1)
+    return res
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "stats":
+        print(stats_table(sys.argv[2]))
+    elif sys.argv[1] == "traffic":
+        print(json.dumps(traffic(sys.argv[2], sys.argv[3], sys.argv[4]), indent=1))
+    else:
+        raise SystemExit(__doc__)
