@@ -19,7 +19,7 @@ int check_problem(int B, int H, int L, int D, int n_h) {
   if (B <= 0 || H <= 0 || L <= 0 || D <= 0 || n_h <= 0) return LSH_ERR_SHAPE;
   if (D != kD) return LSH_ERR_UNSUPPORTED;
   if (n_h > kMaxHashes) return LSH_ERR_UNSUPPORTED;
-  if (L % kChunk != 0) return LSH_ERR_SHAPE;
+  if (L % kChunk != 0 || L > kMaxLen) return LSH_ERR_SHAPE;
   const uint64_t slots = (uint64_t)B * (uint64_t)H * (uint64_t)n_h * (uint64_t)L;
   if (slots > 0x7FFFFFFFull) return LSH_ERR_SHAPE;
   return LSH_OK;
@@ -28,7 +28,7 @@ int check_problem(int B, int H, int L, int D, int n_h) {
 int check_buckets(int n_b, int L) {
   if (n_b < 1 || n_b > kMaxBuckets) return LSH_ERR_BUCKETS;
   if (n_b > 1 && (n_b % 2) != 0) return LSH_ERR_BUCKETS;
-  if ((uint64_t)n_b * (uint64_t)sort_tiles(L) > 0x7FFFFFFFull) return LSH_ERR_SHAPE;
+  if ((uint64_t)n_b * (uint64_t)sort_tiles(L, n_b) > 0x7FFFFFFFull) return LSH_ERR_SHAPE;
   return LSH_OK;
 }
 
@@ -63,7 +63,7 @@ HashWs hash_ws(int BH, int L, int n_b, int n_h, lsh_dtype dt) {
 }
 
 size_t sort_ws_bytes(int BH, int L, int n_b, int n_h) {
-  return align_up((size_t)BH * n_h * n_b * sort_tiles(L) * sizeof(int), kAlign);
+  return align_up((size_t)BH * n_h * n_b * sort_tiles(L, n_b) * sizeof(int), kAlign);
 }
 
 struct FwdWs {
@@ -140,7 +140,7 @@ const char* lsh_status_string(int status) {
   switch (status) {
     case LSH_OK: return "ok";
     case LSH_ERR_NULL: return "a required pointer is NULL";
-    case LSH_ERR_SHAPE: return "invalid shape (dimension <= 0, L not a multiple of 64, or int32 index overflow)";
+    case LSH_ERR_SHAPE: return "invalid shape (dimension <= 0, L not a multiple of 64 or above 2^24, or int32 index overflow)";
     case LSH_ERR_BUCKETS: return "invalid bucket count (must be 1 or even, at most 4096)";
     case LSH_ERR_UNSUPPORTED: return "unsupported configuration (D and chunk_len must be 64, n_hashes <= 16, dtype f32 or bf16)";
     case LSH_ERR_WORKSPACE: return "workspace missing or too small";
@@ -228,7 +228,7 @@ int lsh_chunk_attn(const void* qk, const void* v, const int32_t* sorted_idx, voi
     if (overlaps(o_sorted, o_bytes, ins[a], in_n[a]) || overlaps(lse_sorted, l_bytes, ins[a], in_n[a]))
       return LSH_ERR_ALIAS;
   if (overlaps(o_sorted, o_bytes, lse_sorted, l_bytes)) return LSH_ERR_ALIAS;
-  return hip_status(launch_chunk_attn(qk, v, sorted_idx, o_sorted, lse_sorted, BH, L, n_h, causal, dt,
+  return hip_status(launch_chunk_attn(qk, v, sorted_idx, o_sorted, lse_sorted, BH, L, n_h, causal, false, dt,
                                       (hipStream_t)stream));
 }
 
@@ -304,9 +304,10 @@ int reformer_lsh_attn_fwd(const void* qk, const void* v, const void* rot, int n_
   if (e == hipSuccess)
     e = enqueue_sort(buckets, sorted_idx, undo_idx, (int*)(base + w.sort_base), BH, L, n_b, n_h, s, stage_events,
                      &k);
-  if (e == hipSuccess) e = launch_chunk_attn(qk, v, sorted_idx, o_sorted, lse_sorted, BH, L, n_h, causal, dt, s);
+  // The fused path keeps the per-round results in token order, so the combine streams them.
+  if (e == hipSuccess) e = launch_chunk_attn(qk, v, sorted_idx, o_sorted, lse_sorted, BH, L, n_h, causal, true, dt, s);
   if (e == hipSuccess && stage_events != nullptr) e = hipEventRecord((hipEvent_t)stage_events[++k], s);
-  if (e == hipSuccess) e = launch_combine(o_sorted, lse_sorted, undo_idx, out, lse_out, BH, L, n_h, dt, s);
+  if (e == hipSuccess) e = launch_combine_token_order(o_sorted, lse_sorted, out, lse_out, BH, L, n_h, dt, s);
   if (e == hipSuccess && stage_events != nullptr) e = hipEventRecord((hipEvent_t)stage_events[++k], s);
   return hip_status(e);
 }

@@ -19,9 +19,11 @@
 //    while chunk c is computed, then written to LDS.  The previous chunk's
 //    rows stay resident (two-slot ring), so each row is gathered once per
 //    block.  The block's slice of sorted_idx is staged in LDS up front.
-//  * V is stored transposed in LDS for the P.V product.  Each thread gathers
-//    one 4-byte word (two dims) from each of 8 rows and writes two 16-byte
-//    rows of V^T, so the transpose costs 2 LDS writes per thread per chunk.
+//  * V is stored transposed in LDS for the P.V product, with its keys permuted
+//    into the order the P.V operand consumes them, so each lane reads its 8
+//    keys as one 16-byte, bank-conflict-free LDS read.  Each thread gathers one
+//    4-byte word (two dims) from each of 8 rows and writes two 16-byte V^T
+//    pieces, so the transpose costs 2 LDS writes per thread per chunk.
 //  * S^T = K Q^T on MFMA (keys are MFMA rows, queries MFMA columns), so each
 //    lane holds one query's logits for 4 consecutive keys per 16-key tile.
 //  * O^T = V^T P^T on MFMA: the P^T operand is exactly the lane's own
@@ -65,14 +67,18 @@ struct AttnTraits<false> {
   static constexpr int kVWords = 16;  // 1 dim x 16 rows
 };
 
-__device__ inline uint16_t f32_to_bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 
-template <bool BF16, bool CAUSAL>
+// TOKEN_ORDER = false: o and lse are written per sorted slot ([B,H,n_h*L,64], [B,H,n_h*L]).
+// TOKEN_ORDER = true: per token and round ([B,H,L,n_h,64], [B,H,L,n_h]), which lets the
+// combine read each token's rounds as one contiguous stream.
+template <bool BF16, bool CAUSAL, bool TOKEN_ORDER>
 __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTraits<BF16>::T* __restrict__ qk,
                                                          const typename AttnTraits<BF16>::T* __restrict__ v,
                                                          const int32_t* __restrict__ sorted_idx,
-                                                         typename AttnTraits<BF16>::T* __restrict__ o_sorted,
-                                                         float* __restrict__ lse_sorted, int L, int n_slots,
+                                                         typename AttnTraits<BF16>::T* __restrict__ o_out,
+                                                         float* __restrict__ lse_out, int L, int n_slots,
                                                          int n_chunks, int blocks_per_bh) {
   using T = typename AttnTraits<BF16>::T;
   constexpr int kXRow = AttnTraits<BF16>::kXRow;
@@ -93,11 +99,15 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
   const int col = lane & 15;  // query (column) of the MFMA tiles
   const int grp = lane >> 4;  // 4-key group within a 16-key tile
 
-  const T* xq = qk + (size_t)bh * L * kD;
-  const T* vq = v + (size_t)bh * L * kD;
+  // Per-(b,h) bases; rows are addressed with 32-bit byte offsets (L * 64 * 4 < 2^32).
+  constexpr uint32_t kRowBytes = kD * sizeof(T);
+  const char* xq = (const char*)(qk + (size_t)bh * L * kD);
+  const char* vq = (const char*)(v + (size_t)bh * L * kD);
   const int32_t* sidx = sorted_idx + (size_t)bh * n_slots;
-  T* obase = o_sorted + (size_t)bh * n_slots * kD;
-  float* lbase = lse_sorted + (size_t)bh * n_slots;
+  T* obase = o_out + (size_t)bh * n_slots * kD;
+  float* lbase = lse_out + (size_t)bh * n_slots;
+  const int n_h = n_slots / L;
+  const int chunks_per_round = L / kChunk;
 
   // Positions of the previous chunk of c0 and of chunks c0..c1-1 (entry k <-> chunk c0-1+k).
   // Positions come from a permutation of [0, L); the clamp only keeps a
@@ -117,17 +127,19 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
   const int xrow = tid >> 2, xq4 = tid & 3;
   auto gather = [&](int k) {
     const int* pos = sPos[k];
-    const T* xs = xq + (size_t)pos[xrow] * kD + 16 * xq4;
+    const uint32_t xoff = (uint32_t)pos[xrow] * kRowBytes + 16u * xq4 * (uint32_t)sizeof(T);
 #pragma unroll
-    for (int i = 0; i < kXLoads; ++i) xr[i] = *(const uint4*)(xs + i * (16 / kXLoads));
+    for (int i = 0; i < kXLoads; ++i) xr[i] = *(const uint4*)(xq + xoff + 16u * i);
     if constexpr (BF16) {
-      const int p = tid & 31, r0 = 8 * (tid >> 5);
+      const uint32_t p4 = 4u * (tid & 31);
+      const int j = tid >> 5, r0 = 32 * (j >> 2) + 4 * (j & 3);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) vw[i] = *(const uint32_t*)(vq + (size_t)pos[r0 + i] * kD + 2 * p);
+      for (int i = 0; i < 8; ++i) vw[i] = *(const uint32_t*)(vq + (uint32_t)pos[r0 + (i & 3) + 16 * (i >> 2)] * kRowBytes + p4);
     } else {
-      const int p = tid & 63, r0 = 16 * (tid >> 6);
+      const uint32_t p4 = 4u * (tid & 63);
+      const int r0 = 16 * (tid >> 6);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) vw[i] = __float_as_uint(vq[(size_t)pos[r0 + i] * kD + p]);
+      for (int i = 0; i < 16; ++i) vw[i] = *(const uint32_t*)(vq + (uint32_t)pos[r0 + i] * kRowBytes + p4);
     }
   };
   auto commit = [&](int slot) {
@@ -153,13 +165,16 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
     ss += __shfl_xor(ss, 1);
     ss += __shfl_xor(ss, 2);
     if (xq4 == 0) {
-      const float nrm = sqrtf(ss);
-      sKs[slot][xrow] = kScale2 / fmaxf(nrm, 1e-12f);
+      const float nrm = __builtin_amdgcn_sqrtf(ss);
+      sKs[slot][xrow] = kScale2 * __builtin_amdgcn_rcpf(fmaxf(nrm, 1e-12f));
       sM[slot][xrow] = kScale2 * nrm;
     }
     if constexpr (BF16) {
-      const int p = tid & 31, r0 = 8 * (tid >> 5);
-      // low halves = dim 2p, high halves = dim 2p+1, of rows r0..r0+7
+      // V^T columns are keys in the order of the P.V operand: column 32h + 8g + 4b + e holds
+      // chunk row 32h + 16b + 4g + e.  This thread holds rows 32h + 4g + e and 32h + 16 + 4g + e
+      // (h, g from its index), i.e. columns 32h + 8g + 0..7.
+      const int p = tid & 31, j = tid >> 5, r0 = 32 * (j >> 2) + 8 * (j & 3);
+      // low halves = dim 2p, high halves = dim 2p+1, of the 8 rows in column order
       uint4 lo, hi;
       lo.x = __builtin_amdgcn_perm(vw[1], vw[0], 0x05040100u);
       lo.y = __builtin_amdgcn_perm(vw[3], vw[2], 0x05040100u);
@@ -309,15 +324,12 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
           bp[4 + e] = (__bf16)p[2 * ks + 1][e];
         }
         const int slot = ks < 2 ? prv : cur;
-        const int kc0 = 64 * slot + 16 * ((2 * ks) & 3) + 4 * grp;
-        const int kc1 = 64 * slot + 16 * ((2 * ks + 1) & 3) + 4 * grp;
+        // keys of tiles 2ks and 2ks+1 seen by lane group grp: V^T columns 32 (ks & 1) + 8 grp + 0..7
+        const int kc = 64 * slot + 32 * (ks & 1) + 8 * grp;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const T* vr = &sVT[(16 * dt + col) * kVRow];
-          const uint2 lo = *(const uint2*)(vr + kc0);
-          const uint2 hi = *(const uint2*)(vr + kc1);
-          const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), bp, oacc[dt], 0, 0, 0);
+          const bf16x8 a = *(const bf16x8*)(&sVT[(16 * dt + col) * kVRow + kc]);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bp, oacc[dt], 0, 0, 0);
         }
       }
     } else {
@@ -337,21 +349,26 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
     }
 
     // ---- normalise and store: lane holds dims 16 dt + 4 grp + 0..3 of its query ----
-    const float rs = 1.0f / sum;
-    const size_t slot_g = (size_t)c * kChunk + qrow;
-    T* orow = obase + slot_g * kD;
+    const float rs = __builtin_amdgcn_rcpf(sum);
+    size_t row_g;
+    if constexpr (TOKEN_ORDER)
+      row_g = (size_t)qpos * n_h + c / chunks_per_round;
+    else
+      row_g = (size_t)c * kChunk + qrow;
+    T* orow = obase + row_g * kD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       const float o0 = oacc[dt][0] * rs, o1 = oacc[dt][1] * rs, o2 = oacc[dt][2] * rs, o3 = oacc[dt][3] * rs;
       if constexpr (BF16) {
-        const uint32_t w0 = (uint32_t)f32_to_bf16_bits(o0) | ((uint32_t)f32_to_bf16_bits(o1) << 16);
-        const uint32_t w1 = (uint32_t)f32_to_bf16_bits(o2) | ((uint32_t)f32_to_bf16_bits(o3) << 16);
-        *(uint2*)(orow + 16 * dt + 4 * grp) = make_uint2(w0, w1);
+        const bf16x2 w0 = __builtin_convertvector(f32x2{o0, o1}, bf16x2);
+        const bf16x2 w1 = __builtin_convertvector(f32x2{o2, o3}, bf16x2);
+        *(uint2*)(orow + 16 * dt + 4 * grp) =
+            make_uint2(__builtin_bit_cast(uint32_t, w0), __builtin_bit_cast(uint32_t, w1));
       } else {
         *(float4*)(orow + 16 * dt + 4 * grp) = make_float4(o0, o1, o2, o3);
       }
     }
-    if (grp == 0) lbase[slot_g] = (off + __log2f(sum)) * kLn2;
+    if (grp == 0) lbase[row_g] = (off + __builtin_amdgcn_logf(sum)) * kLn2;
 
     __syncthreads();  // every wave is done with slot prv
     if (c + 1 < c1) {
@@ -361,30 +378,33 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
   }
 }
 
-template <bool BF16>
-hipError_t launch_attn_t(const void* qk, const void* v, const int32_t* sorted_idx, void* o_sorted,
-                         float* lse_sorted, int BH, int L, int n_h, int causal, hipStream_t s) {
+template <bool BF16, bool TOKEN_ORDER>
+hipError_t launch_attn_t(const void* qk, const void* v, const int32_t* sorted_idx, void* o_out, float* lse_out,
+                         int BH, int L, int n_h, int causal, hipStream_t s) {
   using T = typename AttnTraits<BF16>::T;
   const int n_slots = n_h * L;
   const int n_chunks = n_slots / kChunk;
   const int blocks_per_bh = (n_chunks + kChunksPerBlock - 1) / kChunksPerBlock;
   const unsigned grid = (unsigned)blocks_per_bh * (unsigned)BH;
   if (causal)
-    chunk_attn_kernel<BF16, true><<<grid, 256, 0, s>>>((const T*)qk, (const T*)v, sorted_idx, (T*)o_sorted,
-                                                       lse_sorted, L, n_slots, n_chunks, blocks_per_bh);
+    chunk_attn_kernel<BF16, true, TOKEN_ORDER><<<grid, 256, 0, s>>>(
+        (const T*)qk, (const T*)v, sorted_idx, (T*)o_out, lse_out, L, n_slots, n_chunks, blocks_per_bh);
   else
-    chunk_attn_kernel<BF16, false><<<grid, 256, 0, s>>>((const T*)qk, (const T*)v, sorted_idx, (T*)o_sorted,
-                                                        lse_sorted, L, n_slots, n_chunks, blocks_per_bh);
+    chunk_attn_kernel<BF16, false, TOKEN_ORDER><<<grid, 256, 0, s>>>(
+        (const T*)qk, (const T*)v, sorted_idx, (T*)o_out, lse_out, L, n_slots, n_chunks, blocks_per_bh);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_chunk_attn(const void* qk, const void* v, const int32_t* sorted_idx, void* o_sorted,
-                             float* lse_sorted, int BH, int L, int n_h, int causal, lsh_dtype dt,
+hipError_t launch_chunk_attn(const void* qk, const void* v, const int32_t* sorted_idx, void* o_out,
+                             float* lse_out, int BH, int L, int n_h, int causal, bool token_order, lsh_dtype dt,
                              hipStream_t s) {
-  if (dt == LSH_BF16) return launch_attn_t<true>(qk, v, sorted_idx, o_sorted, lse_sorted, BH, L, n_h, causal, s);
-  return launch_attn_t<false>(qk, v, sorted_idx, o_sorted, lse_sorted, BH, L, n_h, causal, s);
+  if (dt == LSH_BF16)
+    return token_order ? launch_attn_t<true, true>(qk, v, sorted_idx, o_out, lse_out, BH, L, n_h, causal, s)
+                       : launch_attn_t<true, false>(qk, v, sorted_idx, o_out, lse_out, BH, L, n_h, causal, s);
+  return token_order ? launch_attn_t<false, true>(qk, v, sorted_idx, o_out, lse_out, BH, L, n_h, causal, s)
+                     : launch_attn_t<false, false>(qk, v, sorted_idx, o_out, lse_out, BH, L, n_h, causal, s);
 }
 
 }  // namespace lsh

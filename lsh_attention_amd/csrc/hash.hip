@@ -13,9 +13,10 @@
 //    accumulators hold one token's scores for 16 rotation columns.
 //  * The argmax is fused into the MFMA epilogue.  Each score becomes a sort
 //    key: |score| with its low mantissa bits replaced by a column code; the
-//    running top-2 keys are kept per lane with max3/med3 (2.5 VALU ops per
-//    score).  The winner's index comes from its code; its sign from one dot
-//    product.
+//    running top-2 keys are kept per lane with max3/med3 (2.25 VALU
+//    instructions per score; on gfx950 MFMA and VALU time add up, so the
+//    VALU count per score is what matters).  The winner's index comes from its
+//    code, its sign from one recomputed dot product per token-round.
 //  * The decision is certified: an fp32 sum of 64 exact bf16 products (or
 //    rounded fp32 products) is within eps = 65 * 2^-23 * |x| * max_j |r_j| of
 //    the exact value, and the key truncation adds at most one key-grid step
@@ -24,7 +25,8 @@
 //    exact-arithmetic argmax.
 //  * The rotation is shared by every (batch, head): it is transposed once per
 //    call into [n_h][n_b/2 padded to 32][D] so a workgroup stages it into LDS
-//    with 16-byte row loads, and read by all four waves from there.
+//    with 16-byte row loads (the next 128-column block is loaded into
+//    registers while the current one is used), and read by all four waves.
 #include "lsh_internal.h"
 
 namespace lsh {
@@ -88,7 +90,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ rot, T*
 // groups), 256 tokens per block; grid = (ceil(L / 256), B*H).
 // ---------------------------------------------------------------------------
 constexpr int kHashTok = 256;
-constexpr int kHashCB = 128;  // rotation columns staged in LDS per pass
+constexpr int kHashCB = 64;  // rotation columns staged in LDS per pass
 
 template <bool BF16>
 struct HashTraits;
@@ -104,7 +106,7 @@ struct HashTraits<false> {
 };
 
 template <bool BF16>
-__global__ __launch_bounds__(256) void hash_kernel(const typename HashTraits<BF16>::T* __restrict__ qk,
+__global__ __launch_bounds__(256, 4) void hash_kernel(const typename HashTraits<BF16>::T* __restrict__ qk,
                                                    const typename HashTraits<BF16>::T* __restrict__ rot_t,
                                                    const float* __restrict__ colmax,
                                                    int32_t* __restrict__ buckets, int* __restrict__ fix_queue,
@@ -131,7 +133,6 @@ __global__ __launch_bounds__(256) void hash_kernel(const typename HashTraits<BF1
   // B operand (tokens), kept in registers for every round.
   //  bf16: k-step s covers dims 16s..16s+15; this lane holds dims 16s + 8hb + 0..7.
   //  fp32: k-step s covers dims {s, s+32}; this lane holds dim s + 32hb.
-  constexpr int kSteps = BF16 ? 4 : 32;
   bf16x8 bq16[2][4];
   float bq32[2][BF16 ? 1 : 32];
   float nrm2[2];
@@ -165,71 +166,108 @@ __global__ __launch_bounds__(256) void hash_kernel(const typename HashTraits<BF1
     }
     nrm2[q] = acc + __shfl_xor(acc, 32);
   }
-  (void)kSteps;
 
-  for (int r = 0; r < n_h; ++r) {
-    uint32_t m1[2] = {0u, 0u}, m2[2] = {0u, 0u};
-    const T* src_round = rot_t + (size_t)r * halfp * kD;
-    for (int cb = 0; cb < halfp; cb += kHashCB) {
-      const int ncols = min(kHashCB, halfp - cb);
-      __syncthreads();
-      {
-        constexpr int kPieces = BF16 ? 8 : 16;  // 16-byte pieces per 64-element row
-        constexpr int kPer = BF16 ? 8 : 4;      // elements per piece
-        const T* src = src_round + (size_t)cb * kD;
-        for (int c = threadIdx.x; c < ncols * kPieces; c += 256) {
-          const int row = c / kPieces, piece = c % kPieces;
-          *(uint4*)(sR + row * kRow + piece * kPer) = *(const uint4*)(src + row * kD + piece * kPer);
-        }
-      }
-      __syncthreads();
-      for (int t = 0; t < ncols / 32; ++t) {
-        f32x16 acc0 = {}, acc1 = {};
-        const T* arow = sR + (32 * t + n) * kRow;
-        if constexpr (BF16) {
-          for (int s = 0; s < 4; ++s) {
-            bf16x8 a = *(const bf16x8*)(arow + 16 * s + 8 * hb);
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq16[0][s], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq16[1][s], acc1, 0, 0, 0);
-          }
-        } else {
-          for (int s4 = 0; s4 < 8; ++s4) {
-            float4 a4 = *(const float4*)(arow + 32 * hb + 4 * s4);
-            const float a[4] = {a4.x, a4.y, a4.z, a4.w};
-            for (int e = 0; e < 4; ++e) {
-              acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], bq32[0][4 * s4 + e], acc0, 0, 0, 0);
-              acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], bq32[1][4 * s4 + e], acc1, 0, 0, 0);
-            }
-          }
-        }
-        // Column code of accumulator e of tile tg: lowmask - (16 tg + e).
-        const uint32_t tg = (uint32_t)((cb >> 5) + t);
-        const uint32_t cbase = lowmask - 16u * tg;
-#pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-          uint32_t a0 = (__float_as_uint(acc0[e]) & kmask_v) | (cbase - e);
-          uint32_t b0 = (__float_as_uint(acc0[e + 1]) & kmask_v) | (cbase - e - 1);
-          uint32_t hi0 = umax3(m1[0], a0, b0);
-          m2[0] = max(m2[0], umed3(m1[0], a0, b0));
-          m1[0] = hi0;
-          uint32_t a1 = (__float_as_uint(acc1[e]) & kmask_v) | (cbase - e);
-          uint32_t b1 = (__float_as_uint(acc1[e + 1]) & kmask_v) | (cbase - e - 1);
-          uint32_t hi1 = umax3(m1[1], a1, b1);
-          m2[1] = max(m2[1], umed3(m1[1], a1, b1));
-          m1[1] = hi1;
-        }
-      }
+  // Rotation blocks of kHashCB columns, over all rounds in order; block it+1 is
+  // loaded into registers while block it is being used.
+  constexpr int kPieces = BF16 ? 8 : 16;  // 16-byte pieces per 64-element row
+  constexpr int kPer = BF16 ? 8 : 4;      // elements per piece
+  constexpr int kPF = kHashCB * kPieces / 256;
+  const int nbpr = (halfp + kHashCB - 1) / kHashCB;  // blocks per round
+  const int total = n_h * nbpr;
+  u32x4 pf[kPF];  // native vector type: HIP's uint4 struct copies defeat register promotion here
+  // Load rotation block `it` into registers (rows clamped in bounds, so every
+  // load is unconditional and the array stays in registers) / write it to LDS.
+#define LSH_HASH_PREFETCH(it_)                                                                 \
+  {                                                                                            \
+    const int r_ = (it_) / nbpr, cb_ = ((it_) % nbpr) * kHashCB;                               \
+    const int lim_ = min(kHashCB, halfp - cb_) * kPieces - 1;                                  \
+    const T* src_ = rot_t + ((size_t)r_ * halfp + cb_) * kD;                                   \
+    _Pragma("unroll") for (int k_ = 0; k_ < kPF; ++k_) {                                       \
+      const int c_ = min((int)threadIdx.x + 256 * k_, lim_);                                   \
+      pf[k_] = *(const u32x4*)(src_ + (c_ / kPieces) * kD + (c_ % kPieces) * kPer);                  \
+    }                                                                                          \
+  }
+#define LSH_HASH_STAGE(it_)                                                                    \
+  {                                                                                            \
+    const int cb_ = ((it_) % nbpr) * kHashCB;                                                  \
+    const int lim_ = min(kHashCB, halfp - cb_) * kPieces;                                      \
+    _Pragma("unroll") for (int k_ = 0; k_ < kPF; ++k_) {                                       \
+      const int c_ = (int)threadIdx.x + 256 * k_;                                              \
+      if (c_ < lim_) *(u32x4*)(sR + (c_ / kPieces) * kRow + (c_ % kPieces) * kPer) = pf[k_];   \
+    }                                                                                          \
+  }
+
+  uint32_t m1[2], m2[2];  // running top-2 keys per token group
+  LSH_HASH_PREFETCH(0);
+  for (int it = 0; it < total; ++it) {
+    const int r = it / nbpr, cb = (it % nbpr) * kHashCB;
+    const int ncols = min(kHashCB, halfp - cb);
+    if (cb == 0) {
+      m1[0] = m1[1] = m2[0] = m2[1] = 0u;
     }
+    __syncthreads();
+    LSH_HASH_STAGE(it);
+    __syncthreads();
+    if (it + 1 < total) LSH_HASH_PREFETCH(it + 1);
+    const int nt = ncols / 32;
+    auto project = [&](int t, f32x16& acc0, f32x16& acc1) {
+      acc0 = f32x16{};
+      acc1 = f32x16{};
+      const T* arow = sR + (32 * t + n) * kRow;
+      if constexpr (BF16) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          bf16x8 a = *(const bf16x8*)(arow + 16 * s + 8 * hb);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq16[0][s], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq16[1][s], acc1, 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int s4 = 0; s4 < 8; ++s4) {
+          float4 a4 = *(const float4*)(arow + 32 * hb + 4 * s4);
+          const float a[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], bq32[0][4 * s4 + e], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], bq32[1][4 * s4 + e], acc1, 0, 0, 0);
+          }
+        }
+      }
+    };
+    auto select = [&](int t, const f32x16& acc0, const f32x16& acc1) {
+      // Column code of accumulator e of tile tg: lowmask - (16 tg + e).
+      const uint32_t tg = (uint32_t)((cb >> 5) + t);
+      const uint32_t cbase = lowmask - 16u * tg;
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        uint32_t a0 = (__float_as_uint(acc0[e]) & kmask_v) | (cbase - e);
+        uint32_t b0 = (__float_as_uint(acc0[e + 1]) & kmask_v) | (cbase - e - 1);
+        uint32_t hi0 = umax3(m1[0], a0, b0);
+        m2[0] = max(m2[0], umed3(m1[0], a0, b0));
+        m1[0] = hi0;
+        uint32_t a1 = (__float_as_uint(acc1[e]) & kmask_v) | (cbase - e);
+        uint32_t b1 = (__float_as_uint(acc1[e + 1]) & kmask_v) | (cbase - e - 1);
+        uint32_t hi1 = umax3(m1[1], a1, b1);
+        m2[1] = max(m2[1], umed3(m1[1], a1, b1));
+        m1[1] = hi1;
+      }
+    };
+    for (int t = 0; t < nt; ++t) {
+      f32x16 ca0, ca1;
+      project(t, ca0, ca1);
+      select(t, ca0, ca1);
+    }
+    if (cb + kHashCB < halfp) continue;
 
-    // Merge with the partner lane (same tokens, the other 16 rows of each tile),
-    // decode the winner, recompute its signed score, certify.
-    // Largest column norm of this round's rotation.
+    // End of round r: merge with the partner lane (same tokens, the other 16 rows
+    // of each tile), decode the winner, certify, take the sign.
     const int nblk = (halfp + 63) / 64;
-    float rho = 0.f;
+    float rho = 0.f;  // largest column norm of this round's rotation
     for (int k = 0; k < nblk; ++k) rho = fmaxf(rho, colmax[r * nblk + k]);
     const float eps_scale = 65.0f * 0x1p-23f * rho;
     int32_t result[2];
     bool certified[2];
+#pragma unroll
     for (int q = 0; q < 2; ++q) {
       const uint32_t pm1 = __shfl_xor(m1[q], 32), pm2 = __shfl_xor(m2[q], 32);
       const uint32_t M1 = max(m1[q], pm1);
@@ -239,29 +277,32 @@ __global__ __launch_bounds__(256) void hash_kernel(const typename HashTraits<BF1
       const int win_h = m1[q] > pm1 ? hb : (m1[q] < pm1 ? (hb ^ 1) : 0);
       const uint32_t u = lowmask - (M1 & lowmask);  // 16 tg + e
       const int tg = (int)(u >> 4), e = (int)(u & 15);
-      const int jstar = 32 * tg + 8 * (e >> 2) + 4 * win_h + (e & 3);  // < halfp
+      const int jstar = 32 * tg + 8 * (e >> 2) + 4 * win_h + (e & 3);
       const float t1 = __uint_as_float(M1 & kmask), t2 = __uint_as_float(M2 & kmask);
       const float eps = eps_scale * (sqrtf(nrm2[q]) * 1.000001f);
       const int ebits = (int)((M1 >> 23) & 0xFFu) - 23 + ibits;
       const float delta = ebits >= 1 ? __uint_as_float((uint32_t)ebits << 23) : 0x1p-126f;
       certified[q] = (t1 - t2) > 2.0f * eps + delta;
-      // Signed score of the winner: this lane's half of the dot product plus the partner's.
+      // Sign of the winner: its score recomputed from this lane's half of the
+      // token (the MFMA operand registers) and the partner lane's half.  When the
+      // decision is certified |score| > 2 eps, so the fp32 sign is exact.
       const T* rr = rot_t + ((size_t)r * halfp + jstar) * kD;
       float dp = 0.f;
       if constexpr (BF16) {
+#pragma unroll
         for (int s = 0; s < 4; ++s) {
-          uint4 raw = *(const uint4*)(rr + 16 * s + 8 * hb);
-          const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-          const uint4 xb = __builtin_bit_cast(uint4, bq16[q][s]);
-          const uint32_t xw[4] = {xb.x, xb.y, xb.z, xb.w};
+          const u32x4 w = *(const u32x4*)(rr + 16 * s + 8 * hb);
+          const u32x4 xb = __builtin_bit_cast(u32x4, bq16[q][s]);
+#pragma unroll
           for (int k = 0; k < 4; ++k) {
-            dp = fmaf(__uint_as_float(w[k] << 16), __uint_as_float(xw[k] << 16), dp);
-            dp = fmaf(__uint_as_float(w[k] & 0xFFFF0000u), __uint_as_float(xw[k] & 0xFFFF0000u), dp);
+            dp = fmaf(__uint_as_float(w[k] << 16), __uint_as_float(xb[k] << 16), dp);
+            dp = fmaf(__uint_as_float(w[k] & 0xFFFF0000u), __uint_as_float(xb[k] & 0xFFFF0000u), dp);
           }
         }
       } else {
+#pragma unroll
         for (int s4 = 0; s4 < 8; ++s4) {
-          float4 a4 = *(const float4*)(rr + 32 * hb + 4 * s4);
+          const float4 a4 = *(const float4*)(rr + 32 * hb + 4 * s4);
           dp = fmaf(a4.x, bq32[q][4 * s4 + 0], dp);
           dp = fmaf(a4.y, bq32[q][4 * s4 + 1], dp);
           dp = fmaf(a4.z, bq32[q][4 * s4 + 2], dp);
@@ -273,11 +314,11 @@ __global__ __launch_bounds__(256) void hash_kernel(const typename HashTraits<BF1
     }
     if (wave_valid) {
       // Lanes 0-31 store group 0, lanes 32-63 group 1: 64 consecutive tokens.
-      const int q = hb;
-      const int tok = tok_base + 32 * q + n;
+      const int tok = tok_base + 32 * hb + n;
       const size_t idx = ((size_t)bh * n_h + r) * L + tok;
-      if (certified[q]) {
-        buckets[idx] = result[q];
+      const bool cert = hb ? certified[1] : certified[0];
+      if (cert) {
+        buckets[idx] = hb ? result[1] : result[0];
       } else {
         buckets[idx] = -1;
         const int slot = atomicAdd(fix_count, 1);
@@ -286,6 +327,9 @@ __global__ __launch_bounds__(256) void hash_kernel(const typename HashTraits<BF1
     }
   }
 }
+
+#undef LSH_HASH_PREFETCH
+#undef LSH_HASH_STAGE
 
 // ---------------------------------------------------------------------------
 // Float64 re-decision of queued tokens: one wave per token-round, lane l scores

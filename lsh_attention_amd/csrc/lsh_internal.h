@@ -13,17 +13,29 @@ constexpr int kD = 64;          // head dimension handled by the kernels
 constexpr int kChunk = 64;      // chunk length handled by the attention kernel
 constexpr int kMaxHashes = 16;  // upper bound on hash rounds
 constexpr int kMaxBuckets = 4096;
-constexpr int kSortTile = 2048; // tokens per sort workgroup
+constexpr int kSortWaveTokens = 512;  // tokens ranked by one wave of the sort scatter
+constexpr int kMaxLen = 1 << 24; // rows are addressed with 32-bit byte offsets
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Columns of the transposed rotation, padded to whole 32-column MFMA tiles.
 inline int padded_half(int n_b) { return n_b == 1 ? 0 : (int)align_up((size_t)(n_b / 2), 32); }
-inline int sort_tiles(int L) { return (L + kSortTile - 1) / kSortTile; }
+// Waves per sort tile: as many as the per-wave LDS counters allow (4 * n_b bytes
+// each, 64 KiB per block) and the sequence needs, 1..16.  Larger tiles give
+// longer runs of consecutive output slots per bucket (fewer partial-line writes).
+inline int sort_waves(int L, int n_b) {
+  int w = 16384 / (n_b < 1 ? 1 : n_b);
+  const int need = (L + kSortWaveTokens - 1) / kSortWaveTokens;
+  if (w > need) w = need;
+  return w < 1 ? 1 : (w > 16 ? 16 : w);
+}
+inline int sort_tile(int L, int n_b) { return kSortWaveTokens * sort_waves(L, n_b); }
+inline int sort_tiles(int L, int n_b) { return (L + sort_tile(L, n_b) - 1) / sort_tile(L, n_b); }
 
 // ---- launchers (stream-ordered, no synchronisation) ----
 // Rotation transpose [n_h][D][half] -> [n_h][halfp][D] with zero padding, the
@@ -47,12 +59,19 @@ hipError_t launch_sort_scatter(const int32_t* buckets, const int* hist, int32_t*
                                int32_t* undo_idx, int BHR, int L, int n_b, int n_h,
                                hipStream_t s);
 
+// token_order = false: outputs per sorted slot ([BH][n_h*L][64], [BH][n_h*L]);
+// token_order = true: per token and round ([BH][L][n_h][64], [BH][L][n_h]).
 hipError_t launch_chunk_attn(const void* qk, const void* v, const int32_t* sorted_idx,
-                             void* o_sorted, float* lse_sorted, int BH, int L, int n_h,
-                             int causal, lsh_dtype dt, hipStream_t s);
+                             void* o_out, float* lse_out, int BH, int L, int n_h,
+                             int causal, bool token_order, lsh_dtype dt, hipStream_t s);
 
+// Unsort + combine from the per-slot layout, through undo_idx.
 hipError_t launch_combine(const void* o_sorted, const float* lse_sorted, const int32_t* undo_idx,
                           void* out, float* lse_out, int BH, int L, int n_h, lsh_dtype dt,
                           hipStream_t s);
+// Combine from the per-token layout (no index needed: each token's rounds are contiguous).
+hipError_t launch_combine_token_order(const void* o_tok, const float* lse_tok, void* out,
+                                      float* lse_out, int BH, int L, int n_h, lsh_dtype dt,
+                                      hipStream_t s);
 
 }  // namespace lsh

@@ -7,7 +7,7 @@
 //
 // With at most 4096 buckets this is a counting sort, O(n) rather than the
 // explainer's O(n log n) comparison sort, in three launches per call:
-//   hist    - per (problem, round, tile of kSortTile tokens) bucket histogram
+//   hist    - per (problem, round, tile of sort_tile() tokens) bucket histogram
 //             in LDS, stored hist[bhr][tile][bucket] (coalesced rows);
 //   scan    - per (problem, round): bucket totals over tiles, an exclusive
 //             scan over buckets, then the running sum down the tiles, which
@@ -28,12 +28,12 @@ __device__ inline int clamp_bucket(int32_t b, int n_b) { return (int)min((uint32
 
 __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t* __restrict__ buckets,
                                                         int* __restrict__ hist, int L, int n_b,
-                                                        int n_tiles) {
+                                                        int n_tiles, int tile_len) {
   extern __shared__ int sh[];  // n_b counters
   const int bhr = blockIdx.x / n_tiles, tile = blockIdx.x % n_tiles;
   for (int b = threadIdx.x; b < n_b; b += blockDim.x) sh[b] = 0;
   __syncthreads();
-  const int t0 = tile * kSortTile, t1 = min(L, t0 + kSortTile);
+  const int t0 = tile * tile_len, t1 = min(L, t0 + tile_len);
   const int32_t* bk = buckets + (size_t)bhr * L;
   for (int i = t0 + (int)threadIdx.x; i < t1; i += blockDim.x) atomicAdd(&sh[clamp_bucket(bk[i], n_b)], 1);
   __syncthreads();
@@ -43,7 +43,10 @@ __global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t* __restric
 
 // One block of 1024 threads per (problem, round).  Offsets in the order
 // (bucket, tile): slot(b, t) = sum_{b' < b} total(b') + sum_{t' < t} count(b', t).
+// Each thread owns buckets b, b + 1024, ...; counts are read in groups of 32
+// tiles held in registers, so the loads of a group are all in flight together.
 constexpr int kScanThreads = 1024;
+constexpr int kScanGroup = 32;
 __global__ __launch_bounds__(kScanThreads) void sort_scan_kernel(int* __restrict__ hist, int n_b, int n_tiles) {
   int* h = hist + (size_t)blockIdx.x * n_tiles * n_b;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -52,9 +55,15 @@ __global__ __launch_bounds__(kScanThreads) void sort_scan_kernel(int* __restrict
   int carry = 0;
   for (int b0 = 0; b0 < n_b; b0 += kScanThreads) {
     const int b = b0 + (int)threadIdx.x;
+    const bool own = b < n_b;
     int tot = 0;
-    if (b < n_b)
-      for (int t = 0; t < n_tiles; ++t) tot += h[(size_t)t * n_b + b];
+    for (int t0 = 0; t0 < n_tiles; t0 += kScanGroup) {
+      int v[kScanGroup];
+#pragma unroll
+      for (int k = 0; k < kScanGroup; ++k) v[k] = (own && t0 + k < n_tiles) ? h[(size_t)(t0 + k) * n_b + b] : 0;
+#pragma unroll
+      for (int k = 0; k < kScanGroup; ++k) tot += v[k];
+    }
     int incl = tot;
     for (int off = 1; off < 64; off <<= 1) {
       const int y = __shfl_up(incl, off);
@@ -67,12 +76,15 @@ __global__ __launch_bounds__(kScanThreads) void sort_scan_kernel(int* __restrict
       if (w < wave) woff += wsum[w];
       all += wsum[w];
     }
-    if (b < n_b) {
-      int run = carry + woff + incl - tot;
-      for (int t = 0; t < n_tiles; ++t) {
-        const int c = h[(size_t)t * n_b + b];
-        h[(size_t)t * n_b + b] = run;
-        run += c;
+    int run = carry + woff + incl - tot;
+    for (int t0 = 0; t0 < n_tiles; t0 += kScanGroup) {
+      int v[kScanGroup];
+#pragma unroll
+      for (int k = 0; k < kScanGroup; ++k) v[k] = (own && t0 + k < n_tiles) ? h[(size_t)(t0 + k) * n_b + b] : 0;
+#pragma unroll
+      for (int k = 0; k < kScanGroup; ++k) {
+        if (own && t0 + k < n_tiles) h[(size_t)(t0 + k) * n_b + b] = run;
+        run += v[k];
       }
     }
     carry += all;
@@ -80,19 +92,19 @@ __global__ __launch_bounds__(kScanThreads) void sort_scan_kernel(int* __restrict
   }
 }
 
-__global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __restrict__ buckets,
-                                                           const int* __restrict__ hist,
-                                                           int32_t* __restrict__ sorted_idx,
-                                                           int32_t* __restrict__ undo_idx, int L, int n_b,
-                                                           int n_h, int n_tiles, int nbits) {
-  extern __shared__ int sh[];  // 4 waves x n_b running offsets
+__global__ __launch_bounds__(1024) void sort_scatter_kernel(const int32_t* __restrict__ buckets,
+                                                            const int* __restrict__ hist,
+                                                            int32_t* __restrict__ sorted_idx,
+                                                            int32_t* __restrict__ undo_idx, int L, int n_b,
+                                                            int n_h, int n_tiles, int nbits) {
+  extern __shared__ int sh[];  // waves x n_b running offsets
+  const int waves = blockDim.x >> 6;
   const int bhr = blockIdx.x / n_tiles, tile = blockIdx.x % n_tiles;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = tile * kSortTile, t1 = min(L, t0 + kSortTile);
-  constexpr int kPerWave = kSortTile / 4;
-  const int w0 = t0 + wave * kPerWave, w1 = min(t1, w0 + kPerWave);
+  const int t0 = tile * waves * kSortWaveTokens, t1 = min(L, t0 + waves * kSortWaveTokens);
+  const int w0 = t0 + wave * kSortWaveTokens, w1 = min(t1, w0 + kSortWaveTokens);
   int* cnt = sh + wave * n_b;
-  for (int b = threadIdx.x; b < 4 * n_b; b += blockDim.x) sh[b] = 0;
+  for (int b = threadIdx.x; b < waves * n_b; b += blockDim.x) sh[b] = 0;
   __syncthreads();
   const int32_t* bk = buckets + (size_t)bhr * L;
   // 1. per-wave counts of its sub-tile
@@ -103,7 +115,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
   const int* hs = hist + ((size_t)bhr * n_tiles + tile) * n_b;
   for (int b = threadIdx.x; b < n_b; b += blockDim.x) {
     int run = hs[b];
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < waves; ++w) {
       const int c = sh[w * n_b + b];
       sh[w * n_b + b] = run;
       run += c;
@@ -139,23 +151,23 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
 }  // namespace
 
 hipError_t launch_sort_hist(const int32_t* buckets, int* hist, int BHR, int L, int n_b, hipStream_t s) {
-  const int nt = sort_tiles(L);
-  sort_hist_kernel<<<nt * BHR, 256, n_b * sizeof(int), s>>>(buckets, hist, L, n_b, nt);
+  const int nt = sort_tiles(L, n_b);
+  sort_hist_kernel<<<nt * BHR, 256, n_b * sizeof(int), s>>>(buckets, hist, L, n_b, nt, sort_tile(L, n_b));
   return hipGetLastError();
 }
 
 hipError_t launch_sort_scan(int* hist, int BHR, int L, int n_b, hipStream_t s) {
-  sort_scan_kernel<<<BHR, kScanThreads, 0, s>>>(hist, n_b, sort_tiles(L));
+  sort_scan_kernel<<<BHR, kScanThreads, 0, s>>>(hist, n_b, sort_tiles(L, n_b));
   return hipGetLastError();
 }
 
 hipError_t launch_sort_scatter(const int32_t* buckets, const int* hist, int32_t* sorted_idx,
                                int32_t* undo_idx, int BHR, int L, int n_b, int n_h, hipStream_t s) {
-  const int nt = sort_tiles(L);
+  const int nt = sort_tiles(L, n_b), waves = sort_waves(L, n_b);
   int nbits = 0;
   while ((1 << nbits) < n_b) ++nbits;
-  sort_scatter_kernel<<<nt * BHR, 256, 4 * n_b * sizeof(int), s>>>(buckets, hist, sorted_idx, undo_idx, L,
-                                                                        n_b, n_h, nt, nbits);
+  sort_scatter_kernel<<<nt * BHR, 64 * waves, waves * n_b * sizeof(int), s>>>(buckets, hist, sorted_idx,
+                                                                             undo_idx, L, n_b, n_h, nt, nbits);
   return hipGetLastError();
 }
 
