@@ -68,7 +68,7 @@ size_t sort_ws_bytes(int BH, int L, int n_b, int n_h) {
 
 struct FwdWs {
   HashWs hash;
-  size_t hash_base, sort_base, buckets, sorted_idx, undo_idx, o_sorted, lse_sorted, total;
+  size_t hash_base, sort_base, buckets, sorted_idx, undo_idx, o_sorted, lse_sorted, token_scales, total;
 };
 FwdWs fwd_ws(int BH, int L, int n_b, int n_h, lsh_dtype dt) {
   Carver c;
@@ -82,6 +82,7 @@ FwdWs fwd_ws(int BH, int L, int n_b, int n_h, lsh_dtype dt) {
   w.undo_idx = c.take(slots * sizeof(int32_t));
   w.o_sorted = c.take(slots * kD * elem_size(dt));
   w.lse_sorted = c.take(slots * sizeof(float));
+  w.token_scales = c.take((size_t)BH * L * sizeof(float2));
   w.total = c.off;
   return w;
 }
@@ -89,8 +90,9 @@ FwdWs fwd_ws(int BH, int L, int n_b, int n_h, lsh_dtype dt) {
 int hip_status(hipError_t e) { return e == hipSuccess ? LSH_OK : LSH_ERR_HIP; }
 
 // Enqueue hashing (prep, MFMA hash, fixup) into the given scratch regions.
-hipError_t enqueue_hash(const void* qk, const void* rot, int32_t* buckets, char* ws, const HashWs& w, int BH,
-                        int L, int n_b, int n_h, lsh_dtype dt, hipStream_t s, void* const* ev, int* k) {
+hipError_t enqueue_hash(const void* qk, const void* rot, int32_t* buckets, float2* token_scales, char* ws,
+                        const HashWs& w, int BH, int L, int n_b, int n_h, lsh_dtype dt, hipStream_t s,
+                        void* const* ev, int* k) {
   auto mark = [&](void) -> hipError_t {
     if (ev == nullptr) return hipSuccess;
     ++*k;
@@ -109,7 +111,9 @@ hipError_t enqueue_hash(const void* qk, const void* rot, int32_t* buckets, char*
   void* rot_t = ws + w.rot_t;
   if ((e = launch_prep(rot, rot_t, colmax, count, n_h, n_b, dt, s)) != hipSuccess) return e;
   if ((e = mark()) != hipSuccess) return e;
-  if ((e = launch_hash(qk, rot_t, colmax, buckets, queue, count, BH, L, n_b, n_h, dt, s)) != hipSuccess) return e;
+  if ((e = launch_hash(qk, rot_t, colmax, buckets, queue, count, token_scales, BH, L, n_b, n_h, dt, s)) !=
+      hipSuccess)
+    return e;
   if ((e = mark()) != hipSuccess) return e;
   if ((e = launch_fixup(qk, rot_t, buckets, queue, count, L, n_b, n_h, dt, s)) != hipSuccess) return e;
   return mark();
@@ -177,8 +181,8 @@ int lsh_hash(const void* qk, const void* rot, int32_t* buckets, int B, int H, in
       overlaps(buckets, nb_bytes, ws, n_b > 1 ? ws_bytes : 0))
     return LSH_ERR_ALIAS;
   int k = 0;
-  return hip_status(enqueue_hash(qk, rot, buckets, (char*)ws, w, BH, L, n_b, n_h, dt, (hipStream_t)stream,
-                                 nullptr, &k));
+  return hip_status(enqueue_hash(qk, rot, buckets, nullptr, (char*)ws, w, BH, L, n_b, n_h, dt,
+                                 (hipStream_t)stream, nullptr, &k));
 }
 
 int lsh_sort_workspace_bytes(int B, int H, int L, int n_b, int n_h, size_t* bytes) {
@@ -228,7 +232,7 @@ int lsh_chunk_attn(const void* qk, const void* v, const int32_t* sorted_idx, voi
     if (overlaps(o_sorted, o_bytes, ins[a], in_n[a]) || overlaps(lse_sorted, l_bytes, ins[a], in_n[a]))
       return LSH_ERR_ALIAS;
   if (overlaps(o_sorted, o_bytes, lse_sorted, l_bytes)) return LSH_ERR_ALIAS;
-  return hip_status(launch_chunk_attn(qk, v, sorted_idx, o_sorted, lse_sorted, BH, L, n_h, causal, false, dt,
+  return hip_status(launch_chunk_attn(qk, v, sorted_idx, o_sorted, lse_sorted, nullptr, BH, L, n_h, causal, dt,
                                       (hipStream_t)stream));
 }
 
@@ -296,18 +300,22 @@ int reformer_lsh_attn_fwd(const void* qk, const void* v, const void* rot, int n_
   int32_t* undo_idx = (int32_t*)(base + w.undo_idx);
   void* o_sorted = base + w.o_sorted;
   float* lse_sorted = (float*)(base + w.lse_sorted);
+  // Per-token attention scales are a by-product of hashing; with one bucket there is
+  // no hash pass and the attention computes them itself.
+  float2* token_scales = n_b > 1 ? (float2*)(base + w.token_scales) : nullptr;
   int k = 0;
   hipError_t e = hipSuccess;
   if (stage_events != nullptr) e = hipEventRecord((hipEvent_t)stage_events[0], s);
   if (e == hipSuccess)
-    e = enqueue_hash(qk, rot, buckets, base + w.hash_base, w.hash, BH, L, n_b, n_h, dt, s, stage_events, &k);
+    e = enqueue_hash(qk, rot, buckets, token_scales, base + w.hash_base, w.hash, BH, L, n_b, n_h, dt, s,
+                     stage_events, &k);
   if (e == hipSuccess)
     e = enqueue_sort(buckets, sorted_idx, undo_idx, (int*)(base + w.sort_base), BH, L, n_b, n_h, s, stage_events,
                      &k);
-  // The fused path keeps the per-round results in token order, so the combine streams them.
-  if (e == hipSuccess) e = launch_chunk_attn(qk, v, sorted_idx, o_sorted, lse_sorted, BH, L, n_h, causal, true, dt, s);
+  if (e == hipSuccess)
+    e = launch_chunk_attn(qk, v, sorted_idx, o_sorted, lse_sorted, token_scales, BH, L, n_h, causal, dt, s);
   if (e == hipSuccess && stage_events != nullptr) e = hipEventRecord((hipEvent_t)stage_events[++k], s);
-  if (e == hipSuccess) e = launch_combine_token_order(o_sorted, lse_sorted, out, lse_out, BH, L, n_h, dt, s);
+  if (e == hipSuccess) e = launch_combine(o_sorted, lse_sorted, undo_idx, out, lse_out, BH, L, n_h, dt, s);
   if (e == hipSuccess && stage_events != nullptr) e = hipEventRecord((hipEvent_t)stage_events[++k], s);
   return hip_status(e);
 }

@@ -28,6 +28,8 @@
 //    lane holds one query's logits for 4 consecutive keys per 16-key tile.
 //  * O^T = V^T P^T on MFMA: the P^T operand is exactly the lane's own
 //    probabilities (the K index is permuted to match).
+//  * Per-row key scale and query bound come from the hash pass in the fused
+//    forward (token_scales); the standalone call computes them from the rows.
 //  * Softmax offset: keys are unit-normalised, so every logit is at most
 //    M_i = |x_i| / sqrt(64) (Cauchy-Schwarz).  Offsetting by M_i instead of the
 //    row maximum gives the same softmax and lse, needs no max reduction, and
@@ -41,10 +43,9 @@ namespace lsh {
 
 namespace {
 
-constexpr int kChunksPerBlock = 16;
+constexpr int kChunksPerBlock = 32;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kScale2 = 0.125f * kLog2e;        // 1/sqrt(64), base 2
 constexpr float kSelf2 = -1.0e5f * kLog2e;        // self logit, base 2
 constexpr float kMinSum = 0x1p-60f;               // fast-path validity threshold
 
@@ -70,16 +71,14 @@ struct AttnTraits<false> {
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 
-// TOKEN_ORDER = false: o and lse are written per sorted slot ([B,H,n_h*L,64], [B,H,n_h*L]).
-// TOKEN_ORDER = true: per token and round ([B,H,L,n_h,64], [B,H,L,n_h]), which lets the
-// combine read each token's rounds as one contiguous stream.
-template <bool BF16, bool CAUSAL, bool TOKEN_ORDER>
+template <bool BF16, bool CAUSAL>
 __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTraits<BF16>::T* __restrict__ qk,
                                                          const typename AttnTraits<BF16>::T* __restrict__ v,
                                                          const int32_t* __restrict__ sorted_idx,
                                                          typename AttnTraits<BF16>::T* __restrict__ o_out,
-                                                         float* __restrict__ lse_out, int L, int n_slots,
-                                                         int n_chunks, int blocks_per_bh) {
+                                                         float* __restrict__ lse_out,
+                                                         const float2* __restrict__ token_scales, int L,
+                                                         int n_slots, int n_chunks, int blocks_per_bh) {
   using T = typename AttnTraits<BF16>::T;
   constexpr int kXRow = AttnTraits<BF16>::kXRow;
   constexpr int kVRow = AttnTraits<BF16>::kVRow;
@@ -106,8 +105,6 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
   const int32_t* sidx = sorted_idx + (size_t)bh * n_slots;
   T* obase = o_out + (size_t)bh * n_slots * kD;
   float* lbase = lse_out + (size_t)bh * n_slots;
-  const int n_h = n_slots / L;
-  const int chunks_per_round = L / kChunk;
 
   // Positions of the previous chunk of c0 and of chunks c0..c1-1 (entry k <-> chunk c0-1+k).
   // Positions come from a permutation of [0, L); the clamp only keeps a
@@ -124,9 +121,12 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
   // v: bf16: dims 2p, 2p+1 (p = t&31) of rows 8(t>>5)..+7; fp32: dim t&63 of rows 16(t>>6)..+15.
   uint4 xr[kXLoads];
   uint32_t vw[kVWords];
+  float2 tsc = make_float2(0.f, 0.f);  // (key scale, query bound) of row tid, when precomputed
   const int xrow = tid >> 2, xq4 = tid & 3;
+  const float2* tsq = token_scales == nullptr ? nullptr : token_scales + (size_t)bh * L;
   auto gather = [&](int k) {
     const int* pos = sPos[k];
+    if (tsq != nullptr && tid < 64) tsc = tsq[pos[tid]];
     const uint32_t xoff = (uint32_t)pos[xrow] * kRowBytes + 16u * xq4 * (uint32_t)sizeof(T);
 #pragma unroll
     for (int i = 0; i < kXLoads; ++i) xr[i] = *(const uint4*)(xq + xoff + 16u * i);
@@ -146,6 +146,12 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
 #pragma unroll
     for (int i = 0; i < kXLoads; ++i)
       *(uint4*)(&sX[slot][xrow * kXRow + 16 * xq4 + i * (16 / kXLoads)]) = xr[i];
+    if (tsq != nullptr) {
+      if (tid < 64) {
+        sKs[slot][tid] = tsc.x;
+        sM[slot][tid] = tsc.y;
+      }
+    } else {
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < kXLoads; ++i) {
@@ -165,9 +171,10 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
     ss += __shfl_xor(ss, 1);
     ss += __shfl_xor(ss, 2);
     if (xq4 == 0) {
-      const float nrm = __builtin_amdgcn_sqrtf(ss);
-      sKs[slot][xrow] = kScale2 * __builtin_amdgcn_rcpf(fmaxf(nrm, 1e-12f));
-      sM[slot][xrow] = kScale2 * nrm;
+      const float2 sc = token_scale(ss);
+      sKs[slot][xrow] = sc.x;
+      sM[slot][xrow] = sc.y;
+    }
     }
     if constexpr (BF16) {
       // V^T columns are keys in the order of the P.V operand: column 32h + 8g + 4b + e holds
@@ -350,11 +357,7 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
 
     // ---- normalise and store: lane holds dims 16 dt + 4 grp + 0..3 of its query ----
     const float rs = __builtin_amdgcn_rcpf(sum);
-    size_t row_g;
-    if constexpr (TOKEN_ORDER)
-      row_g = (size_t)qpos * n_h + c / chunks_per_round;
-    else
-      row_g = (size_t)c * kChunk + qrow;
+    const size_t row_g = (size_t)c * kChunk + qrow;
     T* orow = obase + row_g * kD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
@@ -378,33 +381,33 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
   }
 }
 
-template <bool BF16, bool TOKEN_ORDER>
+template <bool BF16>
 hipError_t launch_attn_t(const void* qk, const void* v, const int32_t* sorted_idx, void* o_out, float* lse_out,
-                         int BH, int L, int n_h, int causal, hipStream_t s) {
+                         const float2* token_scales, int BH, int L, int n_h, int causal, hipStream_t s) {
   using T = typename AttnTraits<BF16>::T;
   const int n_slots = n_h * L;
   const int n_chunks = n_slots / kChunk;
   const int blocks_per_bh = (n_chunks + kChunksPerBlock - 1) / kChunksPerBlock;
   const unsigned grid = (unsigned)blocks_per_bh * (unsigned)BH;
   if (causal)
-    chunk_attn_kernel<BF16, true, TOKEN_ORDER><<<grid, 256, 0, s>>>(
-        (const T*)qk, (const T*)v, sorted_idx, (T*)o_out, lse_out, L, n_slots, n_chunks, blocks_per_bh);
+    chunk_attn_kernel<BF16, true><<<grid, 256, 0, s>>>(
+        (const T*)qk, (const T*)v, sorted_idx, (T*)o_out, lse_out, token_scales, L, n_slots, n_chunks,
+        blocks_per_bh);
   else
-    chunk_attn_kernel<BF16, false, TOKEN_ORDER><<<grid, 256, 0, s>>>(
-        (const T*)qk, (const T*)v, sorted_idx, (T*)o_out, lse_out, L, n_slots, n_chunks, blocks_per_bh);
+    chunk_attn_kernel<BF16, false><<<grid, 256, 0, s>>>(
+        (const T*)qk, (const T*)v, sorted_idx, (T*)o_out, lse_out, token_scales, L, n_slots, n_chunks,
+        blocks_per_bh);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_chunk_attn(const void* qk, const void* v, const int32_t* sorted_idx, void* o_out,
-                             float* lse_out, int BH, int L, int n_h, int causal, bool token_order, lsh_dtype dt,
-                             hipStream_t s) {
+                             float* lse_out, const float2* token_scales, int BH, int L, int n_h, int causal,
+                             lsh_dtype dt, hipStream_t s) {
   if (dt == LSH_BF16)
-    return token_order ? launch_attn_t<true, true>(qk, v, sorted_idx, o_out, lse_out, BH, L, n_h, causal, s)
-                       : launch_attn_t<true, false>(qk, v, sorted_idx, o_out, lse_out, BH, L, n_h, causal, s);
-  return token_order ? launch_attn_t<false, true>(qk, v, sorted_idx, o_out, lse_out, BH, L, n_h, causal, s)
-                     : launch_attn_t<false, false>(qk, v, sorted_idx, o_out, lse_out, BH, L, n_h, causal, s);
+    return launch_attn_t<true>(qk, v, sorted_idx, o_out, lse_out, token_scales, BH, L, n_h, causal, s);
+  return launch_attn_t<false>(qk, v, sorted_idx, o_out, lse_out, token_scales, BH, L, n_h, causal, s);
 }
 
 }  // namespace lsh

@@ -97,104 +97,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ o
   if (lse_out != nullptr && sub == 0) lse_out[tok] = m + __logf(tot);
 }
 
-// Token-order layout: token i's n_h rows are contiguous ([BH][L][n_h][64]) and so are
-// its n_h lse values; 8 (bf16) or 16 (fp32) lanes per token, each owning 16 bytes of
-// every row, so the kernel is a pure stream.
-template <bool BF16, int NH>
-__global__ __launch_bounds__(256) void combine_tok_kernel(const char* __restrict__ o_tok,
-                                                          const float* __restrict__ lse_tok,
-                                                          char* __restrict__ out, float* __restrict__ lse_out,
-                                                          int n_h_rt, size_t n_tokens) {
-  constexpr int kLanesPerTok = BF16 ? 8 : 16;
-  constexpr int kRowBytes = kD * (BF16 ? 2 : 4);
-  constexpr int kMaxH = NH > 0 ? NH : kMaxHashes;
-  const int n_h = NH > 0 ? NH : n_h_rt;
-  const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const size_t tok = gid / kLanesPerTok;
-  const int sub = (int)(gid % kLanesPerTok);
-  if (tok >= n_tokens) return;
-  const char* rows = o_tok + tok * (size_t)n_h * kRowBytes + 16 * sub;
-  const float* lt = lse_tok + tok * (size_t)n_h;
-  uint4 raw[kMaxH];
-  float l[kMaxH];
-#pragma unroll
-  for (int r = 0; r < kMaxH; ++r)
-    if (r < n_h) raw[r] = *(const uint4*)(rows + (size_t)r * kRowBytes);
-#pragma unroll
-  for (int r = 0; r < kMaxH; ++r)
-    if (r < n_h) l[r] = lt[r];
-  float m = -INFINITY;
-#pragma unroll
-  for (int r = 0; r < kMaxH; ++r)
-    if (r < n_h) m = fmaxf(m, l[r]);
-  float w[kMaxH];
-  float tot = 0.f;
-#pragma unroll
-  for (int r = 0; r < kMaxH; ++r)
-    if (r < n_h) {
-      w[r] = __expf(l[r] - m);
-      tot += w[r];
-    }
-  const float inv = __builtin_amdgcn_rcpf(tot);
-  constexpr int kE = BF16 ? 8 : 4;
-  float acc[kE];
-#pragma unroll
-  for (int e = 0; e < kE; ++e) acc[e] = 0.f;
-#pragma unroll
-  for (int r = 0; r < kMaxH; ++r)
-    if (r < n_h) {
-      const float wr = w[r] * inv;
-      const uint32_t ww[4] = {raw[r].x, raw[r].y, raw[r].z, raw[r].w};
-      if constexpr (BF16) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          acc[2 * k] = fmaf(wr, __uint_as_float(ww[k] << 16), acc[2 * k]);
-          acc[2 * k + 1] = fmaf(wr, __uint_as_float(ww[k] & 0xFFFF0000u), acc[2 * k + 1]);
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) acc[k] = fmaf(wr, __uint_as_float(ww[k]), acc[k]);
-      }
-    }
-  char* orow = out + tok * kRowBytes + 16 * sub;
-  if constexpr (BF16) {
-    uint32_t pk[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      pk[k] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[2 * k]) |
-              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[2 * k + 1]) << 16);
-    *(uint4*)orow = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-  } else {
-    *(float4*)orow = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  }
-  if (lse_out != nullptr && sub == 0) lse_out[tok] = m + __logf(tot);
-}
-
-template <bool BF16>
-hipError_t launch_combine_tok_t(const void* o_tok, const float* lse_tok, void* out, float* lse_out, int BH, int L,
-                                int n_h, hipStream_t s) {
-  const size_t n_tokens = (size_t)BH * L;
-  const size_t threads = n_tokens * (BF16 ? 8 : 16);
-  const unsigned grid = (unsigned)((threads + 255) / 256);
-#define LSH_COMBINE_TOK_CASE(NHV)                                                                          \
-  case NHV:                                                                                                \
-    combine_tok_kernel<BF16, NHV><<<grid, 256, 0, s>>>((const char*)o_tok, lse_tok, (char*)out, lse_out,   \
-                                                       n_h, n_tokens);                                     \
-    break;
-  switch (n_h) {
-    LSH_COMBINE_TOK_CASE(1)
-    LSH_COMBINE_TOK_CASE(2)
-    LSH_COMBINE_TOK_CASE(3)
-    LSH_COMBINE_TOK_CASE(4)
-    LSH_COMBINE_TOK_CASE(8)
-    default:
-      combine_tok_kernel<BF16, 0><<<grid, 256, 0, s>>>((const char*)o_tok, lse_tok, (char*)out, lse_out, n_h,
-                                                       n_tokens);
-  }
-#undef LSH_COMBINE_TOK_CASE
-  return hipGetLastError();
-}
-
 template <bool BF16>
 hipError_t launch_combine_t(const void* o_sorted, const float* lse_sorted, const int32_t* undo_idx, void* out,
                             float* lse_out, int BH, int L, int n_h, hipStream_t s) {
@@ -221,12 +123,6 @@ hipError_t launch_combine_t(const void* o_sorted, const float* lse_sorted, const
 }
 
 }  // namespace
-
-hipError_t launch_combine_token_order(const void* o_tok, const float* lse_tok, void* out, float* lse_out, int BH,
-                                      int L, int n_h, lsh_dtype dt, hipStream_t s) {
-  if (dt == LSH_BF16) return launch_combine_tok_t<true>(o_tok, lse_tok, out, lse_out, BH, L, n_h, s);
-  return launch_combine_tok_t<false>(o_tok, lse_tok, out, lse_out, BH, L, n_h, s);
-}
 
 hipError_t launch_combine(const void* o_sorted, const float* lse_sorted, const int32_t* undo_idx, void* out,
                           float* lse_out, int BH, int L, int n_h, lsh_dtype dt, hipStream_t s) {

@@ -110,8 +110,9 @@ __global__ __launch_bounds__(256, 4) void hash_kernel(const typename HashTraits<
                                                    const typename HashTraits<BF16>::T* __restrict__ rot_t,
                                                    const float* __restrict__ colmax,
                                                    int32_t* __restrict__ buckets, int* __restrict__ fix_queue,
-                                                   int* __restrict__ fix_count, int L, int n_h, int half,
-                                                   int halfp, uint32_t lowmask, int ibits) {
+                                                   int* __restrict__ fix_count, float2* __restrict__ token_scales,
+                                                   int L, int n_h, int half, int halfp, uint32_t lowmask,
+                                                   int ibits) {
   using T = typename HashTraits<BF16>::T;
   constexpr int kRow = HashTraits<BF16>::kRow;
   __shared__ __attribute__((aligned(16))) T sR[kHashCB * kRow];
@@ -166,6 +167,8 @@ __global__ __launch_bounds__(256, 4) void hash_kernel(const typename HashTraits<
     }
     nrm2[q] = acc + __shfl_xor(acc, 32);
   }
+  if (token_scales != nullptr && wave_valid)  // lanes 0-31: group 0, lanes 32-63: group 1
+    token_scales[(size_t)bh * L + tok_base + 32 * hb + n] = token_scale(hb ? nrm2[1] : nrm2[0]);
 
   // Rotation blocks of kHashCB columns, over all rounds in order; block it+1 is
   // loaded into registers while block it is being used.
@@ -407,7 +410,7 @@ hipError_t launch_prep(const void* rot, void* rot_t, float* colmax, int* fix_cou
 }
 
 hipError_t launch_hash(const void* qk, const void* rot_t, const float* colmax, int32_t* buckets,
-                       int* fix_queue, int* fix_count, int BH, int L, int n_b, int n_h,
+                       int* fix_queue, int* fix_count, float2* token_scales, int BH, int L, int n_b, int n_h,
                        lsh_dtype dt, hipStream_t s) {
   const int half = n_b / 2, halfp = padded_half(n_b);
   // Codes 16 tg + e < halfp / 2 must fit in the low bits of the key.
@@ -417,10 +420,10 @@ hipError_t launch_hash(const void* qk, const void* rot_t, const float* colmax, i
   const unsigned grid = (unsigned)((L + kHashTok - 1) / kHashTok) * (unsigned)BH;
   if (dt == LSH_BF16)
     hash_kernel<true><<<grid, 256, 0, s>>>((const uint16_t*)qk, (const uint16_t*)rot_t, colmax, buckets, fix_queue,
-                                           fix_count, L, n_h, half, halfp, lowmask, ibits);
+                                           fix_count, token_scales, L, n_h, half, halfp, lowmask, ibits);
   else
     hash_kernel<false><<<grid, 256, 0, s>>>((const float*)qk, (const float*)rot_t, colmax, buckets, fix_queue,
-                                            fix_count, L, n_h, half, halfp, lowmask, ibits);
+                                            fix_count, token_scales, L, n_h, half, halfp, lowmask, ibits);
   return hipGetLastError();
 }
 

@@ -23,6 +23,15 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Attention logits are handled in base 2: logit * log2(e) = (x_i . x_j) * ks_j with
+// ks_j = log2(e) / (8 |x_j|) (scale 1/sqrt(64), key norm floored at 1e-12), and every
+// logit of query i is at most M_i = log2(e) |x_i| / 8.  From |x|^2: (ks, M).
+constexpr float kScale2 = 0.125f * 1.4426950408889634f;
+__device__ inline float2 token_scale(float norm2) {
+  const float nrm = __builtin_amdgcn_sqrtf(norm2);
+  return make_float2(kScale2 * __builtin_amdgcn_rcpf(fmaxf(nrm, 1e-12f)), kScale2 * nrm);
+}
+
 // Columns of the transposed rotation, padded to whole 32-column MFMA tiles.
 inline int padded_half(int n_b) { return n_b == 1 ? 0 : (int)align_up((size_t)(n_b / 2), 32); }
 // Waves per sort tile: as many as the per-wave LDS counters allow (4 * n_b bytes
@@ -44,9 +53,10 @@ inline int sort_tiles(int L, int n_b) { return (L + sort_tile(L, n_b) - 1) / sor
 inline int colmax_blocks(int n_b) { return (padded_half(n_b) + 63) / 64; }
 hipError_t launch_prep(const void* rot, void* rot_t, float* colmax, int* fix_count, int n_h, int n_b,
                        lsh_dtype dt, hipStream_t s);
+// token_scales (nullable): per token (key scale, query bound) for the attention pass.
 hipError_t launch_hash(const void* qk, const void* rot_t, const float* colmax, int32_t* buckets,
-                       int* fix_queue, int* fix_count, int BH, int L, int n_b, int n_h,
-                       lsh_dtype dt, hipStream_t s);
+                       int* fix_queue, int* fix_count, float2* token_scales, int BH, int L, int n_b,
+                       int n_h, lsh_dtype dt, hipStream_t s);
 hipError_t launch_fixup(const void* qk, const void* rot_t, int32_t* buckets, const int* fix_queue,
                         const int* fix_count, int L, int n_b, int n_h, lsh_dtype dt,
                         hipStream_t s);
@@ -59,19 +69,15 @@ hipError_t launch_sort_scatter(const int32_t* buckets, const int* hist, int32_t*
                                int32_t* undo_idx, int BHR, int L, int n_b, int n_h,
                                hipStream_t s);
 
-// token_order = false: outputs per sorted slot ([BH][n_h*L][64], [BH][n_h*L]);
-// token_order = true: per token and round ([BH][L][n_h][64], [BH][L][n_h]).
+// Outputs per sorted slot ([BH][n_h*L][64], [BH][n_h*L]).  token_scales (nullable): per
+// token (key scale, query bound) from the hash pass.
 hipError_t launch_chunk_attn(const void* qk, const void* v, const int32_t* sorted_idx,
-                             void* o_out, float* lse_out, int BH, int L, int n_h,
-                             int causal, bool token_order, lsh_dtype dt, hipStream_t s);
+                             void* o_out, float* lse_out, const float2* token_scales, int BH, int L,
+                             int n_h, int causal, lsh_dtype dt, hipStream_t s);
 
 // Unsort + combine from the per-slot layout, through undo_idx.
 hipError_t launch_combine(const void* o_sorted, const float* lse_sorted, const int32_t* undo_idx,
                           void* out, float* lse_out, int BH, int L, int n_h, lsh_dtype dt,
                           hipStream_t s);
-// Combine from the per-token layout (no index needed: each token's rounds are contiguous).
-hipError_t launch_combine_token_order(const void* o_tok, const float* lse_tok, void* out,
-                                      float* lse_out, int BH, int L, int n_h, lsh_dtype dt,
-                                      hipStream_t s);
 
 }  // namespace lsh

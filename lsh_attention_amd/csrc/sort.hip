@@ -26,7 +26,7 @@ namespace {
 
 __device__ inline int clamp_bucket(int32_t b, int n_b) { return (int)min((uint32_t)b, (uint32_t)(n_b - 1)); }
 
-__global__ __launch_bounds__(256) void sort_hist_kernel(const int32_t* __restrict__ buckets,
+__global__ __launch_bounds__(1024) void sort_hist_kernel(const int32_t* __restrict__ buckets,
                                                         int* __restrict__ hist, int L, int n_b,
                                                         int n_tiles, int tile_len) {
   extern __shared__ int sh[];  // n_b counters
@@ -152,7 +152,8 @@ __global__ __launch_bounds__(1024) void sort_scatter_kernel(const int32_t* __res
 
 hipError_t launch_sort_hist(const int32_t* buckets, int* hist, int BHR, int L, int n_b, hipStream_t s) {
   const int nt = sort_tiles(L, n_b);
-  sort_hist_kernel<<<nt * BHR, 256, n_b * sizeof(int), s>>>(buckets, hist, L, n_b, nt, sort_tile(L, n_b));
+  const int threads = min(1024, sort_tile(L, n_b));
+  sort_hist_kernel<<<nt * BHR, threads, n_b * sizeof(int), s>>>(buckets, hist, L, n_b, nt, sort_tile(L, n_b));
   return hipGetLastError();
 }
 

@@ -51,9 +51,11 @@ def test_all_stages_match_oracle(gpu_lib, name, shape, n_h):
     buckets, sidx, undo, o_s, l_s, out, lse = run_stages(qk, v, rot, w.n_buckets, n_h, w.causal)
     out_f, lse_f = bd.reformer_lsh_attn_fwd(qk, v, rot, w.n_buckets, n_h, 64, w.causal)
     torch.cuda.synchronize()
-    # The fused call runs the same kernels: identical bits.
-    assert torch.equal(out_f, out) and torch.equal(lse_f, lse)
     tol = TOL[w.dtype]
+    # The fused call takes its per-token scales from the hash pass and keeps the
+    # per-round results in token order; it agrees with the staged calls to rounding.
+    rel_check(f64(out_f), f64(out), tol, "fused vs staged")
+    gfo, gfl = f64(out_f), f64(lse_f)
     gb, gs, gu = buckets.cpu().numpy(), sidx.cpu().numpy(), undo.cpu().numpy()
     go, gl, gout, glse = f64(o_s), f64(l_s), f64(out), f64(lse)
     rot64 = None if inp.rot is None else inp.rot.values.astype(np.float64)
@@ -75,8 +77,10 @@ def test_all_stages_match_oracle(gpu_lib, name, shape, n_h):
             rel_check(gout[b, h], co, tol, f"combine b{b} h{h}")
             lse_check(glse[b, h], cl, f"combine lse b{b} h{h}")
             ref = O.forward_problem(x, vv, rot64, w.n_buckets, n_h, 64, w.causal)
-            rel_check(gout[b, h], ref["out"], tol, f"end-to-end b{b} h{h}")
-            lse_check(glse[b, h], ref["lse"], f"end-to-end lse b{b} h{h}")
+            rel_check(gout[b, h], ref["out"], tol, f"staged end-to-end b{b} h{h}")
+            lse_check(glse[b, h], ref["lse"], f"staged end-to-end lse b{b} h{h}")
+            rel_check(gfo[b, h], ref["out"], tol, f"fused end-to-end b{b} h{h}")
+            lse_check(gfl[b, h], ref["lse"], f"fused end-to-end lse b{b} h{h}")
     say(f"  ok; oracle near-ties (margin < 1e-6): {near} of {B * H * n_h * L} token-rounds")
 
 
