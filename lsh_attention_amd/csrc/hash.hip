@@ -24,9 +24,14 @@
 //    re-decided from float64 sums by `fixup_kernel`, so the result equals the
 //    exact-arithmetic argmax.
 //  * The rotation is shared by every (batch, head): it is transposed once per
-//    call into [n_h][n_b/2 padded to 32][D] so a workgroup stages it into LDS
-//    with 16-byte row loads (the next 128-column block is loaded into
-//    registers while the current one is used), and read by all four waves.
+//    call into [n_h][n_b/2 padded to 64][D] so a workgroup stages it into LDS
+//    in 64-column blocks with 16-byte row loads (block k+2 is loaded into
+//    registers while block k is used and block k+1 waits in the other LDS
+//    buffer), and read by all four waves.
+//  * Each wave runs a software pipeline over 32-column tiles: the MFMAs of
+//    tile t+1 are issued before the vector top-2 selection of tile t, so the
+//    matrix and vector work of a wave overlap (they hardly overlap across
+//    waves on gfx950).
 #include "lsh_internal.h"
 
 namespace lsh {
@@ -106,7 +111,7 @@ struct HashTraits<false> {
 };
 
 template <bool BF16>
-__global__ __launch_bounds__(256, 4) void hash_kernel(const typename HashTraits<BF16>::T* __restrict__ qk,
+__global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<BF16>::T* __restrict__ qk,
                                                    const typename HashTraits<BF16>::T* __restrict__ rot_t,
                                                    const float* __restrict__ colmax,
                                                    int32_t* __restrict__ buckets, int* __restrict__ fix_queue,
@@ -115,7 +120,7 @@ __global__ __launch_bounds__(256, 4) void hash_kernel(const typename HashTraits<
                                                    int ibits) {
   using T = typename HashTraits<BF16>::T;
   constexpr int kRow = HashTraits<BF16>::kRow;
-  __shared__ __attribute__((aligned(16))) T sR[kHashCB * kRow];
+  __shared__ __attribute__((aligned(16))) T sR[2][kHashCB * kRow];
 
   const int blocks_per_bh = (L + kHashTok - 1) / kHashTok;
   const int bh = blockIdx.x / blocks_per_bh;
@@ -170,97 +175,138 @@ __global__ __launch_bounds__(256, 4) void hash_kernel(const typename HashTraits<
   if (token_scales != nullptr && wave_valid)  // lanes 0-31: group 0, lanes 32-63: group 1
     token_scales[(size_t)bh * L + tok_base + 32 * hb + n] = token_scale(hb ? nrm2[1] : nrm2[0]);
 
-  // Rotation blocks of kHashCB columns, over all rounds in order; block it+1 is
-  // loaded into registers while block it is being used.
+  // Rotation blocks of kHashCB columns, over all rounds in order.  halfp is a
+  // multiple of kHashCB and rot_t is [n_h][halfp][D], so block k is the k-th
+  // contiguous run of kHashCB rows: thread t moves the 16-byte pieces
+  // t + 256 i of it, at fixed offsets.  Block k+2 is loaded into registers
+  // while block k is used and block k+1 waits in the other LDS buffer.
   constexpr int kPieces = BF16 ? 8 : 16;  // 16-byte pieces per 64-element row
   constexpr int kPer = BF16 ? 8 : 4;      // elements per piece
   constexpr int kPF = kHashCB * kPieces / 256;
-  const int nbpr = (halfp + kHashCB - 1) / kHashCB;  // blocks per round
+  constexpr uint32_t kBlockBytes = kHashCB * kD * sizeof(T);
+  const int nbpr = halfp / kHashCB;  // blocks per round
   const int total = n_h * nbpr;
+  int lds_off[kPF];
+#pragma unroll
+  for (int i = 0; i < kPF; ++i) {
+    const int c = (int)threadIdx.x + 256 * i;
+    lds_off[i] = (c / kPieces) * kRow + (c % kPieces) * kPer;
+  }
+  const uint32_t piece_off = 16u * threadIdx.x;
   u32x4 pf[kPF];  // native vector type: HIP's uint4 struct copies defeat register promotion here
-  // Load rotation block `it` into registers (rows clamped in bounds, so every
-  // load is unconditional and the array stays in registers) / write it to LDS.
-#define LSH_HASH_PREFETCH(it_)                                                                 \
-  {                                                                                            \
-    const int r_ = (it_) / nbpr, cb_ = ((it_) % nbpr) * kHashCB;                               \
-    const int lim_ = min(kHashCB, halfp - cb_) * kPieces - 1;                                  \
-    const T* src_ = rot_t + ((size_t)r_ * halfp + cb_) * kD;                                   \
-    _Pragma("unroll") for (int k_ = 0; k_ < kPF; ++k_) {                                       \
-      const int c_ = min((int)threadIdx.x + 256 * k_, lim_);                                   \
-      pf[k_] = *(const u32x4*)(src_ + (c_ / kPieces) * kD + (c_ % kPieces) * kPer);                  \
-    }                                                                                          \
-  }
-#define LSH_HASH_STAGE(it_)                                                                    \
-  {                                                                                            \
-    const int cb_ = ((it_) % nbpr) * kHashCB;                                                  \
-    const int lim_ = min(kHashCB, halfp - cb_) * kPieces;                                      \
-    _Pragma("unroll") for (int k_ = 0; k_ < kPF; ++k_) {                                       \
-      const int c_ = (int)threadIdx.x + 256 * k_;                                              \
-      if (c_ < lim_) *(u32x4*)(sR + (c_ / kPieces) * kRow + (c_ % kPieces) * kPer) = pf[k_];   \
-    }                                                                                          \
-  }
+  auto prefetch = [&](int k) {
+    const char* src = (const char*)rot_t + (size_t)k * kBlockBytes;  // wave-uniform
+#pragma unroll
+    for (int i = 0; i < kPF; ++i) pf[i] = *(const u32x4*)(src + (piece_off + 4096u * i));
+  };
+  auto stage = [&](int k) {
+    T* dst = sR[k & 1];
+#pragma unroll
+    for (int i = 0; i < kPF; ++i) *(u32x4*)(dst + lds_off[i]) = pf[i];
+  };
 
-  uint32_t m1[2], m2[2];  // running top-2 keys per token group
-  LSH_HASH_PREFETCH(0);
+  // Software pipeline over the stream of 32-column tiles (two per staged block):
+  // the MFMAs of the next tile are issued between the top-2 selection steps of
+  // the current one, so matrix and vector work of one wave overlap.  Blocks are
+  // double-buffered in LDS (block k in sR[k & 1]), one barrier per block.
+  uint32_t m1[2] = {0u, 0u}, m2[2] = {0u, 0u};  // running top-2 keys per token group
+  // One pipeline step: the MFMAs of tile t_next (from LDS buffer buf) into
+  // (n0, n1), interleaved in issue order with the top-2 selection of the
+  // finished tile tg_cur in (c0, c1).  In-order issue means a dependent MFMA
+  // blocks the instructions behind it, so each MFMA is followed by a share of
+  // the selection (two pair-steps, ten VALU ops) and sched_barrier pins that
+  // order.
+  auto step = [&](const T* buf, int t_next, f32x16& n0, f32x16& n1, int tg_cur, const f32x16& c0,
+                  const f32x16& c1) {
+    const uint32_t cbase = lowmask - 16u * (uint32_t)tg_cur;
+    auto pair = [&](int q, int e) {
+      const f32x16& c = q ? c1 : c0;
+      const uint32_t a = (__float_as_uint(c[e]) & kmask_v) | (cbase - e);
+      const uint32_t b = (__float_as_uint(c[e + 1]) & kmask_v) | (cbase - e - 1);
+      const uint32_t hi = umax3(m1[q], a, b);
+      m2[q] = max(m2[q], umed3(m1[q], a, b));
+      m1[q] = hi;
+    };
+    n0 = f32x16{};
+    n1 = f32x16{};
+    const T* arow = buf + (32 * t_next + n) * kRow;
+    if constexpr (BF16) {
+      bf16x8 a[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) a[s] = *(const bf16x8*)(arow + 16 * s + 8 * hb);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], bq16[0][s], n0, 0, 0, 0);
+        pair(0, 4 * s);
+        pair(0, 4 * s + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], bq16[1][s], n1, 0, 0, 0);
+        pair(1, 4 * s);
+        pair(1, 4 * s + 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      // fp32: 64 MFMA 32x32x2 per tile, one pair-step after every fourth.
+#pragma unroll
+      for (int s4 = 0; s4 < 8; ++s4) {
+        float4 a4 = *(const float4*)(arow + 32 * hb + 4 * s4);
+        const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          n0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[e], bq32[0][4 * s4 + e], n0, 0, 0, 0);
+          n1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[e], bq32[1][4 * s4 + e], n1, 0, 0, 0);
+        }
+        pair(0, 2 * s4);
+        pair(1, 2 * s4);
+      }
+    }
+  };
+  // First tile of the stream: MFMAs only.
+  auto project0 = [&](f32x16& n0, f32x16& n1) {
+    n0 = f32x16{};
+    n1 = f32x16{};
+    const T* arow = sR[0] + n * kRow;
+    if constexpr (BF16) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 a = *(const bf16x8*)(arow + 16 * s + 8 * hb);
+        n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq16[0][s], n0, 0, 0, 0);
+        n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq16[1][s], n1, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int s4 = 0; s4 < 8; ++s4) {
+        const float4 a4 = *(const float4*)(arow + 32 * hb + 4 * s4);
+        const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          n0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[e], bq32[0][4 * s4 + e], n0, 0, 0, 0);
+          n1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av[e], bq32[1][4 * s4 + e], n1, 0, 0, 0);
+        }
+      }
+    }
+  };
+  f32x16 ea0, ea1, ob0, ob1;  // accumulators of the even / odd tile of a block
+  prefetch(0);
+  stage(0);
+  if (total > 1) prefetch(1);
+  __syncthreads();
+  project0(ea0, ea1);
+  int r = 0, cb = 0;  // round and first column of block it
   for (int it = 0; it < total; ++it) {
-    const int r = it / nbpr, cb = (it % nbpr) * kHashCB;
-    const int ncols = min(kHashCB, halfp - cb);
-    if (cb == 0) {
-      m1[0] = m1[1] = m2[0] = m2[1] = 0u;
+    step(sR[it & 1], 1, ob0, ob1, cb >> 5, ea0, ea1);
+    if (it + 1 < total) {
+      // sR[(it + 1) & 1] was last read before the previous iteration's barrier.
+      stage(it + 1);
+      if (it + 2 < total) prefetch(it + 2);
     }
     __syncthreads();
-    LSH_HASH_STAGE(it);
-    __syncthreads();
-    if (it + 1 < total) LSH_HASH_PREFETCH(it + 1);
-    const int nt = ncols / 32;
-    auto project = [&](int t, f32x16& acc0, f32x16& acc1) {
-      acc0 = f32x16{};
-      acc1 = f32x16{};
-      const T* arow = sR + (32 * t + n) * kRow;
-      if constexpr (BF16) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          bf16x8 a = *(const bf16x8*)(arow + 16 * s + 8 * hb);
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq16[0][s], acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq16[1][s], acc1, 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int s4 = 0; s4 < 8; ++s4) {
-          float4 a4 = *(const float4*)(arow + 32 * hb + 4 * s4);
-          const float a[4] = {a4.x, a4.y, a4.z, a4.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], bq32[0][4 * s4 + e], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], bq32[1][4 * s4 + e], acc1, 0, 0, 0);
-          }
-        }
-      }
-    };
-    auto select = [&](int t, const f32x16& acc0, const f32x16& acc1) {
-      // Column code of accumulator e of tile tg: lowmask - (16 tg + e).
-      const uint32_t tg = (uint32_t)((cb >> 5) + t);
-      const uint32_t cbase = lowmask - 16u * tg;
-#pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        uint32_t a0 = (__float_as_uint(acc0[e]) & kmask_v) | (cbase - e);
-        uint32_t b0 = (__float_as_uint(acc0[e + 1]) & kmask_v) | (cbase - e - 1);
-        uint32_t hi0 = umax3(m1[0], a0, b0);
-        m2[0] = max(m2[0], umed3(m1[0], a0, b0));
-        m1[0] = hi0;
-        uint32_t a1 = (__float_as_uint(acc1[e]) & kmask_v) | (cbase - e);
-        uint32_t b1 = (__float_as_uint(acc1[e + 1]) & kmask_v) | (cbase - e - 1);
-        uint32_t hi1 = umax3(m1[1], a1, b1);
-        m2[1] = max(m2[1], umed3(m1[1], a1, b1));
-        m1[1] = hi1;
-      }
-    };
-    for (int t = 0; t < nt; ++t) {
-      f32x16 ca0, ca1;
-      project(t, ca0, ca1);
-      select(t, ca0, ca1);
-    }
-    if (cb + kHashCB < halfp) continue;
+    // After the last block this reads the other (stale but in-bounds) buffer
+    // and the result is unused: it keeps the step free of branches.
+    step(sR[(it + 1) & 1], 0, ea0, ea1, (cb >> 5) + 1, ob0, ob1);
+    cb += kHashCB;
+    if (cb < halfp) continue;
+    cb = 0;
 
     // End of round r: merge with the partner lane (same tokens, the other 16 rows
     // of each tile), decode the winner, certify, take the sign.
@@ -328,11 +374,11 @@ __global__ __launch_bounds__(256, 4) void hash_kernel(const typename HashTraits<
         fix_queue[slot] = (int)idx;
       }
     }
+    m1[0] = m1[1] = m2[0] = m2[1] = 0u;
+    ++r;
   }
 }
 
-#undef LSH_HASH_PREFETCH
-#undef LSH_HASH_STAGE
 
 // ---------------------------------------------------------------------------
 // Float64 re-decision of queued tokens: one wave per token-round, lane l scores

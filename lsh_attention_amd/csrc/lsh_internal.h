@@ -32,8 +32,9 @@ __device__ inline float2 token_scale(float norm2) {
   return make_float2(kScale2 * __builtin_amdgcn_rcpf(fmaxf(nrm, 1e-12f)), kScale2 * nrm);
 }
 
-// Columns of the transposed rotation, padded to whole 32-column MFMA tiles.
-inline int padded_half(int n_b) { return n_b == 1 ? 0 : (int)align_up((size_t)(n_b / 2), 32); }
+// Columns of the transposed rotation, padded to whole 64-column staging blocks
+// (two 32-column MFMA tiles).
+inline int padded_half(int n_b) { return n_b == 1 ? 0 : (int)align_up((size_t)(n_b / 2), 64); }
 // Waves per sort tile: as many as the per-wave LDS counters allow (4 * n_b bytes
 // each, 64 KiB per block) and the sequence needs, 1..16.  Larger tiles give
 // longer runs of consecutive output slots per bucket (fewer partial-line writes).
