@@ -12,8 +12,9 @@
 // Per slot the kernel writes the softmax-weighted sum of V and the logits'
 // log-sum-exp.
 //
-// gfx950 design (one block of 4 waves walks a run of consecutive chunks of one
-// (batch, head); wave w owns queries 16w..16w+15 of the current chunk):
+// gfx950 design (one block of 4 waves walks a run of 8 consecutive chunks of
+// one (batch, head); wave w owns queries 16w..16w+15 of the current chunk; 128
+// VGPRs and 38 KiB of LDS per block, so 4 blocks share a CU):
 //  * Gathers are software-pipelined: the 64 x rows and 64 v rows of chunk c+1
 //    (128-byte rows addressed through sorted_idx) are loaded into registers
 //    while chunk c is computed, then written to LDS.  The previous chunk's
@@ -30,6 +31,8 @@
 //    probabilities (the K index is permuted to match).
 //  * Per-row key scale and query bound come from the hash pass in the fused
 //    forward (token_scales); the standalone call computes them from the rows.
+//  * A query's 128 logits sit in 4 lanes (l, l^16, l^32, l^48); their sums and
+//    maxima use the gfx950 permlane32/permlane16 swaps, not LDS.
 //  * Softmax offset: keys are unit-normalised, so every logit is at most
 //    M_i = |x_i| / sqrt(64) (Cauchy-Schwarz).  Offsetting by M_i instead of the
 //    row maximum gives the same softmax and lse, needs no max reduction, and
@@ -43,7 +46,7 @@ namespace lsh {
 
 namespace {
 
-constexpr int kChunksPerBlock = 32;
+constexpr int kChunksPerBlock = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSelf2 = -1.0e5f * kLog2e;        // self logit, base 2
@@ -70,9 +73,10 @@ struct AttnTraits<false> {
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 
 template <bool BF16, bool CAUSAL>
-__global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTraits<BF16>::T* __restrict__ qk,
+__global__ __launch_bounds__(256, BF16 ? 4 : 2) void chunk_attn_kernel(const typename AttnTraits<BF16>::T* __restrict__ qk,
                                                          const typename AttnTraits<BF16>::T* __restrict__ v,
                                                          const int32_t* __restrict__ sorted_idx,
                                                          typename AttnTraits<BF16>::T* __restrict__ o_out,
@@ -134,12 +138,12 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
       const uint32_t p4 = 4u * (tid & 31);
       const int j = tid >> 5, r0 = 32 * (j >> 2) + 4 * (j & 3);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) vw[i] = *(const uint32_t*)(vq + (uint32_t)pos[r0 + (i & 3) + 16 * (i >> 2)] * kRowBytes + p4);
+      for (int i = 0; i < 8; ++i) vw[i] = *(const uint32_t*)(vq + ((uint32_t)pos[r0 + (i & 3) + 16 * (i >> 2)] * kRowBytes + p4));
     } else {
       const uint32_t p4 = 4u * (tid & 63);
       const int r0 = 16 * (tid >> 6);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) vw[i] = *(const uint32_t*)(vq + (uint32_t)pos[r0 + i] * kRowBytes + p4);
+      for (int i = 0; i < 16; ++i) vw[i] = *(const uint32_t*)(vq + ((uint32_t)pos[r0 + i] * kRowBytes + p4));
     }
   };
   auto commit = [&](int slot) {
@@ -208,6 +212,21 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
   commit(c0 & 1);
   __syncthreads();
 
+  // Sum / max over the 4 lanes holding one query (lanes l, l^16, l^32, l^48)
+  // with the gfx950 cross-lane swaps (no LDS round trip).
+  auto qsum = [](float x) {
+    auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+    auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+  };
+  auto qmax = [](float x) {
+    auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+    auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+  };
+
   for (int c = c0; c < c1; ++c) {
     const int cur = c & 1, prv = cur ^ 1;
     const int kc = c - c0 + 1;  // sPos entry of chunk c
@@ -218,47 +237,89 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
     const float M2 = sM[cur][qrow];
 
     // ---- S^T = K Q^T : 8 key tiles of 16 (tiles 0-3 previous chunk, 4-7 current) ----
-    f32x4 acc[8];
-    if constexpr (BF16) {
-      const bf16x8 bq0 = *(const bf16x8*)(&sX[cur][qrow * kXRow + 8 * grp]);
-      const bf16x8 bq1 = *(const bf16x8*)(&sX[cur][qrow * kXRow + 32 + 8 * grp]);
+    auto scores = [&](f32x4 (&acc)[8]) {
+      if constexpr (BF16) {
+        const bf16x8 bq0 = *(const bf16x8*)(&sX[cur][qrow * kXRow + 8 * grp]);
+        const bf16x8 bq1 = *(const bf16x8*)(&sX[cur][qrow * kXRow + 32 + 8 * grp]);
 #pragma unroll
-      for (int kt = 0; kt < 8; ++kt) {
-        const T* kr = &sX[kt < 4 ? prv : cur][(16 * (kt & 3) + col) * kXRow];
-        const bf16x8 a0 = *(const bf16x8*)(kr + 8 * grp);
-        const bf16x8 a1 = *(const bf16x8*)(kr + 32 + 8 * grp);
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bq0, z, 0, 0, 0);
-        acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bq1, z, 0, 0, 0);
-      }
-    } else {
-      // k-step s of 4 dims: lane group g feeds dim 16g + s.
-      float bq[16];
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const float4 t = *(const float4*)(&sX[cur][qrow * kXRow + 16 * grp + 4 * s4]);
-        bq[4 * s4] = t.x;
-        bq[4 * s4 + 1] = t.y;
-        bq[4 * s4 + 2] = t.z;
-        bq[4 * s4 + 3] = t.w;
-      }
-#pragma unroll
-      for (int kt = 0; kt < 8; ++kt) {
-        const T* kr = &sX[kt < 4 ? prv : cur][(16 * (kt & 3) + col) * kXRow + 16 * grp];
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        for (int kt = 0; kt < 8; ++kt) {
+          const T* kr = &sX[kt < 4 ? prv : cur][(16 * (kt & 3) + col) * kXRow];
+          const bf16x8 a0 = *(const bf16x8*)(kr + 8 * grp);
+          const bf16x8 a1 = *(const bf16x8*)(kr + 32 + 8 * grp);
+          f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bq0, z, 0, 0, 0);
+          acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bq1, z, 0, 0, 0);
+        }
+      } else {
+        // k-step s of 4 dims: lane group g feeds dim 16g + s.
+        float bq[16];
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
-          const float4 t = *(const float4*)(kr + 4 * s4);
-          z = __builtin_amdgcn_mfma_f32_16x16x4f32(t.x, bq[4 * s4 + 0], z, 0, 0, 0);
-          z = __builtin_amdgcn_mfma_f32_16x16x4f32(t.y, bq[4 * s4 + 1], z, 0, 0, 0);
-          z = __builtin_amdgcn_mfma_f32_16x16x4f32(t.z, bq[4 * s4 + 2], z, 0, 0, 0);
-          z = __builtin_amdgcn_mfma_f32_16x16x4f32(t.w, bq[4 * s4 + 3], z, 0, 0, 0);
+          const float4 t = *(const float4*)(&sX[cur][qrow * kXRow + 16 * grp + 4 * s4]);
+          bq[4 * s4] = t.x;
+          bq[4 * s4 + 1] = t.y;
+          bq[4 * s4 + 2] = t.z;
+          bq[4 * s4 + 3] = t.w;
         }
-        acc[kt] = z;
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) {
+          const T* kr = &sX[kt < 4 ? prv : cur][(16 * (kt & 3) + col) * kXRow + 16 * grp];
+          f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4) {
+            const float4 t = *(const float4*)(kr + 4 * s4);
+            z = __builtin_amdgcn_mfma_f32_16x16x4f32(t.x, bq[4 * s4 + 0], z, 0, 0, 0);
+            z = __builtin_amdgcn_mfma_f32_16x16x4f32(t.y, bq[4 * s4 + 1], z, 0, 0, 0);
+            z = __builtin_amdgcn_mfma_f32_16x16x4f32(t.z, bq[4 * s4 + 2], z, 0, 0, 0);
+            z = __builtin_amdgcn_mfma_f32_16x16x4f32(t.w, bq[4 * s4 + 3], z, 0, 0, 0);
+          }
+          acc[kt] = z;
+        }
       }
-    }
+    };
 
-    // ---- probabilities, offset by the a-priori bound M2 ----
+    // ---- O^T = V^T P^T ----
+    auto pv = [&](const float (&p)[8][4], f32x4 (&oacc)[4]) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (BF16) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          // K index (grp, e): e < 4 -> key 4 grp + e of tile 2ks; e >= 4 -> of tile 2ks + 1.
+          const f32x4 lo = {p[2 * ks][0], p[2 * ks][1], p[2 * ks][2], p[2 * ks][3]};
+          const f32x4 hi = {p[2 * ks + 1][0], p[2 * ks + 1][1], p[2 * ks + 1][2], p[2 * ks + 1][3]};
+          const bf16x4 blo = __builtin_convertvector(lo, bf16x4);
+          const bf16x4 bhi = __builtin_convertvector(hi, bf16x4);
+          const bf16x8 bp = __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7);
+          const int slot = ks < 2 ? prv : cur;
+          // keys of tiles 2ks and 2ks+1 seen by lane group grp: V^T columns 32 (ks & 1) + 8 grp + 0..7
+          const int vcol = 64 * slot + 32 * (ks & 1) + 8 * grp;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const bf16x8 a = *(const bf16x8*)(&sVT[(16 * dt + col) * kVRow + vcol]);
+            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bp, oacc[dt], 0, 0, 0);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) {
+          const int slot = kt < 4 ? prv : cur;
+          const int kcol = 64 * slot + 16 * (kt & 3) + 4 * grp;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const float4 a = *(const float4*)(&sVT[(16 * dt + col) * kVRow + kcol]);
+            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, p[kt][0], oacc[dt], 0, 0, 0);
+            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, p[kt][1], oacc[dt], 0, 0, 0);
+            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, p[kt][2], oacc[dt], 0, 0, 0);
+            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, p[kt][3], oacc[dt], 0, 0, 0);
+          }
+        }
+      }
+    };
+
+    f32x4 acc[8];
+    scores(acc);
+    // ---- fast path: probabilities offset by the a-priori bound M2, masks as zeroes ----
     float p[8][4];
     float sum = 0.f;
 #pragma unroll
@@ -277,12 +338,16 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
         sum += p[kt][e];
       }
     }
-    sum += __shfl_xor(sum, 16);
-    sum += __shfl_xor(sum, 32);
+    sum = qsum(sum);
+    f32x4 oacc[4];
+    pv(p, oacc);
     float off = M2;
-    const bool slow = !(sum >= kMinSum);
-    if (__ballot(slow) != 0ull) {
-      // Exact path for the wave: logits with the -1e5 self value, row maximum.
+    if (__builtin_expect(__ballot(!(sum >= kMinSum)) != 0ull, 0)) {
+      // Exact path for the wave (rare): logits with the -1e5 self value and the
+      // row maximum, recomputed from the LDS tiles.  The clobber makes this path
+      // reload its LDS operands instead of keeping the fast path's loads live.
+      asm volatile("" ::: "memory");
+      scores(acc);
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 8; ++kt) {
@@ -294,15 +359,14 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
         const int kpos[4] = {kp.x, kp.y, kp.z, kp.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float s = acc[kt][e] * ksv[e];
-          if (kpos[e] == qpos) s = kSelf2;
-          if (CAUSAL && kpos[e] > qpos) s = -INFINITY;
-          p[kt][e] = s;
-          mx = fmaxf(mx, s);
+          float sc = acc[kt][e] * ksv[e];
+          if (kpos[e] == qpos) sc = kSelf2;
+          if (CAUSAL && kpos[e] > qpos) sc = -INFINITY;
+          p[kt][e] = sc;
+          mx = fmaxf(mx, sc);
         }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = qmax(mx);
       sum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 8; ++kt)
@@ -311,48 +375,9 @@ __global__ __launch_bounds__(256) void chunk_attn_kernel(const typename AttnTrai
           p[kt][e] = __builtin_amdgcn_exp2f(p[kt][e] - mx);
           sum += p[kt][e];
         }
-      sum += __shfl_xor(sum, 16);
-      sum += __shfl_xor(sum, 32);
+      sum = qsum(sum);
       off = mx;
-    }
-
-    // ---- O^T = V^T P^T ----
-    f32x4 oacc[4];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (BF16) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        // K index (grp, e): e < 4 -> key 4 grp + e of tile 2ks; e >= 4 -> of tile 2ks + 1.
-        bf16x8 bp;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bp[e] = (__bf16)p[2 * ks][e];
-          bp[4 + e] = (__bf16)p[2 * ks + 1][e];
-        }
-        const int slot = ks < 2 ? prv : cur;
-        // keys of tiles 2ks and 2ks+1 seen by lane group grp: V^T columns 32 (ks & 1) + 8 grp + 0..7
-        const int kc = 64 * slot + 32 * (ks & 1) + 8 * grp;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const bf16x8 a = *(const bf16x8*)(&sVT[(16 * dt + col) * kVRow + kc]);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bp, oacc[dt], 0, 0, 0);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int kt = 0; kt < 8; ++kt) {
-        const int slot = kt < 4 ? prv : cur;
-        const int kcol = 64 * slot + 16 * (kt & 3) + 4 * grp;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const float4 a = *(const float4*)(&sVT[(16 * dt + col) * kVRow + kcol]);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, p[kt][0], oacc[dt], 0, 0, 0);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, p[kt][1], oacc[dt], 0, 0, 0);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, p[kt][2], oacc[dt], 0, 0, 0);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, p[kt][3], oacc[dt], 0, 0, 0);
-        }
-      }
+      pv(p, oacc);
     }
 
     // ---- normalise and store: lane holds dims 16 dt + 4 grp + 0..3 of its query ----
