@@ -42,10 +42,12 @@ def algorithmic_work(B, H, L, D, n_b, n_h, es):
         "sort_hist": {"bytes": tr * 4, "flops": 0},
         "sort_scan": {"bytes": 0, "flops": 0},
         "sort_scatter": {"bytes": tr * 12, "flops": 0},
-        # index + one output row + lse per token-round, QK and V rows read once per token-head
-        "chunk_attn": {"bytes": tr * (4 + D * es + 4) + th * 2 * D * es, "flops": tr * 4 * D * 128},
-        # per token-head: n_h rows + lse + undo index, one output row
-        "combine": {"bytes": th * (n_h * (D * es + 8) + D * es), "flops": 0},
+        # per token-round (slot of the sorted order): its index, its gathered QK and V
+        # rows, its output row and lse.  Each round's chunks read their rows in that
+        # round's order, so every row is gathered once per round.
+        "chunk_attn": {"bytes": tr * (4 + 3 * D * es + 4), "flops": tr * 4 * D * 128},
+        # per token-head: n_h rows + lse + undo index read, one output row + LSE written
+        "combine": {"bytes": th * (n_h * (D * es + 8) + D * es + 4), "flops": 0},
     }
 
 
