@@ -32,6 +32,15 @@ __device__ inline float2 token_scale(float norm2) {
   return make_float2(kScale2 * __builtin_amdgcn_rcpf(fmaxf(nrm, 1e-12f)), kScale2 * nrm);
 }
 
+// Work-item order for launches whose consecutive items share data.  The chip's 8
+// XCDs each have their own L2, and workgroups are handed to XCDs round-robin by
+// block index.  A launch of xcd_grid(n) blocks that maps block b to item
+// xcd_item(b, gridDim.x) (items >= n return at once) runs items
+// [x*g/8, (x+1)*g/8) on XCD x, in order (g = xcd_grid(n)).
+constexpr unsigned kXcds = 8;
+inline unsigned xcd_grid(unsigned n) { return (n + kXcds - 1) / kXcds * kXcds; }
+__device__ inline unsigned xcd_item(unsigned b, unsigned grid) { return (b % kXcds) * (grid / kXcds) + b / kXcds; }
+
 // Columns of the transposed rotation, padded to whole 64-column staging blocks
 // (two 32-column MFMA tiles).
 inline int padded_half(int n_b) { return n_b == 1 ? 0 : (int)align_up((size_t)(n_b / 2), 64); }

@@ -28,9 +28,11 @@ __device__ inline int clamp_bucket(int32_t b, int n_b) { return (int)min((uint32
 
 __global__ __launch_bounds__(1024) void sort_hist_kernel(const int32_t* __restrict__ buckets,
                                                         int* __restrict__ hist, int L, int n_b,
-                                                        int n_tiles, int tile_len) {
+                                                        int n_tiles, int tile_len, int n_items) {
   extern __shared__ int sh[];  // n_b counters
-  const int bhr = blockIdx.x / n_tiles, tile = blockIdx.x % n_tiles;
+  const unsigned item = xcd_item(blockIdx.x, gridDim.x);  // the tiles of one problem share an XCD
+  if (item >= (unsigned)n_items) return;
+  const int bhr = (int)item / n_tiles, tile = (int)item % n_tiles;
   for (int b = threadIdx.x; b < n_b; b += blockDim.x) sh[b] = 0;
   __syncthreads();
   const int t0 = tile * tile_len, t1 = min(L, t0 + tile_len);
@@ -96,10 +98,14 @@ __global__ __launch_bounds__(1024) void sort_scatter_kernel(const int32_t* __res
                                                             const int* __restrict__ hist,
                                                             int32_t* __restrict__ sorted_idx,
                                                             int32_t* __restrict__ undo_idx, int L, int n_b,
-                                                            int n_h, int n_tiles, int nbits) {
+                                                            int n_h, int n_tiles, int nbits, int n_items) {
   extern __shared__ int sh[];  // waves x n_b running offsets
   const int waves = blockDim.x >> 6;
-  const int bhr = blockIdx.x / n_tiles, tile = blockIdx.x % n_tiles;
+  // The tiles of one problem share an XCD, so the scattered writes of one
+  // problem's sorted index meet in one L2 and leave it as whole lines.
+  const unsigned item = xcd_item(blockIdx.x, gridDim.x);
+  if (item >= (unsigned)n_items) return;
+  const int bhr = (int)item / n_tiles, tile = (int)item % n_tiles;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t0 = tile * waves * kSortWaveTokens, t1 = min(L, t0 + waves * kSortWaveTokens);
   const int w0 = t0 + wave * kSortWaveTokens, w1 = min(t1, w0 + kSortWaveTokens);
@@ -153,7 +159,8 @@ __global__ __launch_bounds__(1024) void sort_scatter_kernel(const int32_t* __res
 hipError_t launch_sort_hist(const int32_t* buckets, int* hist, int BHR, int L, int n_b, hipStream_t s) {
   const int nt = sort_tiles(L, n_b);
   const int threads = min(1024, sort_tile(L, n_b));
-  sort_hist_kernel<<<nt * BHR, threads, n_b * sizeof(int), s>>>(buckets, hist, L, n_b, nt, sort_tile(L, n_b));
+  sort_hist_kernel<<<xcd_grid(nt * BHR), threads, n_b * sizeof(int), s>>>(buckets, hist, L, n_b, nt,
+                                                                           sort_tile(L, n_b), nt * BHR);
   return hipGetLastError();
 }
 
@@ -167,8 +174,8 @@ hipError_t launch_sort_scatter(const int32_t* buckets, const int* hist, int32_t*
   const int nt = sort_tiles(L, n_b), waves = sort_waves(L, n_b);
   int nbits = 0;
   while ((1 << nbits) < n_b) ++nbits;
-  sort_scatter_kernel<<<nt * BHR, 64 * waves, waves * n_b * sizeof(int), s>>>(buckets, hist, sorted_idx,
-                                                                             undo_idx, L, n_b, n_h, nt, nbits);
+  sort_scatter_kernel<<<xcd_grid(nt * BHR), 64 * waves, waves * n_b * sizeof(int), s>>>(
+      buckets, hist, sorted_idx, undo_idx, L, n_b, n_h, nt, nbits, nt * BHR);
   return hipGetLastError();
 }
 
