@@ -40,7 +40,7 @@ def algorithmic_work(B, H, L, D, n_b, n_h, es):
         "hash": {"bytes": th * (D * es + 4 * n_h), "flops": 2 * th * D * half * n_h},
         "fixup": {"bytes": 0, "flops": 0},
         "sort_hist": {"bytes": tr * 4, "flops": 0},
-        "sort_scan": {"bytes": 0, "flops": 0},
+        # scatter: read each bucket id, write its sorted index and unsort index
         "sort_scatter": {"bytes": tr * 12, "flops": 0},
         # per token-round (slot of the sorted order): its index, its gathered QK and V
         # rows, its output row and lse.  Each round's chunks read their rows in that

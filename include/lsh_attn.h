@@ -115,11 +115,10 @@ int lsh_unsort_combine(const void* o_sorted, const float* lse_sorted, const int3
 #define LSH_FWD_KERNEL_HASH 1      /* MFMA projection + certified argmax */
 #define LSH_FWD_KERNEL_FIXUP 2     /* float64 re-decision of uncertified tokens */
 #define LSH_FWD_KERNEL_HIST 3      /* per-tile bucket histograms */
-#define LSH_FWD_KERNEL_SCAN 4      /* exclusive scan of the histograms */
-#define LSH_FWD_KERNEL_SCATTER 5   /* stable in-tile ranking + scatter */
-#define LSH_FWD_KERNEL_ATTN 6      /* chunked attention */
-#define LSH_FWD_KERNEL_COMBINE 7   /* unsort + combine */
-#define LSH_FWD_N_KERNELS 8
+#define LSH_FWD_KERNEL_SCATTER 4   /* histogram scan + stable in-tile ranking + scatter */
+#define LSH_FWD_KERNEL_ATTN 5      /* chunked attention */
+#define LSH_FWD_KERNEL_COMBINE 6   /* unsort + combine */
+#define LSH_FWD_N_KERNELS 7
 #define LSH_FWD_N_EVENTS (LSH_FWD_N_KERNELS + 1)
 
 int lsh_fwd_workspace_bytes(int B, int H, int L, int D, int n_b, int n_h, int C, lsh_dtype dt,

@@ -19,9 +19,9 @@ _HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__)
 _lib = None
 
 LSH_F32, LSH_BF16 = 0, 1
-N_KERNELS = 8
+N_KERNELS = 7
 N_EVENTS = N_KERNELS + 1
-KERNEL_NAMES = ["prep", "hash", "fixup", "sort_hist", "sort_scan", "sort_scatter", "chunk_attn", "combine"]
+KERNEL_NAMES = ["prep", "hash", "fixup", "sort_hist", "sort_scatter", "chunk_attn", "combine"]
 
 _c_int, _c_size, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 _SIGS = {

@@ -130,8 +130,6 @@ hipError_t enqueue_sort(const int32_t* buckets, int32_t* sorted_idx, int32_t* un
   hipError_t e;
   if ((e = launch_sort_hist(buckets, hist, BHR, L, n_b, s)) != hipSuccess) return e;
   if ((e = mark()) != hipSuccess) return e;
-  if ((e = launch_sort_scan(hist, BHR, L, n_b, s)) != hipSuccess) return e;
-  if ((e = mark()) != hipSuccess) return e;
   if ((e = launch_sort_scatter(buckets, hist, sorted_idx, undo_idx, BHR, L, n_b, n_h, s)) != hipSuccess) return e;
   return mark();
 }

@@ -74,7 +74,6 @@ hipError_t launch_fill_zero(int32_t* p, size_t n, hipStream_t s);
 
 hipError_t launch_sort_hist(const int32_t* buckets, int* hist, int BHR, int L, int n_b,
                             hipStream_t s);
-hipError_t launch_sort_scan(int* hist, int BHR, int L, int n_b, hipStream_t s);
 hipError_t launch_sort_scatter(const int32_t* buckets, const int* hist, int32_t* sorted_idx,
                                int32_t* undo_idx, int BHR, int L, int n_b, int n_h,
                                hipStream_t s);

@@ -6,13 +6,13 @@
 // is unique the permutation is fully determined.
 //
 // With at most 4096 buckets this is a counting sort, O(n) rather than the
-// explainer's O(n log n) comparison sort, in three launches per call:
+// explainer's O(n log n) comparison sort, in two launches per call:
 //   hist    - per (problem, round, tile of sort_tile() tokens) bucket histogram
 //             in LDS, stored hist[bhr][tile][bucket] (coalesced rows);
-//   scan    - per (problem, round): bucket totals over tiles, an exclusive
-//             scan over buckets, then the running sum down the tiles, which
-//             gives every (tile, bucket) its first output slot;
-//   scatter - each wave of a tile ranks its sub-tile's tokens in order: the
+//   scatter - each block first turns its problem's tile histograms into the
+//             first output slot of every (bucket, tile, wave) (bucket totals,
+//             an exclusive scan over buckets, the counts of earlier tiles and
+//             waves); then each wave ranks its sub-tile's tokens in order: the
 //             lanes holding the same bucket are found with one ballot per key
 //             bit, their rank is a popcount below the lane, and a per-wave LDS
 //             counter per bucket carries the running offset.
@@ -43,63 +43,13 @@ __global__ __launch_bounds__(1024) void sort_hist_kernel(const int32_t* __restri
   for (int b = threadIdx.x; b < n_b; b += blockDim.x) out[b] = sh[b];
 }
 
-// One block of 1024 threads per (problem, round).  Offsets in the order
-// (bucket, tile): slot(b, t) = sum_{b' < b} total(b') + sum_{t' < t} count(b', t).
-// Each thread owns buckets b, b + 1024, ...; counts are read in groups of 32
-// tiles held in registers, so the loads of a group are all in flight together.
-constexpr int kScanThreads = 1024;
-constexpr int kScanGroup = 32;
-__global__ __launch_bounds__(kScanThreads) void sort_scan_kernel(int* __restrict__ hist, int n_b, int n_tiles) {
-  int* h = hist + (size_t)blockIdx.x * n_tiles * n_b;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int kWaves = kScanThreads / 64;
-  __shared__ int wsum[kWaves];
-  int carry = 0;
-  for (int b0 = 0; b0 < n_b; b0 += kScanThreads) {
-    const int b = b0 + (int)threadIdx.x;
-    const bool own = b < n_b;
-    int tot = 0;
-    for (int t0 = 0; t0 < n_tiles; t0 += kScanGroup) {
-      int v[kScanGroup];
-#pragma unroll
-      for (int k = 0; k < kScanGroup; ++k) v[k] = (own && t0 + k < n_tiles) ? h[(size_t)(t0 + k) * n_b + b] : 0;
-#pragma unroll
-      for (int k = 0; k < kScanGroup; ++k) tot += v[k];
-    }
-    int incl = tot;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    int woff = 0, all = 0;
-    for (int w = 0; w < kWaves; ++w) {
-      if (w < wave) woff += wsum[w];
-      all += wsum[w];
-    }
-    int run = carry + woff + incl - tot;
-    for (int t0 = 0; t0 < n_tiles; t0 += kScanGroup) {
-      int v[kScanGroup];
-#pragma unroll
-      for (int k = 0; k < kScanGroup; ++k) v[k] = (own && t0 + k < n_tiles) ? h[(size_t)(t0 + k) * n_b + b] : 0;
-#pragma unroll
-      for (int k = 0; k < kScanGroup; ++k) {
-        if (own && t0 + k < n_tiles) h[(size_t)(t0 + k) * n_b + b] = run;
-        run += v[k];
-      }
-    }
-    carry += all;
-    __syncthreads();
-  }
-}
-
 __global__ __launch_bounds__(1024) void sort_scatter_kernel(const int32_t* __restrict__ buckets,
                                                             const int* __restrict__ hist,
                                                             int32_t* __restrict__ sorted_idx,
                                                             int32_t* __restrict__ undo_idx, int L, int n_b,
                                                             int n_h, int n_tiles, int nbits, int n_items) {
   extern __shared__ int sh[];  // waves x n_b running offsets
+  __shared__ int wtot[16];      // per-wave sums of the bucket scan
   const int waves = blockDim.x >> 6;
   // The tiles of one problem share an XCD, so the scattered writes of one
   // problem's sorted index meet in one L2 and leave it as whole lines.
@@ -116,16 +66,42 @@ __global__ __launch_bounds__(1024) void sort_scatter_kernel(const int32_t* __res
   // 1. per-wave counts of its sub-tile
   for (int i = w0 + lane; i < w1; i += 64) atomicAdd(&cnt[clamp_bucket(bk[i], n_b)], 1);
   __syncthreads();
-  // 2. first slot of (bucket, wave): the scanned (bucket, tile) offset plus the
-  //    counts of the earlier waves of this tile.
-  const int* hs = hist + ((size_t)bhr * n_tiles + tile) * n_b;
-  for (int b = threadIdx.x; b < n_b; b += blockDim.x) {
-    int run = hs[b];
+  // 2. first slot of (bucket, wave) in the round's output: the totals of all
+  //    smaller buckets, plus this bucket's counts in earlier tiles, plus its
+  //    counts in the earlier waves of this tile.  Each block scans the problem's
+  //    tile histograms itself (the same scan in every tile of the problem).
+  //    Thread t owns the contiguous buckets [t*per, (t+1)*per).
+  const int* hp = hist + (size_t)bhr * n_tiles * n_b;  // [tile][bucket] counts
+  const int nthr = (int)blockDim.x;
+  const int per = (n_b + nthr - 1) / nthr;
+  const int bb0 = min(n_b, (int)threadIdx.x * per), bb1 = min(n_b, bb0 + per);
+  int mine = 0;
+  for (int b = bb0; b < bb1; ++b)
+    for (int t = 0; t < n_tiles; ++t) mine += hp[(size_t)t * n_b + b];
+  // exclusive scan of `mine` over the threads of the block
+  int incl = mine;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  int run = incl - mine;
+  for (int w = 0; w < wave; ++w) run += wtot[w];
+  for (int b = bb0; b < bb1; ++b) {
+    int before = 0, total = 0;
+    for (int t = 0; t < n_tiles; ++t) {
+      const int c = hp[(size_t)t * n_b + b];
+      before += t < tile ? c : 0;
+      total += c;
+    }
+    int slot = run + before;
     for (int w = 0; w < waves; ++w) {
       const int c = sh[w * n_b + b];
-      sh[w * n_b + b] = run;
-      run += c;
+      sh[w * n_b + b] = slot;
+      slot += c;
     }
+    run += total;
   }
   __syncthreads();
   // 3. ordered walk, 64 tokens at a time.
@@ -161,11 +137,6 @@ hipError_t launch_sort_hist(const int32_t* buckets, int* hist, int BHR, int L, i
   const int threads = min(1024, sort_tile(L, n_b));
   sort_hist_kernel<<<xcd_grid(nt * BHR), threads, n_b * sizeof(int), s>>>(buckets, hist, L, n_b, nt,
                                                                            sort_tile(L, n_b), nt * BHR);
-  return hipGetLastError();
-}
-
-hipError_t launch_sort_scan(int* hist, int BHR, int L, int n_b, hipStream_t s) {
-  sort_scan_kernel<<<BHR, kScanThreads, 0, s>>>(hist, n_b, sort_tiles(L, n_b));
   return hipGetLastError();
 }
 

@@ -25,7 +25,7 @@ import sys
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 KERNEL_SOURCES = {
     "prep": ["hash.hip"], "hash": ["hash.hip"], "fixup": ["hash.hip"],
-    "sort_hist": ["sort.hip"], "sort_scan": ["sort.hip"], "sort_scatter": ["sort.hip"],
+    "sort_hist": ["sort.hip"], "sort_scatter": ["sort.hip"],
     "chunk_attn": ["chunk_attn.hip"], "combine": ["combine.hip"],
 }
 
