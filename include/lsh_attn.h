@@ -29,6 +29,9 @@
  *     lse arrays are fp32; index arrays are int32.
  *   - Limits: D == 64, C == 64, L % C == 0, n_b == 1 or even in [2, 4096],
  *     1 <= n_h <= 16, B*H*n_h*L <= 2^31 - 1.
+ *   - Empty problems: with B, H or L equal to 0 (and the other arguments
+ *     valid) a call returns LSH_OK without reading any pointer or enqueuing
+ *     any kernel, and the workspace-size queries report 0 bytes.
  *   - Outputs must not overlap inputs (LSH_ERR_ALIAS).
  */
 #ifndef LSH_ATTN_H
@@ -46,7 +49,7 @@ typedef enum { LSH_F32 = 0, LSH_BF16 = 1 } lsh_dtype;
 enum {
   LSH_OK = 0,
   LSH_ERR_NULL = -1,        /* a required pointer is NULL */
-  LSH_ERR_SHAPE = -2,       /* a dimension <= 0, L % C != 0, or an index overflows int32 */
+  LSH_ERR_SHAPE = -2,       /* B, H or L < 0, D or n_h <= 0, L % C != 0, or an index overflows int32 */
   LSH_ERR_BUCKETS = -3,     /* n_b < 1, odd n_b > 1, or n_b > 4096 */
   LSH_ERR_UNSUPPORTED = -4, /* D != 64, C != 64, n_h > 16, or unknown dtype */
   LSH_ERR_WORKSPACE = -5,   /* workspace pointer NULL or smaller than required */

@@ -15,8 +15,12 @@ size_t elem_size(lsh_dtype dt) { return dt == LSH_BF16 ? 2 : 4; }
 
 bool dtype_ok(lsh_dtype dt) { return dt == LSH_F32 || dt == LSH_BF16; }
 
+// B, H or L == 0 is a valid, empty problem: the entry points return LSH_OK at
+// once, with no pointer checked and nothing enqueued (workspace size 0).
+bool is_empty(int B, int H, int L) { return B == 0 || H == 0 || L == 0; }
+
 int check_problem(int B, int H, int L, int D, int n_h) {
-  if (B <= 0 || H <= 0 || L <= 0 || D <= 0 || n_h <= 0) return LSH_ERR_SHAPE;
+  if (B < 0 || H < 0 || L < 0 || D <= 0 || n_h <= 0) return LSH_ERR_SHAPE;
   if (D != kD) return LSH_ERR_UNSUPPORTED;
   if (n_h > kMaxHashes) return LSH_ERR_UNSUPPORTED;
   if (L % kChunk != 0 || L > kMaxLen) return LSH_ERR_SHAPE;
@@ -142,7 +146,7 @@ const char* lsh_status_string(int status) {
   switch (status) {
     case LSH_OK: return "ok";
     case LSH_ERR_NULL: return "a required pointer is NULL";
-    case LSH_ERR_SHAPE: return "invalid shape (dimension <= 0, L not a multiple of 64 or above 2^24, or int32 index overflow)";
+    case LSH_ERR_SHAPE: return "invalid shape (negative dimension, D or n_hashes <= 0, L not a multiple of 64 or above 2^24, or int32 index overflow)";
     case LSH_ERR_BUCKETS: return "invalid bucket count (must be 1 or even, at most 4096)";
     case LSH_ERR_UNSUPPORTED: return "unsupported configuration (D and chunk_len must be 64, n_hashes <= 16, dtype f32 or bf16)";
     case LSH_ERR_WORKSPACE: return "workspace missing or too small";
@@ -158,7 +162,7 @@ int lsh_hash_workspace_bytes(int B, int H, int L, int D, int n_b, int n_h, lsh_d
   if (st == LSH_OK) st = check_buckets(n_b, L);
   if (st == LSH_OK && !dtype_ok(dt)) st = LSH_ERR_UNSUPPORTED;
   if (st != LSH_OK) return st;
-  *bytes = hash_ws(B * H, L, n_b, n_h, dt).total;
+  *bytes = is_empty(B, H, L) ? 0 : hash_ws(B * H, L, n_b, n_h, dt).total;
   return LSH_OK;
 }
 
@@ -168,6 +172,7 @@ int lsh_hash(const void* qk, const void* rot, int32_t* buckets, int B, int H, in
   if (st == LSH_OK) st = check_buckets(n_b, L);
   if (st == LSH_OK && !dtype_ok(dt)) st = LSH_ERR_UNSUPPORTED;
   if (st != LSH_OK) return st;
+  if (is_empty(B, H, L)) return LSH_OK;
   if (qk == nullptr || buckets == nullptr || (n_b > 1 && rot == nullptr)) return LSH_ERR_NULL;
   const int BH = B * H;
   const HashWs w = hash_ws(BH, L, n_b, n_h, dt);
@@ -188,7 +193,7 @@ int lsh_sort_workspace_bytes(int B, int H, int L, int n_b, int n_h, size_t* byte
   int st = check_problem(B, H, L, kD, n_h);
   if (st == LSH_OK) st = check_buckets(n_b, L);
   if (st != LSH_OK) return st;
-  *bytes = sort_ws_bytes(B * H, L, n_b, n_h);
+  *bytes = is_empty(B, H, L) ? 0 : sort_ws_bytes(B * H, L, n_b, n_h);
   return LSH_OK;
 }
 
@@ -197,6 +202,7 @@ int lsh_sort(const int32_t* buckets, int32_t* sorted_idx, int32_t* undo_idx, int
   int st = check_problem(B, H, L, kD, n_h);
   if (st == LSH_OK) st = check_buckets(n_b, L);
   if (st != LSH_OK) return st;
+  if (is_empty(B, H, L)) return LSH_OK;
   if (buckets == nullptr || sorted_idx == nullptr || undo_idx == nullptr) return LSH_ERR_NULL;
   const int BH = B * H;
   const size_t need = sort_ws_bytes(BH, L, n_b, n_h);
@@ -217,6 +223,7 @@ int lsh_chunk_attn(const void* qk, const void* v, const int32_t* sorted_idx, voi
   if (st != LSH_OK) return st;
   if (C != kChunk) return C <= 0 ? LSH_ERR_SHAPE : LSH_ERR_UNSUPPORTED;
   if (!dtype_ok(dt)) return LSH_ERR_UNSUPPORTED;
+  if (is_empty(B, H, L)) return LSH_OK;
   if (qk == nullptr || v == nullptr || sorted_idx == nullptr || o_sorted == nullptr || lse_sorted == nullptr)
     return LSH_ERR_NULL;
   const int BH = B * H;
@@ -239,6 +246,7 @@ int lsh_unsort_combine(const void* o_sorted, const float* lse_sorted, const int3
   int st = check_problem(B, H, L, D, n_h);
   if (st != LSH_OK) return st;
   if (!dtype_ok(dt)) return LSH_ERR_UNSUPPORTED;
+  if (is_empty(B, H, L)) return LSH_OK;
   if (o_sorted == nullptr || lse_sorted == nullptr || undo_idx == nullptr || out == nullptr) return LSH_ERR_NULL;
   const int BH = B * H;
   const size_t es = elem_size(dt);
@@ -261,7 +269,7 @@ int lsh_fwd_workspace_bytes(int B, int H, int L, int D, int n_b, int n_h, int C,
   if (st != LSH_OK) return st;
   if (C != kChunk) return C <= 0 ? LSH_ERR_SHAPE : LSH_ERR_UNSUPPORTED;
   if (!dtype_ok(dt)) return LSH_ERR_UNSUPPORTED;
-  *bytes = fwd_ws(B * H, L, n_b, n_h, dt).total;
+  *bytes = is_empty(B, H, L) ? 0 : fwd_ws(B * H, L, n_b, n_h, dt).total;
   return LSH_OK;
 }
 
@@ -273,6 +281,13 @@ int reformer_lsh_attn_fwd(const void* qk, const void* v, const void* rot, int n_
   if (st != LSH_OK) return st;
   if (chunk_len != kChunk) return chunk_len <= 0 ? LSH_ERR_SHAPE : LSH_ERR_UNSUPPORTED;
   if (!dtype_ok(dt)) return LSH_ERR_UNSUPPORTED;
+  if (is_empty(B, H, L)) {
+    // Nothing to compute; the stage events are still recorded, back to back.
+    if (stage_events != nullptr)
+      for (int k = 0; k < LSH_FWD_N_EVENTS; ++k)
+        if (hipEventRecord((hipEvent_t)stage_events[k], (hipStream_t)stream) != hipSuccess) return LSH_ERR_HIP;
+    return LSH_OK;
+  }
   if (qk == nullptr || v == nullptr || out == nullptr || (n_buckets > 1 && rot == nullptr)) return LSH_ERR_NULL;
   const int BH = B * H, n_h = n_hashes, n_b = n_buckets;
   const FwdWs w = fwd_ws(BH, L, n_b, n_h, dt);

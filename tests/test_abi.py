@@ -55,7 +55,8 @@ def test_workspace_sizes(L):
 
 
 @pytest.mark.parametrize("args,expect", [
-    ((0, 1, 64, 64, 2, 1, 64, BF16), SHAPE),
+    ((-1, 1, 64, 64, 2, 1, 64, BF16), SHAPE),
+    ((1, 1, -64, 64, 2, 1, 64, BF16), SHAPE),
     ((1, 1, 100, 64, 2, 1, 64, BF16), SHAPE),       # L not a multiple of 64
     ((1, 1, 64, 32, 2, 1, 64, BF16), UNSUPPORTED),  # D != 64
     ((1, 1, 64, 64, 2, 1, 32, BF16), UNSUPPORTED),  # chunk_len != 64
@@ -114,6 +115,28 @@ def test_stage_calls_reject_before_launch(L):
     assert L.lsh_unsort_combine(P1, P2, P3, P4, P4, 1, 1, 256, 64, 2, BF16, None) == ALIAS
     assert L.lsh_event_create(None) == NULL
     assert L.lsh_event_elapsed_ms(None, None, None) == NULL
+
+
+@pytest.mark.parametrize("B,H,n", [(0, 1, 64), (1, 0, 64), (1, 1, 0), (0, 0, 0)])
+def test_empty_problems_are_no_ops(L, B, H, n):
+    # Zero-sized problems succeed without touching any pointer (all NULL here)
+    # and need no workspace; the other arguments are still validated.
+    for fn, args in [("lsh_fwd_workspace_bytes", (B, H, n, 64, 8, 2, 64, BF16)),
+                     ("lsh_hash_workspace_bytes", (B, H, n, 64, 8, 2, BF16)),
+                     ("lsh_sort_workspace_bytes", (B, H, n, 8, 2))]:
+        st, nbytes = _ws(fn, *args)
+        assert st == OK and nbytes == 0, fn
+    assert L.reformer_lsh_attn_fwd(None, None, None, 8, 2, 64, 1, B, H, n, 64, BF16, None, None, None, 0, None,
+                                   None) == OK
+    assert L.lsh_hash(None, None, None, B, H, n, 64, 8, 2, BF16, None, 0, None) == OK
+    assert L.lsh_sort(None, None, None, B, H, n, 8, 2, None, 0, None) == OK
+    assert L.lsh_chunk_attn(None, None, None, None, None, B, H, n, 64, 2, 64, 1, BF16, None) == OK
+    assert L.lsh_unsort_combine(None, None, None, None, None, B, H, n, 64, 2, BF16, None) == OK
+    # still validated: bucket count, chunk length, dtype
+    assert L.reformer_lsh_attn_fwd(None, None, None, 7, 2, 64, 1, B, H, n, 64, BF16, None, None, None, 0, None,
+                                   None) == BUCKETS
+    assert L.lsh_chunk_attn(None, None, None, None, None, B, H, n, 64, 2, 32, 1, BF16, None) == UNSUPPORTED
+    assert L.lsh_unsort_combine(None, None, None, None, None, B, H, n, 64, 2, 9, None) == UNSUPPORTED
 
 
 def test_binding_refuses_cpu_tensors():

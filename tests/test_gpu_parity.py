@@ -191,3 +191,19 @@ def test_caller_stream_and_workspace_reuse(gpu_lib):
         got = bd.reformer_lsh_attn_fwd(qk, v, rot, 8, 4, workspace=ws)[0]
     torch.cuda.synchronize()
     assert torch.equal(got, ref)
+
+
+@pytest.mark.parametrize("shape", [(0, 2, 64), (2, 0, 64), (1, 2, 0)])
+def test_empty_problems(gpu_lib, shape):
+    """Zero-sized batch, heads or length: every call succeeds and returns empty
+    outputs of the right shapes (the library enqueues nothing)."""
+    B, H, L = shape
+    say(f"case empty B{B} H{H} L{L}")
+    qk = torch.zeros((B, H, L, 64), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros_like(qk)
+    rot = torch.zeros((2, 64, 8), dtype=torch.bfloat16, device="cuda")
+    out, lse = bd.reformer_lsh_attn_fwd(qk, v, rot, 16, 2, 64, True)
+    buckets, sidx, undo, o_s, l_s, out_s, lse_s = run_stages(qk, v, rot, 16, 2, True)
+    assert out.shape == (B, H, L, 64) and lse.shape == (B, H, L)
+    assert buckets.shape == (B, H, 2, L) and sidx.shape == (B, H, 2 * L) and o_s.shape == (B, H, 2 * L, 64)
+    assert out_s.shape == (B, H, L, 64) and lse_s.shape == (B, H, L)
