@@ -32,6 +32,12 @@ Readings where the pages are silent (each listed in the design notes):
     original position is after the query's.
   * rounds are combined with weights softmax_r(lse_r), i.e. duplicates across
     rounds are counted with multiplicity.
+  * attended-set variants (the explainer's "attends to its bucket-mates" and
+    "unions the buckets", taken literally): with `same_bucket` a key slot
+    counts only if it holds the query's (round, bucket); with `dedup` every
+    distinct key token counts once over the union of the query's windows,
+    by subtracting log N from each occurrence's logit, N = the number of
+    kept (query occurrence, key occurrence) pairs of that token pair.
 """
 from __future__ import annotations
 
@@ -154,12 +160,48 @@ def window_slots(n_slots: int, chunk_len: int, c: int) -> np.ndarray:
                            np.arange(c * chunk_len, (c + 1) * chunk_len)])
 
 
+def slot_codes(buckets: np.ndarray, sorted_idx: np.ndarray) -> np.ndarray:
+    """(round, bucket) of every sorted slot, as one integer per slot: slot g of
+    round r = g // L holds token sorted_idx[g], whose bucket in that round is
+    buckets[r, token]."""
+    n_h, L = buckets.shape
+    g = np.arange(sorted_idx.shape[0])
+    r = g // L
+    return r * (int(buckets.max()) + 1) + buckets[r, sorted_idx]
+
+
+def pair_multiplicity(sorted_idx: np.ndarray, undo_idx: np.ndarray, chunk_len: int, causal: bool,
+                      codes=None) -> list:
+    """For every token i, a dict {token j: N_ij}: how many times j is a kept key
+    of i over all of i's windows (one query occurrence of i per round, each
+    window counted with multiplicity, the masks of the variant applied)."""
+    n_h, L = undo_idx.shape
+    n_slots = sorted_idx.shape[0]
+    counts = []
+    for i in range(L):
+        cnt = {}
+        for r in range(n_h):
+            g = int(undo_idx[r, i])
+            for gk in window_slots(n_slots, chunk_len, g // chunk_len):
+                j = int(sorted_idx[gk])
+                if causal and j > i:
+                    continue
+                if codes is not None and codes[gk] != codes[g]:
+                    continue
+                cnt[j] = cnt.get(j, 0) + 1
+        counts.append(cnt)
+    return counts
+
+
 def chunk_attention(x: np.ndarray, v: np.ndarray, sorted_idx: np.ndarray, chunk_len: int,
-                    causal: bool, chunks=None):
+                    causal: bool, chunks=None, codes=None, mult=None):
     """Per-round attention of every sorted slot over its window.
 
     Returns (o_sorted [n_slots, D], lse_sorted [n_slots]); with `chunks`
-    given, only those chunks' rows are filled (the rest are NaN)."""
+    given, only those chunks' rows are filled (the rest are NaN).
+    Variants: `codes` (from slot_codes) drops key slots whose (round, bucket)
+    differs from the query slot's; `mult` (from pair_multiplicity) subtracts
+    log N_ij from each kept logit."""
     x = np.asarray(x, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     n_slots = sorted_idx.shape[0]
@@ -170,15 +212,22 @@ def chunk_attention(x: np.ndarray, v: np.ndarray, sorted_idx: np.ndarray, chunk_
     o = np.full((n_slots, v.shape[1]), np.nan)
     lse = np.full(n_slots, np.nan)
     for c in (range(n_chunks) if chunks is None else chunks):
-        q_pos = sorted_idx[c * chunk_len:(c + 1) * chunk_len]
-        k_pos = sorted_idx[window_slots(n_slots, chunk_len, c)]
+        q_slots = np.arange(c * chunk_len, (c + 1) * chunk_len)
+        k_slots = window_slots(n_slots, chunk_len, c)
+        q_pos = sorted_idx[q_slots]
+        k_pos = sorted_idx[k_slots]
         q = x[q_pos]
         k = x[k_pos]
         k_hat = k / np.maximum(np.linalg.norm(k, axis=1), KEY_NORM_FLOOR)[:, None]
         s = (q @ k_hat.T) / math.sqrt(D)
         s = np.where(q_pos[:, None] == k_pos[None, :], SELF_LOGIT, s)
+        if mult is not None:  # every kept pair, the self pair included
+            n = np.array([[mult[qi].get(kj, 1) for kj in k_pos] for qi in q_pos], dtype=np.float64)
+            s = s - np.log(n)
         if causal:
             s = np.where(k_pos[None, :] > q_pos[:, None], -np.inf, s)
+        if codes is not None:
+            s = np.where(codes[k_slots][None, :] != codes[q_slots][:, None], -np.inf, s)
         m = np.max(s, axis=1, keepdims=True)
         e = np.exp(s - m)
         den = np.sum(e, axis=1)
@@ -206,7 +255,8 @@ def unsort_combine(o_sorted: np.ndarray, lse_sorted: np.ndarray, undo_idx: np.nd
 # Whole forward pass
 # --------------------------------------------------------------------------
 
-def forward_problem(x, v, rot, n_buckets: int, n_hashes: int, chunk_len: int, causal: bool):
+def forward_problem(x, v, rot, n_buckets: int, n_hashes: int, chunk_len: int, causal: bool,
+                    same_bucket: bool = False, dedup: bool = False):
     """One (batch, head) problem.  Returns a dict with every intermediate."""
     if n_buckets == 1:
         L = x.shape[0]
@@ -215,13 +265,16 @@ def forward_problem(x, v, rot, n_buckets: int, n_hashes: int, chunk_len: int, ca
         assert rot.shape[0] == n_hashes
         buckets, margin = hash_buckets(x, rot, n_buckets)
     sorted_idx, undo_idx = sort_by_bucket(buckets)
-    o_sorted, lse_sorted = chunk_attention(x, v, sorted_idx, chunk_len, causal)
+    codes = slot_codes(buckets, sorted_idx) if same_bucket else None
+    mult = pair_multiplicity(sorted_idx, undo_idx, chunk_len, causal, codes) if dedup else None
+    o_sorted, lse_sorted = chunk_attention(x, v, sorted_idx, chunk_len, causal, codes=codes, mult=mult)
     out, lse = unsort_combine(o_sorted, lse_sorted, undo_idx)
     return dict(buckets=buckets, margin=margin, sorted_idx=sorted_idx, undo_idx=undo_idx,
                 o_sorted=o_sorted, lse_sorted=lse_sorted, out=out, lse=lse)
 
 
-def forward(x, v, rot, n_buckets: int, n_hashes: int, chunk_len: int, causal: bool):
+def forward(x, v, rot, n_buckets: int, n_hashes: int, chunk_len: int, causal: bool,
+            same_bucket: bool = False, dedup: bool = False):
     """x, v: [B, H, L, D]; rot: [n_h, D, n_b/2] shared by every (b, h).
     Returns (out [B, H, L, D], lse [B, H, L]) in float64."""
     B, H, L, D = x.shape
@@ -229,7 +282,7 @@ def forward(x, v, rot, n_buckets: int, n_hashes: int, chunk_len: int, causal: bo
     lse = np.empty((B, H, L))
     for b in range(B):
         for h in range(H):
-            r = forward_problem(x[b, h], v[b, h], rot, n_buckets, n_hashes, chunk_len, causal)
+            r = forward_problem(x[b, h], v[b, h], rot, n_buckets, n_hashes, chunk_len, causal, same_bucket, dedup)
             out[b, h], lse[b, h] = r["out"], r["lse"]
     return out, lse
 
@@ -275,6 +328,39 @@ def full_attention(x, v, causal: bool):
         m = np.max(s)
         e = np.exp(s - m)
         out[i] = (e @ v) / np.sum(e)
+        lse[i] = m + np.log(np.sum(e))
+    return out, lse
+
+
+def union_attention(x, v, sorted_idx, undo_idx, chunk_len: int, causal: bool, codes=None):
+    """Attention of every token over the SET of distinct tokens that are kept
+    keys in any of its windows (each counted once), computed directly from
+    that set: the definition the set-union variant must reproduce."""
+    x = np.asarray(x, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n_h, L = undo_idx.shape
+    n_slots = sorted_idx.shape[0]
+    D = x.shape[1]
+    out = np.empty((L, v.shape[1]))
+    lse = np.empty(L)
+    for i in range(L):
+        keys = set()
+        for r in range(n_h):
+            g = int(undo_idx[r, i])
+            for gk in window_slots(n_slots, chunk_len, g // chunk_len):
+                j = int(sorted_idx[gk])
+                if causal and j > i:
+                    continue
+                if codes is not None and codes[gk] != codes[g]:
+                    continue
+                keys.add(j)
+        ks = np.array(sorted(keys))
+        k = x[ks]
+        s = (x[i] @ (k / np.maximum(np.linalg.norm(k, axis=1), KEY_NORM_FLOOR)[:, None]).T) / math.sqrt(D)
+        s = np.where(ks == i, SELF_LOGIT, s)
+        m = np.max(s)
+        e = np.exp(s - m)
+        out[i] = e @ v[ks] / np.sum(e)
         lse[i] = m + np.log(np.sum(e))
     return out, lse
 

@@ -395,3 +395,156 @@ def test_more_rounds_raise_recall_on_clustered_keys():
         s, u = O.sort_by_bucket(b)
         rec[n_h] = O.recall_at_k(x, s, u, 64, q, 16)
     assert rec[8] > rec[2]
+
+
+# ----------------------------------------------- attended-set variants --
+# Explainer page: a token "attends to its bucket-mates" (same_bucket) and the
+# rounds' buckets are "unioned" (dedup: every distinct key once).
+
+def _attend(x, v, i, keys, causal):
+    """Loop softmax of query i over an explicit key multiset (self at -1e5,
+    causal drops j > i); returns (out, lse)."""
+    D = x.shape[1]
+    logits = []
+    for j in keys:
+        if causal and j > i:
+            continue
+        s = -1e5 if j == i else float(x[i] @ x[j]) / math.sqrt(float(x[j] @ x[j])) / math.sqrt(D)
+        logits.append((j, s))
+    m = max(s for _, s in logits)
+    z = sum(math.exp(s - m) for _, s in logits)
+    out = sum(math.exp(s - m) / z * v[j] for j, s in logits)
+    return out, m + math.log(z)
+
+
+def _aligned_rotation(x, seed, L):
+    """A one-column rotation (n_b = 2) and sign flips of x such that exactly
+    L/2 tokens fall in bucket 0 (x . r > 0) and L/2 in bucket 1."""
+    rng = np.random.default_rng(seed)
+    r = rng.standard_normal(x.shape[1])
+    pos = rng.permutation(L)[: L // 2]
+    x = x.copy()
+    p = x @ r
+    for i in range(L):
+        want = i in set(pos.tolist())
+        if (p[i] > 0) != want:
+            x[i] = -x[i]
+    return x, r
+
+
+def test_same_bucket_with_one_bucket_and_round_is_the_base_method():
+    """n_b = 1, one round: every key slot holds the query's (round, bucket), so
+    the mask removes nothing."""
+    x, v, _ = _problem(31, 192, 1, 1)
+    for causal in (False, True):
+        a = O.forward_problem(x, v, None, 1, 1, 64, causal)
+        b = O.forward_problem(x, v, None, 1, 1, 64, causal, same_bucket=True)
+        np.testing.assert_array_equal(a["out"], b["out"])
+        np.testing.assert_array_equal(a["lse"], b["lse"])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_same_bucket_aligned_buckets_is_attention_among_bucket_mates(causal):
+    """Two buckets of exactly 64 tokens, one round: each bucket is one chunk, the
+    look-back chunk is the other bucket and masked, so every token attends to
+    exactly its bucket-mates (computed here straight from the bucket sets)."""
+    x, v, _ = _problem(32, 128, 2, 1)
+    x, r = _aligned_rotation(x, 5, 128)
+    rot = r[None, :, None]
+    res = O.forward_problem(x, v, rot, 2, 1, 64, causal, same_bucket=True)
+    bk = (x @ r <= 0).astype(int)  # argmax of [p, -p]: bucket 0 iff p > 0
+    assert np.array_equal(res["buckets"][0], bk)
+    for i in range(128):
+        mates = [j for j in range(128) if bk[j] == bk[i]]
+        out, lse = _attend(x, v, i, mates, causal)
+        np.testing.assert_allclose(res["out"][i], out, rtol=0, atol=1e-10)
+        assert abs(res["lse"][i] - lse) < 1e-9
+
+
+def test_same_bucket_two_aligned_rounds_is_the_multiset_union_of_bucket_mates():
+    """Two rounds, each with exactly-aligned buckets: the combine is softmax over
+    the multiset union of the two rounds' bucket-mate sets."""
+    x, v, _ = _problem(33, 128, 2, 2)
+    x, r0 = _aligned_rotation(x, 6, 128)
+    # second round: another column that splits the (flipped) tokens 64/64
+    rng = np.random.default_rng(7)
+    while True:
+        r1 = rng.standard_normal(64)
+        if int(np.sum(x @ r1 > 0)) == 64:
+            break
+    rot = np.stack([r0, r1])[:, :, None]
+    res = O.forward_problem(x, v, rot, 2, 2, 64, False, same_bucket=True)
+    b0, b1 = (x @ r0 <= 0).astype(int), (x @ r1 <= 0).astype(int)
+    for i in range(0, 128, 5):
+        keys = [j for j in range(128) if b0[j] == b0[i]] + [j for j in range(128) if b1[j] == b1[i]]
+        out, lse = _attend(x, v, i, keys, False)
+        np.testing.assert_allclose(res["out"][i], out, rtol=0, atol=1e-10)
+        assert abs(res["lse"][i] - lse) < 1e-9
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dedup_with_identical_rounds_is_one_round(causal):
+    """All rounds use the same rotation, so every round's windows hold the same
+    tokens: the union of n_h rounds is one round's window set, and the
+    set-union variant must equal the one-round result (lse included)."""
+    x, v, rot = _problem(34, 256, 8, 1)
+    one = O.forward_problem(x, v, rot, 8, 1, 64, causal)
+    rot3 = np.repeat(rot, 3, axis=0)
+    three = O.forward_problem(x, v, rot3, 8, 3, 64, causal, dedup=True)
+    np.testing.assert_allclose(three["out"], one["out"], rtol=0, atol=1e-10)
+    np.testing.assert_allclose(three["lse"], one["lse"], rtol=0, atol=1e-9)
+    plain = O.forward_problem(x, v, rot3, 8, 3, 64, causal)  # with multiplicity: lse + log 3
+    np.testing.assert_allclose(plain["lse"], one["lse"] + math.log(3), rtol=0, atol=1e-9)
+
+
+def test_dedup_in_one_round_changes_nothing():
+    """One round, at least two chunks: a window never holds a token twice."""
+    x, v, rot = _problem(35, 192, 8, 1)
+    for causal in (False, True):
+        a = O.forward_problem(x, v, rot, 8, 1, 64, causal)
+        b = O.forward_problem(x, v, rot, 8, 1, 64, causal, dedup=True)
+        np.testing.assert_allclose(a["out"], b["out"], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(a["lse"], b["lse"], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("same_bucket", [False, True])
+def test_dedup_equals_attention_over_the_union_set(causal, same_bucket):
+    """The per-occurrence -log N route (round softmaxes + combine) equals plain
+    softmax over the set of distinct kept keys, built directly per token."""
+    x, v, rot = _problem(36, 192, 4, 3)
+    res = O.forward_problem(x, v, rot, 4, 3, 64, causal, same_bucket=same_bucket, dedup=True)
+    codes = O.slot_codes(res["buckets"], res["sorted_idx"]) if same_bucket else None
+    uo, ul = O.union_attention(x, v, res["sorted_idx"], res["undo_idx"], 64, causal, codes)
+    np.testing.assert_allclose(res["out"], uo, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(res["lse"], ul, rtol=0, atol=1e-9)
+
+
+def test_dedup_causal_first_position_lse_is_the_self_logit():
+    """Causal position 0 keeps only itself in every window; counted once over the
+    union, its lse is exactly the self logit."""
+    x, v, rot = _problem(37, 128, 4, 3)
+    res = O.forward_problem(x, v, rot, 4, 3, 64, True, dedup=True)
+    np.testing.assert_allclose(res["out"][0], v[0], rtol=0, atol=1e-10)
+    assert abs(res["lse"][0] - (-1e5)) < 1e-9
+
+
+def test_same_bucket_masks_equal_bucket_ids_of_another_round():
+    """Round 0 puts every token in bucket 0 (a zero rotation column: [0, -0]
+    ties, lowest index); round 1 splits them 64/64.  Round 1's first chunk
+    (bucket 0) looks back at round 0's last chunk, also bucket 0 but another
+    round, which must stay masked.  Round 0's chunks hold positions 0-63 and
+    64-127 (one bucket, position order); its first chunk looks back at round
+    1's last chunk (masked), its second at its first."""
+    x, v, _ = _problem(38, 128, 2, 2)
+    x, r1 = _aligned_rotation(x, 8, 128)
+    rot = np.stack([np.zeros(64), r1])[:, :, None]
+    res = O.forward_problem(x, v, rot, 2, 2, 64, False, same_bucket=True)
+    assert np.all(res["buckets"][0] == 0)
+    b1 = (x @ r1 <= 0).astype(int)
+    for i in range(0, 128, 3):
+        keys = list(range(64)) if i < 64 else list(range(128))
+        keys += [j for j in range(128) if b1[j] == b1[i]]
+        out, lse = _attend(x, v, i, keys, False)
+        np.testing.assert_allclose(res["out"][i], out, rtol=0, atol=1e-10)
+        assert abs(res["lse"][i] - lse) < 1e-9
