@@ -51,7 +51,7 @@ enum {
   LSH_ERR_NULL = -1,        /* a required pointer is NULL */
   LSH_ERR_SHAPE = -2,       /* B, H or L < 0, D or n_h <= 0, L % C != 0, or an index overflows int32 */
   LSH_ERR_BUCKETS = -3,     /* n_b < 1, odd n_b > 1, or n_b > 4096 */
-  LSH_ERR_UNSUPPORTED = -4, /* D != 64, C != 64, n_h > 16, or unknown dtype */
+  LSH_ERR_UNSUPPORTED = -4, /* D != 64, C != 64, n_h > 16, unknown dtype or attend bits */
   LSH_ERR_WORKSPACE = -5,   /* workspace pointer NULL or smaller than required */
   LSH_ERR_ALIAS = -6,       /* an output overlaps an input */
   LSH_ERR_HIP = -7          /* a kernel launch or event record failed */
@@ -100,6 +100,35 @@ int lsh_chunk_attn(const void* qk, const void* v, const int32_t* sorted_idx, voi
                    float* lse_sorted, int B, int H, int L, int D, int n_h, int C, int causal,
                    lsh_dtype dt, void* stream);
 
+/* Step 3 with a different attended set (explainer page: each token "attends to
+ * its bucket-mates" after the sort, and the rounds "union the buckets"; read
+ * literally, these name two variants of the window above).  `attend` is 0 (the
+ * window as in lsh_chunk_attn, identical results) or an OR of:
+ *   LSH_ATTEND_SAME_BUCKET - a key slot counts only if it holds the query's
+ *       (round, bucket): the window is cut down to bucket-mates of the same
+ *       round.  The self logit and the causal rule are as above.
+ *   LSH_ATTEND_DEDUP - every distinct key token counts once over the union of
+ *       the query's windows in all rounds: each kept logit of the pair (i, j),
+ *       the self pair included, is lowered by ln N_ij, with N_ij the number of
+ *       (occurrence of i, occurrence of j) pairs over all rounds' windows that
+ *       the other masks keep.  After the combine step, out_i is then the
+ *       softmax over the set union of i's keys, each key once.
+ *   buckets  [B, H, n_h, L]  from lsh_hash; read with LSH_ATTEND_SAME_BUCKET
+ *                            (may be NULL otherwise).
+ *   undo_idx [B, H, n_h, L]  from lsh_sort; read with LSH_ATTEND_DEDUP (may be
+ *                            NULL otherwise).
+ * Other arguments as in lsh_chunk_attn.  Bucket values must be in [0, 4096)
+ * and undo_idx must be lsh_sort's inverse of sorted_idx (neither is checked on
+ * the device; other values give meaningless results but no out-of-bounds
+ * access).  With a variant bit set every chunk takes the exact softmax path,
+ * so expect the call to be slower than lsh_chunk_attn. */
+#define LSH_ATTEND_SAME_BUCKET 1
+#define LSH_ATTEND_DEDUP 2
+int lsh_chunk_attn_ex(const void* qk, const void* v, const int32_t* sorted_idx,
+                      const int32_t* buckets, const int32_t* undo_idx, void* o_sorted,
+                      float* lse_sorted, int B, int H, int L, int D, int n_h, int C, int causal,
+                      int attend, lsh_dtype dt, void* stream);
+
 /* Steps 4-5, unsort and combine (explainer page: union of the rounds).
  * LSE_i = logsumexp_r lse_r(i), out_i = sum_r exp(lse_r(i) - LSE_i) o_r(i), with
  * o_r(i) = o_sorted[undo_idx[r][i]].
@@ -130,6 +159,14 @@ int reformer_lsh_attn_fwd(const void* qk, const void* v, const void* rot, int n_
                           int n_hashes, int chunk_len, int causal, int B, int H, int L, int D,
                           lsh_dtype dt, void* out, float* lse_out, void* ws, size_t ws_bytes,
                           void* stream, void* const* stage_events);
+
+/* The whole forward pass with an attended-set variant (`attend` as in
+ * lsh_chunk_attn_ex; 0 gives reformer_lsh_attn_fwd).  Same workspace size as
+ * reformer_lsh_attn_fwd; other arguments as there. */
+int reformer_lsh_attn_fwd_ex(const void* qk, const void* v, const void* rot, int n_buckets,
+                             int n_hashes, int chunk_len, int causal, int attend, int B, int H,
+                             int L, int D, lsh_dtype dt, void* out, float* lse_out, void* ws,
+                             size_t ws_bytes, void* stream, void* const* stage_events);
 
 /* Timing helpers for callers that have no HIP runtime binding of their own:
  * create/destroy a hipEvent_t (returned as void*), and the elapsed time in

@@ -19,6 +19,7 @@ _HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__)
 _lib = None
 
 LSH_F32, LSH_BF16 = 0, 1
+LSH_ATTEND_SAME_BUCKET, LSH_ATTEND_DEDUP = 1, 2
 N_KERNELS = 7
 N_EVENTS = N_KERNELS + 1
 KERNEL_NAMES = ["prep", "hash", "fixup", "sort_hist", "sort_scatter", "chunk_attn", "combine"]
@@ -31,9 +32,11 @@ _SIGS = {
     "lsh_sort_workspace_bytes": (_c_int, [_c_int] * 5 + [ctypes.POINTER(_c_size)]),
     "lsh_sort": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [_vp, _c_size, _vp]),
     "lsh_chunk_attn": (_c_int, [_vp] * 5 + [_c_int] * 8 + [_vp]),
+    "lsh_chunk_attn_ex": (_c_int, [_vp] * 7 + [_c_int] * 9 + [_vp]),
     "lsh_unsort_combine": (_c_int, [_vp] * 5 + [_c_int] * 6 + [_vp]),
     "lsh_fwd_workspace_bytes": (_c_int, [_c_int] * 8 + [ctypes.POINTER(_c_size)]),
     "reformer_lsh_attn_fwd": (_c_int, [_vp] * 3 + [_c_int] * 9 + [_vp, _vp, _vp, _c_size, _vp, _vp]),
+    "reformer_lsh_attn_fwd_ex": (_c_int, [_vp] * 3 + [_c_int] * 10 + [_vp, _vp, _vp, _c_size, _vp, _vp]),
     "lsh_event_create": (_c_int, [ctypes.POINTER(_vp)]),
     "lsh_event_destroy": (_c_int, [_vp]),
     "lsh_event_record": (_c_int, [_vp, _vp]),
@@ -157,21 +160,41 @@ def lsh_sort(buckets: torch.Tensor, n_buckets: int):
     return sorted_idx, undo_idx
 
 
+def attend_flags(same_bucket: bool = False, dedup: bool = False) -> int:
+    """The `attend` argument of the *_ex entry points."""
+    return (LSH_ATTEND_SAME_BUCKET if same_bucket else 0) | (LSH_ATTEND_DEDUP if dedup else 0)
+
+
 def lsh_chunk_attn(qk: torch.Tensor, v: torch.Tensor, sorted_idx: torch.Tensor, n_hashes: int, chunk_len: int,
-                   causal: bool):
-    """-> (o_sorted [B,H,n_h*L,D] in qk's dtype, lse_sorted float32 [B,H,n_h*L])."""
-    _dev(qk, v, sorted_idx)
+                   causal: bool, buckets: torch.Tensor | None = None, undo_idx: torch.Tensor | None = None,
+                   same_bucket: bool = False, dedup: bool = False):
+    """-> (o_sorted [B,H,n_h*L,D] in qk's dtype, lse_sorted float32 [B,H,n_h*L]).
+    With `same_bucket` (needs `buckets` [B,H,n_h,L]) or `dedup` (needs `undo_idx`
+    [B,H,n_h,L]) the attended-set variant of lsh_chunk_attn_ex runs."""
+    _dev(qk, v, sorted_idx, buckets, undo_idx)
     B, H, L, D = qk.shape
     dt = _dtype_code(qk)
     if v.shape != qk.shape or v.dtype != qk.dtype:
         raise ValueError("v must match qk in shape and dtype")
     if sorted_idx.dtype != torch.int32 or sorted_idx.shape != (B, H, n_hashes * L):
         raise ValueError("sorted_idx must be int32 [B,H,n_h*L]")
+    for name, t, need in (("buckets", buckets, same_bucket), ("undo_idx", undo_idx, dedup)):
+        if need and t is None:
+            raise ValueError(f"{name} is required for this variant")
+        if t is not None and (t.dtype != torch.int32 or t.shape != (B, H, n_hashes, L)):
+            raise ValueError(f"{name} must be int32 [B,H,n_h,L]")
     o_sorted = torch.empty((B, H, n_hashes * L, D), dtype=qk.dtype, device=qk.device)
     lse_sorted = torch.empty((B, H, n_hashes * L), dtype=torch.float32, device=qk.device)
-    _check("lsh_chunk_attn", lib().lsh_chunk_attn(qk.data_ptr(), v.data_ptr(), sorted_idx.data_ptr(),
-                                                  o_sorted.data_ptr(), lse_sorted.data_ptr(), B, H, L, D, n_hashes,
-                                                  chunk_len, int(bool(causal)), dt, _stream(qk.device)))
+    attend = attend_flags(same_bucket, dedup)
+    if attend == 0:
+        _check("lsh_chunk_attn", lib().lsh_chunk_attn(qk.data_ptr(), v.data_ptr(), sorted_idx.data_ptr(),
+                                                      o_sorted.data_ptr(), lse_sorted.data_ptr(), B, H, L, D,
+                                                      n_hashes, chunk_len, int(bool(causal)), dt, _stream(qk.device)))
+    else:
+        _check("lsh_chunk_attn_ex", lib().lsh_chunk_attn_ex(
+            qk.data_ptr(), v.data_ptr(), sorted_idx.data_ptr(), _ptr(buckets), _ptr(undo_idx), o_sorted.data_ptr(),
+            lse_sorted.data_ptr(), B, H, L, D, n_hashes, chunk_len, int(bool(causal)), attend, dt,
+            _stream(qk.device)))
     return o_sorted, lse_sorted
 
 
@@ -193,10 +216,12 @@ def lsh_unsort_combine(o_sorted: torch.Tensor, lse_sorted: torch.Tensor, undo_id
 def reformer_lsh_attn_fwd(qk: torch.Tensor, v: torch.Tensor, rot: torch.Tensor | None, n_buckets: int,
                           n_hashes: int, chunk_len: int = 64, causal: bool = False, want_lse: bool = True,
                           out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
-                          workspace: torch.Tensor | None = None, stage_events=None):
+                          workspace: torch.Tensor | None = None, stage_events=None, same_bucket: bool = False,
+                          dedup: bool = False):
     """The fused forward pass.  Returns (out [B,H,L,D], lse float32 [B,H,L] or None).
     `workspace` (uint8, at least fwd_workspace_bytes) and `out`/`lse` may be passed
-    in to avoid allocation; `stage_events` is an EventSet for per-kernel timing."""
+    in to avoid allocation; `stage_events` is an EventSet for per-kernel timing.
+    `same_bucket` / `dedup` select the attended-set variants (reformer_lsh_attn_fwd_ex)."""
     _dev(qk, v, rot, out, lse, workspace)
     B, H, L, D = qk.shape
     dt = _dtype_code(qk)
@@ -211,9 +236,15 @@ def reformer_lsh_attn_fwd(qk: torch.Tensor, v: torch.Tensor, rot: torch.Tensor |
     if workspace is None:
         workspace = _workspace(fwd_workspace_bytes(B, H, L, D, n_buckets, n_hashes, chunk_len, dt), qk.device)
     ev = None if stage_events is None else stage_events.array()
-    _check("reformer_lsh_attn_fwd", lib().reformer_lsh_attn_fwd(
-        qk.data_ptr(), v.data_ptr(), _ptr(rot), n_buckets, n_hashes, chunk_len, int(bool(causal)), B, H, L, D, dt,
-        out.data_ptr(), _ptr(lse), workspace.data_ptr(), workspace.numel(), _stream(qk.device), ev))
+    attend = attend_flags(same_bucket, dedup)
+    if attend == 0:
+        _check("reformer_lsh_attn_fwd", lib().reformer_lsh_attn_fwd(
+            qk.data_ptr(), v.data_ptr(), _ptr(rot), n_buckets, n_hashes, chunk_len, int(bool(causal)), B, H, L, D,
+            dt, out.data_ptr(), _ptr(lse), workspace.data_ptr(), workspace.numel(), _stream(qk.device), ev))
+    else:
+        _check("reformer_lsh_attn_fwd_ex", lib().reformer_lsh_attn_fwd_ex(
+            qk.data_ptr(), v.data_ptr(), _ptr(rot), n_buckets, n_hashes, chunk_len, int(bool(causal)), attend, B, H,
+            L, D, dt, out.data_ptr(), _ptr(lse), workspace.data_ptr(), workspace.numel(), _stream(qk.device), ev))
     return out, lse
 
 

@@ -15,6 +15,8 @@ size_t elem_size(lsh_dtype dt) { return dt == LSH_BF16 ? 2 : 4; }
 
 bool dtype_ok(lsh_dtype dt) { return dt == LSH_F32 || dt == LSH_BF16; }
 
+bool attend_ok(int attend) { return (attend & ~(LSH_ATTEND_SAME_BUCKET | LSH_ATTEND_DEDUP)) == 0; }
+
 // B, H or L == 0 is a valid, empty problem: the entry points return LSH_OK at
 // once, with no pointer checked and nothing enqueued (workspace size 0).
 bool is_empty(int B, int H, int L) { return B == 0 || H == 0 || L == 0; }
@@ -148,7 +150,7 @@ const char* lsh_status_string(int status) {
     case LSH_ERR_NULL: return "a required pointer is NULL";
     case LSH_ERR_SHAPE: return "invalid shape (negative dimension, D or n_hashes <= 0, L not a multiple of 64 or above 2^24, or int32 index overflow)";
     case LSH_ERR_BUCKETS: return "invalid bucket count (must be 1 or even, at most 4096)";
-    case LSH_ERR_UNSUPPORTED: return "unsupported configuration (D and chunk_len must be 64, n_hashes <= 16, dtype f32 or bf16)";
+    case LSH_ERR_UNSUPPORTED: return "unsupported configuration (D and chunk_len must be 64, n_hashes <= 16, dtype f32 or bf16, attend a combination of the LSH_ATTEND_* bits)";
     case LSH_ERR_WORKSPACE: return "workspace missing or too small";
     case LSH_ERR_ALIAS: return "an output overlaps an input";
     case LSH_ERR_HIP: return "HIP launch or event error";
@@ -217,28 +219,38 @@ int lsh_sort(const int32_t* buckets, int32_t* sorted_idx, int32_t* undo_idx, int
                                  nullptr, &k));
 }
 
-int lsh_chunk_attn(const void* qk, const void* v, const int32_t* sorted_idx, void* o_sorted, float* lse_sorted,
-                   int B, int H, int L, int D, int n_h, int C, int causal, lsh_dtype dt, void* stream) {
+int lsh_chunk_attn_ex(const void* qk, const void* v, const int32_t* sorted_idx, const int32_t* buckets,
+                      const int32_t* undo_idx, void* o_sorted, float* lse_sorted, int B, int H, int L, int D,
+                      int n_h, int C, int causal, int attend, lsh_dtype dt, void* stream) {
   int st = check_problem(B, H, L, D, n_h);
   if (st != LSH_OK) return st;
   if (C != kChunk) return C <= 0 ? LSH_ERR_SHAPE : LSH_ERR_UNSUPPORTED;
-  if (!dtype_ok(dt)) return LSH_ERR_UNSUPPORTED;
+  if (!dtype_ok(dt) || !attend_ok(attend)) return LSH_ERR_UNSUPPORTED;
   if (is_empty(B, H, L)) return LSH_OK;
-  if (qk == nullptr || v == nullptr || sorted_idx == nullptr || o_sorted == nullptr || lse_sorted == nullptr)
+  const bool sb = (attend & LSH_ATTEND_SAME_BUCKET) != 0, dd = (attend & LSH_ATTEND_DEDUP) != 0;
+  if (qk == nullptr || v == nullptr || sorted_idx == nullptr || o_sorted == nullptr || lse_sorted == nullptr ||
+      (sb && buckets == nullptr) || (dd && undo_idx == nullptr))
     return LSH_ERR_NULL;
   const int BH = B * H;
   const size_t es = elem_size(dt);
   const size_t slots = (size_t)BH * n_h * L;
   const size_t in_bytes = (size_t)BH * L * kD * es;
   const size_t o_bytes = slots * kD * es, l_bytes = slots * sizeof(float), i_bytes = slots * sizeof(int32_t);
-  const void* ins[3] = {qk, v, sorted_idx};
-  const size_t in_n[3] = {in_bytes, in_bytes, i_bytes};
-  for (int a = 0; a < 3; ++a)
+  const void* ins[5] = {qk, v, sorted_idx, sb ? buckets : nullptr, dd ? undo_idx : nullptr};
+  const size_t in_n[5] = {in_bytes, in_bytes, i_bytes, i_bytes, i_bytes};
+  for (int a = 0; a < 5; ++a)
     if (overlaps(o_sorted, o_bytes, ins[a], in_n[a]) || overlaps(lse_sorted, l_bytes, ins[a], in_n[a]))
       return LSH_ERR_ALIAS;
   if (overlaps(o_sorted, o_bytes, lse_sorted, l_bytes)) return LSH_ERR_ALIAS;
-  return hip_status(launch_chunk_attn(qk, v, sorted_idx, o_sorted, lse_sorted, nullptr, BH, L, n_h, causal, dt,
+  return hip_status(launch_chunk_attn(qk, v, sorted_idx, o_sorted, lse_sorted, nullptr, sb ? buckets : nullptr,
+                                      dd ? undo_idx : nullptr, BH, L, n_h, causal, attend, dt,
                                       (hipStream_t)stream));
+}
+
+int lsh_chunk_attn(const void* qk, const void* v, const int32_t* sorted_idx, void* o_sorted, float* lse_sorted,
+                   int B, int H, int L, int D, int n_h, int C, int causal, lsh_dtype dt, void* stream) {
+  return lsh_chunk_attn_ex(qk, v, sorted_idx, nullptr, nullptr, o_sorted, lse_sorted, B, H, L, D, n_h, C, causal, 0,
+                           dt, stream);
 }
 
 int lsh_unsort_combine(const void* o_sorted, const float* lse_sorted, const int32_t* undo_idx, void* out,
@@ -273,14 +285,15 @@ int lsh_fwd_workspace_bytes(int B, int H, int L, int D, int n_b, int n_h, int C,
   return LSH_OK;
 }
 
-int reformer_lsh_attn_fwd(const void* qk, const void* v, const void* rot, int n_buckets, int n_hashes, int chunk_len,
-                          int causal, int B, int H, int L, int D, lsh_dtype dt, void* out, float* lse_out, void* ws,
-                          size_t ws_bytes, void* stream, void* const* stage_events) {
+int reformer_lsh_attn_fwd_ex(const void* qk, const void* v, const void* rot, int n_buckets, int n_hashes,
+                             int chunk_len, int causal, int attend, int B, int H, int L, int D, lsh_dtype dt,
+                             void* out, float* lse_out, void* ws, size_t ws_bytes, void* stream,
+                             void* const* stage_events) {
   int st = check_problem(B, H, L, D, n_hashes);
   if (st == LSH_OK) st = check_buckets(n_buckets, L);
   if (st != LSH_OK) return st;
   if (chunk_len != kChunk) return chunk_len <= 0 ? LSH_ERR_SHAPE : LSH_ERR_UNSUPPORTED;
-  if (!dtype_ok(dt)) return LSH_ERR_UNSUPPORTED;
+  if (!dtype_ok(dt) || !attend_ok(attend)) return LSH_ERR_UNSUPPORTED;
   if (is_empty(B, H, L)) {
     // Nothing to compute; the stage events are still recorded, back to back.
     if (stage_events != nullptr)
@@ -326,11 +339,19 @@ int reformer_lsh_attn_fwd(const void* qk, const void* v, const void* rot, int n_
     e = enqueue_sort(buckets, sorted_idx, undo_idx, (int*)(base + w.sort_base), BH, L, n_b, n_h, s, stage_events,
                      &k);
   if (e == hipSuccess)
-    e = launch_chunk_attn(qk, v, sorted_idx, o_sorted, lse_sorted, token_scales, BH, L, n_h, causal, dt, s);
+    e = launch_chunk_attn(qk, v, sorted_idx, o_sorted, lse_sorted, token_scales, buckets, undo_idx, BH, L, n_h,
+                          causal, attend, dt, s);
   if (e == hipSuccess && stage_events != nullptr) e = hipEventRecord((hipEvent_t)stage_events[++k], s);
   if (e == hipSuccess) e = launch_combine(o_sorted, lse_sorted, undo_idx, out, lse_out, BH, L, n_h, dt, s);
   if (e == hipSuccess && stage_events != nullptr) e = hipEventRecord((hipEvent_t)stage_events[++k], s);
   return hip_status(e);
+}
+
+int reformer_lsh_attn_fwd(const void* qk, const void* v, const void* rot, int n_buckets, int n_hashes, int chunk_len,
+                          int causal, int B, int H, int L, int D, lsh_dtype dt, void* out, float* lse_out, void* ws,
+                          size_t ws_bytes, void* stream, void* const* stage_events) {
+  return reformer_lsh_attn_fwd_ex(qk, v, rot, n_buckets, n_hashes, chunk_len, causal, 0, B, H, L, D, dt, out, lse_out,
+                                  ws, ws_bytes, stream, stage_events);
 }
 
 int lsh_event_create(void** event) {

@@ -75,14 +75,33 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 
-template <bool BF16, bool CAUSAL>
-__global__ __launch_bounds__(256, BF16 ? 4 : 2) void chunk_attn_kernel(const typename AttnTraits<BF16>::T* __restrict__ qk,
-                                                         const typename AttnTraits<BF16>::T* __restrict__ v,
-                                                         const int32_t* __restrict__ sorted_idx,
-                                                         typename AttnTraits<BF16>::T* __restrict__ o_out,
-                                                         float* __restrict__ lse_out,
-                                                         const float2* __restrict__ token_scales, int L,
-                                                         int n_slots, int n_chunks, int blocks_per_bh) {
+// ATTEND: 0 = the method as described; bit 0 = same-bucket keys only, bit 1 =
+// set union over the rounds (each distinct key once).  The variants take the
+// exact softmax path for every chunk, walk 4 chunks per block and keep their
+// per-row tables in dynamic LDS (variant_lds_bytes), so the base kernel's
+// resources are unchanged.
+template <int ATTEND>
+constexpr int chunks_per_block() { return ATTEND ? 4 : kChunksPerBlock; }
+
+// Dynamic LDS of a variant, as ints per sPos entry (kCPB + 1 of them) and row:
+//   same-bucket: 1 code, (round << 13) | bucket;
+//   set union:   n_h words, one per round r: the token's chunk index within
+//                round r, or with same-bucket (bucket_r << 18) | that index;
+//                plus 2 masks (last / first, below).
+inline size_t variant_lds_bytes(int attend, int n_h) {
+  if (attend == 0) return 0;
+  const int per_row = ((attend & 1) ? 1 : 0) + ((attend & 2) ? n_h + 2 : 0);
+  return (size_t)(chunks_per_block<1>() + 1) * 64 * per_row * sizeof(int);
+}
+
+template <bool BF16, bool CAUSAL, int ATTEND>
+__global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn_kernel(
+    const typename AttnTraits<BF16>::T* __restrict__ qk, const typename AttnTraits<BF16>::T* __restrict__ v,
+    const int32_t* __restrict__ sorted_idx, typename AttnTraits<BF16>::T* __restrict__ o_out,
+    float* __restrict__ lse_out, const float2* __restrict__ token_scales, const int32_t* __restrict__ buckets,
+    const int32_t* __restrict__ undo_idx, int L, int n_h, int n_slots, int n_chunks, int blocks_per_bh) {
+  constexpr int kCPB = chunks_per_block<ATTEND>();
+  constexpr bool kSB = (ATTEND & 1) != 0, kDD = (ATTEND & 2) != 0;
   using T = typename AttnTraits<BF16>::T;
   constexpr int kXRow = AttnTraits<BF16>::kXRow;
   constexpr int kVRow = AttnTraits<BF16>::kVRow;
@@ -92,11 +111,18 @@ __global__ __launch_bounds__(256, BF16 ? 4 : 2) void chunk_attn_kernel(const typ
   __shared__ __attribute__((aligned(16))) T sVT[64 * kVRow];  // [dim][64 * slot + key]
   __shared__ __attribute__((aligned(16))) float sKs[2][64];   // key scale: log2(e) / (8 |x_j|)
   __shared__ __attribute__((aligned(16))) float sM[2][64];    // query bound: log2(e) |x_i| / 8
-  __shared__ __attribute__((aligned(16))) int sPos[kChunksPerBlock + 1][64];
+  __shared__ __attribute__((aligned(16))) int sPos[kCPB + 1][64];
+  // Variant tables (dynamic LDS, [entry][row] each, rounds inner for sChk):
+  // sCode, sChk[entry][round][row], sLast, sFirst.
+  extern __shared__ __attribute__((aligned(16))) int sVar[];
+  int* const sCode = sVar;
+  int* const sChk = sVar + (kSB ? (kCPB + 1) * 64 : 0);
+  int* const sLast = sChk + (kDD ? (kCPB + 1) * n_h * 64 : 0);
+  int* const sFirst = sLast + (kDD ? (kCPB + 1) * 64 : 0);
 
   const int bh = blockIdx.x / blocks_per_bh;
-  const int c0 = (blockIdx.x % blocks_per_bh) * kChunksPerBlock;
-  const int c1 = min(n_chunks, c0 + kChunksPerBlock);
+  const int c0 = (blockIdx.x % blocks_per_bh) * kCPB;
+  const int c1 = min(n_chunks, c0 + kCPB);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15;  // query (column) of the MFMA tiles
@@ -119,6 +145,34 @@ __global__ __launch_bounds__(256, BF16 ? 4 : 2) void chunk_attn_kernel(const typ
     sPos[k][r] = (int)min((uint32_t)sidx[(size_t)c * kChunk + r], (uint32_t)(L - 1));
   }
   __syncthreads();
+  if constexpr (ATTEND != 0) {
+    const int cpr = L / kChunk;  // chunks per round
+    const int32_t* bk = buckets + (size_t)bh * n_h * L;
+    const int32_t* ud = undo_idx + (size_t)bh * n_slots;
+    for (int e = tid; e < (c1 - c0 + 1) * 64; e += 256) {
+      const int k = e >> 6, r = e & 63;
+      const int c = (k == 0) ? (c0 - 1 + n_chunks) % n_chunks : c0 - 1 + k;
+      const int pos = sPos[k][r];
+      if constexpr (kSB) {
+        const int rnd = c / cpr;
+        sCode[k * 64 + r] = (rnd << 13) | (bk[(size_t)rnd * L + pos] & 0xFFF);
+      }
+      if constexpr (kDD) {
+        int last = 0, first = 0;
+        for (int b = 0; b < n_h; ++b) {
+          // chunk of this token in round b, as an index within the round
+          const int cb = (int)min((uint32_t)ud[(size_t)b * L + pos], (uint32_t)(n_slots - 1)) / kChunk % cpr;
+          sChk[(k * n_h + b) * 64 + r] = kSB ? ((bk[(size_t)b * L + pos] & 0xFFF) << 18) | cb : cb;
+          last |= (cb == cpr - 1 ? 1 : 0) << b;
+          // bit b: this token's chunk in round b+1 (cyclically) is that round's first
+          first |= (cb == 0 ? 1 : 0) << ((b + n_h - 1) % n_h);
+        }
+        sLast[k * 64 + r] = last;
+        sFirst[k * 64 + r] = first;
+      }
+    }
+    __syncthreads();
+  }
 
   // ---- gather of one chunk into registers, and from registers into LDS ----
   // x: thread t holds 16 dims (quarter t&3) of row t>>2.
@@ -319,36 +373,12 @@ __global__ __launch_bounds__(256, BF16 ? 4 : 2) void chunk_attn_kernel(const typ
 
     f32x4 acc[8];
     scores(acc);
-    // ---- fast path: probabilities offset by the a-priori bound M2, masks as zeroes ----
     float p[8][4];
     float sum = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 8; ++kt) {
-      const int slot = kt < 4 ? prv : cur;
-      const int kr0 = 16 * (kt & 3) + 4 * grp;
-      const float4 ks = *(const float4*)(&sKs[slot][kr0]);
-      const int4 kp = *(const int4*)(&sPos[kt < 4 ? kc - 1 : kc][kr0]);
-      const float ksv[4] = {ks.x, ks.y, ks.z, ks.w};
-      const int kpos[4] = {kp.x, kp.y, kp.z, kp.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float q = __builtin_amdgcn_exp2f(fmaf(acc[kt][e], ksv[e], -M2));
-        const bool drop = CAUSAL ? (kpos[e] >= qpos) : (kpos[e] == qpos);
-        p[kt][e] = drop ? 0.f : q;
-        sum += p[kt][e];
-      }
-    }
-    sum = qsum(sum);
     f32x4 oacc[4];
-    pv(p, oacc);
     float off = M2;
-    if (__builtin_expect(__ballot(!(sum >= kMinSum)) != 0ull, 0)) {
-      // Exact path for the wave (rare): logits with the -1e5 self value and the
-      // row maximum, recomputed from the LDS tiles.  The clobber makes this path
-      // reload its LDS operands instead of keeping the fast path's loads live.
-      asm volatile("" ::: "memory");
-      scores(acc);
-      float mx = -INFINITY;
+    if constexpr (ATTEND == 0) {
+    // ---- fast path: probabilities offset by the a-priori bound M2, masks as zeroes ----
 #pragma unroll
       for (int kt = 0; kt < 8; ++kt) {
         const int slot = kt < 4 ? prv : cur;
@@ -359,15 +389,130 @@ __global__ __launch_bounds__(256, BF16 ? 4 : 2) void chunk_attn_kernel(const typ
         const int kpos[4] = {kp.x, kp.y, kp.z, kp.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
+          const float q = __builtin_amdgcn_exp2f(fmaf(acc[kt][e], ksv[e], -M2));
+          const bool drop = CAUSAL ? (kpos[e] >= qpos) : (kpos[e] == qpos);
+          p[kt][e] = drop ? 0.f : q;
+          sum += p[kt][e];
+        }
+      }
+      sum = qsum(sum);
+      pv(p, oacc);
+      if (__builtin_expect(__ballot(!(sum >= kMinSum)) != 0ull, 0)) {
+        // Exact path for the wave (rare): logits with the -1e5 self value and the
+        // row maximum, recomputed from the LDS tiles.  The clobber makes this path
+        // reload its LDS operands instead of keeping the fast path's loads live.
+        asm volatile("" ::: "memory");
+        scores(acc);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) {
+          const int slot = kt < 4 ? prv : cur;
+          const int kr0 = 16 * (kt & 3) + 4 * grp;
+          const float4 ks = *(const float4*)(&sKs[slot][kr0]);
+          const int4 kp = *(const int4*)(&sPos[kt < 4 ? kc - 1 : kc][kr0]);
+          const float ksv[4] = {ks.x, ks.y, ks.z, ks.w};
+          const int kpos[4] = {kp.x, kp.y, kp.z, kp.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float sc = acc[kt][e] * ksv[e];
+            if (kpos[e] == qpos) sc = kSelf2;
+            if (CAUSAL && kpos[e] > qpos) sc = -INFINITY;
+            p[kt][e] = sc;
+            mx = fmaxf(mx, sc);
+          }
+        }
+        mx = qmax(mx);
+        sum = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            p[kt][e] = __builtin_amdgcn_exp2f(p[kt][e] - mx);
+            sum += p[kt][e];
+          }
+        sum = qsum(sum);
+        off = mx;
+        pv(p, oacc);
+      }
+    } else {
+      // ---- attended-set variants: exact path (row maximum) for every chunk ----
+      // same-bucket: keys with another (round, bucket) code than the query are
+      // dropped.  set union: each kept logit, the self's included, gets
+      // -log2 N, N = the number of (query occurrence, key occurrence) pairs of
+      // the token pair over all rounds' windows:
+      //   N = sum_r [0 <= chunk_r(query) - chunk_r(key) <= 1]   (the window of
+      //         the query's round-r chunk; with same-bucket only if the two
+      //         share the round-r bucket: the packed words differ by 0 or 1)
+      //     + #{r : the key's round-r chunk is that round's last and the
+      //         query's round-(r+1) chunk is that round's first}   (the look-back
+      //         across a round boundary; with same-bucket it joins one round's
+      //         ends, so only for n_h == 1 and equal buckets).
+      int nn[8][4];
+      if constexpr (kDD) {
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) nn[kt][e] = 0;
+        for (int b = 0; b < n_h; ++b) {
+          const int qw = sChk[(kc * n_h + b) * 64 + qrow];
+#pragma unroll
+          for (int kt = 0; kt < 8; ++kt) {
+            const int ke = kt < 4 ? kc - 1 : kc;
+            const int4 w4 = *(const int4*)(&sChk[(ke * n_h + b) * 64 + 16 * (kt & 3) + 4 * grp]);
+            nn[kt][0] += (uint32_t)(qw - w4.x) <= 1u ? 1 : 0;
+            nn[kt][1] += (uint32_t)(qw - w4.y) <= 1u ? 1 : 0;
+            nn[kt][2] += (uint32_t)(qw - w4.z) <= 1u ? 1 : 0;
+            nn[kt][3] += (uint32_t)(qw - w4.w) <= 1u ? 1 : 0;
+          }
+        }
+        if (!kSB || n_h == 1) {
+          const int qf = sFirst[kc * 64 + qrow];
+          const int qb = sChk[kc * n_h * 64 + qrow] >> 18;  // round-0 bucket (same-bucket only)
+#pragma unroll
+          for (int kt = 0; kt < 8; ++kt) {
+            const int ke = kt < 4 ? kc - 1 : kc;
+            const int kr0 = 16 * (kt & 3) + 4 * grp;
+            const int4 l4 = *(const int4*)(&sLast[ke * 64 + kr0]);
+            const int kl[4] = {l4.x, l4.y, l4.z, l4.w};
+            int same[4] = {1, 1, 1, 1};
+            if constexpr (kSB) {
+              const int4 w4 = *(const int4*)(&sChk[ke * n_h * 64 + kr0]);
+              same[0] = (w4.x >> 18) == qb; same[1] = (w4.y >> 18) == qb;
+              same[2] = (w4.z >> 18) == qb; same[3] = (w4.w >> 18) == qb;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) nn[kt][e] += same[e] ? __popc((uint32_t)(kl[e] & qf)) : 0;
+          }
+        }
+      }
+      const int qcode = kSB ? sCode[kc * 64 + qrow] : 0;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 8; ++kt) {
+        const int ke = kt < 4 ? kc - 1 : kc;
+        const int slot = kt < 4 ? prv : cur;
+        const int kr0 = 16 * (kt & 3) + 4 * grp;
+        const float4 ks = *(const float4*)(&sKs[slot][kr0]);
+        const int4 kp = *(const int4*)(&sPos[ke][kr0]);
+        const float ksv[4] = {ks.x, ks.y, ks.z, ks.w};
+        const int kpos[4] = {kp.x, kp.y, kp.z, kp.w};
+        int kcode[4] = {0, 0, 0, 0};
+        if constexpr (kSB) {
+          const int4 c4 = *(const int4*)(&sCode[ke * 64 + kr0]);
+          kcode[0] = c4.x; kcode[1] = c4.y; kcode[2] = c4.z; kcode[3] = c4.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
           float sc = acc[kt][e] * ksv[e];
           if (kpos[e] == qpos) sc = kSelf2;
           if (CAUSAL && kpos[e] > qpos) sc = -INFINITY;
+          if (kSB && kcode[e] != qcode) sc = -INFINITY;
+          if (kDD && nn[kt][e] > 1) sc -= __builtin_amdgcn_logf((float)nn[kt][e]);  // log2
           p[kt][e] = sc;
           mx = fmaxf(mx, sc);
         }
       }
       mx = qmax(mx);
-      sum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
@@ -406,33 +551,61 @@ __global__ __launch_bounds__(256, BF16 ? 4 : 2) void chunk_attn_kernel(const typ
   }
 }
 
-template <bool BF16>
+template <bool BF16, int ATTEND>
 hipError_t launch_attn_t(const void* qk, const void* v, const int32_t* sorted_idx, void* o_out, float* lse_out,
-                         const float2* token_scales, int BH, int L, int n_h, int causal, hipStream_t s) {
+                         const float2* token_scales, const int32_t* buckets, const int32_t* undo_idx, int BH,
+                         int L, int n_h, int causal, hipStream_t s) {
   using T = typename AttnTraits<BF16>::T;
+  constexpr int kCPB = chunks_per_block<ATTEND>();
   const int n_slots = n_h * L;
   const int n_chunks = n_slots / kChunk;
-  const int blocks_per_bh = (n_chunks + kChunksPerBlock - 1) / kChunksPerBlock;
+  const int blocks_per_bh = (n_chunks + kCPB - 1) / kCPB;
   const unsigned grid = (unsigned)blocks_per_bh * (unsigned)BH;
+  const size_t dyn = variant_lds_bytes(ATTEND, n_h);
   if (causal)
-    chunk_attn_kernel<BF16, true><<<grid, 256, 0, s>>>(
-        (const T*)qk, (const T*)v, sorted_idx, (T*)o_out, lse_out, token_scales, L, n_slots, n_chunks,
-        blocks_per_bh);
+    chunk_attn_kernel<BF16, true, ATTEND><<<grid, 256, dyn, s>>>(
+        (const T*)qk, (const T*)v, sorted_idx, (T*)o_out, lse_out, token_scales, buckets, undo_idx, L, n_h,
+        n_slots, n_chunks, blocks_per_bh);
   else
-    chunk_attn_kernel<BF16, false><<<grid, 256, 0, s>>>(
-        (const T*)qk, (const T*)v, sorted_idx, (T*)o_out, lse_out, token_scales, L, n_slots, n_chunks,
-        blocks_per_bh);
+    chunk_attn_kernel<BF16, false, ATTEND><<<grid, 256, dyn, s>>>(
+        (const T*)qk, (const T*)v, sorted_idx, (T*)o_out, lse_out, token_scales, buckets, undo_idx, L, n_h,
+        n_slots, n_chunks, blocks_per_bh);
   return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_attn_d(const void* qk, const void* v, const int32_t* sorted_idx, void* o_out, float* lse_out,
+                         const float2* token_scales, const int32_t* buckets, const int32_t* undo_idx, int BH,
+                         int L, int n_h, int causal, int attend, hipStream_t s) {
+  switch (attend) {
+    case 0:
+      return launch_attn_t<BF16, 0>(qk, v, sorted_idx, o_out, lse_out, token_scales, nullptr, nullptr, BH, L, n_h,
+                                    causal, s);
+    case 1:
+      return launch_attn_t<BF16, 1>(qk, v, sorted_idx, o_out, lse_out, token_scales, buckets, nullptr, BH, L, n_h,
+                                    causal, s);
+    case 2:
+      return launch_attn_t<BF16, 2>(qk, v, sorted_idx, o_out, lse_out, token_scales, nullptr, undo_idx, BH, L,
+                                    n_h, causal, s);
+    case 3:
+      return launch_attn_t<BF16, 3>(qk, v, sorted_idx, o_out, lse_out, token_scales, buckets, undo_idx, BH, L,
+                                    n_h, causal, s);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_chunk_attn(const void* qk, const void* v, const int32_t* sorted_idx, void* o_out,
-                             float* lse_out, const float2* token_scales, int BH, int L, int n_h, int causal,
+                             float* lse_out, const float2* token_scales, const int32_t* buckets,
+                             const int32_t* undo_idx, int BH, int L, int n_h, int causal, int attend,
                              lsh_dtype dt, hipStream_t s) {
   if (dt == LSH_BF16)
-    return launch_attn_t<true>(qk, v, sorted_idx, o_out, lse_out, token_scales, BH, L, n_h, causal, s);
-  return launch_attn_t<false>(qk, v, sorted_idx, o_out, lse_out, token_scales, BH, L, n_h, causal, s);
+    return launch_attn_d<true>(qk, v, sorted_idx, o_out, lse_out, token_scales, buckets, undo_idx, BH, L, n_h,
+                               causal, attend, s);
+  return launch_attn_d<false>(qk, v, sorted_idx, o_out, lse_out, token_scales, buckets, undo_idx, BH, L, n_h,
+                              causal, attend, s);
 }
 
 }  // namespace lsh

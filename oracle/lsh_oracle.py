@@ -171,15 +171,21 @@ def slot_codes(buckets: np.ndarray, sorted_idx: np.ndarray) -> np.ndarray:
 
 
 def pair_multiplicity(sorted_idx: np.ndarray, undo_idx: np.ndarray, chunk_len: int, causal: bool,
-                      codes=None) -> list:
+                      codes=None, tokens=None) -> list:
     """For every token i, a dict {token j: N_ij}: how many times j is a kept key
     of i over all of i's windows (one query occurrence of i per round, each
-    window counted with multiplicity, the masks of the variant applied)."""
+    window counted with multiplicity, the masks of the variant applied).
+    With `tokens` given, only those query tokens are counted (the others get
+    empty dicts), for sampled checks of long sequences."""
     n_h, L = undo_idx.shape
     n_slots = sorted_idx.shape[0]
+    wanted = None if tokens is None else set(int(t) for t in tokens)
     counts = []
     for i in range(L):
         cnt = {}
+        if wanted is not None and i not in wanted:
+            counts.append(cnt)
+            continue
         for r in range(n_h):
             g = int(undo_idx[r, i])
             for gk in window_slots(n_slots, chunk_len, g // chunk_len):
@@ -287,16 +293,16 @@ def forward(x, v, rot, n_buckets: int, n_hashes: int, chunk_len: int, causal: bo
     return out, lse
 
 
-def token_output(x, v, sorted_idx, undo_idx, chunk_len: int, causal: bool, i: int):
+def token_output(x, v, sorted_idx, undo_idx, chunk_len: int, causal: bool, i: int, codes=None, mult=None):
     """Output and LSE of the single token i of one problem, computed from its
     own window in every round (for sampled checks at sizes where the full
-    oracle would be slow)."""
+    oracle would be slow).  `codes` / `mult` as in chunk_attention."""
     n_h, L = undo_idx.shape
     o_r, l_r = [], []
     for r in range(n_h):
         g = int(undo_idx[r, i])
         c = g // chunk_len
-        o, l = chunk_attention(x, v, sorted_idx, chunk_len, causal, chunks=[c])
+        o, l = chunk_attention(x, v, sorted_idx, chunk_len, causal, chunks=[c], codes=codes, mult=mult)
         o_r.append(o[g])
         l_r.append(l[g])
     l_r = np.array(l_r)

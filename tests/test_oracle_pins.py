@@ -548,3 +548,23 @@ def test_same_bucket_masks_equal_bucket_ids_of_another_round():
         out, lse = _attend(x, v, i, keys, False)
         np.testing.assert_allclose(res["out"][i], out, rtol=0, atol=1e-10)
         assert abs(res["lse"][i] - lse) < 1e-9
+
+
+def test_sampled_multiplicity_and_token_output_agree_with_the_full_variant():
+    """The sampled forms used at long sequence lengths (multiplicity for a
+    subset of query tokens, one token's output from its own windows) give the
+    full variant computation's values for those tokens."""
+    x, v, rot = _problem(35, 256, 4, 3)
+    for causal in (False, True):
+        full = O.forward_problem(x, v, rot, 4, 3, 64, causal, same_bucket=True, dedup=True)
+        si, ui = full["sorted_idx"], full["undo_idx"]
+        codes = O.slot_codes(full["buckets"], si)
+        every = O.pair_multiplicity(si, ui, 64, causal, codes)
+        toks = [0, 5, 131, 255]
+        some = O.pair_multiplicity(si, ui, 64, causal, codes, tokens=toks)
+        for i in range(256):
+            assert some[i] == (every[i] if i in toks else {})
+        for i in toks:
+            o, l = O.token_output(x, v, si, ui, 64, causal, i, codes=codes, mult=some)
+            np.testing.assert_allclose(o, full["out"][i], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(l, full["lse"][i], rtol=1e-12, atol=1e-12)
