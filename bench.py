@@ -6,6 +6,11 @@ workspace and outputs are resident in HBM before timing starts.  Prints one
 JSON line on stdout; diagnostics go to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_seq_64k]
+                  [--attend none|same_bucket|dedup|both]
+
+--attend times an attended-set variant (reformer_lsh_attn_fwd_ex) instead of
+the method as described; such a line names the variant in its config and
+carries no cpu_baseline leg.
 """
 from __future__ import annotations
 
@@ -29,11 +34,16 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def algorithmic_work(B, H, L, D, n_b, n_h, es):
+ATTEND = {"none": (False, False), "same_bucket": (True, False), "dedup": (False, True), "both": (True, True)}
+
+
+def algorithmic_work(B, H, L, D, n_b, n_h, es, same_bucket=False, dedup=False):
     """Per-launch algorithmic bytes and flops of each kernel (see the design
     notes): what the method must read and write, not what a kernel happens to."""
     th = B * H * L            # token-heads
     tr = th * n_h             # token-rounds
+    # variants: the slot's bucket (same-bucket), every round's unsort index (set union)
+    extra = 4 * tr * (int(same_bucket) + int(dedup))
     half = n_b // 2
     return {
         "prep": {"bytes": 2 * n_h * D * half * es, "flops": 0},
@@ -45,18 +55,19 @@ def algorithmic_work(B, H, L, D, n_b, n_h, es):
         # per token-round (slot of the sorted order): its index, its gathered QK and V
         # rows, its output row and lse.  Each round's chunks read their rows in that
         # round's order, so every row is gathered once per round.
-        "chunk_attn": {"bytes": tr * (4 + 3 * D * es + 4), "flops": tr * 4 * D * 128},
+        "chunk_attn": {"bytes": tr * (4 + 3 * D * es + 4) + extra, "flops": tr * 4 * D * 128},
         # per token-head: n_h rows + lse + undo index read, one output row + LSE written
         "combine": {"bytes": th * (n_h * (D * es + 8) + D * es + 4), "flops": 0},
     }
 
 
-def measured_traffic(workload: str, kernel: str):
+def measured_traffic(workload: str, kernel: str, attend: str = "none"):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE record (profiles/traffic_<workload>.json), or None when there is
-    no record or the kernel's source has changed since it was taken."""
+    WRITE_SIZE record (profiles/traffic_<workload>[_<attend>].json), or None when
+    there is no record or the kernel's source has changed since it was taken."""
     from lsh_attention_amd.prof_summary import source_sha256
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    tag = workload if attend == "none" else f"{workload}_{attend}"
+    path = os.path.join(ROOT, "profiles", f"traffic_{tag}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get("kernels", {}).get(kernel)
@@ -96,6 +107,8 @@ def main():
     ap.add_argument("--workload", default="long_seq_64k")
     ap.add_argument("--n-hashes", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--attend", choices=sorted(ATTEND), default="none",
+                    help="attended-set variant: same-bucket mask, set-union correction, or both")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device-to-device copy of this many MiB "
                          "(a reference kernel of known traffic for hardware byte counters)")
@@ -116,8 +129,9 @@ def main():
     B, H, L, D = inp.qk.values.shape
     n_h, n_b = inp.n_hashes, w.n_buckets
     es = 2 if w.dtype == "bf16" else 4
-    log(f"workload {w.name}: B{B} H{H} L{L} D{D} n_b{n_b} n_h{n_h} causal={w.causal} {w.dtype}; "
-        f"sha256(qk)={inp.meta['qk_sha256'][:16]}")
+    same_bucket, dedup = ATTEND[args.attend]
+    log(f"workload {w.name}: B{B} H{H} L{L} D{D} n_b{n_b} n_h{n_h} causal={w.causal} {w.dtype} "
+        f"attend={args.attend}; sha256(qk)={inp.meta['qk_sha256'][:16]}")
 
     def dev(t):
         if t is None:
@@ -134,7 +148,7 @@ def main():
 
     def step(events=None):
         bd.reformer_lsh_attn_fwd(qk, v, rot, n_b, n_h, 64, w.causal, out=out, lse=lse, workspace=ws,
-                                 stage_events=events)
+                                 stage_events=events, same_bucket=same_bucket, dedup=dedup)
 
     for _ in range(args.warmup):
         step()
@@ -161,7 +175,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    work = algorithmic_work(B, H, L, D, n_b, n_h, es)
+    work = algorithmic_work(B, H, L, D, n_b, n_h, es, same_bucket, dedup)
     peak_flops = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
     kernels = {}
     for i, name in enumerate(bd.KERNEL_NAMES):
@@ -189,7 +203,7 @@ def main():
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["kernel"] = dom
-    roof["traffic"] = measured_traffic(w.name, dom)
+    roof["traffic"] = measured_traffic(w.name, dom, args.attend)
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -200,7 +214,9 @@ def main():
         "roofline": roof,
         "kernels": kernels,
     }
-    if not args.no_cpu_baseline:
+    if args.attend != "none":
+        result["config"]["attend"] = args.attend
+    if not args.no_cpu_baseline and args.attend == "none":
         log("timing the oracle on the host (cpu_baseline leg)")
         result["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(result), flush=True)

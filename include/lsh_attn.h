@@ -117,6 +117,9 @@ int lsh_chunk_attn(const void* qk, const void* v, const int32_t* sorted_idx, voi
  *                            (may be NULL otherwise).
  *   undo_idx [B, H, n_h, L]  from lsh_sort; read with LSH_ATTEND_DEDUP (may be
  *                            NULL otherwise).
+ *   ws       workspace of at least lsh_chunk_attn_ex_workspace_bytes(...) bytes
+ *            (0 without LSH_ATTEND_DEDUP, when ws may be NULL): a token-major
+ *            copy of every round's bucket and chunk, B*H*L*n_h int32.
  * Other arguments as in lsh_chunk_attn.  Bucket values must be in [0, 4096)
  * and undo_idx must be lsh_sort's inverse of sorted_idx (neither is checked on
  * the device; other values give meaningless results but no out-of-bounds
@@ -124,10 +127,11 @@ int lsh_chunk_attn(const void* qk, const void* v, const int32_t* sorted_idx, voi
  * so expect the call to be slower than lsh_chunk_attn. */
 #define LSH_ATTEND_SAME_BUCKET 1
 #define LSH_ATTEND_DEDUP 2
+int lsh_chunk_attn_ex_workspace_bytes(int B, int H, int L, int n_h, int attend, size_t* bytes);
 int lsh_chunk_attn_ex(const void* qk, const void* v, const int32_t* sorted_idx,
                       const int32_t* buckets, const int32_t* undo_idx, void* o_sorted,
                       float* lse_sorted, int B, int H, int L, int D, int n_h, int C, int causal,
-                      int attend, lsh_dtype dt, void* stream);
+                      int attend, lsh_dtype dt, void* ws, size_t ws_bytes, void* stream);
 
 /* Steps 4-5, unsort and combine (explainer page: union of the rounds).
  * LSE_i = logsumexp_r lse_r(i), out_i = sum_r exp(lse_r(i) - LSE_i) o_r(i), with
@@ -161,8 +165,10 @@ int reformer_lsh_attn_fwd(const void* qk, const void* v, const void* rot, int n_
                           void* stream, void* const* stage_events);
 
 /* The whole forward pass with an attended-set variant (`attend` as in
- * lsh_chunk_attn_ex; 0 gives reformer_lsh_attn_fwd).  Same workspace size as
- * reformer_lsh_attn_fwd; other arguments as there. */
+ * lsh_chunk_attn_ex; 0 gives reformer_lsh_attn_fwd).  lsh_fwd_workspace_bytes
+ * covers both calls; other arguments as in reformer_lsh_attn_fwd.  The
+ * LSH_ATTEND_DEDUP variant adds one kernel before the attention, timed with it
+ * (the LSH_FWD_KERNEL_ATTN stage). */
 int reformer_lsh_attn_fwd_ex(const void* qk, const void* v, const void* rot, int n_buckets,
                              int n_hashes, int chunk_len, int causal, int attend, int B, int H,
                              int L, int D, lsh_dtype dt, void* out, float* lse_out, void* ws,

@@ -32,7 +32,8 @@ _SIGS = {
     "lsh_sort_workspace_bytes": (_c_int, [_c_int] * 5 + [ctypes.POINTER(_c_size)]),
     "lsh_sort": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [_vp, _c_size, _vp]),
     "lsh_chunk_attn": (_c_int, [_vp] * 5 + [_c_int] * 8 + [_vp]),
-    "lsh_chunk_attn_ex": (_c_int, [_vp] * 7 + [_c_int] * 9 + [_vp]),
+    "lsh_chunk_attn_ex_workspace_bytes": (_c_int, [_c_int] * 5 + [ctypes.POINTER(_c_size)]),
+    "lsh_chunk_attn_ex": (_c_int, [_vp] * 7 + [_c_int] * 9 + [_vp, _c_size, _vp]),
     "lsh_unsort_combine": (_c_int, [_vp] * 5 + [_c_int] * 6 + [_vp]),
     "lsh_fwd_workspace_bytes": (_c_int, [_c_int] * 8 + [ctypes.POINTER(_c_size)]),
     "reformer_lsh_attn_fwd": (_c_int, [_vp] * 3 + [_c_int] * 9 + [_vp, _vp, _vp, _c_size, _vp, _vp]),
@@ -191,10 +192,14 @@ def lsh_chunk_attn(qk: torch.Tensor, v: torch.Tensor, sorted_idx: torch.Tensor, 
                                                       o_sorted.data_ptr(), lse_sorted.data_ptr(), B, H, L, D,
                                                       n_hashes, chunk_len, int(bool(causal)), dt, _stream(qk.device)))
     else:
+        n = ctypes.c_size_t()
+        _check("lsh_chunk_attn_ex_workspace_bytes",
+               lib().lsh_chunk_attn_ex_workspace_bytes(B, H, L, n_hashes, attend, ctypes.byref(n)))
+        ws = _workspace(n.value, qk.device) if n.value else None
         _check("lsh_chunk_attn_ex", lib().lsh_chunk_attn_ex(
             qk.data_ptr(), v.data_ptr(), sorted_idx.data_ptr(), _ptr(buckets), _ptr(undo_idx), o_sorted.data_ptr(),
-            lse_sorted.data_ptr(), B, H, L, D, n_hashes, chunk_len, int(bool(causal)), attend, dt,
-            _stream(qk.device)))
+            lse_sorted.data_ptr(), B, H, L, D, n_hashes, chunk_len, int(bool(causal)), attend, dt, _ptr(ws),
+            0 if ws is None else ws.numel(), _stream(qk.device)))
     return o_sorted, lse_sorted
 
 

@@ -74,7 +74,7 @@ size_t sort_ws_bytes(int BH, int L, int n_b, int n_h) {
 
 struct FwdWs {
   HashWs hash;
-  size_t hash_base, sort_base, buckets, sorted_idx, undo_idx, o_sorted, lse_sorted, token_scales, total;
+  size_t hash_base, sort_base, buckets, sorted_idx, undo_idx, o_sorted, lse_sorted, token_scales, tok_rec, total;
 };
 FwdWs fwd_ws(int BH, int L, int n_b, int n_h, lsh_dtype dt) {
   Carver c;
@@ -89,6 +89,7 @@ FwdWs fwd_ws(int BH, int L, int n_b, int n_h, lsh_dtype dt) {
   w.o_sorted = c.take(slots * kD * elem_size(dt));
   w.lse_sorted = c.take(slots * sizeof(float));
   w.token_scales = c.take((size_t)BH * L * sizeof(float2));
+  w.tok_rec = c.take(slots * sizeof(int32_t));  // set-union variant only
   w.total = c.off;
   return w;
 }
@@ -219,9 +220,31 @@ int lsh_sort(const int32_t* buckets, int32_t* sorted_idx, int32_t* undo_idx, int
                                  nullptr, &k));
 }
 
+}  // extern "C"
+
+namespace {
+
+size_t chunk_attn_ws_bytes(int BH, int L, int n_h, int attend) {
+  return (attend & LSH_ATTEND_DEDUP) ? align_up((size_t)BH * n_h * L * sizeof(int32_t), kAlign) : 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lsh_chunk_attn_ex_workspace_bytes(int B, int H, int L, int n_h, int attend, size_t* bytes) {
+  if (bytes == nullptr) return LSH_ERR_NULL;
+  const int st = check_problem(B, H, L, kD, n_h);
+  if (st != LSH_OK) return st;
+  if (!attend_ok(attend)) return LSH_ERR_UNSUPPORTED;
+  *bytes = is_empty(B, H, L) ? 0 : chunk_attn_ws_bytes(B * H, L, n_h, attend);
+  return LSH_OK;
+}
+
 int lsh_chunk_attn_ex(const void* qk, const void* v, const int32_t* sorted_idx, const int32_t* buckets,
                       const int32_t* undo_idx, void* o_sorted, float* lse_sorted, int B, int H, int L, int D,
-                      int n_h, int C, int causal, int attend, lsh_dtype dt, void* stream) {
+                      int n_h, int C, int causal, int attend, lsh_dtype dt, void* ws, size_t ws_bytes,
+                      void* stream) {
   int st = check_problem(B, H, L, D, n_h);
   if (st != LSH_OK) return st;
   if (C != kChunk) return C <= 0 ? LSH_ERR_SHAPE : LSH_ERR_UNSUPPORTED;
@@ -232,25 +255,31 @@ int lsh_chunk_attn_ex(const void* qk, const void* v, const int32_t* sorted_idx, 
       (sb && buckets == nullptr) || (dd && undo_idx == nullptr))
     return LSH_ERR_NULL;
   const int BH = B * H;
+  const size_t need = chunk_attn_ws_bytes(BH, L, n_h, attend);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return LSH_ERR_WORKSPACE;
   const size_t es = elem_size(dt);
   const size_t slots = (size_t)BH * n_h * L;
   const size_t in_bytes = (size_t)BH * L * kD * es;
   const size_t o_bytes = slots * kD * es, l_bytes = slots * sizeof(float), i_bytes = slots * sizeof(int32_t);
+  const size_t w_bytes = need > 0 ? ws_bytes : 0;
   const void* ins[5] = {qk, v, sorted_idx, sb ? buckets : nullptr, dd ? undo_idx : nullptr};
   const size_t in_n[5] = {in_bytes, in_bytes, i_bytes, i_bytes, i_bytes};
   for (int a = 0; a < 5; ++a)
-    if (overlaps(o_sorted, o_bytes, ins[a], in_n[a]) || overlaps(lse_sorted, l_bytes, ins[a], in_n[a]))
+    if (overlaps(o_sorted, o_bytes, ins[a], in_n[a]) || overlaps(lse_sorted, l_bytes, ins[a], in_n[a]) ||
+        overlaps(ws, w_bytes, ins[a], in_n[a]))
       return LSH_ERR_ALIAS;
-  if (overlaps(o_sorted, o_bytes, lse_sorted, l_bytes)) return LSH_ERR_ALIAS;
+  if (overlaps(o_sorted, o_bytes, lse_sorted, l_bytes) || overlaps(ws, w_bytes, o_sorted, o_bytes) ||
+      overlaps(ws, w_bytes, lse_sorted, l_bytes))
+    return LSH_ERR_ALIAS;
   return hip_status(launch_chunk_attn(qk, v, sorted_idx, o_sorted, lse_sorted, nullptr, sb ? buckets : nullptr,
-                                      dd ? undo_idx : nullptr, BH, L, n_h, causal, attend, dt,
-                                      (hipStream_t)stream));
+                                      dd ? undo_idx : nullptr, dd ? (int32_t*)ws : nullptr, BH, L, n_h, causal,
+                                      attend, dt, (hipStream_t)stream));
 }
 
 int lsh_chunk_attn(const void* qk, const void* v, const int32_t* sorted_idx, void* o_sorted, float* lse_sorted,
                    int B, int H, int L, int D, int n_h, int C, int causal, lsh_dtype dt, void* stream) {
   return lsh_chunk_attn_ex(qk, v, sorted_idx, nullptr, nullptr, o_sorted, lse_sorted, B, H, L, D, n_h, C, causal, 0,
-                           dt, stream);
+                           dt, nullptr, 0, stream);
 }
 
 int lsh_unsort_combine(const void* o_sorted, const float* lse_sorted, const int32_t* undo_idx, void* out,
@@ -339,8 +368,8 @@ int reformer_lsh_attn_fwd_ex(const void* qk, const void* v, const void* rot, int
     e = enqueue_sort(buckets, sorted_idx, undo_idx, (int*)(base + w.sort_base), BH, L, n_b, n_h, s, stage_events,
                      &k);
   if (e == hipSuccess)
-    e = launch_chunk_attn(qk, v, sorted_idx, o_sorted, lse_sorted, token_scales, buckets, undo_idx, BH, L, n_h,
-                          causal, attend, dt, s);
+    e = launch_chunk_attn(qk, v, sorted_idx, o_sorted, lse_sorted, token_scales, buckets, undo_idx,
+                          (int32_t*)(base + w.tok_rec), BH, L, n_h, causal, attend, dt, s);
   if (e == hipSuccess && stage_events != nullptr) e = hipEventRecord((hipEvent_t)stage_events[++k], s);
   if (e == hipSuccess) e = launch_combine(o_sorted, lse_sorted, undo_idx, out, lse_out, BH, L, n_h, dt, s);
   if (e == hipSuccess && stage_events != nullptr) e = hipEventRecord((hipEvent_t)stage_events[++k], s);

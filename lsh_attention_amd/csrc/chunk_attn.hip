@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
     const typename AttnTraits<BF16>::T* __restrict__ qk, const typename AttnTraits<BF16>::T* __restrict__ v,
     const int32_t* __restrict__ sorted_idx, typename AttnTraits<BF16>::T* __restrict__ o_out,
     float* __restrict__ lse_out, const float2* __restrict__ token_scales, const int32_t* __restrict__ buckets,
-    const int32_t* __restrict__ undo_idx, int L, int n_h, int n_slots, int n_chunks, int blocks_per_bh) {
+    const int32_t* __restrict__ tok_rec, int L, int n_h, int n_slots, int n_chunks, int blocks_per_bh) {
   constexpr int kCPB = chunks_per_block<ATTEND>();
   constexpr bool kSB = (ATTEND & 1) != 0, kDD = (ATTEND & 2) != 0;
   using T = typename AttnTraits<BF16>::T;
@@ -148,25 +148,32 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
   if constexpr (ATTEND != 0) {
     const int cpr = L / kChunk;  // chunks per round
     const int32_t* bk = buckets + (size_t)bh * n_h * L;
-    const int32_t* ud = undo_idx + (size_t)bh * n_slots;
     for (int e = tid; e < (c1 - c0 + 1) * 64; e += 256) {
       const int k = e >> 6, r = e & 63;
       const int c = (k == 0) ? (c0 - 1 + n_chunks) % n_chunks : c0 - 1 + k;
       const int pos = sPos[k][r];
+      // the token's record: per round, (bucket << 18) | chunk index within the round
+      const int32_t* rec = kDD ? tok_rec + ((size_t)bh * L + pos) * n_h : nullptr;
       if constexpr (kSB) {
         const int rnd = c / cpr;
-        sCode[k * 64 + r] = (rnd << 13) | (bk[(size_t)rnd * L + pos] & 0xFFF);
+        const int bucket = kDD ? rec[rnd] >> 18 : bk[(size_t)rnd * L + pos] & 0xFFF;
+        sCode[k * 64 + r] = (rnd << 13) | bucket;
       }
       if constexpr (kDD) {
+        int32_t wv[kMaxHashes];
+#pragma unroll
+        for (int b = 0; b < kMaxHashes; ++b)
+          if (b < n_h) wv[b] = rec[b];
         int last = 0, first = 0;
-        for (int b = 0; b < n_h; ++b) {
-          // chunk of this token in round b, as an index within the round
-          const int cb = (int)min((uint32_t)ud[(size_t)b * L + pos], (uint32_t)(n_slots - 1)) / kChunk % cpr;
-          sChk[(k * n_h + b) * 64 + r] = kSB ? ((bk[(size_t)b * L + pos] & 0xFFF) << 18) | cb : cb;
-          last |= (cb == cpr - 1 ? 1 : 0) << b;
-          // bit b: this token's chunk in round b+1 (cyclically) is that round's first
-          first |= (cb == 0 ? 1 : 0) << ((b + n_h - 1) % n_h);
-        }
+#pragma unroll
+        for (int b = 0; b < kMaxHashes; ++b)
+          if (b < n_h) {
+            const int cb = wv[b] & 0x3FFFF;
+            sChk[(k * n_h + b) * 64 + r] = kSB ? wv[b] : cb;
+            last |= (cb == cpr - 1 ? 1 : 0) << b;
+            // bit b: this token's chunk in round b+1 (cyclically) is that round's first
+            first |= (cb == 0 ? 1 : 0) << ((b + n_h - 1) % n_h);
+          }
         sLast[k * 64 + r] = last;
         sFirst[k * 64 + r] = first;
       }
@@ -551,9 +558,32 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
   }
 }
 
+// Token-major record of the set-union variant: rec[bh][i][r] = (bucket of i in
+// round r << 18, 0 without buckets) | (chunk of i in round r, as an index within
+// the round).  One
+// contiguous n_h-word record per token, so the attention kernel reads a row's
+// rounds as one sector instead of 2 n_h scattered words.  Undo values of round
+// r lie in [r L, (r+1) L); out-of-range values only give wrong table data.
+__global__ __launch_bounds__(256) void variant_rec_kernel(const int32_t* __restrict__ buckets,
+                                                          const int32_t* __restrict__ undo_idx,
+                                                          int32_t* __restrict__ rec, int L, int n_h,
+                                                          int blocks_per_bh) {
+  const int bh = blockIdx.x / blocks_per_bh;
+  const int i = (blockIdx.x % blocks_per_bh) * 256 + threadIdx.x;
+  if (i >= L) return;
+  const int cpr = L / kChunk;
+  const int32_t* ud = undo_idx + (size_t)bh * n_h * L;
+  int32_t* out = rec + ((size_t)bh * L + i) * n_h;
+  for (int r = 0; r < n_h; ++r) {
+    const int cb = (ud[(size_t)r * L + i] >> 6) - r * cpr;
+    const int bucket = buckets == nullptr ? 0 : buckets[((size_t)bh * n_h + r) * L + i] & 0xFFF;
+    out[r] = (bucket << 18) | (cb & 0x3FFFF);
+  }
+}
+
 template <bool BF16, int ATTEND>
 hipError_t launch_attn_t(const void* qk, const void* v, const int32_t* sorted_idx, void* o_out, float* lse_out,
-                         const float2* token_scales, const int32_t* buckets, const int32_t* undo_idx, int BH,
+                         const float2* token_scales, const int32_t* buckets, const int32_t* tok_rec, int BH,
                          int L, int n_h, int causal, hipStream_t s) {
   using T = typename AttnTraits<BF16>::T;
   constexpr int kCPB = chunks_per_block<ATTEND>();
@@ -564,18 +594,18 @@ hipError_t launch_attn_t(const void* qk, const void* v, const int32_t* sorted_id
   const size_t dyn = variant_lds_bytes(ATTEND, n_h);
   if (causal)
     chunk_attn_kernel<BF16, true, ATTEND><<<grid, 256, dyn, s>>>(
-        (const T*)qk, (const T*)v, sorted_idx, (T*)o_out, lse_out, token_scales, buckets, undo_idx, L, n_h,
+        (const T*)qk, (const T*)v, sorted_idx, (T*)o_out, lse_out, token_scales, buckets, tok_rec, L, n_h,
         n_slots, n_chunks, blocks_per_bh);
   else
     chunk_attn_kernel<BF16, false, ATTEND><<<grid, 256, dyn, s>>>(
-        (const T*)qk, (const T*)v, sorted_idx, (T*)o_out, lse_out, token_scales, buckets, undo_idx, L, n_h,
+        (const T*)qk, (const T*)v, sorted_idx, (T*)o_out, lse_out, token_scales, buckets, tok_rec, L, n_h,
         n_slots, n_chunks, blocks_per_bh);
   return hipGetLastError();
 }
 
 template <bool BF16>
 hipError_t launch_attn_d(const void* qk, const void* v, const int32_t* sorted_idx, void* o_out, float* lse_out,
-                         const float2* token_scales, const int32_t* buckets, const int32_t* undo_idx, int BH,
+                         const float2* token_scales, const int32_t* buckets, const int32_t* tok_rec, int BH,
                          int L, int n_h, int causal, int attend, hipStream_t s) {
   switch (attend) {
     case 0:
@@ -585,11 +615,11 @@ hipError_t launch_attn_d(const void* qk, const void* v, const int32_t* sorted_id
       return launch_attn_t<BF16, 1>(qk, v, sorted_idx, o_out, lse_out, token_scales, buckets, nullptr, BH, L, n_h,
                                     causal, s);
     case 2:
-      return launch_attn_t<BF16, 2>(qk, v, sorted_idx, o_out, lse_out, token_scales, nullptr, undo_idx, BH, L,
-                                    n_h, causal, s);
+      return launch_attn_t<BF16, 2>(qk, v, sorted_idx, o_out, lse_out, token_scales, nullptr, tok_rec, BH, L, n_h,
+                                    causal, s);
     case 3:
-      return launch_attn_t<BF16, 3>(qk, v, sorted_idx, o_out, lse_out, token_scales, buckets, undo_idx, BH, L,
-                                    n_h, causal, s);
+      return launch_attn_t<BF16, 3>(qk, v, sorted_idx, o_out, lse_out, token_scales, nullptr, tok_rec, BH, L, n_h,
+                                    causal, s);
     default:
       return hipErrorInvalidValue;
   }
@@ -599,12 +629,19 @@ hipError_t launch_attn_d(const void* qk, const void* v, const int32_t* sorted_id
 
 hipError_t launch_chunk_attn(const void* qk, const void* v, const int32_t* sorted_idx, void* o_out,
                              float* lse_out, const float2* token_scales, const int32_t* buckets,
-                             const int32_t* undo_idx, int BH, int L, int n_h, int causal, int attend,
-                             lsh_dtype dt, hipStream_t s) {
+                             const int32_t* undo_idx, int32_t* tok_rec, int BH, int L, int n_h, int causal,
+                             int attend, lsh_dtype dt, hipStream_t s) {
+  if (attend & 2) {
+    const int blocks_per_bh = (L + 255) / 256;
+    variant_rec_kernel<<<(unsigned)blocks_per_bh * (unsigned)BH, 256, 0, s>>>(buckets, undo_idx, tok_rec, L, n_h,
+                                                                             blocks_per_bh);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (dt == LSH_BF16)
-    return launch_attn_d<true>(qk, v, sorted_idx, o_out, lse_out, token_scales, buckets, undo_idx, BH, L, n_h,
+    return launch_attn_d<true>(qk, v, sorted_idx, o_out, lse_out, token_scales, buckets, tok_rec, BH, L, n_h,
                                causal, attend, s);
-  return launch_attn_d<false>(qk, v, sorted_idx, o_out, lse_out, token_scales, buckets, undo_idx, BH, L, n_h,
+  return launch_attn_d<false>(qk, v, sorted_idx, o_out, lse_out, token_scales, buckets, tok_rec, BH, L, n_h,
                               causal, attend, s);
 }
 

@@ -81,11 +81,13 @@ hipError_t launch_sort_scatter(const int32_t* buckets, const int* hist, int32_t*
 // Outputs per sorted slot ([BH][n_h*L][64], [BH][n_h*L]).  token_scales (nullable): per
 // token (key scale, query bound) from the hash pass.  attend: 0, or the
 // LSH_ATTEND_* bits; buckets ([BH][n_h][L]) are read with LSH_ATTEND_SAME_BUCKET,
-// undo_idx ([BH][n_h][L]) with LSH_ATTEND_DEDUP (nullptr otherwise).
+// undo_idx ([BH][n_h][L]) with LSH_ATTEND_DEDUP, which first writes a token-major
+// record to tok_rec (BH * L * n_h ints of scratch); nullptr where unused.
 hipError_t launch_chunk_attn(const void* qk, const void* v, const int32_t* sorted_idx,
                              void* o_out, float* lse_out, const float2* token_scales,
-                             const int32_t* buckets, const int32_t* undo_idx, int BH, int L,
-                             int n_h, int causal, int attend, lsh_dtype dt, hipStream_t s);
+                             const int32_t* buckets, const int32_t* undo_idx, int32_t* tok_rec,
+                             int BH, int L, int n_h, int causal, int attend, lsh_dtype dt,
+                             hipStream_t s);
 
 // Unsort + combine from the per-slot layout, through undo_idx.
 hipError_t launch_combine(const void* o_sorted, const float* lse_sorted, const int32_t* undo_idx,

@@ -148,20 +148,28 @@ def test_binding_refuses_cpu_tensors():
 
 def test_variant_calls_reject_before_launch(L):
     SB, DD = bd.LSH_ATTEND_SAME_BUCKET, bd.LSH_ATTEND_DEDUP
-    P6, P7 = 0x60000000, 0x70000000
+    P6, P7, P8 = 0x60000000, 0x70000000, 0x80000000
+    st, need = _ws("lsh_chunk_attn_ex_workspace_bytes", 1, 1, 256, 2, DD)
+    assert st == OK and need >= 256 * 2 * 4
+    assert _ws("lsh_chunk_attn_ex_workspace_bytes", 1, 1, 256, 2, SB) == (OK, 0)
+    assert _ws("lsh_chunk_attn_ex_workspace_bytes", 1, 1, 256, 2, 4)[0] == UNSUPPORTED
+    assert _ws("lsh_chunk_attn_ex_workspace_bytes", 0, 1, 256, 2, DD) == (OK, 0)
     ex = L.lsh_chunk_attn_ex
-    # args: qk, v, sorted_idx, buckets, undo_idx, o, lse, B, H, L, D, n_h, C, causal, attend, dt, stream
-    assert ex(P1, P2, P3, None, None, P6, P7, 1, 1, 256, 64, 2, 64, 0, SB, BF16, None) == NULL  # buckets needed
-    assert ex(P1, P2, P3, None, None, P6, P7, 1, 1, 256, 64, 2, 64, 0, DD, BF16, None) == NULL  # undo needed
-    assert ex(P1, P2, P3, P4, None, P6, P7, 1, 1, 256, 64, 2, 64, 0, SB | DD, BF16, None) == NULL
-    assert ex(P1, P2, P3, P4, P5, P6, P7, 1, 1, 256, 64, 2, 64, 0, 4, BF16, None) == UNSUPPORTED  # unknown bit
-    assert ex(P1, P2, P3, P4, P5, P6, P7, 1, 1, 256, 64, 2, 64, 0, -1, BF16, None) == UNSUPPORTED
-    # outputs on top of the variant's inputs; an unread input may alias
-    assert ex(P1, P2, P3, P4, None, P4, P7, 1, 1, 256, 64, 2, 64, 0, SB, BF16, None) == ALIAS
-    assert ex(P1, P2, P3, None, P5, P6, P5, 1, 1, 256, 64, 2, 64, 0, DD, BF16, None) == ALIAS
-    assert ex(P1, P2, P3, None, P5, P5 + 64, P7, 1, 1, 256, 64, 2, 64, 0, DD, BF16, None) == ALIAS
-    assert ex(None, None, None, None, None, None, None, 0, 1, 256, 64, 2, 64, 0, SB | DD, BF16, None) == OK
-    assert ex(None, None, None, None, None, None, None, 1, 1, 100, 64, 2, 64, 0, SB, BF16, None) == SHAPE
+    # args: qk, v, sorted_idx, buckets, undo_idx, o, lse, B, H, L, D, n_h, C, causal, attend, dt, ws, ws_bytes, stream
+    assert ex(P1, P2, P3, None, None, P6, P7, 1, 1, 256, 64, 2, 64, 0, SB, BF16, None, 0, None) == NULL  # buckets
+    assert ex(P1, P2, P3, None, None, P6, P7, 1, 1, 256, 64, 2, 64, 0, DD, BF16, P8, need, None) == NULL  # undo
+    assert ex(P1, P2, P3, P4, None, P6, P7, 1, 1, 256, 64, 2, 64, 0, SB | DD, BF16, P8, need, None) == NULL
+    assert ex(P1, P2, P3, None, P5, P6, P7, 1, 1, 256, 64, 2, 64, 0, DD, BF16, None, 0, None) == WORKSPACE
+    assert ex(P1, P2, P3, None, P5, P6, P7, 1, 1, 256, 64, 2, 64, 0, DD, BF16, P8, need - 1, None) == WORKSPACE
+    assert ex(P1, P2, P3, P4, P5, P6, P7, 1, 1, 256, 64, 2, 64, 0, 4, BF16, P8, need, None) == UNSUPPORTED
+    assert ex(P1, P2, P3, P4, P5, P6, P7, 1, 1, 256, 64, 2, 64, 0, -1, BF16, P8, need, None) == UNSUPPORTED
+    # outputs or workspace on top of the variant's inputs; an unread input may alias
+    assert ex(P1, P2, P3, P4, None, P4, P7, 1, 1, 256, 64, 2, 64, 0, SB, BF16, None, 0, None) == ALIAS
+    assert ex(P1, P2, P3, None, P5, P6, P5, 1, 1, 256, 64, 2, 64, 0, DD, BF16, P8, need, None) == ALIAS
+    assert ex(P1, P2, P3, None, P5, P6, P7, 1, 1, 256, 64, 2, 64, 0, DD, BF16, P5 + 64, need, None) == ALIAS
+    assert ex(P1, P2, P3, None, P5, P6, P7, 1, 1, 256, 64, 2, 64, 0, DD, BF16, P6, need, None) == ALIAS
+    assert ex(None, None, None, None, None, None, None, 0, 1, 256, 64, 2, 64, 0, SB | DD, BF16, None, 0, None) == OK
+    assert ex(None, None, None, None, None, None, None, 1, 1, 100, 64, 2, 64, 0, SB, BF16, None, 0, None) == SHAPE
     st, need = _ws("lsh_fwd_workspace_bytes", 1, 2, 128, 64, 8, 2, 64, BF16)
     f = L.reformer_lsh_attn_fwd_ex
     # args: qk, v, rot, n_b, n_h, C, causal, attend, B, H, L, D, dt, out, lse, ws, ws_bytes, stream, events

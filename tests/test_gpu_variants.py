@@ -121,7 +121,7 @@ def test_attend_zero_is_the_base_call(gpu_lib):
     o1, l1 = torch.empty_like(o0), torch.empty_like(l0)
     B, H, L, D = qk.shape
     st = gpu_lib.lsh_chunk_attn_ex(qk.data_ptr(), v.data_ptr(), sidx.data_ptr(), None, None, o1.data_ptr(),
-                                   l1.data_ptr(), B, H, L, D, 4, 64, int(w.causal), 0, bd.LSH_BF16,
+                                   l1.data_ptr(), B, H, L, D, 4, 64, int(w.causal), 0, bd.LSH_BF16, None, 0,
                                    torch.cuda.current_stream().cuda_stream)
     assert st == 0
     torch.cuda.synchronize()
