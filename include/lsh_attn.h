@@ -174,6 +174,31 @@ int reformer_lsh_attn_fwd_ex(const void* qk, const void* v, const void* rot, int
                              int L, int D, lsh_dtype dt, void* out, float* lse_out, void* ws,
                              size_t ws_bytes, void* stream, void* const* stage_events);
 
+/* Backward of the forward pass with respect to qk and v (Reformer explainer:
+ * the method's pipeline, differentiated; hashing and sorting are piecewise
+ * constant, so the forward's permutation is reused and no gradient flows
+ * through them).  The loss is sum_i dout_i . out_i + dlse_i LSE_i.
+ *   qk, v       [B, H, L, D]     the forward's inputs (dt).
+ *   sorted_idx  [B, H, n_h*L]    from lsh_sort (the forward's permutation).
+ *   undo_idx    [B, H, n_h, L]   from lsh_sort.
+ *   lse_sorted  [B, H, n_h*L]    from lsh_chunk_attn (per-round log-sum-exp).
+ *   out         [B, H, L, D]     the forward's output (dt).
+ *   dout        [B, H, L, D]     gradient of the loss w.r.t. out (dt).
+ *   dlse        [B, H, L]        gradient w.r.t. the forward's lse output
+ *                                (fp32), or NULL for none.
+ *   dqk, dv     [B, H, L, D]     out: gradients w.r.t. qk and v (dt).
+ *   ws          workspace of at least lsh_attn_bwd_workspace_bytes(...) bytes.
+ * Per slot the combined weight of every key occurrence is recomputed from qk
+ * and lse_sorted; the self key (logit -1e5) passes no gradient to qk.  A
+ * round in which only the self key is left (lse near -1e5) is recognised as
+ * such; the method assumes |qk_i| / 8 stays far below 1e5. */
+int lsh_attn_bwd_workspace_bytes(int B, int H, int L, int D, int n_h, int C, lsh_dtype dt,
+                                 size_t* bytes);
+int lsh_attn_bwd(const void* qk, const void* v, const int32_t* sorted_idx, const int32_t* undo_idx,
+                 const float* lse_sorted, const void* out, const void* dout, const float* dlse,
+                 void* dqk, void* dv, int B, int H, int L, int D, int n_h, int C, int causal,
+                 lsh_dtype dt, void* ws, size_t ws_bytes, void* stream);
+
 /* Timing helpers for callers that have no HIP runtime binding of their own:
  * create/destroy a hipEvent_t (returned as void*), and the elapsed time in
  * milliseconds between two recorded events (synchronises on `end`). */

@@ -38,6 +38,8 @@ _SIGS = {
     "lsh_fwd_workspace_bytes": (_c_int, [_c_int] * 8 + [ctypes.POINTER(_c_size)]),
     "reformer_lsh_attn_fwd": (_c_int, [_vp] * 3 + [_c_int] * 9 + [_vp, _vp, _vp, _c_size, _vp, _vp]),
     "reformer_lsh_attn_fwd_ex": (_c_int, [_vp] * 3 + [_c_int] * 10 + [_vp, _vp, _vp, _c_size, _vp, _vp]),
+    "lsh_attn_bwd_workspace_bytes": (_c_int, [_c_int] * 7 + [ctypes.POINTER(_c_size)]),
+    "lsh_attn_bwd": (_c_int, [_vp] * 10 + [_c_int] * 8 + [_vp, _c_size, _vp]),
     "lsh_event_create": (_c_int, [ctypes.POINTER(_vp)]),
     "lsh_event_destroy": (_c_int, [_vp]),
     "lsh_event_record": (_c_int, [_vp, _vp]),
@@ -251,6 +253,40 @@ def reformer_lsh_attn_fwd(qk: torch.Tensor, v: torch.Tensor, rot: torch.Tensor |
             qk.data_ptr(), v.data_ptr(), _ptr(rot), n_buckets, n_hashes, chunk_len, int(bool(causal)), attend, B, H,
             L, D, dt, out.data_ptr(), _ptr(lse), workspace.data_ptr(), workspace.numel(), _stream(qk.device), ev))
     return out, lse
+
+
+def lsh_attn_bwd(qk: torch.Tensor, v: torch.Tensor, sorted_idx: torch.Tensor, undo_idx: torch.Tensor,
+                 lse_sorted: torch.Tensor, out: torch.Tensor, dout: torch.Tensor, dlse: torch.Tensor | None,
+                 n_hashes: int, chunk_len: int = 64, causal: bool = False, dqk: torch.Tensor | None = None,
+                 dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Gradients (dqk, dv) of sum(dout * out) + sum(dlse * lse) through the forward pass
+    whose permutation (sorted_idx, undo_idx) and per-round lse (lse_sorted) are given."""
+    _dev(qk, v, sorted_idx, undo_idx, lse_sorted, out, dout, dlse, dqk, dv, workspace)
+    B, H, L, D = qk.shape
+    dt = _dtype_code(qk)
+    for name, t in (("v", v), ("out", out), ("dout", dout)):
+        if t.shape != qk.shape or t.dtype != qk.dtype:
+            raise ValueError(f"{name} must match qk in shape and dtype")
+    if sorted_idx.dtype != torch.int32 or sorted_idx.shape != (B, H, n_hashes * L):
+        raise ValueError("sorted_idx must be int32 [B,H,n_h*L]")
+    if undo_idx.dtype != torch.int32 or undo_idx.shape != (B, H, n_hashes, L):
+        raise ValueError("undo_idx must be int32 [B,H,n_h,L]")
+    if lse_sorted.dtype != torch.float32 or lse_sorted.shape != (B, H, n_hashes * L):
+        raise ValueError("lse_sorted must be float32 [B,H,n_h*L]")
+    if dlse is not None and (dlse.dtype != torch.float32 or dlse.shape != (B, H, L)):
+        raise ValueError("dlse must be float32 [B,H,L]")
+    dqk = torch.empty_like(qk) if dqk is None else dqk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        n = ctypes.c_size_t()
+        _check("lsh_attn_bwd_workspace_bytes",
+               lib().lsh_attn_bwd_workspace_bytes(B, H, L, D, n_hashes, chunk_len, dt, ctypes.byref(n)))
+        workspace = _workspace(n.value, qk.device)
+    _check("lsh_attn_bwd", lib().lsh_attn_bwd(
+        qk.data_ptr(), v.data_ptr(), sorted_idx.data_ptr(), undo_idx.data_ptr(), lse_sorted.data_ptr(),
+        out.data_ptr(), dout.data_ptr(), _ptr(dlse), dqk.data_ptr(), dv.data_ptr(), B, H, L, D, n_hashes, chunk_len,
+        int(bool(causal)), dt, _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(qk.device)))
+    return dqk, dv
 
 
 class EventSet:

@@ -3,7 +3,7 @@
 // entirely on the host and returns before anything is enqueued.
 #include <string.h>
 
-#include "lsh_internal.h"
+#include "lsh_bwd.h"
 
 using namespace lsh;
 
@@ -90,6 +90,21 @@ FwdWs fwd_ws(int BH, int L, int n_b, int n_h, lsh_dtype dt) {
   w.lse_sorted = c.take(slots * sizeof(float));
   w.token_scales = c.take((size_t)BH * L * sizeof(float2));
   w.tok_rec = c.take(slots * sizeof(int32_t));  // set-union variant only
+  w.total = c.off;
+  return w;
+}
+
+struct BwdWs {
+  size_t slot_w, tok_scale, dx_slot, dv_slot, total;
+};
+BwdWs bwd_ws(int BH, int L, int n_h, lsh_dtype dt) {
+  Carver c;
+  BwdWs w;
+  const size_t slots = (size_t)BH * n_h * L;
+  w.slot_w = c.take(slots * sizeof(float2));
+  w.tok_scale = c.take((size_t)BH * L * sizeof(float2));
+  w.dx_slot = c.take(slots * kD * elem_size(dt));
+  w.dv_slot = c.take(slots * kD * elem_size(dt));
   w.total = c.off;
   return w;
 }
@@ -381,6 +396,56 @@ int reformer_lsh_attn_fwd(const void* qk, const void* v, const void* rot, int n_
                           size_t ws_bytes, void* stream, void* const* stage_events) {
   return reformer_lsh_attn_fwd_ex(qk, v, rot, n_buckets, n_hashes, chunk_len, causal, 0, B, H, L, D, dt, out, lse_out,
                                   ws, ws_bytes, stream, stage_events);
+}
+
+int lsh_attn_bwd_workspace_bytes(int B, int H, int L, int D, int n_h, int C, lsh_dtype dt, size_t* bytes) {
+  if (bytes == nullptr) return LSH_ERR_NULL;
+  const int st = check_problem(B, H, L, D, n_h);
+  if (st != LSH_OK) return st;
+  if (C != kChunk) return C <= 0 ? LSH_ERR_SHAPE : LSH_ERR_UNSUPPORTED;
+  if (!dtype_ok(dt)) return LSH_ERR_UNSUPPORTED;
+  *bytes = is_empty(B, H, L) ? 0 : bwd_ws(B * H, L, n_h, dt).total;
+  return LSH_OK;
+}
+
+int lsh_attn_bwd(const void* qk, const void* v, const int32_t* sorted_idx, const int32_t* undo_idx,
+                 const float* lse_sorted, const void* out, const void* dout, const float* dlse, void* dqk, void* dv,
+                 int B, int H, int L, int D, int n_h, int C, int causal, lsh_dtype dt, void* ws, size_t ws_bytes,
+                 void* stream) {
+  int st = check_problem(B, H, L, D, n_h);
+  if (st != LSH_OK) return st;
+  if (C != kChunk) return C <= 0 ? LSH_ERR_SHAPE : LSH_ERR_UNSUPPORTED;
+  if (!dtype_ok(dt)) return LSH_ERR_UNSUPPORTED;
+  if (is_empty(B, H, L)) return LSH_OK;
+  if (qk == nullptr || v == nullptr || sorted_idx == nullptr || undo_idx == nullptr || lse_sorted == nullptr ||
+      out == nullptr || dout == nullptr || dqk == nullptr || dv == nullptr)
+    return LSH_ERR_NULL;
+  const int BH = B * H;
+  const BwdWs w = bwd_ws(BH, L, n_h, dt);
+  if (ws == nullptr || ws_bytes < w.total) return LSH_ERR_WORKSPACE;
+  const size_t es = elem_size(dt);
+  const size_t slots = (size_t)BH * n_h * L;
+  const size_t tok_bytes = (size_t)BH * L * kD * es, i_bytes = slots * sizeof(int32_t);
+  const void* ins[9] = {qk, v, sorted_idx, undo_idx, lse_sorted, out, dout, dlse, ws};
+  const size_t in_n[9] = {tok_bytes, tok_bytes, i_bytes, i_bytes, slots * sizeof(float), tok_bytes, tok_bytes,
+                          (size_t)BH * L * sizeof(float), ws_bytes};
+  for (int a = 0; a < 9; ++a)
+    if (overlaps(dqk, tok_bytes, ins[a], in_n[a]) || overlaps(dv, tok_bytes, ins[a], in_n[a])) return LSH_ERR_ALIAS;
+  if (overlaps(dqk, tok_bytes, dv, tok_bytes)) return LSH_ERR_ALIAS;
+  for (int a = 0; a < 8; ++a)
+    if (overlaps(ws, ws_bytes, ins[a], in_n[a])) return LSH_ERR_ALIAS;
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)ws;
+  float2* slot_w = (float2*)(base + w.slot_w);
+  float2* tok_scale = (float2*)(base + w.tok_scale);
+  void* dx_slot = base + w.dx_slot;
+  void* dv_slot = base + w.dv_slot;
+  hipError_t e = launch_bwd_prep(qk, out, dout, dlse, lse_sorted, undo_idx, slot_w, tok_scale, BH, L, n_h, dt, s);
+  if (e == hipSuccess)
+    e = launch_attn_bwd(qk, v, dout, sorted_idx, lse_sorted, slot_w, tok_scale, dx_slot, dv_slot, BH, L, n_h, causal,
+                        dt, s);
+  if (e == hipSuccess) e = launch_bwd_reduce(dx_slot, dv_slot, undo_idx, dqk, dv, BH, L, n_h, dt, s);
+  return hip_status(e);
 }
 
 int lsh_event_create(void** event) {

@@ -1,0 +1,684 @@
+// Backward of the shared-QK LSH attention forward pass: gradients with respect
+// to the shared query/key vectors and the values.
+//
+// Reformer explainer (akshathtiwari.co.in/blog/reformer): tokens are hashed,
+// sorted by bucket and attended in equal chunks (each chunk and the one before
+// it), and several rounds are unioned.  Hashing and sorting are piecewise
+// constant, so the forward's permutation is reused and the gradient flows
+// through the chunk attention and the combine only.
+//
+// Maths.  For query slot g of token i in round r and key occurrence k (token j)
+// in its window, with P_gk the round's softmax weight and w_g = exp(lse_r(i) -
+// LSE_i) the combine weight, the loss sum_i dout_i . out_i + dLSE_i LSE_i gives
+//   dlogit_gk = w_g P_gk (dout_i . v_j + c_i),   c_i = dLSE_i - dout_i . out_i
+//   dv_j     += w_g P_gk dout_i
+// (the per-round output o_r cancels out of the combine's derivative).  With
+// logit = x_i . khat_j / 8, khat_j = x_j / max(|x_j|, 1e-12) and kn_j = 1 /
+// (8 max(|x_j|, 1e-12)):
+//   dx_i (query role) += dlogit_gk kn_j x_j
+//   a_j              += dlogit_gk x_i,     dx_j (key role) = kn_j (a_j - khat_j (khat_j . a_j))
+// (kn_j a_j when |x_j| <= 1e-12).  The self logit is the constant -1e5 and a
+// causally dropped key has weight 0: neither passes a gradient to x.
+//
+// Kernels:
+//   bwd_prep   - per token: the combine weights w of its n_h slots (written per
+//                slot, with w c_i), and its key scales.
+//   attn_bwd   - per block, 8 consecutive chunks as keys.  Step c takes the
+//                queries of chunk c against the keys of chunks c-1 and c (the
+//                forward's window).  A chunk's keys are attended by the
+//                queries of its own chunk and of the next one, so the two
+//                waves that own a ring slot's keys keep that chunk's dv, a and
+//                dq accumulators over two consecutive steps and then write the
+//                slot's finished dx (query role + key role) and dv.  One extra
+//                step at the end of the run completes its last chunk; the
+//                first step's look-back keys belong to the previous run and
+//                only feed the dq of the first chunk.  No atomics: every slot
+//                is finished inside one block.
+//   bwd_reduce - per token: dx_i = sum over its n_h slots, dv_i likewise.
+//
+// gfx950 layout of attn_bwd (8 waves; wave w owns keys 16 (w & 3) .. +15 of
+// ring slot w >> 2):
+//   S = Q K^T and dP = dO V^T on MFMA with queries as rows, so each lane holds
+//   4 consecutive queries of one key;  dV^T += dO^T Pw and A^T += Xq^T dS take
+//   the lane's own Pw / dS as the B operand, the A operand from LDS copies of
+//   dO and x stored transposed with the queries permuted into operand order;
+//   dS kn is written to LDS (bf16) and the key-owning waves of the current
+//   chunk form dQ^T = Xk^T (dS kn)^T over all 128 keys for their 16 queries,
+//   whose layout equals their own key accumulators.  The dS tile reuses the
+//   dO row and dO^T buffers (a barrier separates the uses).  fp32 inputs take
+//   the fp32 MFMA and read the transposed operands from the row copies.
+#include "lsh_bwd.h"
+
+namespace lsh {
+
+namespace {
+
+constexpr int kBwdChunksPerBlock = 8;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kSelf2 = -1.0e5f * kLog2e;
+// A row whose lse is below this (natural log) has only its self key left: every
+// real logit is at least -|x_i| / 8, far above the -1e5 of the self key.
+constexpr float kSelfOnly2 = (-1.0e5f + 0.5f) * kLog2e;
+
+template <bool BF16>
+struct BwdTraits;
+template <>
+struct BwdTraits<true> {
+  using T = uint16_t;
+  static constexpr int kXRow = 72;    // row copies: 64 dims + 8 pad (144 B)
+  static constexpr int kTRow = 136;   // transposed x: 2 slots x 64 + 8 pad
+  static constexpr int kQRow = 72;    // transposed dO: 64 queries + 8 pad
+  static constexpr int kSRow = 136;   // dS kn: 128 keys + 8 pad
+  static constexpr int kXLoads = 2;
+};
+template <>
+struct BwdTraits<false> {
+  using T = float;
+  static constexpr int kXRow = 68;
+  static constexpr int kTRow = 4;     // unused
+  static constexpr int kQRow = 4;     // unused
+  static constexpr int kSRow = 132;
+  static constexpr int kXLoads = 4;
+};
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+
+__device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ inline uint16_t to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Column of chunk row r in the transposed operand layout: column 32h + 8g + 4b + e
+// holds row 32h + 16b + 4g + e.
+__device__ inline int permcol(int r) {
+  return (r & ~31) | (((r >> 2) & 3) << 3) | (((r >> 4) & 1) << 2) | (r & 3);
+}
+
+// ---------------------------------------------------------------------------
+// bwd_prep: 16 lanes per token, 4 dims each.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ x_v, const void* __restrict__ out_v,
+                                                       const void* __restrict__ dout_v,
+                                                       const float* __restrict__ dlse,
+                                                       const float* __restrict__ lse_sorted,
+                                                       const int32_t* __restrict__ undo_idx,
+                                                       float2* __restrict__ slot_w, float2* __restrict__ tok_scale,
+                                                       int L, int n_h, size_t n_tokens) {
+  const size_t t = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  if (t >= n_tokens) return;  // whole 16-lane groups leave together
+  const size_t bh = t / L;
+  const int i = (int)(t % L);
+  const size_t n_slots = (size_t)n_h * L;
+  float xs[4], os[4], ds[4];
+  if constexpr (BF16) {
+    const uint2 a = *(const uint2*)((const uint16_t*)x_v + t * kD + 4 * sub);
+    const uint2 b = *(const uint2*)((const uint16_t*)out_v + t * kD + 4 * sub);
+    const uint2 c = *(const uint2*)((const uint16_t*)dout_v + t * kD + 4 * sub);
+    xs[0] = bf_lo(a.x); xs[1] = bf_hi(a.x); xs[2] = bf_lo(a.y); xs[3] = bf_hi(a.y);
+    os[0] = bf_lo(b.x); os[1] = bf_hi(b.x); os[2] = bf_lo(b.y); os[3] = bf_hi(b.y);
+    ds[0] = bf_lo(c.x); ds[1] = bf_hi(c.x); ds[2] = bf_lo(c.y); ds[3] = bf_hi(c.y);
+  } else {
+    const float4 a = *(const float4*)((const float*)x_v + t * kD + 4 * sub);
+    const float4 b = *(const float4*)((const float*)out_v + t * kD + 4 * sub);
+    const float4 c = *(const float4*)((const float*)dout_v + t * kD + 4 * sub);
+    xs[0] = a.x; xs[1] = a.y; xs[2] = a.z; xs[3] = a.w;
+    os[0] = b.x; os[1] = b.y; os[2] = b.z; os[3] = b.w;
+    ds[0] = c.x; ds[1] = c.y; ds[2] = c.z; ds[3] = c.w;
+  }
+  float ss = 0.f, dd = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    ss = fmaf(xs[e], xs[e], ss);
+    dd = fmaf(ds[e], os[e], dd);
+  }
+  int g = 0;
+  float l = -INFINITY;
+  if (sub < n_h) {
+    g = (int)min((uint32_t)undo_idx[(bh * n_h + sub) * L + i], (uint32_t)(n_slots - 1));
+    l = lse_sorted[bh * n_slots + g];
+  }
+  float m = l;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    ss += __shfl_xor(ss, o);
+    dd += __shfl_xor(dd, o);
+    m = fmaxf(m, __shfl_xor(m, o));
+  }
+  const float e = sub < n_h ? __expf(l - m) : 0.f;
+  float z = e;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o);
+  const float c = (dlse == nullptr ? 0.f : dlse[t]) - dd;
+  if (sub < n_h) {
+    const float w = e * __builtin_amdgcn_rcpf(z);
+    slot_w[bh * n_slots + g] = make_float2(w, w * c);
+  }
+  if (sub == 0) {
+    const float kn = 0.125f * __builtin_amdgcn_rcpf(fmaxf(__builtin_amdgcn_sqrtf(ss), 1e-12f));
+    tok_scale[t] = make_float2(kLog2e * kn, kn);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// attn_bwd
+// ---------------------------------------------------------------------------
+template <bool BF16, bool CAUSAL>
+__global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
+    const typename BwdTraits<BF16>::T* __restrict__ qk, const typename BwdTraits<BF16>::T* __restrict__ v,
+    const typename BwdTraits<BF16>::T* __restrict__ dout, const int32_t* __restrict__ sorted_idx,
+    const float* __restrict__ lse_sorted, const float2* __restrict__ slot_w, const float2* __restrict__ tok_scale,
+    typename BwdTraits<BF16>::T* __restrict__ dx_slot, typename BwdTraits<BF16>::T* __restrict__ dv_slot, int L,
+    int n_slots, int n_chunks, int blocks_per_bh) {
+  using T = typename BwdTraits<BF16>::T;
+  constexpr int kXRow = BwdTraits<BF16>::kXRow;
+  constexpr int kTRow = BwdTraits<BF16>::kTRow;
+  constexpr int kQRow = BwdTraits<BF16>::kQRow;
+  constexpr int kSRow = BwdTraits<BF16>::kSRow;
+  constexpr int kCPB = kBwdChunksPerBlock;
+  constexpr int kLoads = BF16 ? 1 : 2;  // 16-byte row pieces per thread (8 per bf16 row, 16 per fp32 row)
+
+  __shared__ __attribute__((aligned(16))) T sX[2][64 * kXRow];   // x rows per ring slot
+  __shared__ __attribute__((aligned(16))) T sV[2][64 * kXRow];   // v rows per ring slot
+  __shared__ __attribute__((aligned(16))) T sXT[BF16 ? 64 * kTRow : 1];  // [dim][64 slot + permcol(row)]
+  // dO rows + dO^T (bf16), or dO rows (fp32); the bf16 dS kn tile reuses the space.
+  constexpr int kDoElems = 64 * kXRow + (BF16 ? 64 * kQRow : 0);
+  constexpr int kSElems = 64 * kSRow;
+  constexpr int kUnion = BF16 ? (kDoElems > kSElems ? kDoElems : kSElems) : kDoElems;
+  __shared__ __attribute__((aligned(16))) T sDoBuf[kUnion];
+  __shared__ __attribute__((aligned(16))) float sDsF[BF16 ? 1 : kSElems];  // fp32 dS kn tile
+  __shared__ __attribute__((aligned(16))) float sKs2[2][64], sKn[2][64];   // key scales per slot
+  __shared__ __attribute__((aligned(16))) float sLse2[64], sW[64], sWc[64];  // current queries
+  __shared__ __attribute__((aligned(16))) int sPos[kCPB + 2][64];
+  T* const sDO = sDoBuf;                      // [query][dim]
+  T* const sDOT = sDoBuf + 64 * kXRow;        // [dim][permcol(query)] (bf16)
+  uint16_t* const sDS16 = (uint16_t*)sDoBuf;  // [query][64 slot + permcol(key)] (bf16)
+
+  const int bh = blockIdx.x / blocks_per_bh;
+  const int c0 = (blockIdx.x % blocks_per_bh) * kCPB;
+  const int c1 = min(n_chunks, c0 + kCPB);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int sw = wave >> 2, kt = wave & 3;  // owned keys: rows 16 kt .. 16 kt + 15 of ring slot sw
+  const int kr = 16 * kt + col;             // this lane's key row
+
+  constexpr uint32_t kRowBytes = kD * sizeof(T);
+  const char* xq = (const char*)(qk + (size_t)bh * L * kD);
+  const char* vq = (const char*)(v + (size_t)bh * L * kD);
+  const char* dq_in = (const char*)(dout + (size_t)bh * L * kD);
+  const int32_t* sidx = sorted_idx + (size_t)bh * n_slots;
+  const float* lseb = lse_sorted + (size_t)bh * n_slots;
+  const float2* swb = slot_w + (size_t)bh * n_slots;
+  const float2* tsb = tok_scale + (size_t)bh * L;
+  T* dxb = dx_slot + (size_t)bh * n_slots * kD;
+  T* dvb = dv_slot + (size_t)bh * n_slots * kD;
+
+  // Positions of steps c0-1 .. c1 (entry k <-> step c0-1+k, chunk (c0-1+k) mod n_chunks).
+  for (int e = tid; e < (c1 - c0 + 2) * 64; e += 512) {
+    const int k = e >> 6, r = e & 63;
+    const int c = (c0 - 1 + k + n_chunks) % n_chunks;
+    sPos[k][r] = (int)min((uint32_t)sidx[(size_t)c * kChunk + r], (uint32_t)(L - 1));
+  }
+  __syncthreads();
+
+  // ---- gathers (registers) and commits (LDS) ----
+  // rows: thread t holds 16-byte pieces (t & 7) * kLoads + i of row t >> 3.
+  // transposed (bf16): dims 2p, 2p+1 (p = t & 31) of rows 32h + 16b + 4g + 0..3,
+  // (h, g, b) from j = t >> 5, which land in columns 32h + 8g + 4b + 0..3.
+  const int prow = tid >> 3, ppc = (tid & 7) * kLoads;
+  const int tp = tid & 31, tj = tid >> 5;
+  const int trow = 32 * (tj >> 3) + 16 * (tj & 1) + 4 * ((tj >> 1) & 3);
+  const int tcol = 32 * (tj >> 3) + 8 * ((tj >> 1) & 3) + 4 * (tj & 1);
+  uint4 xr[kLoads], vr[kLoads], dr[kLoads];
+  uint32_t xw[BF16 ? 4 : 1], dw[BF16 ? 4 : 1];
+  float2 ksc = make_float2(0.f, 0.f), qsw = make_float2(0.f, 0.f);
+  float qlse = 0.f;
+  auto gather = [&](int k) {  // entry k: its keys, and (for every entry but the first) its queries
+    const int* pos = sPos[k];
+    const int chunk = (c0 - 1 + k + n_chunks) % n_chunks;
+    const uint32_t off = (uint32_t)pos[prow] * kRowBytes + 16u * (uint32_t)ppc;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      xr[i] = *(const uint4*)(xq + off + 16u * i);
+      vr[i] = *(const uint4*)(vq + off + 16u * i);
+      dr[i] = *(const uint4*)(dq_in + off + 16u * i);
+    }
+    if constexpr (BF16) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t o = (uint32_t)pos[trow + e] * kRowBytes + 4u * tp;
+        xw[e] = *(const uint32_t*)(xq + o);
+        dw[e] = *(const uint32_t*)(dq_in + o);
+      }
+    }
+    if (tid < 64) {
+      ksc = tsb[pos[tid]];
+      qlse = lseb[(size_t)chunk * kChunk + tid];
+      qsw = swb[(size_t)chunk * kChunk + tid];
+    }
+  };
+  auto commit_t = [&](T* dst, int rowlen, int base, const uint32_t (&w)[BF16 ? 4 : 1]) {
+    if constexpr (BF16) {
+      uint2 lo, hi;
+      lo.x = __builtin_amdgcn_perm(w[1], w[0], 0x05040100u);
+      lo.y = __builtin_amdgcn_perm(w[3], w[2], 0x05040100u);
+      hi.x = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);
+      hi.y = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
+      *(uint2*)(&dst[(2 * tp) * rowlen + base + tcol]) = lo;
+      *(uint2*)(&dst[(2 * tp + 1) * rowlen + base + tcol]) = hi;
+    }
+  };
+  auto commit = [&](int slot, bool queries) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      *(uint4*)(&sX[slot][prow * kXRow + (ppc + i) * (16 / sizeof(T))]) = xr[i];
+      *(uint4*)(&sV[slot][prow * kXRow + (ppc + i) * (16 / sizeof(T))]) = vr[i];
+    }
+    if (tid < 64) {
+      sKs2[slot][tid] = ksc.x;
+      sKn[slot][tid] = ksc.y;
+    }
+    if constexpr (BF16) commit_t(sXT, kTRow, 64 * slot, xw);
+    if (queries) {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) *(uint4*)(&sDO[prow * kXRow + (ppc + i) * (16 / sizeof(T))]) = dr[i];
+      if constexpr (BF16) commit_t(sDOT, kQRow, 0, dw);
+      if (tid < 64) {
+        sLse2[tid] = qlse * kLog2e;
+        sW[tid] = qsw.x;
+        sWc[tid] = qsw.y;
+      }
+    }
+  };
+
+  // prologue: step c0-1's keys (entry 0), then step c0's keys and queries (entry 1)
+  gather(0);
+  commit((c0 + 1) & 1, false);
+  gather(1);
+  commit(c0 & 1, true);
+  __syncthreads();
+
+  // accumulators of the owned keys: [dim tile], lane holds dims 16 dt + 4 grp + e of key kr
+  f32x4 acc_v[4], acc_a[4], acc_q[4];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      acc_v[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc_a[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc_q[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  zero_acc();
+
+  for (int c = c0; c <= c1; ++c) {
+    const int cur = c & 1, prv = cur ^ 1;
+    const int ec = c - c0 + 1;  // sPos entry of step c
+    if (c < c1) gather(ec + 1);
+    const bool mine_cur = (sw == cur);
+    const int ek = mine_cur ? ec : ec - 1;  // sPos entry of the owned keys
+    const bool do_kv = mine_cur ? (c < c1) : (c > c0);
+    const bool do_ds = (c < c1);
+    const bool active = do_kv || do_ds;
+
+    uint32_t dsk16[8];  // dS kn of the owned key for the 16 queries of this lane (bf16 pairs)
+    float dskf[16];
+
+    if (active) {
+      const int kpos = sPos[ek][kr];
+      const float ks2 = sKs2[sw][kr], kn = sKn[sw][kr];
+      // Pw = w P (for dv) and dS (for x) from one query tile's S = Q K^T and dP = dO V^T
+      auto elementwise = [&](int qt, const f32x4& S, const f32x4& dP, float (&pw)[4], float (&dsv)[4]) {
+        const int q0 = 16 * qt + 4 * grp;
+        const float4 l4 = *(const float4*)(&sLse2[q0]);
+        const float4 w4 = *(const float4*)(&sW[q0]);
+        const float4 c4 = *(const float4*)(&sWc[q0]);
+        const int4 p4 = *(const int4*)(&sPos[ec][q0]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, wv[4] = {w4.x, w4.y, w4.z, w4.w};
+        const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+        const int qp[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool self = kpos == qp[e];
+          const bool drop = CAUSAL && kpos > qp[e];
+          float p = __builtin_amdgcn_exp2f((self ? kSelf2 : S[e] * ks2) - lv[e]);
+          if (lv[e] < kSelfOnly2) p = self ? 1.f : 0.f;
+          p = drop ? 0.f : p;
+          pw[e] = wv[e] * p;
+          const float dl = p * fmaf(wv[e], dP[e], cv[e]);
+          dsv[e] = self ? 0.f : dl;
+        }
+      };
+      if constexpr (BF16) {
+        const bf16x8 k0 = *(const bf16x8*)(&sX[sw][kr * kXRow + 8 * grp]);
+        const bf16x8 k1 = *(const bf16x8*)(&sX[sw][kr * kXRow + 32 + 8 * grp]);
+        const bf16x8 v0 = *(const bf16x8*)(&sV[sw][kr * kXRow + 8 * grp]);
+        const bf16x8 v1 = *(const bf16x8*)(&sV[sw][kr * kXRow + 32 + 8 * grp]);
+        bf16x4 bp4[4], bs4[4];
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) {
+          const int qr = 16 * qt + col;
+          const bf16x8 q0 = *(const bf16x8*)(&sX[cur][qr * kXRow + 8 * grp]);
+          const bf16x8 q1 = *(const bf16x8*)(&sX[cur][qr * kXRow + 32 + 8 * grp]);
+          const bf16x8 d0 = *(const bf16x8*)(&sDO[qr * kXRow + 8 * grp]);
+          const bf16x8 d1 = *(const bf16x8*)(&sDO[qr * kXRow + 32 + 8 * grp]);
+          f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q0, k0, z, 0, 0, 0);
+          const f32x4 S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q1, k1, z, 0, 0, 0);
+          f32x4 y = {0.f, 0.f, 0.f, 0.f};
+          y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(d0, v0, y, 0, 0, 0);
+          const f32x4 dP = __builtin_amdgcn_mfma_f32_16x16x32_bf16(d1, v1, y, 0, 0, 0);
+          float pw[4], dsv[4];
+          elementwise(qt, S, dP, pw, dsv);
+          bp4[qt] = __builtin_convertvector((f32x4{pw[0], pw[1], pw[2], pw[3]}), bf16x4);
+          bs4[qt] = __builtin_convertvector((f32x4{dsv[0], dsv[1], dsv[2], dsv[3]}), bf16x4);
+          const uint2 u = __builtin_bit_cast(
+              uint2, __builtin_convertvector((f32x4{dsv[0] * kn, dsv[1] * kn, dsv[2] * kn, dsv[3] * kn}), bf16x4));
+          dsk16[2 * qt] = u.x;
+          dsk16[2 * qt + 1] = u.y;
+        }
+        // ---- dV^T += dO^T Pw, A^T += Xq^T dS (K = the 64 queries, permuted) ----
+        if (do_kv) {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8 bp = __builtin_shufflevector(bp4[2 * ks], bp4[2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8 bs = __builtin_shufflevector(bs4[2 * ks], bs4[2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+              const bf16x8 ad = *(const bf16x8*)(&sDOT[(16 * dt + col) * kQRow + 32 * ks + 8 * grp]);
+              const bf16x8 ax = *(const bf16x8*)(&sXT[(16 * dt + col) * kTRow + 64 * cur + 32 * ks + 8 * grp]);
+              acc_v[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad, bp, acc_v[dt], 0, 0, 0);
+              acc_a[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bs, acc_a[dt], 0, 0, 0);
+            }
+          }
+        }
+      } else {
+        // k-step s: lane group g feeds dim 16 g + s
+        float kk[16], vv[16];
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const float4 a = *(const float4*)(&sX[sw][kr * kXRow + 16 * grp + 4 * s4]);
+          const float4 b = *(const float4*)(&sV[sw][kr * kXRow + 16 * grp + 4 * s4]);
+          kk[4 * s4] = a.x; kk[4 * s4 + 1] = a.y; kk[4 * s4 + 2] = a.z; kk[4 * s4 + 3] = a.w;
+          vv[4 * s4] = b.x; vv[4 * s4 + 1] = b.y; vv[4 * s4 + 2] = b.z; vv[4 * s4 + 3] = b.w;
+        }
+        float pw[4][4], dsv[4][4];
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) {
+          const int qr = 16 * qt + col;
+          f32x4 z = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4) {
+            const float4 a = *(const float4*)(&sX[cur][qr * kXRow + 16 * grp + 4 * s4]);
+            const float4 b = *(const float4*)(&sDO[qr * kXRow + 16 * grp + 4 * s4]);
+            const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              z = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], kk[4 * s4 + u], z, 0, 0, 0);
+              y = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[u], vv[4 * s4 + u], y, 0, 0, 0);
+            }
+          }
+          elementwise(qt, z, y, pw[qt], dsv[qt]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dskf[4 * qt + e] = dsv[qt][e] * kn;
+        }
+        if (do_kv) {
+          // K index grp <-> query 16 qt + 4 grp + e, one MFMA per (qt, e)
+#pragma unroll
+          for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int qr = 16 * qt + 4 * grp + e;
+#pragma unroll
+              for (int dt = 0; dt < 4; ++dt) {
+                const float ad = sDO[qr * kXRow + 16 * dt + col];
+                const float ax = sX[cur][qr * kXRow + 16 * dt + col];
+                acc_v[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ad, pw[qt][e], acc_v[dt], 0, 0, 0);
+                acc_a[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ax, dsv[qt][e], acc_a[dt], 0, 0, 0);
+              }
+            }
+        }
+      }
+    }
+
+    // ---- dQ^T = Xk^T (dS kn)^T for the current chunk's queries ----
+    if (do_ds) {
+      __syncthreads();  // every wave is done reading dO (the bf16 dS tile reuses its space)
+      if (active) {
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int q = 16 * qt + 4 * grp + e;
+            if constexpr (BF16) {
+              const uint32_t wv = dsk16[2 * qt + (e >> 1)];
+              sDS16[q * kSRow + 64 * sw + permcol(kr)] = (uint16_t)((e & 1) ? (wv >> 16) : (wv & 0xFFFFu));
+            } else {
+              sDsF[q * kSRow + 64 * sw + kr] = dskf[4 * qt + e];
+            }
+          }
+      }
+      __syncthreads();
+      if (mine_cur) {
+        // this wave's queries are its own key rows 16 kt + col of the current chunk
+        if constexpr (BF16) {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const int kcol = 64 * (ks < 2 ? prv : cur) + 32 * (ks & 1) + 8 * grp;
+            const bf16x8 bq = *(const bf16x8*)(&sDS16[kr * kSRow + kcol]);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+              const bf16x8 a = *(const bf16x8*)(&sXT[(16 * dt + col) * kTRow + kcol]);
+              acc_q[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq, acc_q[dt], 0, 0, 0);
+            }
+          }
+        } else {
+          // K index grp <-> key 4 (s & 15) + grp of slot (s < 16 ? prv : cur)
+#pragma unroll 4
+          for (int s = 0; s < 32; ++s) {
+            const int sl = s < 16 ? prv : cur;
+            const int kk = 4 * (s & 15) + grp;
+            const float bq = sDsF[kr * kSRow + 64 * sl + kk];
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+              const float a = sX[sl][kk * kXRow + 16 * dt + col];
+              acc_q[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bq, acc_q[dt], 0, 0, 0);
+            }
+          }
+        }
+      }
+    }
+
+    // ---- the previous chunk's keys are complete: dx = dq + kn (a - khat (khat . a)), dv ----
+    if (!mine_cur && c > c0) {
+      const int chunk = (c - 1 + n_chunks) % n_chunks;
+      const float kn = sKn[sw][kr];
+      const bool tiny = kn > 0.12e12f;  // |x| at the 1e-12 floor: khat = x / 1e-12, no projection
+      float xv[4][4];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        if constexpr (BF16) {
+          const uint2 r = *(const uint2*)(&sX[sw][kr * kXRow + 16 * dt + 4 * grp]);
+          xv[dt][0] = bf_lo(r.x); xv[dt][1] = bf_hi(r.x); xv[dt][2] = bf_lo(r.y); xv[dt][3] = bf_hi(r.y);
+        } else {
+          const float4 r = *(const float4*)(&sX[sw][kr * kXRow + 16 * dt + 4 * grp]);
+          xv[dt][0] = r.x; xv[dt][1] = r.y; xv[dt][2] = r.z; xv[dt][3] = r.w;
+        }
+      }
+      float dot = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dot = fmaf(xv[dt][e], acc_a[dt][e], dot);
+      // sum over the 4 lanes holding this key (lanes l, l^16, l^32, l^48)
+      {
+        auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(dot), __float_as_uint(dot), false, false);
+        dot = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+        auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(dot), __float_as_uint(dot), false, false);
+        dot = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+      }
+      // khat = 8 kn x, so khat (khat . a) = 64 kn^2 x (x . a)
+      const float proj = tiny ? 0.f : 64.f * kn * kn * dot;
+      const size_t row = (size_t)chunk * kChunk + kr;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        float ox[4], ov[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ox[e] = acc_q[dt][e] + kn * (acc_a[dt][e] - proj * xv[dt][e]);
+          ov[e] = acc_v[dt][e];
+        }
+        T* px = dxb + row * kD + 16 * dt + 4 * grp;
+        T* pv = dvb + row * kD + 16 * dt + 4 * grp;
+        if constexpr (BF16) {
+          const bf16x2 x0 = __builtin_convertvector(f32x2{ox[0], ox[1]}, bf16x2);
+          const bf16x2 x1 = __builtin_convertvector(f32x2{ox[2], ox[3]}, bf16x2);
+          const bf16x2 v0 = __builtin_convertvector(f32x2{ov[0], ov[1]}, bf16x2);
+          const bf16x2 v1 = __builtin_convertvector(f32x2{ov[2], ov[3]}, bf16x2);
+          *(uint2*)px = make_uint2(__builtin_bit_cast(uint32_t, x0), __builtin_bit_cast(uint32_t, x1));
+          *(uint2*)pv = make_uint2(__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1));
+        } else {
+          *(float4*)px = make_float4(ox[0], ox[1], ox[2], ox[3]);
+          *(float4*)pv = make_float4(ov[0], ov[1], ov[2], ov[3]);
+        }
+      }
+      zero_acc();
+    }
+
+    __syncthreads();  // every wave is done with slot prv, dO and the dS tile
+    if (c < c1) {
+      commit(prv, true);  // step c+1: its keys in slot (c+1) & 1 = prv, its queries
+      __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_reduce: dx_i = sum_r dx_slot[undo_r(i)], dv_i likewise; 8 lanes (bf16) or
+// 16 lanes (fp32) per token, 16 bytes each.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const void* __restrict__ dx_slot,
+                                                         const void* __restrict__ dv_slot,
+                                                         const int32_t* __restrict__ undo_idx, void* __restrict__ dx,
+                                                         void* __restrict__ dv, int L, int n_h, size_t n_tokens) {
+  constexpr int kLanesPerTok = BF16 ? 8 : 16;
+  constexpr int kE = BF16 ? 8 : 4;
+  constexpr size_t kEs = BF16 ? 2 : 4;
+  const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t tok = gid / kLanesPerTok;
+  const int sub = (int)(gid % kLanesPerTok);
+  if (tok >= n_tokens) return;
+  const size_t bh = tok / L;
+  const int i = (int)(tok % L);
+  const size_t n_slots = (size_t)n_h * L;
+  const int32_t* u = undo_idx + bh * n_slots + i;
+  int g[kMaxHashes];
+#pragma unroll
+  for (int r = 0; r < kMaxHashes; ++r)
+    if (r < n_h) g[r] = (int)min((uint32_t)u[(size_t)r * L], (uint32_t)(n_slots - 1));
+  uint4 rx[kMaxHashes], rv[kMaxHashes];
+#pragma unroll
+  for (int r = 0; r < kMaxHashes; ++r)
+    if (r < n_h) {
+      const size_t off = ((bh * n_slots + g[r]) * kD) * kEs + 16 * sub;
+      rx[r] = *(const uint4*)((const char*)dx_slot + off);
+      rv[r] = *(const uint4*)((const char*)dv_slot + off);
+    }
+  float ax[kE], av[kE];
+#pragma unroll
+  for (int e = 0; e < kE; ++e) ax[e] = av[e] = 0.f;
+#pragma unroll
+  for (int r = 0; r < kMaxHashes; ++r)
+    if (r < n_h) {
+      const uint32_t wx[4] = {rx[r].x, rx[r].y, rx[r].z, rx[r].w};
+      const uint32_t wv[4] = {rv[r].x, rv[r].y, rv[r].z, rv[r].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (BF16) {
+          ax[2 * k] += bf_lo(wx[k]);
+          ax[2 * k + 1] += bf_hi(wx[k]);
+          av[2 * k] += bf_lo(wv[k]);
+          av[2 * k + 1] += bf_hi(wv[k]);
+        } else {
+          ax[k] += __uint_as_float(wx[k]);
+          av[k] += __uint_as_float(wv[k]);
+        }
+      }
+    }
+  const size_t off = (tok * kD) * kEs + 16 * sub;
+  if constexpr (BF16) {
+    uint4 ox, ov;
+    uint32_t px[4], pv[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      px[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{ax[2 * k], ax[2 * k + 1]}, bf16x2));
+      pv[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{av[2 * k], av[2 * k + 1]}, bf16x2));
+    }
+    ox = make_uint4(px[0], px[1], px[2], px[3]);
+    ov = make_uint4(pv[0], pv[1], pv[2], pv[3]);
+    *(uint4*)((char*)dx + off) = ox;
+    *(uint4*)((char*)dv + off) = ov;
+  } else {
+    *(float4*)((char*)dx + off) = make_float4(ax[0], ax[1], ax[2], ax[3]);
+    *(float4*)((char*)dv + off) = make_float4(av[0], av[1], av[2], av[3]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_prep(const void* qk, const void* out, const void* dout, const float* dlse,
+                           const float* lse_sorted, const int32_t* undo_idx, float2* slot_w, float2* tok_scale,
+                           int BH, int L, int n_h, lsh_dtype dt, hipStream_t s) {
+  const size_t n_tok = (size_t)BH * L;
+  const unsigned grid = (unsigned)((n_tok + 15) / 16);
+  if (dt == LSH_BF16)
+    bwd_prep_kernel<true><<<grid, 256, 0, s>>>(qk, out, dout, dlse, lse_sorted, undo_idx, slot_w, tok_scale, L, n_h,
+                                               n_tok);
+  else
+    bwd_prep_kernel<false><<<grid, 256, 0, s>>>(qk, out, dout, dlse, lse_sorted, undo_idx, slot_w, tok_scale, L,
+                                                n_h, n_tok);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd(const void* qk, const void* v, const void* dout, const int32_t* sorted_idx,
+                           const float* lse_sorted, const float2* slot_w, const float2* tok_scale, void* dx_slot,
+                           void* dv_slot, int BH, int L, int n_h, int causal, lsh_dtype dt, hipStream_t s) {
+  const int n_slots = n_h * L;
+  const int n_chunks = n_slots / kChunk;
+  const int blocks_per_bh = (n_chunks + kBwdChunksPerBlock - 1) / kBwdChunksPerBlock;
+  const unsigned grid = (unsigned)blocks_per_bh * (unsigned)BH;
+#define LSH_BWD_LAUNCH(B16, CA)                                                                               \
+  attn_bwd_kernel<B16, CA><<<grid, 512, 0, s>>>(                                                              \
+      (const typename BwdTraits<B16>::T*)qk, (const typename BwdTraits<B16>::T*)v,                           \
+      (const typename BwdTraits<B16>::T*)dout, sorted_idx, lse_sorted, slot_w, tok_scale,                    \
+      (typename BwdTraits<B16>::T*)dx_slot, (typename BwdTraits<B16>::T*)dv_slot, L, n_slots, n_chunks,      \
+      blocks_per_bh)
+  if (dt == LSH_BF16) {
+    if (causal) LSH_BWD_LAUNCH(true, true);
+    else LSH_BWD_LAUNCH(true, false);
+  } else {
+    if (causal) LSH_BWD_LAUNCH(false, true);
+    else LSH_BWD_LAUNCH(false, false);
+  }
+#undef LSH_BWD_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_reduce(const void* dx_slot, const void* dv_slot, const int32_t* undo_idx, void* dx, void* dv,
+                             int BH, int L, int n_h, lsh_dtype dt, hipStream_t s) {
+  const size_t n_tok = (size_t)BH * L;
+  const int lanes = dt == LSH_BF16 ? 8 : 16;
+  const unsigned grid = (unsigned)((n_tok * lanes + 255) / 256);
+  if (dt == LSH_BF16)
+    bwd_reduce_kernel<true><<<grid, 256, 0, s>>>(dx_slot, dv_slot, undo_idx, dx, dv, L, n_h, n_tok);
+  else
+    bwd_reduce_kernel<false><<<grid, 256, 0, s>>>(dx_slot, dv_slot, undo_idx, dx, dv, L, n_h, n_tok);
+  return hipGetLastError();
+}
+
+}  // namespace lsh
