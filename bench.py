@@ -10,7 +10,10 @@ JSON line on stdout; diagnostics go to stderr.
 
 --attend times an attended-set variant (reformer_lsh_attn_fwd_ex) instead of
 the method as described; such a line names the variant in its config and
-carries no cpu_baseline leg.
+carries no cpu_baseline leg.  --backward times a training step of the layer
+instead: the fused forward that keeps its permutation and per-round lse
+(reformer_lsh_attn_fwd_train) followed by lsh_attn_bwd, with seeded output
+gradients; its line has "pass": "fwd+bwd" in its config.
 """
 from __future__ import annotations
 
@@ -25,6 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "LSH-attn fwd tokens/sec at L=64K, 8 hashes; % HBM / MFMA roofline"
+METRIC_TRAIN = "LSH-attn fwd+bwd (training step) tokens/sec at L=64K, 8 hashes; % HBM / MFMA roofline"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 MFMA / packed vector
@@ -58,13 +62,22 @@ def algorithmic_work(B, H, L, D, n_b, n_h, es, same_bucket=False, dedup=False):
         "chunk_attn": {"bytes": tr * (4 + 3 * D * es + 4) + extra, "flops": tr * 4 * D * 128},
         # per token-head: n_h rows + lse + undo index read, one output row + LSE written
         "combine": {"bytes": th * (n_h * (D * es + 8) + D * es + 4), "flops": 0},
+        # backward: per token x, out, dout rows and dLSE read, key scales written; per slot
+        # its undo index and lse read, its combine weights written
+        "bwd_prep": {"bytes": th * (3 * D * es + 12) + tr * 16, "flops": 0},
+        # per slot: index, gathered x, v and dout rows, lse, weights, key scales read;
+        # its dx and dv rows written.  flops: S, dP, dV, dK, dQ over its 128 keys
+        "attn_bwd": {"bytes": tr * (5 * D * es + 24), "flops": tr * 128 * 10 * D},
+        # per token: its n_h slots' dx and dv rows (and undo indices) read, dx and dv written
+        "bwd_reduce": {"bytes": tr * (4 + 2 * D * es) + th * 2 * D * es, "flops": 0},
     }
 
 
 def measured_traffic(workload: str, kernel: str, attend: str = "none"):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE record (profiles/traffic_<workload>[_<attend>].json), or None when
-    there is no record or the kernel's source has changed since it was taken."""
+    WRITE_SIZE record (profiles/traffic_<workload>[_<attend>].json, "train" for the
+    training step), or None when there is no record or the kernel's source has
+    changed since it was taken."""
     from lsh_attention_amd.prof_summary import source_sha256
     tag = workload if attend == "none" else f"{workload}_{attend}"
     path = os.path.join(ROOT, "profiles", f"traffic_{tag}.json")
@@ -109,6 +122,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attend", choices=sorted(ATTEND), default="none",
                     help="attended-set variant: same-bucket mask, set-union correction, or both")
+    ap.add_argument("--backward", action="store_true",
+                    help="time a training step (forward keeping its state, then the backward pass)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device-to-device copy of this many MiB "
                          "(a reference kernel of known traffic for hardware byte counters)")
@@ -146,23 +161,48 @@ def main():
     out = torch.empty_like(qk)
     lse = torch.empty((B, H, L), dtype=torch.float32, device="cuda")
 
+    if args.backward and args.attend != "none":
+        raise SystemExit("--backward covers the method as described (no --attend)")
+    names = list(bd.KERNEL_NAMES)
+    if args.backward:
+        n_slots = n_h * L
+        sidx = torch.empty((B, H, n_slots), dtype=torch.int32, device="cuda")
+        undo = torch.empty((B, H, n_h, L), dtype=torch.int32, device="cuda")
+        lse_s = torch.empty((B, H, n_slots), dtype=torch.float32, device="cuda")
+        dout = dev(I.gaussian(4242, (B, H, L, D), w.dtype))
+        dlse = dev(I.gaussian(4243, (B, H, L), "f32"))
+        dqk, dv = torch.empty_like(qk), torch.empty_like(v)
+        bws = torch.empty(bd.bwd_workspace_bytes(B, H, L, D, n_h, 64, dt), dtype=torch.uint8, device="cuda")
+        names += bd.BWD_KERNEL_NAMES
+
     def step(events=None):
-        bd.reformer_lsh_attn_fwd(qk, v, rot, n_b, n_h, 64, w.causal, out=out, lse=lse, workspace=ws,
-                                 stage_events=events, same_bucket=same_bucket, dedup=dedup)
+        if args.backward:
+            bd.reformer_lsh_attn_fwd_train(qk, v, rot, n_b, n_h, 64, w.causal, out=out, lse=lse, sorted_idx=sidx,
+                                           undo_idx=undo, lse_sorted=lse_s, workspace=ws,
+                                           stage_events=None if events is None else events[0])
+            bd.lsh_attn_bwd(qk, v, sidx, undo, lse_s, out, dout, dlse, n_h, 64, w.causal, dqk=dqk, dv=dv,
+                            workspace=bws, stage_events=None if events is None else events[1])
+        else:
+            bd.reformer_lsh_attn_fwd(qk, v, rot, n_b, n_h, 64, w.causal, out=out, lse=lse, workspace=ws,
+                                     stage_events=None if events is None else events[0], same_bucket=same_bucket,
+                                     dedup=dedup)
 
     for _ in range(args.warmup):
         step()
-    events = [bd.EventSet() for _ in range(args.steps)]
+    events = [(bd.EventSet(), bd.EventSet(bd.BWD_N_EVENTS) if args.backward else None) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         step(events[k])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    per_kernel = np.array([e.durations_ms() for e in events])  # [steps, kernels]
-    gpu_ms = float(np.mean([e.elapsed_ms(0, bd.N_EVENTS - 1) for e in events]))
+    per_kernel = np.array([e[0].durations_ms() + (e[1].durations_ms() if e[1] else []) for e in events])
+    gpu_ms = float(np.mean([e[0].elapsed_ms(0, bd.N_EVENTS - 1) + (e[1].elapsed_ms(0, bd.BWD_N_EVENTS - 1)
+                                                                   if e[1] else 0.0) for e in events]))
     for e in events:
-        e.close()
+        e[0].close()
+        if e[1]:
+            e[1].close()
     ms_per_step = elapsed * 1e3 / args.steps
     tokens = B * L
     value = tokens / (elapsed / args.steps)
@@ -178,7 +218,7 @@ def main():
     work = algorithmic_work(B, H, L, D, n_b, n_h, es, same_bucket, dedup)
     peak_flops = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
     kernels = {}
-    for i, name in enumerate(bd.KERNEL_NAMES):
+    for i, name in enumerate(names):
         us = float(np.mean(per_kernel[:, i])) * 1e3
         wk = work[name]
         ent = {"us": round(us, 2)}
@@ -203,7 +243,7 @@ def main():
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["kernel"] = dom
-    roof["traffic"] = measured_traffic(w.name, dom, args.attend)
+    roof["traffic"] = measured_traffic(w.name, dom, "train" if args.backward else args.attend)
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -216,7 +256,10 @@ def main():
     }
     if args.attend != "none":
         result["config"]["attend"] = args.attend
-    if not args.no_cpu_baseline and args.attend == "none":
+    if args.backward:
+        result["metric"] = METRIC_TRAIN
+        result["config"]["pass"] = "fwd+bwd"
+    if not args.no_cpu_baseline and args.attend == "none" and not args.backward:
         log("timing the oracle on the host (cpu_baseline leg)")
         result["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(result), flush=True)

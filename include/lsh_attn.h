@@ -188,16 +188,35 @@ int reformer_lsh_attn_fwd_ex(const void* qk, const void* v, const void* rot, int
  *                                (fp32), or NULL for none.
  *   dqk, dv     [B, H, L, D]     out: gradients w.r.t. qk and v (dt).
  *   ws          workspace of at least lsh_attn_bwd_workspace_bytes(...) bytes.
+ *   stage_events  NULL, or LSH_BWD_N_EVENTS hipEvent_t recorded before the
+ *               first and after every kernel (LSH_BWD_KERNEL_* order).
  * Per slot the combined weight of every key occurrence is recomputed from qk
  * and lse_sorted; the self key (logit -1e5) passes no gradient to qk.  A
  * round in which only the self key is left (lse near -1e5) is recognised as
- * such; the method assumes |qk_i| / 8 stays far below 1e5. */
+ * such; the method assumes |qk_i| / 8 stays far below 1e5.  The call is
+ * deterministic (no atomics): repeated calls give identical bits. */
+#define LSH_BWD_KERNEL_PREP 0    /* combine weights per slot, key scales */
+#define LSH_BWD_KERNEL_ATTN 1    /* chunk attention backward, per slot */
+#define LSH_BWD_KERNEL_REDUCE 2  /* sum of each token's rounds */
+#define LSH_BWD_N_KERNELS 3
+#define LSH_BWD_N_EVENTS (LSH_BWD_N_KERNELS + 1)
 int lsh_attn_bwd_workspace_bytes(int B, int H, int L, int D, int n_h, int C, lsh_dtype dt,
                                  size_t* bytes);
 int lsh_attn_bwd(const void* qk, const void* v, const int32_t* sorted_idx, const int32_t* undo_idx,
                  const float* lse_sorted, const void* out, const void* dout, const float* dlse,
                  void* dqk, void* dv, int B, int H, int L, int D, int n_h, int C, int causal,
-                 lsh_dtype dt, void* ws, size_t ws_bytes, void* stream);
+                 lsh_dtype dt, void* ws, size_t ws_bytes, void* stream, void* const* stage_events);
+
+/* The fused forward for training: as reformer_lsh_attn_fwd, and it also writes
+ * the state lsh_attn_bwd reuses to caller buffers (not the workspace):
+ *   sorted_idx [B, H, n_h*L], undo_idx [B, H, n_h, L] (int32) and
+ *   lse_sorted [B, H, n_h*L] (fp32); none may be NULL, none may overlap. */
+int reformer_lsh_attn_fwd_train(const void* qk, const void* v, const void* rot, int n_buckets,
+                                int n_hashes, int chunk_len, int causal, int B, int H, int L,
+                                int D, lsh_dtype dt, void* out, float* lse_out,
+                                int32_t* sorted_idx, int32_t* undo_idx, float* lse_sorted,
+                                void* ws, size_t ws_bytes, void* stream,
+                                void* const* stage_events);
 
 /* Timing helpers for callers that have no HIP runtime binding of their own:
  * create/destroy a hipEvent_t (returned as void*), and the elapsed time in

@@ -23,6 +23,9 @@ LSH_ATTEND_SAME_BUCKET, LSH_ATTEND_DEDUP = 1, 2
 N_KERNELS = 7
 N_EVENTS = N_KERNELS + 1
 KERNEL_NAMES = ["prep", "hash", "fixup", "sort_hist", "sort_scatter", "chunk_attn", "combine"]
+BWD_N_KERNELS = 3
+BWD_N_EVENTS = BWD_N_KERNELS + 1
+BWD_KERNEL_NAMES = ["bwd_prep", "attn_bwd", "bwd_reduce"]
 
 _c_int, _c_size, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 _SIGS = {
@@ -39,7 +42,8 @@ _SIGS = {
     "reformer_lsh_attn_fwd": (_c_int, [_vp] * 3 + [_c_int] * 9 + [_vp, _vp, _vp, _c_size, _vp, _vp]),
     "reformer_lsh_attn_fwd_ex": (_c_int, [_vp] * 3 + [_c_int] * 10 + [_vp, _vp, _vp, _c_size, _vp, _vp]),
     "lsh_attn_bwd_workspace_bytes": (_c_int, [_c_int] * 7 + [ctypes.POINTER(_c_size)]),
-    "lsh_attn_bwd": (_c_int, [_vp] * 10 + [_c_int] * 8 + [_vp, _c_size, _vp]),
+    "lsh_attn_bwd": (_c_int, [_vp] * 10 + [_c_int] * 8 + [_vp, _c_size, _vp, _vp]),
+    "reformer_lsh_attn_fwd_train": (_c_int, [_vp] * 3 + [_c_int] * 9 + [_vp] * 6 + [_c_size, _vp, _vp]),
     "lsh_event_create": (_c_int, [ctypes.POINTER(_vp)]),
     "lsh_event_destroy": (_c_int, [_vp]),
     "lsh_event_record": (_c_int, [_vp, _vp]),
@@ -258,9 +262,10 @@ def reformer_lsh_attn_fwd(qk: torch.Tensor, v: torch.Tensor, rot: torch.Tensor |
 def lsh_attn_bwd(qk: torch.Tensor, v: torch.Tensor, sorted_idx: torch.Tensor, undo_idx: torch.Tensor,
                  lse_sorted: torch.Tensor, out: torch.Tensor, dout: torch.Tensor, dlse: torch.Tensor | None,
                  n_hashes: int, chunk_len: int = 64, causal: bool = False, dqk: torch.Tensor | None = None,
-                 dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+                 dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stage_events=None):
     """Gradients (dqk, dv) of sum(dout * out) + sum(dlse * lse) through the forward pass
-    whose permutation (sorted_idx, undo_idx) and per-round lse (lse_sorted) are given."""
+    whose permutation (sorted_idx, undo_idx) and per-round lse (lse_sorted) are given.
+    `stage_events`: an EventSet of BWD_N_EVENTS events for per-kernel timing."""
     _dev(qk, v, sorted_idx, undo_idx, lse_sorted, out, dout, dlse, dqk, dv, workspace)
     B, H, L, D = qk.shape
     dt = _dtype_code(qk)
@@ -285,8 +290,45 @@ def lsh_attn_bwd(qk: torch.Tensor, v: torch.Tensor, sorted_idx: torch.Tensor, un
     _check("lsh_attn_bwd", lib().lsh_attn_bwd(
         qk.data_ptr(), v.data_ptr(), sorted_idx.data_ptr(), undo_idx.data_ptr(), lse_sorted.data_ptr(),
         out.data_ptr(), dout.data_ptr(), _ptr(dlse), dqk.data_ptr(), dv.data_ptr(), B, H, L, D, n_hashes, chunk_len,
-        int(bool(causal)), dt, _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(qk.device)))
+        int(bool(causal)), dt, _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(qk.device),
+        None if stage_events is None else stage_events.array()))
     return dqk, dv
+
+
+def bwd_workspace_bytes(B: int, H: int, L: int, D: int, n_hashes: int, chunk_len: int, dt: int) -> int:
+    n = ctypes.c_size_t()
+    _check("lsh_attn_bwd_workspace_bytes",
+           lib().lsh_attn_bwd_workspace_bytes(B, H, L, D, n_hashes, chunk_len, dt, ctypes.byref(n)))
+    return n.value
+
+
+def reformer_lsh_attn_fwd_train(qk: torch.Tensor, v: torch.Tensor, rot: torch.Tensor | None, n_buckets: int,
+                                n_hashes: int, chunk_len: int = 64, causal: bool = False, out=None, lse=None,
+                                sorted_idx=None, undo_idx=None, lse_sorted=None, workspace=None, stage_events=None):
+    """The fused forward that also returns the state the backward reuses:
+    (out, lse, sorted_idx [B,H,n_h*L], undo_idx [B,H,n_h,L], lse_sorted [B,H,n_h*L])."""
+    _dev(qk, v, rot, out, lse, sorted_idx, undo_idx, lse_sorted, workspace)
+    B, H, L, D = qk.shape
+    dt = _dtype_code(qk)
+    if v.shape != qk.shape or v.dtype != qk.dtype:
+        raise ValueError("v must match qk in shape and dtype")
+    if rot is not None and rot.dtype != qk.dtype:
+        raise TypeError("rot must have the dtype of qk")
+    dev = qk.device
+    out = torch.empty_like(qk) if out is None else out
+    lse = torch.empty((B, H, L), dtype=torch.float32, device=dev) if lse is None else lse
+    n_slots = n_hashes * L
+    sorted_idx = torch.empty((B, H, n_slots), dtype=torch.int32, device=dev) if sorted_idx is None else sorted_idx
+    undo_idx = torch.empty((B, H, n_hashes, L), dtype=torch.int32, device=dev) if undo_idx is None else undo_idx
+    lse_sorted = torch.empty((B, H, n_slots), dtype=torch.float32, device=dev) if lse_sorted is None else lse_sorted
+    if workspace is None:
+        workspace = _workspace(fwd_workspace_bytes(B, H, L, D, n_buckets, n_hashes, chunk_len, dt), dev)
+    ev = None if stage_events is None else stage_events.array()
+    _check("reformer_lsh_attn_fwd_train", lib().reformer_lsh_attn_fwd_train(
+        qk.data_ptr(), v.data_ptr(), _ptr(rot), n_buckets, n_hashes, chunk_len, int(bool(causal)), B, H, L, D, dt,
+        out.data_ptr(), lse.data_ptr(), sorted_idx.data_ptr(), undo_idx.data_ptr(), lse_sorted.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), _stream(dev), ev))
+    return out, lse, sorted_idx, undo_idx, lse_sorted
 
 
 class EventSet:

@@ -329,10 +329,16 @@ int lsh_fwd_workspace_bytes(int B, int H, int L, int D, int n_b, int n_h, int C,
   return LSH_OK;
 }
 
-int reformer_lsh_attn_fwd_ex(const void* qk, const void* v, const void* rot, int n_buckets, int n_hashes,
-                             int chunk_len, int causal, int attend, int B, int H, int L, int D, lsh_dtype dt,
-                             void* out, float* lse_out, void* ws, size_t ws_bytes, void* stream,
-                             void* const* stage_events) {
+}  // extern "C"
+
+namespace {
+
+// The fused forward; sorted_idx / undo_idx / lse_sorted (all or none) receive
+// the state that the backward pass reuses instead of workspace scratch.
+int fused_forward(const void* qk, const void* v, const void* rot, int n_buckets, int n_hashes, int chunk_len,
+                  int causal, int attend, int B, int H, int L, int D, lsh_dtype dt, void* out, float* lse_out,
+                  int32_t* sorted_out, int32_t* undo_out, float* lse_sorted_out, void* ws, size_t ws_bytes,
+                  void* stream, void* const* stage_events) {
   int st = check_problem(B, H, L, D, n_hashes);
   if (st == LSH_OK) st = check_buckets(n_buckets, L);
   if (st != LSH_OK) return st;
@@ -362,14 +368,26 @@ int reformer_lsh_attn_fwd_ex(const void* qk, const void* v, const void* rot, int
   if (overlaps(ws, ws_bytes, qk, in_bytes) || overlaps(ws, ws_bytes, v, in_bytes) ||
       overlaps(ws, ws_bytes, rot, rot_bytes))
     return LSH_ERR_ALIAS;
+  const bool save = sorted_out != nullptr;
+  if (save) {
+    const size_t slots = (size_t)BH * n_h * L;
+    const void* outs[5] = {out, lse_out, sorted_out, undo_out, lse_sorted_out};
+    const size_t out_n[5] = {in_bytes, lse_out ? lo_bytes : 0, slots * 4, slots * 4, slots * 4};
+    for (int a = 2; a < 5; ++a) {
+      for (int b = 0; b < 4; ++b)
+        if (overlaps(outs[a], out_n[a], ins[b], in_n[b])) return LSH_ERR_ALIAS;
+      for (int b = 0; b < 5; ++b)
+        if (b != a && overlaps(outs[a], out_n[a], outs[b], out_n[b])) return LSH_ERR_ALIAS;
+    }
+  }
 
   hipStream_t s = (hipStream_t)stream;
   char* base = (char*)ws;
   int32_t* buckets = (int32_t*)(base + w.buckets);
-  int32_t* sorted_idx = (int32_t*)(base + w.sorted_idx);
-  int32_t* undo_idx = (int32_t*)(base + w.undo_idx);
+  int32_t* sorted_idx = save ? sorted_out : (int32_t*)(base + w.sorted_idx);
+  int32_t* undo_idx = save ? undo_out : (int32_t*)(base + w.undo_idx);
   void* o_sorted = base + w.o_sorted;
-  float* lse_sorted = (float*)(base + w.lse_sorted);
+  float* lse_sorted = save ? lse_sorted_out : (float*)(base + w.lse_sorted);
   // Per-token attention scales are a by-product of hashing; with one bucket there is
   // no hash pass and the attention computes them itself.
   float2* token_scales = n_b > 1 ? (float2*)(base + w.token_scales) : nullptr;
@@ -391,11 +409,35 @@ int reformer_lsh_attn_fwd_ex(const void* qk, const void* v, const void* rot, int
   return hip_status(e);
 }
 
+}  // namespace
+
+extern "C" {
+
+int reformer_lsh_attn_fwd_ex(const void* qk, const void* v, const void* rot, int n_buckets, int n_hashes,
+                             int chunk_len, int causal, int attend, int B, int H, int L, int D, lsh_dtype dt,
+                             void* out, float* lse_out, void* ws, size_t ws_bytes, void* stream,
+                             void* const* stage_events) {
+  return fused_forward(qk, v, rot, n_buckets, n_hashes, chunk_len, causal, attend, B, H, L, D, dt, out, lse_out,
+                       nullptr, nullptr, nullptr, ws, ws_bytes, stream, stage_events);
+}
+
 int reformer_lsh_attn_fwd(const void* qk, const void* v, const void* rot, int n_buckets, int n_hashes, int chunk_len,
                           int causal, int B, int H, int L, int D, lsh_dtype dt, void* out, float* lse_out, void* ws,
                           size_t ws_bytes, void* stream, void* const* stage_events) {
-  return reformer_lsh_attn_fwd_ex(qk, v, rot, n_buckets, n_hashes, chunk_len, causal, 0, B, H, L, D, dt, out, lse_out,
-                                  ws, ws_bytes, stream, stage_events);
+  return fused_forward(qk, v, rot, n_buckets, n_hashes, chunk_len, causal, 0, B, H, L, D, dt, out, lse_out, nullptr,
+                       nullptr, nullptr, ws, ws_bytes, stream, stage_events);
+}
+
+int reformer_lsh_attn_fwd_train(const void* qk, const void* v, const void* rot, int n_buckets, int n_hashes,
+                                int chunk_len, int causal, int B, int H, int L, int D, lsh_dtype dt, void* out,
+                                float* lse_out, int32_t* sorted_idx, int32_t* undo_idx, float* lse_sorted, void* ws,
+                                size_t ws_bytes, void* stream, void* const* stage_events) {
+  const int st = check_problem(B, H, L, D, n_hashes);
+  if (st != LSH_OK) return st;
+  if (!is_empty(B, H, L) && (sorted_idx == nullptr || undo_idx == nullptr || lse_sorted == nullptr))
+    return LSH_ERR_NULL;
+  return fused_forward(qk, v, rot, n_buckets, n_hashes, chunk_len, causal, 0, B, H, L, D, dt, out, lse_out,
+                       sorted_idx, undo_idx, lse_sorted, ws, ws_bytes, stream, stage_events);
 }
 
 int lsh_attn_bwd_workspace_bytes(int B, int H, int L, int D, int n_h, int C, lsh_dtype dt, size_t* bytes) {
@@ -411,12 +453,17 @@ int lsh_attn_bwd_workspace_bytes(int B, int H, int L, int D, int n_h, int C, lsh
 int lsh_attn_bwd(const void* qk, const void* v, const int32_t* sorted_idx, const int32_t* undo_idx,
                  const float* lse_sorted, const void* out, const void* dout, const float* dlse, void* dqk, void* dv,
                  int B, int H, int L, int D, int n_h, int C, int causal, lsh_dtype dt, void* ws, size_t ws_bytes,
-                 void* stream) {
+                 void* stream, void* const* stage_events) {
   int st = check_problem(B, H, L, D, n_h);
   if (st != LSH_OK) return st;
   if (C != kChunk) return C <= 0 ? LSH_ERR_SHAPE : LSH_ERR_UNSUPPORTED;
   if (!dtype_ok(dt)) return LSH_ERR_UNSUPPORTED;
-  if (is_empty(B, H, L)) return LSH_OK;
+  if (is_empty(B, H, L)) {
+    if (stage_events != nullptr)
+      for (int k = 0; k < LSH_BWD_N_EVENTS; ++k)
+        if (hipEventRecord((hipEvent_t)stage_events[k], (hipStream_t)stream) != hipSuccess) return LSH_ERR_HIP;
+    return LSH_OK;
+  }
   if (qk == nullptr || v == nullptr || sorted_idx == nullptr || undo_idx == nullptr || lse_sorted == nullptr ||
       out == nullptr || dout == nullptr || dqk == nullptr || dv == nullptr)
     return LSH_ERR_NULL;
@@ -440,11 +487,20 @@ int lsh_attn_bwd(const void* qk, const void* v, const int32_t* sorted_idx, const
   float2* tok_scale = (float2*)(base + w.tok_scale);
   void* dx_slot = base + w.dx_slot;
   void* dv_slot = base + w.dv_slot;
-  hipError_t e = launch_bwd_prep(qk, out, dout, dlse, lse_sorted, undo_idx, slot_w, tok_scale, BH, L, n_h, dt, s);
+  int k = 0;
+  auto mark = [&](void) -> hipError_t {
+    return stage_events == nullptr ? hipSuccess : hipEventRecord((hipEvent_t)stage_events[k++], s);
+  };
+  hipError_t e = mark();
+  if (e == hipSuccess)
+    e = launch_bwd_prep(qk, out, dout, dlse, lse_sorted, undo_idx, slot_w, tok_scale, BH, L, n_h, dt, s);
+  if (e == hipSuccess) e = mark();
   if (e == hipSuccess)
     e = launch_attn_bwd(qk, v, dout, sorted_idx, lse_sorted, slot_w, tok_scale, dx_slot, dv_slot, BH, L, n_h, causal,
                         dt, s);
+  if (e == hipSuccess) e = mark();
   if (e == hipSuccess) e = launch_bwd_reduce(dx_slot, dv_slot, undo_idx, dqk, dv, BH, L, n_h, dt, s);
+  if (e == hipSuccess) e = mark();
   return hip_status(e);
 }
 

@@ -26,7 +26,9 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 KERNEL_SOURCES = {
     "prep": ["hash.hip"], "hash": ["hash.hip"], "fixup": ["hash.hip"],
     "sort_hist": ["sort.hip"], "sort_scatter": ["sort.hip"],
-    "chunk_attn": ["chunk_attn.hip"], "combine": ["combine.hip"],
+    "chunk_attn": ["chunk_attn.hip"], "variant_rec": ["chunk_attn.hip"], "combine": ["combine.hip"],
+    "bwd_prep": ["attn_bwd.hip", "lsh_bwd.h"], "attn_bwd": ["attn_bwd.hip", "lsh_bwd.h"],
+    "bwd_reduce": ["attn_bwd.hip", "lsh_bwd.h"],
 }
 
 
