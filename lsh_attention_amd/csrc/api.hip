@@ -95,13 +95,13 @@ FwdWs fwd_ws(int BH, int L, int n_b, int n_h, lsh_dtype dt) {
 }
 
 struct BwdWs {
-  size_t slot_w, tok_scale, dx_slot, dv_slot, total;
+  size_t tok_w, tok_scale, dx_slot, dv_slot, total;
 };
 BwdWs bwd_ws(int BH, int L, int n_h, lsh_dtype dt) {
   Carver c;
   BwdWs w;
   const size_t slots = (size_t)BH * n_h * L;
-  w.slot_w = c.take(slots * sizeof(float2));
+  w.tok_w = c.take(slots * sizeof(float2));
   w.tok_scale = c.take((size_t)BH * L * sizeof(float2));
   w.dx_slot = c.take(slots * kD * elem_size(dt));
   w.dv_slot = c.take(slots * kD * elem_size(dt));
@@ -483,7 +483,7 @@ int lsh_attn_bwd(const void* qk, const void* v, const int32_t* sorted_idx, const
     if (overlaps(ws, ws_bytes, ins[a], in_n[a])) return LSH_ERR_ALIAS;
   hipStream_t s = (hipStream_t)stream;
   char* base = (char*)ws;
-  float2* slot_w = (float2*)(base + w.slot_w);
+  float2* tok_w = (float2*)(base + w.tok_w);
   float2* tok_scale = (float2*)(base + w.tok_scale);
   void* dx_slot = base + w.dx_slot;
   void* dv_slot = base + w.dv_slot;
@@ -493,10 +493,10 @@ int lsh_attn_bwd(const void* qk, const void* v, const int32_t* sorted_idx, const
   };
   hipError_t e = mark();
   if (e == hipSuccess)
-    e = launch_bwd_prep(qk, out, dout, dlse, lse_sorted, undo_idx, slot_w, tok_scale, BH, L, n_h, dt, s);
+    e = launch_bwd_prep(qk, out, dout, dlse, lse_sorted, undo_idx, tok_w, tok_scale, BH, L, n_h, dt, s);
   if (e == hipSuccess) e = mark();
   if (e == hipSuccess)
-    e = launch_attn_bwd(qk, v, dout, sorted_idx, lse_sorted, slot_w, tok_scale, dx_slot, dv_slot, BH, L, n_h, causal,
+    e = launch_attn_bwd(qk, v, dout, sorted_idx, lse_sorted, tok_w, tok_scale, dx_slot, dv_slot, BH, L, n_h, causal,
                         dt, s);
   if (e == hipSuccess) e = mark();
   if (e == hipSuccess) e = launch_bwd_reduce(dx_slot, dv_slot, undo_idx, dqk, dv, BH, L, n_h, dt, s);

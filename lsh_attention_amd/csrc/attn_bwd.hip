@@ -21,8 +21,8 @@
 // causally dropped key has weight 0: neither passes a gradient to x.
 //
 // Kernels:
-//   bwd_prep   - per token: the combine weights w of its n_h slots (written per
-//                slot, with w c_i), and its key scales.
+//   bwd_prep   - per token: the combine weights w of its n_h rounds with w c_i
+//                (token-major, one coalesced record per token), its key scales.
 //   attn_bwd   - per block, 8 consecutive chunks as keys.  Step c takes the
 //                queries of chunk c against the keys of chunks c-1 and c (the
 //                forward's window).  A chunk's keys are attended by the
@@ -57,8 +57,14 @@ constexpr int kBwdChunksPerBlock = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSelf2 = -1.0e5f * kLog2e;
 // A row whose lse is below this (natural log) has only its self key left: every
-// real logit is at least -|x_i| / 8, far above the -1e5 of the self key.
-constexpr float kSelfOnly2 = (-1.0e5f + 0.5f) * kLog2e;
+// real logit is at least -|x_i| / 8, far above the -1e5 of the self key.  The
+// self key occurs once or twice in a window (its own chunk, and the look-back
+// chunk when that belongs to the previous round), so a self-only row has lse
+// -1e5 or -1e5 + ln 2 and each self copy the weight 1 or 1/2, told apart by
+// the second threshold (both far from fp32 rounding at 1e5).
+constexpr float kSelfOnlyLse = -1.0e5f + 1.0f;
+constexpr float kSelfOnly2 = kSelfOnlyLse * kLog2e;
+constexpr float kSelfTwice2 = (-1.0e5f + 0.35f) * kLog2e;
 
 template <bool BF16>
 struct BwdTraits;
@@ -106,7 +112,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
                                                        const float* __restrict__ dlse,
                                                        const float* __restrict__ lse_sorted,
                                                        const int32_t* __restrict__ undo_idx,
-                                                       float2* __restrict__ slot_w, float2* __restrict__ tok_scale,
+                                                       float2* __restrict__ tok_w, float2* __restrict__ tok_scale,
                                                        int L, int n_h, size_t n_tokens) {
   const size_t t = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
@@ -156,7 +162,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
   const float c = (dlse == nullptr ? 0.f : dlse[t]) - dd;
   if (sub < n_h) {
     const float w = e * __builtin_amdgcn_rcpf(z);
-    slot_w[bh * n_slots + g] = make_float2(w, w * c);
+    tok_w[t * n_h + sub] = make_float2(w, w * c);
   }
   if (sub == 0) {
     const float kn = 0.125f * __builtin_amdgcn_rcpf(fmaxf(__builtin_amdgcn_sqrtf(ss), 1e-12f));
@@ -171,9 +177,9 @@ template <bool BF16, bool CAUSAL>
 __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
     const typename BwdTraits<BF16>::T* __restrict__ qk, const typename BwdTraits<BF16>::T* __restrict__ v,
     const typename BwdTraits<BF16>::T* __restrict__ dout, const int32_t* __restrict__ sorted_idx,
-    const float* __restrict__ lse_sorted, const float2* __restrict__ slot_w, const float2* __restrict__ tok_scale,
+    const float* __restrict__ lse_sorted, const float2* __restrict__ tok_w, const float2* __restrict__ tok_scale,
     typename BwdTraits<BF16>::T* __restrict__ dx_slot, typename BwdTraits<BF16>::T* __restrict__ dv_slot, int L,
-    int n_slots, int n_chunks, int blocks_per_bh) {
+    int n_h, int n_slots, int n_chunks, int blocks_per_bh) {
   using T = typename BwdTraits<BF16>::T;
   constexpr int kXRow = BwdTraits<BF16>::kXRow;
   constexpr int kTRow = BwdTraits<BF16>::kTRow;
@@ -194,6 +200,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
   __shared__ __attribute__((aligned(16))) float sKs2[2][64], sKn[2][64];   // key scales per slot
   __shared__ __attribute__((aligned(16))) float sLse2[64], sW[64], sWc[64];  // current queries
   __shared__ __attribute__((aligned(16))) int sPos[kCPB + 2][64];
+  __shared__ int sSelfOnly;  // the current chunk has a self-only query row
   T* const sDO = sDoBuf;                      // [query][dim]
   T* const sDOT = sDoBuf + 64 * kXRow;        // [dim][permcol(query)] (bf16)
   uint16_t* const sDS16 = (uint16_t*)sDoBuf;  // [query][64 slot + permcol(key)] (bf16)
@@ -213,7 +220,8 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
   const char* dq_in = (const char*)(dout + (size_t)bh * L * kD);
   const int32_t* sidx = sorted_idx + (size_t)bh * n_slots;
   const float* lseb = lse_sorted + (size_t)bh * n_slots;
-  const float2* swb = slot_w + (size_t)bh * n_slots;
+  const float2* twb = tok_w + (size_t)bh * L * n_h;
+  const int cpr = L / kChunk;  // chunks per round
   const float2* tsb = tok_scale + (size_t)bh * L;
   T* dxb = dx_slot + (size_t)bh * n_slots * kD;
   T* dvb = dv_slot + (size_t)bh * n_slots * kD;
@@ -259,7 +267,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
     if (tid < 64) {
       ksc = tsb[pos[tid]];
       qlse = lseb[(size_t)chunk * kChunk + tid];
-      qsw = swb[(size_t)chunk * kChunk + tid];
+      qsw = twb[(size_t)pos[tid] * n_h + chunk / cpr];
     }
   };
   auto commit_t = [&](T* dst, int rowlen, int base, const uint32_t (&w)[BF16 ? 4 : 1]) {
@@ -292,6 +300,8 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
         sLse2[tid] = qlse * kLog2e;
         sW[tid] = qsw.x;
         sWc[tid] = qsw.y;
+        const uint64_t so = __ballot(qlse < kSelfOnlyLse);  // wave 0: the chunk's 64 queries
+        if (tid == 0) sSelfOnly = so != 0ull ? 1 : 0;
       }
     }
   };
@@ -318,7 +328,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
   for (int c = c0; c <= c1; ++c) {
     const int cur = c & 1, prv = cur ^ 1;
     const int ec = c - c0 + 1;  // sPos entry of step c
-    if (c < c1) gather(ec + 1);
+    if (c < c1) gather(ec + 1);  // next step's rows, in flight during this step
     const bool mine_cur = (sw == cur);
     const int ek = mine_cur ? ec : ec - 1;  // sPos entry of the owned keys
     const bool do_kv = mine_cur ? (c < c1) : (c > c0);
@@ -328,10 +338,17 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
     uint32_t dsk16[8];  // dS kn of the owned key for the 16 queries of this lane (bf16 pairs)
     float dskf[16];
 
-    if (active) {
+    // Straight-line per chunk (no branch between query tiles, so the compiler can
+    // overlap one tile's MFMAs with another's vector work); the look-back keys of
+    // the run's first step are computed (their dS feeds dq) and then discarded.
+    auto compute = [&](auto exact_tag) {
+      constexpr bool EXACT = decltype(exact_tag)::value;
       const int kpos = sPos[ek][kr];
       const float ks2 = sKs2[sw][kr], kn = sKn[sw][kr];
       // Pw = w P (for dv) and dS (for x) from one query tile's S = Q K^T and dP = dO V^T
+      // In a row with any real key the self key's weight exp(-1e5 - lse) is exactly 0,
+      // so the self and causal masks are one compare that zeroes P.  Chunks with a
+      // self-only row (lse near -1e5, flagged at commit) take the explicit path.
       auto elementwise = [&](int qt, const f32x4& S, const f32x4& dP, float (&pw)[4], float (&dsv)[4]) {
         const int q0 = 16 * qt + 4 * grp;
         const float4 l4 = *(const float4*)(&sLse2[q0]);
@@ -341,16 +358,26 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, wv[4] = {w4.x, w4.y, w4.z, w4.w};
         const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
         const int qp[4] = {p4.x, p4.y, p4.z, p4.w};
+        if constexpr (!EXACT) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool self = kpos == qp[e];
-          const bool drop = CAUSAL && kpos > qp[e];
-          float p = __builtin_amdgcn_exp2f((self ? kSelf2 : S[e] * ks2) - lv[e]);
-          if (lv[e] < kSelfOnly2) p = self ? 1.f : 0.f;
-          p = drop ? 0.f : p;
-          pw[e] = wv[e] * p;
-          const float dl = p * fmaf(wv[e], dP[e], cv[e]);
-          dsv[e] = self ? 0.f : dl;
+          for (int e = 0; e < 4; ++e) {
+            const bool drop = CAUSAL ? (kpos >= qp[e]) : (kpos == qp[e]);
+            const float p = drop ? 0.f : __builtin_amdgcn_exp2f(fmaf(S[e], ks2, -lv[e]));
+            pw[e] = wv[e] * p;
+            dsv[e] = p * fmaf(wv[e], dP[e], cv[e]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool self = kpos == qp[e];
+            const bool drop = CAUSAL && kpos > qp[e];
+            float p = __builtin_amdgcn_exp2f((self ? kSelf2 : S[e] * ks2) - lv[e]);
+            if (lv[e] < kSelfOnly2) p = self ? (lv[e] > kSelfTwice2 ? 0.5f : 1.f) : 0.f;
+            p = drop ? 0.f : p;
+            pw[e] = wv[e] * p;
+            const float dl = p * fmaf(wv[e], dP[e], cv[e]);
+            dsv[e] = self ? 0.f : dl;
+          }
         }
       };
       if constexpr (BF16) {
@@ -358,42 +385,41 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
         const bf16x8 k1 = *(const bf16x8*)(&sX[sw][kr * kXRow + 32 + 8 * grp]);
         const bf16x8 v0 = *(const bf16x8*)(&sV[sw][kr * kXRow + 8 * grp]);
         const bf16x8 v1 = *(const bf16x8*)(&sV[sw][kr * kXRow + 32 + 8 * grp]);
-        bf16x4 bp4[4], bs4[4];
 #pragma unroll
-        for (int qt = 0; qt < 4; ++qt) {
-          const int qr = 16 * qt + col;
-          const bf16x8 q0 = *(const bf16x8*)(&sX[cur][qr * kXRow + 8 * grp]);
-          const bf16x8 q1 = *(const bf16x8*)(&sX[cur][qr * kXRow + 32 + 8 * grp]);
-          const bf16x8 d0 = *(const bf16x8*)(&sDO[qr * kXRow + 8 * grp]);
-          const bf16x8 d1 = *(const bf16x8*)(&sDO[qr * kXRow + 32 + 8 * grp]);
-          f32x4 z = {0.f, 0.f, 0.f, 0.f};
-          z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q0, k0, z, 0, 0, 0);
-          const f32x4 S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q1, k1, z, 0, 0, 0);
-          f32x4 y = {0.f, 0.f, 0.f, 0.f};
-          y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(d0, v0, y, 0, 0, 0);
-          const f32x4 dP = __builtin_amdgcn_mfma_f32_16x16x32_bf16(d1, v1, y, 0, 0, 0);
-          float pw[4], dsv[4];
-          elementwise(qt, S, dP, pw, dsv);
-          bp4[qt] = __builtin_convertvector((f32x4{pw[0], pw[1], pw[2], pw[3]}), bf16x4);
-          bs4[qt] = __builtin_convertvector((f32x4{dsv[0], dsv[1], dsv[2], dsv[3]}), bf16x4);
-          const uint2 u = __builtin_bit_cast(
-              uint2, __builtin_convertvector((f32x4{dsv[0] * kn, dsv[1] * kn, dsv[2] * kn, dsv[3] * kn}), bf16x4));
-          dsk16[2 * qt] = u.x;
-          dsk16[2 * qt + 1] = u.y;
-        }
-        // ---- dV^T += dO^T Pw, A^T += Xq^T dS (K = the 64 queries, permuted) ----
-        if (do_kv) {
+        for (int ks = 0; ks < 2; ++ks) {
+          bf16x4 bp4[2], bs4[2];
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 bp = __builtin_shufflevector(bp4[2 * ks], bp4[2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-            const bf16x8 bs = __builtin_shufflevector(bs4[2 * ks], bs4[2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+          for (int h = 0; h < 2; ++h) {
+            const int qt = 2 * ks + h;
+            const int qr = 16 * qt + col;
+            const bf16x8 q0 = *(const bf16x8*)(&sX[cur][qr * kXRow + 8 * grp]);
+            const bf16x8 q1 = *(const bf16x8*)(&sX[cur][qr * kXRow + 32 + 8 * grp]);
+            const bf16x8 d0 = *(const bf16x8*)(&sDO[qr * kXRow + 8 * grp]);
+            const bf16x8 d1 = *(const bf16x8*)(&sDO[qr * kXRow + 32 + 8 * grp]);
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q0, k0, z, 0, 0, 0);
+            const f32x4 S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q1, k1, z, 0, 0, 0);
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+            y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(d0, v0, y, 0, 0, 0);
+            const f32x4 dP = __builtin_amdgcn_mfma_f32_16x16x32_bf16(d1, v1, y, 0, 0, 0);
+            float pw[4], dsv[4];
+            elementwise(qt, S, dP, pw, dsv);
+            bp4[h] = __builtin_convertvector((f32x4{pw[0], pw[1], pw[2], pw[3]}), bf16x4);
+            bs4[h] = __builtin_convertvector((f32x4{dsv[0], dsv[1], dsv[2], dsv[3]}), bf16x4);
+            const uint2 u = __builtin_bit_cast(
+                uint2, __builtin_convertvector((f32x4{dsv[0] * kn, dsv[1] * kn, dsv[2] * kn, dsv[3] * kn}), bf16x4));
+            dsk16[2 * qt] = u.x;
+            dsk16[2 * qt + 1] = u.y;
+          }
+          // ---- dV^T += dO^T Pw, A^T += Xq^T dS (K = queries 32 ks .. 32 ks + 31, permuted) ----
+          const bf16x8 bp = __builtin_shufflevector(bp4[0], bp4[1], 0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16x8 bs = __builtin_shufflevector(bs4[0], bs4[1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-              const bf16x8 ad = *(const bf16x8*)(&sDOT[(16 * dt + col) * kQRow + 32 * ks + 8 * grp]);
-              const bf16x8 ax = *(const bf16x8*)(&sXT[(16 * dt + col) * kTRow + 64 * cur + 32 * ks + 8 * grp]);
-              acc_v[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad, bp, acc_v[dt], 0, 0, 0);
-              acc_a[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bs, acc_a[dt], 0, 0, 0);
-            }
+          for (int dt = 0; dt < 4; ++dt) {
+            const bf16x8 ad = *(const bf16x8*)(&sDOT[(16 * dt + col) * kQRow + 32 * ks + 8 * grp]);
+            const bf16x8 ax = *(const bf16x8*)(&sXT[(16 * dt + col) * kTRow + 64 * cur + 32 * ks + 8 * grp]);
+            acc_v[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad, bp, acc_v[dt], 0, 0, 0);
+            acc_a[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bs, acc_a[dt], 0, 0, 0);
           }
         }
       } else {
@@ -426,23 +452,26 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) dskf[4 * qt + e] = dsv[qt][e] * kn;
         }
-        if (do_kv) {
-          // K index grp <-> query 16 qt + 4 grp + e, one MFMA per (qt, e)
+        // K index grp <-> query 16 qt + 4 grp + e, one MFMA per (qt, e)
 #pragma unroll
-          for (int qt = 0; qt < 4; ++qt)
+        for (int qt = 0; qt < 4; ++qt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int qr = 16 * qt + 4 * grp + e;
+          for (int e = 0; e < 4; ++e) {
+            const int qr = 16 * qt + 4 * grp + e;
 #pragma unroll
-              for (int dt = 0; dt < 4; ++dt) {
-                const float ad = sDO[qr * kXRow + 16 * dt + col];
-                const float ax = sX[cur][qr * kXRow + 16 * dt + col];
-                acc_v[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ad, pw[qt][e], acc_v[dt], 0, 0, 0);
-                acc_a[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ax, dsv[qt][e], acc_a[dt], 0, 0, 0);
-              }
+            for (int dt = 0; dt < 4; ++dt) {
+              const float ad = sDO[qr * kXRow + 16 * dt + col];
+              const float ax = sX[cur][qr * kXRow + 16 * dt + col];
+              acc_v[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ad, pw[qt][e], acc_v[dt], 0, 0, 0);
+              acc_a[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ax, dsv[qt][e], acc_a[dt], 0, 0, 0);
             }
-        }
+          }
       }
+    };
+    if (active) {
+      if (sSelfOnly != 0) compute(std::true_type{});
+      else compute(std::false_type{});
+      if (!do_kv) zero_acc();  // look-back keys of the first step: not this run's
     }
 
     // ---- dQ^T = Xk^T (dS kn)^T for the current chunk's queries ----
@@ -632,21 +661,21 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const void* __restrict_
 }  // namespace
 
 hipError_t launch_bwd_prep(const void* qk, const void* out, const void* dout, const float* dlse,
-                           const float* lse_sorted, const int32_t* undo_idx, float2* slot_w, float2* tok_scale,
+                           const float* lse_sorted, const int32_t* undo_idx, float2* tok_w, float2* tok_scale,
                            int BH, int L, int n_h, lsh_dtype dt, hipStream_t s) {
   const size_t n_tok = (size_t)BH * L;
   const unsigned grid = (unsigned)((n_tok + 15) / 16);
   if (dt == LSH_BF16)
-    bwd_prep_kernel<true><<<grid, 256, 0, s>>>(qk, out, dout, dlse, lse_sorted, undo_idx, slot_w, tok_scale, L, n_h,
+    bwd_prep_kernel<true><<<grid, 256, 0, s>>>(qk, out, dout, dlse, lse_sorted, undo_idx, tok_w, tok_scale, L, n_h,
                                                n_tok);
   else
-    bwd_prep_kernel<false><<<grid, 256, 0, s>>>(qk, out, dout, dlse, lse_sorted, undo_idx, slot_w, tok_scale, L,
+    bwd_prep_kernel<false><<<grid, 256, 0, s>>>(qk, out, dout, dlse, lse_sorted, undo_idx, tok_w, tok_scale, L,
                                                 n_h, n_tok);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_bwd(const void* qk, const void* v, const void* dout, const int32_t* sorted_idx,
-                           const float* lse_sorted, const float2* slot_w, const float2* tok_scale, void* dx_slot,
+                           const float* lse_sorted, const float2* tok_w, const float2* tok_scale, void* dx_slot,
                            void* dv_slot, int BH, int L, int n_h, int causal, lsh_dtype dt, hipStream_t s) {
   const int n_slots = n_h * L;
   const int n_chunks = n_slots / kChunk;
@@ -655,8 +684,8 @@ hipError_t launch_attn_bwd(const void* qk, const void* v, const void* dout, cons
 #define LSH_BWD_LAUNCH(B16, CA)                                                                               \
   attn_bwd_kernel<B16, CA><<<grid, 512, 0, s>>>(                                                              \
       (const typename BwdTraits<B16>::T*)qk, (const typename BwdTraits<B16>::T*)v,                           \
-      (const typename BwdTraits<B16>::T*)dout, sorted_idx, lse_sorted, slot_w, tok_scale,                    \
-      (typename BwdTraits<B16>::T*)dx_slot, (typename BwdTraits<B16>::T*)dv_slot, L, n_slots, n_chunks,      \
+      (const typename BwdTraits<B16>::T*)dout, sorted_idx, lse_sorted, tok_w, tok_scale,                     \
+      (typename BwdTraits<B16>::T*)dx_slot, (typename BwdTraits<B16>::T*)dv_slot, L, n_h, n_slots, n_chunks, \
       blocks_per_bh)
   if (dt == LSH_BF16) {
     if (causal) LSH_BWD_LAUNCH(true, true);
