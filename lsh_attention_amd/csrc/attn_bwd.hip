@@ -553,26 +553,58 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
       // khat = 8 kn x, so khat (khat . a) = 64 kn^2 x (x . a)
       const float proj = tiny ? 0.f : 64.f * kn * kn * dot;
       const size_t row = (size_t)chunk * kChunk + kr;
+      if constexpr (BF16) {
+        // bf16 pairs: rx[dt][h] / rv[dt][h] hold dims 16 dt + 4 grp + 2h, +1
+        uint32_t rx[4][2], rv[4][2];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        float ox[4], ov[4];
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ox[e] = acc_q[dt][e] + kn * (acc_a[dt][e] - proj * xv[dt][e]);
-          ov[e] = acc_v[dt][e];
-        }
-        T* px = dxb + row * kD + 16 * dt + 4 * grp;
-        T* pv = dvb + row * kD + 16 * dt + 4 * grp;
-        if constexpr (BF16) {
-          const bf16x2 x0 = __builtin_convertvector(f32x2{ox[0], ox[1]}, bf16x2);
-          const bf16x2 x1 = __builtin_convertvector(f32x2{ox[2], ox[3]}, bf16x2);
-          const bf16x2 v0 = __builtin_convertvector(f32x2{ov[0], ov[1]}, bf16x2);
-          const bf16x2 v1 = __builtin_convertvector(f32x2{ov[2], ov[3]}, bf16x2);
-          *(uint2*)px = make_uint2(__builtin_bit_cast(uint32_t, x0), __builtin_bit_cast(uint32_t, x1));
-          *(uint2*)pv = make_uint2(__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1));
-        } else {
-          *(float4*)px = make_float4(ox[0], ox[1], ox[2], ox[3]);
-          *(float4*)pv = make_float4(ov[0], ov[1], ov[2], ov[3]);
+          for (int h = 0; h < 2; ++h) {
+            const float x0 = acc_q[dt][2 * h] + kn * (acc_a[dt][2 * h] - proj * xv[dt][2 * h]);
+            const float x1 = acc_q[dt][2 * h + 1] + kn * (acc_a[dt][2 * h + 1] - proj * xv[dt][2 * h + 1]);
+            rx[dt][h] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+            rv[dt][h] = __builtin_bit_cast(
+                uint32_t, __builtin_convertvector(f32x2{acc_v[dt][2 * h], acc_v[dt][2 * h + 1]}, bf16x2));
+          }
+        // 4 x 4 transpose over the lanes holding this key (lane groups g) and dt:
+        // afterwards lane group g holds, in slot j, dims 16 g + 4 j .. +3, so it
+        // stores 32 contiguous bytes and one instruction writes whole rows.
+        auto transpose = [](uint32_t (&r)[4][2]) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {  // lane groups 2,3 of r[d] <-> lane groups 0,1 of r[d + 2]
+              const auto t = __builtin_amdgcn_permlane32_swap(r[d][h], r[d + 2][h], false, false);
+              r[d][h] = t[0];
+              r[d + 2][h] = t[1];
+            }
+#pragma unroll
+            for (int d = 0; d < 4; d += 2) {  // odd lane groups of r[d] <-> even lane groups of r[d + 1]
+              const auto t = __builtin_amdgcn_permlane16_swap(r[d][h], r[d + 1][h], false, false);
+              r[d][h] = t[0];
+              r[d + 1][h] = t[1];
+            }
+          }
+        };
+        transpose(rx);
+        transpose(rv);
+        T* px = dxb + row * kD + 16 * grp;
+        T* pv = dvb + row * kD + 16 * grp;
+        *(uint4*)px = make_uint4(rx[0][0], rx[0][1], rx[1][0], rx[1][1]);
+        *(uint4*)(px + 8) = make_uint4(rx[2][0], rx[2][1], rx[3][0], rx[3][1]);
+        *(uint4*)pv = make_uint4(rv[0][0], rv[0][1], rv[1][0], rv[1][1]);
+        *(uint4*)(pv + 8) = make_uint4(rv[2][0], rv[2][1], rv[3][0], rv[3][1]);
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          float ox[4], ov[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ox[e] = acc_q[dt][e] + kn * (acc_a[dt][e] - proj * xv[dt][e]);
+            ov[e] = acc_v[dt][e];
+          }
+          *(float4*)(dxb + row * kD + 16 * dt + 4 * grp) = make_float4(ox[0], ox[1], ox[2], ox[3]);
+          *(float4*)(dvb + row * kD + 16 * dt + 4 * grp) = make_float4(ov[0], ov[1], ov[2], ov[3]);
         }
       }
       zero_acc();
