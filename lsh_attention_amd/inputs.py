@@ -199,3 +199,56 @@ def make_inputs(name: str, n_hashes: int | None = None, B: int | None = None,
     meta = {"seed_base": s, "qk_sha256": qk.sha256(), "v_sha256": v.sha256(),
             "rot_sha256": None if rot is None else rot.sha256()}
     return Inputs(w, n_h, qk, v, rot, meta)
+
+
+# ---- one reversible block (attention sublayer + feed-forward sublayer) ----
+@dataclass
+class BlockInputs:
+    """Seeded synthetic inputs of one reversible block: the two input streams
+    x1, x2 [B, L, dim], the rotations of the attention, and the parameters.
+    Weights are stored [out, in] (a Linear layer's layout); `params_math`
+    gives them [in, out] for x @ W.  Random weights scaled by 1/sqrt(in) keep
+    the activations of order one; there are no trained weights."""
+    workload: Workload
+    n_hashes: int
+    x1: Tensor
+    x2: Tensor
+    rot: Tensor | None
+    params: dict  # name -> Tensor
+
+    def params_math(self) -> dict:
+        out = {}
+        for k, t in self.params.items():
+            a = t.values.astype(np.float64)
+            out[k] = a.T if a.ndim == 2 else a
+        return out
+
+
+def make_block_inputs(name: str, n_hashes: int | None = None, B: int | None = None, L: int | None = None,
+                      heads: int | None = None) -> BlockInputs:
+    w = WORKLOADS[name]
+    n_h = w.n_hashes[-1] if n_hashes is None else n_hashes
+    B = w.B if B is None else B
+    L = w.L if L is None else L
+    H = w.H if heads is None else heads
+    dim = H * w.D
+    s = 1000 * w.index + 500
+    x1 = gaussian(s + 0, (B, L, dim), w.dtype)
+    x2 = gaussian(s + 1, (B, L, dim), w.dtype)
+    rot = rotations(1000 * w.index + 2, n_h, w.D, w.n_buckets, w.dtype)
+
+    def lin(seed, n_out, n_in):
+        g = gaussian(seed, (n_out, n_in), "f32").values / np.sqrt(n_in)
+        return _store(g, w.dtype)
+
+    def vec(seed, n, mean, scale):
+        return _store(mean + scale * gaussian(seed, (n,), "f32").values, w.dtype)
+
+    p = {
+        "ln1_g": vec(s + 10, dim, 1.0, 0.1), "ln1_b": vec(s + 11, dim, 0.0, 0.1),
+        "w_qk": lin(s + 12, dim, dim), "w_v": lin(s + 13, dim, dim), "w_o": lin(s + 14, dim, dim),
+        "ln2_g": vec(s + 15, dim, 1.0, 0.1), "ln2_b": vec(s + 16, dim, 0.0, 0.1),
+        "w1": lin(s + 17, 4 * dim, dim), "b1": vec(s + 18, 4 * dim, 0.0, 0.1),
+        "w2": lin(s + 19, dim, 4 * dim), "b2": vec(s + 20, dim, 0.0, 0.1),
+    }
+    return BlockInputs(w, n_h, x1, x2, rot, p)
