@@ -218,6 +218,76 @@ int reformer_lsh_attn_fwd_train(const void* qk, const void* v, const void* rot, 
                                 void* ws, size_t ws_bytes, void* stream,
                                 void* const* stage_events);
 
+/* Building blocks of the reversible block below, exposed for staged use.
+ * lsh_layer_norm: y = (x - mean) / sqrt(var + 1e-5) * gamma + beta over each
+ * row of `dim` features (bf16 in and out, fp32 arithmetic; dim % 8 == 0,
+ * dim <= 1024).
+ * lsh_linear: c = epilogue(a . w^T), w [N, K] row-major (a Linear layer's
+ * [out, in]), bf16 in and out, fp32 accumulation; N % 128 == 0, K % 64 == 0.
+ * Layouts: LSH_LAYOUT_ROWS is [M, K] / [M, N] row-major; LSH_LAYOUT_HEADS is
+ * the attention's [B, H, L, 64] with M = B L and K (for a) or N (for c) =
+ * 64 heads (not both).  Epilogue: 0, BIAS|GELU (+ bias[n], then GELU, the erf
+ * form), RESID (+ resid[m][n], rows layout; c must use rows), BIAS|RESID. */
+#define LSH_LAYOUT_ROWS 0
+#define LSH_LAYOUT_HEADS 1
+#define LSH_EPI_BIAS 1
+#define LSH_EPI_GELU 2
+#define LSH_EPI_RESID 4
+int lsh_layer_norm(const void* x, const void* gamma, const void* beta, void* y, int rows, int dim,
+                   lsh_dtype dt, void* stream);
+int lsh_linear(const void* a, int a_layout, const void* w, const void* bias, const void* resid,
+               void* c, int c_layout, int M, int N, int K, int L, int heads, int epilogue,
+               lsh_dtype dt, void* stream);
+
+/* One reversible Reformer block around the LSH attention (Reformer abstract:
+ * reversible residual layers; Reformer explainer: reversible layers and a
+ * chunked feed-forward, with LSH attention, fit about 64K tokens on one
+ * accelerator):
+ *   y1 = x1 + F(x2),  F(x) = W_o . LSHAttn(LN1(x) W_qk^T, LN1(x) W_v^T)
+ *   y2 = x2 + G(y1),  G(y) = W2 . GELU(W1 . LN2(y) + b1) + b2
+ * with LayerNorm LN(x) = (x - mean) / sqrt(var + 1e-5) * g + b over the
+ * features, the attention of reformer_lsh_attn_fwd on each of `heads` heads
+ * (head h takes features 64h .. 64h+63; the rotations rot are shared by all
+ * heads), GELU the erf form, and G taken over chunks of chunk_rows rows (0 =
+ * all rows at once): the hidden activation needs chunk_rows * 4 dim elements.
+ *   x1, x2, y1, y2  [B, L, dim] bf16, dim = 64 heads (heads even, <= 16).
+ *   params          LSH_BLOCK_N_PARAMS device pointers, bf16, in the order
+ *                   below; weights [out, in] row-major (a Linear layer's
+ *                   layout).
+ *   ws              workspace of at least reformer_block_workspace_bytes.
+ *   stage_events    NULL, or LSH_BLOCK_N_EVENTS events recorded between the
+ *                   LSH_BLOCK_STAGE_* stages.
+ * Only bf16 is supported (LSH_ERR_UNSUPPORTED otherwise).  The inverse of the
+ * block (x2 = y2 - G(y1), x1 = y1 - F(x2)) needs no extra kernel: it is two
+ * sublayer evaluations with the residual subtracted, which callers recompute
+ * in a reversible backward pass. */
+#define LSH_BLOCK_LN1_G 0  /* [dim] */
+#define LSH_BLOCK_LN1_B 1  /* [dim] */
+#define LSH_BLOCK_W_QK 2   /* [dim, dim] shared query/key projection */
+#define LSH_BLOCK_W_V 3    /* [dim, dim] */
+#define LSH_BLOCK_W_O 4    /* [dim, dim] */
+#define LSH_BLOCK_LN2_G 5  /* [dim] */
+#define LSH_BLOCK_LN2_B 6  /* [dim] */
+#define LSH_BLOCK_W1 7     /* [4 dim, dim] */
+#define LSH_BLOCK_B1 8     /* [4 dim] */
+#define LSH_BLOCK_W2 9     /* [dim, 4 dim] */
+#define LSH_BLOCK_B2 10    /* [dim] */
+#define LSH_BLOCK_N_PARAMS 11
+#define LSH_BLOCK_STAGE_LN1 0
+#define LSH_BLOCK_STAGE_QKV 1   /* shared-QK and V projections (head-major output) */
+#define LSH_BLOCK_STAGE_ATTN 2  /* the LSH attention forward pass */
+#define LSH_BLOCK_STAGE_OUT 3   /* output projection + residual (head-major input) */
+#define LSH_BLOCK_STAGE_LN2 4
+#define LSH_BLOCK_STAGE_FFN 5   /* both feed-forward GEMMs over all row chunks */
+#define LSH_BLOCK_N_STAGES 6
+#define LSH_BLOCK_N_EVENTS (LSH_BLOCK_N_STAGES + 1)
+int reformer_block_workspace_bytes(int B, int L, int heads, int n_buckets, int n_hashes,
+                                   int chunk_len, int chunk_rows, lsh_dtype dt, size_t* bytes);
+int reformer_block_fwd(const void* x1, const void* x2, const void* rot, const void* const* params,
+                       int B, int L, int heads, int n_buckets, int n_hashes, int chunk_len,
+                       int causal, int chunk_rows, lsh_dtype dt, void* y1, void* y2, void* ws,
+                       size_t ws_bytes, void* stream, void* const* stage_events);
+
 /* Timing helpers for callers that have no HIP runtime binding of their own:
  * create/destroy a hipEvent_t (returned as void*), and the elapsed time in
  * milliseconds between two recorded events (synchronises on `end`). */

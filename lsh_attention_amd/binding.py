@@ -44,6 +44,10 @@ _SIGS = {
     "lsh_attn_bwd_workspace_bytes": (_c_int, [_c_int] * 7 + [ctypes.POINTER(_c_size)]),
     "lsh_attn_bwd": (_c_int, [_vp] * 10 + [_c_int] * 8 + [_vp, _c_size, _vp, _vp]),
     "reformer_lsh_attn_fwd_train": (_c_int, [_vp] * 3 + [_c_int] * 9 + [_vp] * 6 + [_c_size, _vp, _vp]),
+    "lsh_layer_norm": (_c_int, [_vp] * 4 + [_c_int] * 3 + [_vp]),
+    "lsh_linear": (_c_int, [_vp, _c_int, _vp, _vp, _vp, _vp] + [_c_int] * 8 + [_vp]),
+    "reformer_block_workspace_bytes": (_c_int, [_c_int] * 8 + [ctypes.POINTER(_c_size)]),
+    "reformer_block_fwd": (_c_int, [_vp] * 4 + [_c_int] * 9 + [_vp, _vp, _vp, _c_size, _vp, _vp]),
     "lsh_event_create": (_c_int, [ctypes.POINTER(_vp)]),
     "lsh_event_destroy": (_c_int, [_vp]),
     "lsh_event_record": (_c_int, [_vp, _vp]),
@@ -329,6 +333,87 @@ def reformer_lsh_attn_fwd_train(qk: torch.Tensor, v: torch.Tensor, rot: torch.Te
         out.data_ptr(), lse.data_ptr(), sorted_idx.data_ptr(), undo_idx.data_ptr(), lse_sorted.data_ptr(),
         workspace.data_ptr(), workspace.numel(), _stream(dev), ev))
     return out, lse, sorted_idx, undo_idx, lse_sorted
+
+
+LAYOUT_ROWS, LAYOUT_HEADS = 0, 1
+EPI_BIAS, EPI_GELU, EPI_RESID = 1, 2, 4
+BLOCK_PARAMS = ["ln1_g", "ln1_b", "w_qk", "w_v", "w_o", "ln2_g", "ln2_b", "w1", "b1", "w2", "b2"]
+BLOCK_N_STAGES = 6
+BLOCK_N_EVENTS = BLOCK_N_STAGES + 1
+BLOCK_STAGE_NAMES = ["ln1", "qkv_proj", "attention", "out_proj", "ln2", "ffn"]
+
+
+def lsh_layer_norm(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor, out: torch.Tensor | None = None):
+    """LayerNorm over the last dimension (bf16)."""
+    _dev(x, gamma, beta, out)
+    dim = x.shape[-1]
+    rows = x.numel() // dim
+    out = torch.empty_like(x) if out is None else out
+    _check("lsh_layer_norm", lib().lsh_layer_norm(x.data_ptr(), gamma.data_ptr(), beta.data_ptr(), out.data_ptr(),
+                                                  rows, dim, _dtype_code(x), _stream(x.device)))
+    return out
+
+
+def lsh_linear(a: torch.Tensor, w: torch.Tensor, bias=None, resid=None, gelu: bool = False, a_heads: bool = False,
+               out=None):
+    """epilogue(a . w^T) with w [N, K] (bf16), as rows [..., N].  a is rows [..., K],
+    or head-major [B, H, L, 64] (a_heads; the result is then [B, L, N])."""
+    _dev(a, w, bias, resid, out)
+    N, K = w.shape
+    if a_heads:
+        B, H, L, _ = a.shape
+        M, shape, Ld, Hd = B * L, (B, L, N), L, H
+    else:
+        M, shape, Ld, Hd = a.numel() // K, tuple(a.shape[:-1]) + (N,), 1, 1
+    epi = (EPI_BIAS if bias is not None else 0) | (EPI_GELU if gelu else 0) | (EPI_RESID if resid is not None else 0)
+    out = torch.empty(shape, dtype=a.dtype, device=a.device) if out is None else out
+    _check("lsh_linear", lib().lsh_linear(a.data_ptr(), LAYOUT_HEADS if a_heads else LAYOUT_ROWS, w.data_ptr(),
+                                          _ptr(bias), _ptr(resid), out.data_ptr(), LAYOUT_ROWS, M, N, K, Ld, Hd, epi,
+                                          _dtype_code(a), _stream(a.device)))
+    return out
+
+
+def lsh_linear_heads(a: torch.Tensor, w: torch.Tensor, out=None):
+    """a [B, L, K] rows . w^T -> [B, H, L, 64] head-major, H = N / 64 (no epilogue)."""
+    _dev(a, w, out)
+    N, K = w.shape
+    B, L, _ = a.shape
+    H = N // 64
+    out = torch.empty((B, H, L, 64), dtype=a.dtype, device=a.device) if out is None else out
+    _check("lsh_linear", lib().lsh_linear(a.data_ptr(), LAYOUT_ROWS, w.data_ptr(), None, None, out.data_ptr(),
+                                          LAYOUT_HEADS, B * L, N, K, L, H, 0, _dtype_code(a), _stream(a.device)))
+    return out
+
+
+def block_workspace_bytes(B, L, heads, n_buckets, n_hashes, chunk_len=64, chunk_rows=0, dt=LSH_BF16) -> int:
+    n = ctypes.c_size_t()
+    _check("reformer_block_workspace_bytes", lib().reformer_block_workspace_bytes(
+        B, L, heads, n_buckets, n_hashes, chunk_len, chunk_rows, dt, ctypes.byref(n)))
+    return n.value
+
+
+def reformer_block_fwd(x1: torch.Tensor, x2: torch.Tensor, rot, params: dict, n_buckets: int, n_hashes: int,
+                       causal: bool = False, chunk_rows: int = 0, chunk_len: int = 64, y1=None, y2=None,
+                       workspace=None, stage_events=None):
+    """One reversible block: (y1, y2) = (x1 + F(x2), x2 + G(y1)).  x1, x2 [B, L, dim] bf16;
+    params: the BLOCK_PARAMS tensors (weights [out, in])."""
+    plist = [params[k] for k in BLOCK_PARAMS]
+    _dev(x1, x2, rot, y1, y2, workspace, *plist)
+    B, L, dim = x1.shape
+    heads = dim // 64
+    dt = _dtype_code(x1)
+    y1 = torch.empty_like(x1) if y1 is None else y1
+    y2 = torch.empty_like(x2) if y2 is None else y2
+    if workspace is None:
+        workspace = _workspace(block_workspace_bytes(B, L, heads, n_buckets, n_hashes, chunk_len, chunk_rows, dt),
+                               x1.device)
+    parr = (_vp * len(plist))(*[t.data_ptr() for t in plist])
+    ev = None if stage_events is None else stage_events.array()
+    _check("reformer_block_fwd", lib().reformer_block_fwd(
+        x1.data_ptr(), x2.data_ptr(), _ptr(rot), ctypes.cast(parr, _vp), B, L, heads, n_buckets, n_hashes,
+        chunk_len, int(bool(causal)), chunk_rows, dt, y1.data_ptr(), y2.data_ptr(), workspace.data_ptr(),
+        workspace.numel(), _stream(x1.device), ev))
+    return y1, y2
 
 
 class EventSet:

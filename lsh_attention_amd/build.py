@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "liblsh_attn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["api.hip", "hash.hip", "sort.hip", "chunk_attn.hip", "combine.hip", "attn_bwd.hip"]
+SOURCES = ["api.hip", "hash.hip", "sort.hip", "chunk_attn.hip", "combine.hip", "attn_bwd.hip", "gemm.hip"]
 ARCH = "gfx950"
 
 

@@ -3,6 +3,7 @@
 // entirely on the host and returns before anything is enqueued.
 #include <string.h>
 
+#include "lsh_block.h"
 #include "lsh_bwd.h"
 
 using namespace lsh;
@@ -107,6 +108,38 @@ BwdWs bwd_ws(int BH, int L, int n_h, lsh_dtype dt) {
   w.dv_slot = c.take(slots * kD * elem_size(dt));
   w.total = c.off;
   return w;
+}
+
+struct BlockWs {
+  FwdWs attn;
+  size_t h1, qk, v, att, attn_base, h2, hid, total;
+};
+BlockWs block_ws(int B, int L, int heads, int n_b, int n_h, int chunk_rows) {
+  Carver c;
+  BlockWs w;
+  const size_t M = (size_t)B * L, dim = (size_t)heads * kD;
+  const size_t rows = chunk_rows > 0 ? (size_t)chunk_rows : M;
+  w.attn = fwd_ws(B * heads, L, n_b, n_h, LSH_BF16);
+  w.h1 = c.take(M * dim * 2);
+  w.qk = c.take(M * dim * 2);
+  w.v = c.take(M * dim * 2);
+  w.att = c.take(M * dim * 2);
+  w.attn_base = c.take(w.attn.total);
+  w.h2 = c.take(M * dim * 2);
+  w.hid = c.take((rows < M ? rows : M) * 4 * dim * 2);
+  w.total = c.off;
+  return w;
+}
+
+int check_block(int B, int L, int heads, int n_b, int n_h, int chunk_len, int chunk_rows, lsh_dtype dt) {
+  int st = check_problem(B, heads, L, kD, n_h);
+  if (st == LSH_OK) st = check_buckets(n_b, L);
+  if (st != LSH_OK) return st;
+  if (chunk_len != kChunk) return chunk_len <= 0 ? LSH_ERR_SHAPE : LSH_ERR_UNSUPPORTED;
+  if (chunk_rows < 0) return LSH_ERR_SHAPE;
+  if (dt != LSH_BF16 || heads % 2 != 0 || heads > 16) return LSH_ERR_UNSUPPORTED;
+  if ((uint64_t)B * L * heads * kD * 4 > 0x7FFFFFFFull) return LSH_ERR_SHAPE;
+  return LSH_OK;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LSH_OK : LSH_ERR_HIP; }
@@ -500,6 +533,140 @@ int lsh_attn_bwd(const void* qk, const void* v, const int32_t* sorted_idx, const
                         dt, s);
   if (e == hipSuccess) e = mark();
   if (e == hipSuccess) e = launch_bwd_reduce(dx_slot, dv_slot, undo_idx, dqk, dv, BH, L, n_h, dt, s);
+  if (e == hipSuccess) e = mark();
+  return hip_status(e);
+}
+
+int lsh_layer_norm(const void* x, const void* gamma, const void* beta, void* y, int rows, int dim, lsh_dtype dt,
+                   void* stream) {
+  if (rows < 0 || dim <= 0) return LSH_ERR_SHAPE;
+  if (dt != LSH_BF16 || dim % 8 != 0 || dim > 1024) return LSH_ERR_UNSUPPORTED;
+  if (rows == 0) return LSH_OK;
+  if (x == nullptr || gamma == nullptr || beta == nullptr || y == nullptr) return LSH_ERR_NULL;
+  const size_t n = (size_t)rows * dim * 2;
+  if (overlaps(y, n, x, n) || overlaps(y, n, gamma, (size_t)dim * 2) || overlaps(y, n, beta, (size_t)dim * 2))
+    return LSH_ERR_ALIAS;
+  return hip_status(launch_layer_norm(x, gamma, beta, y, rows, dim, (hipStream_t)stream));
+}
+
+int lsh_linear(const void* a, int a_layout, const void* w, const void* bias, const void* resid, void* c, int c_layout,
+               int M, int N, int K, int L, int heads, int epilogue, lsh_dtype dt, void* stream) {
+  if (M < 0 || N <= 0 || K <= 0) return LSH_ERR_SHAPE;
+  if (dt != LSH_BF16 || N % 128 != 0 || K % 64 != 0) return LSH_ERR_UNSUPPORTED;
+  const bool bias_on = (epilogue & LSH_EPI_BIAS) != 0, gelu = (epilogue & LSH_EPI_GELU) != 0,
+             resid_on = (epilogue & LSH_EPI_RESID) != 0;
+  const int epi = (bias_on ? kEpiBias : 0) | (gelu ? kEpiGelu : 0) | (resid_on ? kEpiResid : 0);
+  if ((epilogue & ~(LSH_EPI_BIAS | LSH_EPI_GELU | LSH_EPI_RESID)) != 0 ||
+      (epi != 0 && epi != (kEpiBias | kEpiGelu) && epi != kEpiResid && epi != (kEpiBias | kEpiResid)))
+    return LSH_ERR_UNSUPPORTED;
+  const bool ah = a_layout == LSH_LAYOUT_HEADS, ch = c_layout == LSH_LAYOUT_HEADS;
+  if ((a_layout != LSH_LAYOUT_ROWS && !ah) || (c_layout != LSH_LAYOUT_ROWS && !ch) || (ah && ch) || (ch && resid_on))
+    return LSH_ERR_UNSUPPORTED;
+  if ((ah || ch) && (L <= 0 || heads <= 0 || M % L != 0 || (ah ? K : N) != heads * kD)) return LSH_ERR_SHAPE;
+  if (M == 0) return LSH_OK;
+  if (a == nullptr || w == nullptr || c == nullptr || (bias_on && bias == nullptr) || (resid_on && resid == nullptr))
+    return LSH_ERR_NULL;
+  const size_t na = (size_t)M * K * 2, nc = (size_t)M * N * 2, nw = (size_t)N * K * 2;
+  if (overlaps(c, nc, a, na) || overlaps(c, nc, w, nw) || overlaps(c, nc, bias_on ? bias : nullptr, (size_t)N * 2) ||
+      overlaps(c, nc, resid_on ? resid : nullptr, nc))
+    return LSH_ERR_ALIAS;
+  return hip_status(launch_gemm(a, ah ? kLayoutHeads : kLayoutRows, w, bias, resid, c, ch ? kLayoutHeads : kLayoutRows,
+                                M, N, K, ah || ch ? L : 1, ah || ch ? heads : 1, epi, (hipStream_t)stream));
+}
+
+int reformer_block_workspace_bytes(int B, int L, int heads, int n_buckets, int n_hashes, int chunk_len,
+                                   int chunk_rows, lsh_dtype dt, size_t* bytes) {
+  if (bytes == nullptr) return LSH_ERR_NULL;
+  const int st = check_block(B, L, heads, n_buckets, n_hashes, chunk_len, chunk_rows, dt);
+  if (st != LSH_OK) return st;
+  *bytes = is_empty(B, heads, L) ? 0 : block_ws(B, L, heads, n_buckets, n_hashes, chunk_rows).total;
+  return LSH_OK;
+}
+
+int reformer_block_fwd(const void* x1, const void* x2, const void* rot, const void* const* params, int B, int L,
+                       int heads, int n_buckets, int n_hashes, int chunk_len, int causal, int chunk_rows,
+                       lsh_dtype dt, void* y1, void* y2, void* ws, size_t ws_bytes, void* stream,
+                       void* const* stage_events) {
+  const int st = check_block(B, L, heads, n_buckets, n_hashes, chunk_len, chunk_rows, dt);
+  if (st != LSH_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (is_empty(B, heads, L)) {
+    if (stage_events != nullptr)
+      for (int k = 0; k < LSH_BLOCK_N_EVENTS; ++k)
+        if (hipEventRecord((hipEvent_t)stage_events[k], s) != hipSuccess) return LSH_ERR_HIP;
+    return LSH_OK;
+  }
+  if (x1 == nullptr || x2 == nullptr || params == nullptr || y1 == nullptr || y2 == nullptr ||
+      (n_buckets > 1 && rot == nullptr))
+    return LSH_ERR_NULL;
+  for (int k = 0; k < LSH_BLOCK_N_PARAMS; ++k)
+    if (params[k] == nullptr) return LSH_ERR_NULL;
+  const BlockWs w = block_ws(B, L, heads, n_buckets, n_hashes, chunk_rows);
+  if (ws == nullptr || ws_bytes < w.total) return LSH_ERR_WORKSPACE;
+  const int M = B * L, dim = heads * kD;
+  const size_t act = (size_t)M * dim * 2;
+  const size_t pn[LSH_BLOCK_N_PARAMS] = {(size_t)dim * 2, (size_t)dim * 2, (size_t)dim * dim * 2,
+                                         (size_t)dim * dim * 2, (size_t)dim * dim * 2, (size_t)dim * 2,
+                                         (size_t)dim * 2, (size_t)4 * dim * dim * 2, (size_t)4 * dim * 2,
+                                         (size_t)4 * dim * dim * 2, (size_t)dim * 2};
+  const size_t rot_bytes = n_buckets > 1 ? (size_t)n_hashes * kD * (n_buckets / 2) * 2 : 0;
+  const void* outs[2] = {y1, y2};
+  for (int o = 0; o < 2; ++o) {
+    if (overlaps(outs[o], act, x1, act) || overlaps(outs[o], act, x2, act) ||
+        overlaps(outs[o], act, rot, rot_bytes) || overlaps(outs[o], act, ws, ws_bytes))
+      return LSH_ERR_ALIAS;
+    for (int k = 0; k < LSH_BLOCK_N_PARAMS; ++k)
+      if (overlaps(outs[o], act, params[k], pn[k])) return LSH_ERR_ALIAS;
+  }
+  if (overlaps(y1, act, y2, act) || overlaps(ws, ws_bytes, x1, act) || overlaps(ws, ws_bytes, x2, act) ||
+      overlaps(ws, ws_bytes, rot, rot_bytes))
+    return LSH_ERR_ALIAS;
+  for (int k = 0; k < LSH_BLOCK_N_PARAMS; ++k)
+    if (overlaps(ws, ws_bytes, params[k], pn[k])) return LSH_ERR_ALIAS;
+
+  char* base = (char*)ws;
+  void* h1 = base + w.h1;
+  void* qk = base + w.qk;
+  void* v = base + w.v;
+  void* att = base + w.att;
+  void* h2 = base + w.h2;
+  void* hid = base + w.hid;
+  int k = 0;
+  auto mark = [&](void) -> hipError_t {
+    return stage_events == nullptr ? hipSuccess : hipEventRecord((hipEvent_t)stage_events[k++], s);
+  };
+  const void* const* p = params;
+  hipError_t e = mark();
+  // y1 = x1 + W_o . attention(LN1(x2) W_qk^T, LN1(x2) W_v^T)
+  if (e == hipSuccess) e = launch_layer_norm(x2, p[LSH_BLOCK_LN1_G], p[LSH_BLOCK_LN1_B], h1, M, dim, s);
+  if (e == hipSuccess) e = mark();
+  if (e == hipSuccess)
+    e = launch_gemm(h1, kLayoutRows, p[LSH_BLOCK_W_QK], nullptr, nullptr, qk, kLayoutHeads, M, dim, dim, L, heads, 0, s);
+  if (e == hipSuccess)
+    e = launch_gemm(h1, kLayoutRows, p[LSH_BLOCK_W_V], nullptr, nullptr, v, kLayoutHeads, M, dim, dim, L, heads, 0, s);
+  if (e == hipSuccess) e = mark();
+  if (e != hipSuccess) return hip_status(e);
+  const int ast = fused_forward(qk, v, rot, n_buckets, n_hashes, chunk_len, causal, 0, B, heads, L, kD, dt, att,
+                                nullptr, nullptr, nullptr, nullptr, base + w.attn_base, w.attn.total, stream, nullptr);
+  if (ast != LSH_OK) return ast;
+  e = mark();
+  if (e == hipSuccess)
+    e = launch_gemm(att, kLayoutHeads, p[LSH_BLOCK_W_O], nullptr, x1, y1, kLayoutRows, M, dim, dim, L, heads,
+                    kEpiResid, s);
+  if (e == hipSuccess) e = mark();
+  // y2 = x2 + W2 . GELU(W1 . LN2(y1) + b1) + b2, the hidden activation a chunk of rows at a time
+  if (e == hipSuccess) e = launch_layer_norm(y1, p[LSH_BLOCK_LN2_G], p[LSH_BLOCK_LN2_B], h2, M, dim, s);
+  if (e == hipSuccess) e = mark();
+  const int rows = chunk_rows > 0 && chunk_rows < M ? chunk_rows : M;
+  for (int r0 = 0; r0 < M && e == hipSuccess; r0 += rows) {
+    const int m = M - r0 < rows ? M - r0 : rows;
+    const size_t off = (size_t)r0 * dim * 2;
+    e = launch_gemm((const char*)h2 + off, kLayoutRows, p[LSH_BLOCK_W1], p[LSH_BLOCK_B1], nullptr, hid, kLayoutRows,
+                    m, 4 * dim, dim, L, heads, kEpiBias | kEpiGelu, s);
+    if (e == hipSuccess)
+      e = launch_gemm(hid, kLayoutRows, p[LSH_BLOCK_W2], p[LSH_BLOCK_B2], (const char*)x2 + off, (char*)y2 + off,
+                      kLayoutRows, m, dim, 4 * dim, L, heads, kEpiBias | kEpiResid, s);
+  }
   if (e == hipSuccess) e = mark();
   return hip_status(e);
 }

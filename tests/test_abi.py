@@ -178,3 +178,44 @@ def test_variant_calls_reject_before_launch(L):
     assert f(P1, P2, P3, 8, 2, 64, 0, DD, 1, 2, 128, 64, BF16, P1, None, P5, need, None, None) == ALIAS
     assert f(None, P2, P3, 8, 2, 64, 0, SB, 1, 2, 128, 64, BF16, P4, None, P5, need, None, None) == NULL
     assert f(None, None, None, 8, 2, 64, 0, SB, 1, 0, 128, 64, BF16, None, None, None, 0, None, None) == OK
+
+
+def test_block_calls_reject_before_launch(L):
+    BF = BF16
+    P6, P7 = 0x60000000, 0x70000000
+    ln = L.lsh_layer_norm
+    assert ln(P1, P2, P3, P4, 10, 512, F32, None) == UNSUPPORTED
+    assert ln(P1, P2, P3, P4, 10, 2048, BF, None) == UNSUPPORTED
+    assert ln(P1, P2, P3, P1, 10, 512, BF, None) == ALIAS
+    assert ln(None, P2, P3, P4, 10, 512, BF, None) == NULL
+    assert ln(None, None, None, None, 0, 512, BF, None) == OK
+    lin = L.lsh_linear
+    # args: a, a_layout, w, bias, resid, c, c_layout, M, N, K, L, heads, epilogue, dt, stream
+    assert lin(P1, 0, P2, None, None, P3, 0, 128, 100, 64, 1, 1, 0, BF, None) == UNSUPPORTED   # N % 128
+    assert lin(P1, 0, P2, None, None, P3, 0, 128, 128, 60, 1, 1, 0, BF, None) == UNSUPPORTED   # K % 64
+    assert lin(P1, 0, P2, None, None, P3, 0, 128, 128, 64, 1, 1, 2, BF, None) == UNSUPPORTED   # GELU alone
+    assert lin(P1, 0, P2, None, None, P3, 0, 128, 128, 64, 1, 1, 1, BF, None) == UNSUPPORTED   # bias alone
+    assert lin(P1, 1, P2, None, None, P3, 1, 128, 128, 128, 64, 2, 0, BF, None) == UNSUPPORTED  # heads -> heads
+    assert lin(P1, 0, P2, None, P4, P3, 1, 128, 128, 64, 64, 2, 4, BF, None) == UNSUPPORTED    # resid with heads out
+    assert lin(P1, 1, P2, None, None, P3, 0, 128, 128, 128, 64, 3, 0, BF, None) == SHAPE       # K != 64 heads
+    assert lin(P1, 0, P2, None, None, P3, 0, 128, 128, 64, 1, 1, 0, F32, None) == UNSUPPORTED
+    assert lin(P1, 0, P2, None, None, P1, 0, 128, 128, 64, 1, 1, 0, BF, None) == ALIAS
+    assert lin(P1, 0, P2, None, None, None, 0, 128, 128, 64, 1, 1, 0, BF, None) == NULL
+    assert lin(P1, 0, P2, None, None, P3, 0, 128, 128, 64, 1, 1, 5, BF, None) == NULL          # bias|resid missing
+    assert lin(None, 0, None, None, None, None, 0, 0, 128, 64, 1, 1, 0, BF, None) == OK
+    st, need = _ws("reformer_block_workspace_bytes", 1, 256, 2, 8, 2, 64, 100, BF)
+    assert st == OK and need > 256 * 128 * 2 * 6
+    assert _ws("reformer_block_workspace_bytes", 1, 256, 3, 8, 2, 64, 0, BF)[0] == UNSUPPORTED  # odd heads
+    assert _ws("reformer_block_workspace_bytes", 1, 256, 2, 8, 2, 64, 0, F32)[0] == UNSUPPORTED
+    assert _ws("reformer_block_workspace_bytes", 1, 256, 2, 8, 2, 64, -1, BF)[0] == SHAPE
+    params = (ctypes.c_void_p * 11)(*[0x1000000 * (k + 200) for k in range(11)])
+    pp = ctypes.cast(params, ctypes.c_void_p)
+    f = L.reformer_block_fwd
+    # args: x1, x2, rot, params, B, L, heads, n_b, n_h, C, causal, chunk_rows, dt, y1, y2, ws, ws_bytes, stream, ev
+    assert f(P1, P2, P3, pp, 1, 256, 2, 8, 2, 64, 0, 100, BF, P4, P5, P6, need - 1, None, None) == WORKSPACE
+    assert f(P1, P2, P3, pp, 1, 256, 2, 8, 2, 64, 0, 100, BF, P1, P5, P6, need, None, None) == ALIAS
+    assert f(P1, P2, P3, pp, 1, 256, 2, 8, 2, 64, 0, 100, BF, P4, P4, P6, need, None, None) == ALIAS
+    assert f(P1, P2, P3, None, 1, 256, 2, 8, 2, 64, 0, 100, BF, P4, P5, P6, need, None, None) == NULL
+    params[7] = None
+    assert f(P1, P2, P3, pp, 1, 256, 2, 8, 2, 64, 0, 100, BF, P4, P5, P6, need, None, None) == NULL
+    assert f(None, None, None, None, 1, 0, 2, 8, 2, 64, 0, 100, BF, None, None, None, 0, None, None) == OK
