@@ -15,11 +15,14 @@
 // layer's layout, both operands contiguous in K), bf16 in, fp32 accumulate,
 // bf16 out.  128 x 128 tiles, 4 waves of 64 x 64 on v_mfma_f32_16x16x32_bf16,
 // K staged 64 at a time through double-buffered LDS (rows padded to 144 bytes,
-// so the 16-byte operand reads are conflict-free), one barrier per stage; the
-// next stage's global loads are in flight during the current stage's MFMAs.
+// so the 16-byte operand reads are conflict-free), one barrier per stage; two
+// register sets keep the global loads two stages ahead of the MFMAs.  The
+// epilogue stages the fp32 tile in LDS and writes 16-byte row pieces.
 // Tiles are ordered so that all column tiles of a row tile run on one XCD (its
 // A rows are fetched into one L2).  Epilogue: + bias, GELU, + residual, and the
 // attention's head-major layout [B][H][L][64] on input (A) or output (C).
+#include <type_traits>
+
 #include "lsh_block.h"
 
 namespace lsh {
@@ -50,8 +53,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ bias,
                                                       const uint16_t* __restrict__ resid, uint16_t* __restrict__ C,
                                                       int M, int N, int K, int L, int H, int n_items) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kTM * kRow];
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][kTN * kRow];
+  // [A buf 0][A buf 1][W buf 0][W buf 1]; the epilogue reuses all of it as one fp32 tile
+  __shared__ __attribute__((aligned(16))) uint16_t sBuf[2 * (kTM + kTN) * kRow];
+  uint16_t* const sA0 = sBuf;
+  uint16_t* const sW0 = sBuf + 2 * kTM * kRow;
   const unsigned item = xcd_item(blockIdx.x, gridDim.x);
   if (item >= (unsigned)n_items) return;
   const int n_tiles = N / kTN;
@@ -61,23 +66,36 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint16_t* __restrict
   const int wm = wave >> 1, wn = wave & 1;
 
   // global -> LDS: 128 rows x 8 pieces of 16 bytes per operand; thread t moves
-  // pieces t + 256 i (row p >> 3, piece p & 7)
-  uint4 ra[4], rw[4];
-  auto load = [&](int k0) {
+  // pieces t + 256 i (row p >> 3, piece p & 7).  Two register sets: stage k+2 is
+  // loaded while stage k is computed and stage k+1 waits in the other set, so a
+  // load has two stages of MFMA work to arrive.
+  uint4 ra0[4], rw0[4], ra1[4], rw1[4];  // the two register sets (compile-time selected)
+  auto load = [&](auto set, int k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int p = tid + 256 * i, r = p >> 3, pc = p & 7;
-      const int m = m0 + r;
-      ra[i] = m < M ? *(const uint4*)(A + ofs<AMODE>(m, k0 + 8 * pc, K, L, H)) : make_uint4(0, 0, 0, 0);
-      rw[i] = *(const uint4*)(W + (size_t)(n0 + r) * K + k0 + 8 * pc);
+      // rows past M (a partial last row tile) read row M - 1: they only feed
+      // output rows that are never stored, and the loads stay unconditional
+      const int m = min(m0 + r, M - 1);
+      const uint4 va = *(const uint4*)(A + ofs<AMODE>(m, k0 + 8 * pc, K, L, H));
+      const uint4 vw = *(const uint4*)(W + (size_t)(n0 + r) * K + k0 + 8 * pc);
+      if constexpr (decltype(set)::value == 0) {
+        ra0[i] = va;
+        rw0[i] = vw;
+      } else {
+        ra1[i] = va;
+        rw1[i] = vw;
+      }
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](auto set, int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int p = tid + 256 * i, r = p >> 3, pc = p & 7;
-      *(uint4*)(&sA[buf][r * kRow + 8 * pc]) = ra[i];
-      *(uint4*)(&sW[buf][r * kRow + 8 * pc]) = rw[i];
+      const uint4 va = decltype(set)::value == 0 ? ra0[i] : ra1[i];
+      const uint4 vw = decltype(set)::value == 0 ? rw0[i] : rw1[i];
+      *(uint4*)(&sA0[buf * kTM * kRow + r * kRow + 8 * pc]) = va;
+      *(uint4*)(&sW0[buf * kTN * kRow + r * kRow + 8 * pc]) = vw;
     }
   };
 
@@ -87,46 +105,84 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = K / kTK;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kb = 0; kb < nk; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nk) load((kb + 1) * kTK);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       bf16x8 a[4], b[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        a[i] = *(const bf16x8*)(&sA[buf][(64 * wm + 16 * i + col) * kRow + 32 * s + 8 * grp]);
-        b[i] = *(const bf16x8*)(&sW[buf][(64 * wn + 16 * i + col) * kRow + 32 * s + 8 * grp]);
+        a[i] = *(const bf16x8*)(&sA0[buf * kTM * kRow + (64 * wm + 16 * i + col) * kRow + 32 * s + 8 * grp]);
+        b[i] = *(const bf16x8*)(&sW0[buf * kTN * kRow + (64 * wn + 16 * i + col) * kRow + 32 * s + 8 * grp]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (kb + 1 < nk) store(buf ^ 1);  // that buffer was last read before the previous barrier
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  const int nk = K / kTK;
+  load(S0{}, 0);
+  if (nk > 1) load(S1{}, kTK);
+  store(S0{}, 0);
+  __syncthreads();
+  // stage k: compute buffer k & 1; set k & 1 is free once stage k is in LDS
+  auto step = [&](int kb, auto set, auto other) {
+    constexpr int sv = decltype(set)::value;
+    if (kb + 2 < nk) load(set, (kb + 2) * kTK);
+    compute(sv);
+    if (kb + 1 < nk) store(other, sv ^ 1);  // that buffer was last read before the previous barrier
     __syncthreads();
+  };
+  for (int kb = 0; kb < nk; kb += 2) {
+    step(kb, S0{}, S1{});
+    if (kb + 1 < nk) step(kb + 1, S1{}, S0{});
   }
 
-  // ---- epilogue: lane holds C[64 wm + 16 i + 4 grp + e][64 wn + 16 j + col] ----
+  // ---- epilogue through LDS: lane holds C[64 wm + 16 i + 4 grp + e][64 wn + 16 j + col].
+  // The fp32 tile (+ bias, GELU) is staged in LDS and written as 16-byte row
+  // pieces, the residual added before the one rounding to bf16.
+  constexpr int kCRow = kTN + 4;
+  float* const sC = (float*)sBuf;  // [128][kCRow] fp32, within the operand buffers
+  static_assert(kTM * kCRow * 4 <= 2 * (kTM + kTN) * kRow * 2, "epilogue tile exceeds the LDS buffers");
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int n = n0 + 64 * wn + 16 * j + col;
-    const float bv = (EPI & kEpiBias) ? from_bf16(bias[n]) : 0.f;
+    const int nl = 64 * wn + 16 * j + col;
+    const float bv = (EPI & kEpiBias) ? from_bf16(bias[n0 + nl]) : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int m = m0 + 64 * wm + 16 * i + 4 * grp + e;
-        if (m >= M) continue;
         float x = acc[i][j][e] + bv;
         if constexpr ((EPI & kEpiGelu) != 0) x = 0.5f * x * (1.f + erff(x * 0.70710678118654752f));
-        if constexpr ((EPI & kEpiResid) != 0) x += from_bf16(resid[(size_t)m * N + n]);
-        C[ofs<CMODE>(m, n, N, L, H)] = to_bf16(x);
+        sC[(64 * wm + 16 * i + 4 * grp + e) * kCRow + nl] = x;
       }
+  }
+  __syncthreads();
+  // 128 rows x 16 pieces of 8 columns: thread t writes pieces t + 256 i
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int p = tid + 256 * i, ml = p >> 4, pc = p & 15;
+    const int m = m0 + ml, n = n0 + 8 * pc;
+    if (m >= M) continue;
+    const float4 lo = *(const float4*)(&sC[ml * kCRow + 8 * pc]);
+    const float4 hi = *(const float4*)(&sC[ml * kCRow + 8 * pc + 4]);
+    float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    if constexpr ((EPI & kEpiResid) != 0) {
+      const uint4 r = *(const uint4*)(resid + (size_t)m * N + n);
+      const uint32_t rr[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[2 * k] += bf_lo(rr[k]);
+        v[2 * k + 1] += bf_hi(rr[k]);
+      }
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = (uint32_t)to_bf16(v[2 * k]) | ((uint32_t)to_bf16(v[2 * k + 1]) << 16);
+    *(uint4*)(C + ofs<CMODE>(m, n, N, L, H)) = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
