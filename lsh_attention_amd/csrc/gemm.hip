@@ -37,6 +37,21 @@ __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF000
 __device__ inline uint16_t to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 __device__ inline float from_bf16(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+// GELU(x) = x Phi(x) = x (1 + erf(x / sqrt 2)) / 2, with erf from Abramowitz &
+// Stegun, Handbook of Mathematical Functions, formula 7.1.26: for z >= 0,
+// erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2), t = 1 / (1 + p z),
+// absolute error at most 1.5e-7 (far below bf16 rounding); erf is odd.
+__device__ inline float gelu_as(float x) {
+  constexpr float p = 0.3275911f, a1 = 0.254829592f, a2 = -0.284496736f, a3 = 1.421413741f,
+                  a4 = -1.453152027f, a5 = 1.061405429f;
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(p, z, 1.f));
+  const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, a5, a4), a3), a2), a1);
+  const float e = __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);
+  const float erf_abs = fmaf(-poly, e, 1.f);
+  return 0.5f * x * (1.f + copysignf(erf_abs, x));
+}
+
 // element offset of (row m, column k) of a [M x K] operand in the given layout
 template <int MODE>
 __device__ inline size_t ofs(int m, int k, int K, int L, int H) {
@@ -156,7 +171,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint16_t* __restrict
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float x = acc[i][j][e] + bv;
-        if constexpr ((EPI & kEpiGelu) != 0) x = 0.5f * x * (1.f + erff(x * 0.70710678118654752f));
+        if constexpr ((EPI & kEpiGelu) != 0) x = gelu_as(x);
         sC[(64 * wm + 16 * i + 4 * grp + e) * kCRow + nl] = x;
       }
   }
