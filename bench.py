@@ -13,7 +13,10 @@ the method as described; such a line names the variant in its config and
 carries no cpu_baseline leg.  --backward times a training step of the layer
 instead: the fused forward that keeps its permutation and per-round lse
 (reformer_lsh_attn_fwd_train) followed by lsh_attn_bwd, with seeded output
-gradients; its line has "pass": "fwd+bwd" in its config.
+gradients; its line has "pass": "fwd+bwd" in its config.  --block times one
+reversible Reformer block around the attention (reformer_block_fwd: LayerNorm,
+projections, the attention, output projection, LayerNorm, chunked GELU
+feed-forward) on the workload's sequence with dim = 64 heads; per stage.
 """
 from __future__ import annotations
 
@@ -73,6 +76,26 @@ def algorithmic_work(B, H, L, D, n_b, n_h, es, same_bucket=False, dedup=False):
     }
 
 
+def block_work(B, L, H, n_b, n_h, es=2):
+    """Algorithmic bytes and flops of each block stage: activations read and
+    written once ([B L dim] bf16), weights read once; the feed-forward's hidden
+    activation stays out of the count (a fused design never writes it); the
+    attention stage is the sum of its kernels."""
+    M, dim = B * L, 64 * H
+    act = M * dim * es
+    att = algorithmic_work(B, H, L, 64, n_b, n_h, es)
+    att_b = sum(v["bytes"] for k, v in att.items() if not k.startswith(("bwd", "attn_bwd")))
+    att_f = sum(v["flops"] for k, v in att.items() if not k.startswith(("bwd", "attn_bwd")))
+    return {
+        "ln1": {"bytes": 2 * act, "flops": 0},
+        "qkv_proj": {"bytes": 3 * act + 2 * dim * dim * es, "flops": 2 * 2 * M * dim * dim},
+        "attention": {"bytes": att_b, "flops": att_f},
+        "out_proj": {"bytes": 3 * act + dim * dim * es, "flops": 2 * M * dim * dim},
+        "ln2": {"bytes": 2 * act, "flops": 0},
+        "ffn": {"bytes": 3 * act + 8 * dim * dim * es, "flops": 2 * 2 * M * dim * 4 * dim},
+    }
+
+
 def measured_traffic(workload: str, kernel: str, attend: str = "none"):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE record (profiles/traffic_<workload>[_<attend>].json, "train" for the
@@ -124,6 +147,9 @@ def main():
                     help="attended-set variant: same-bucket mask, set-union correction, or both")
     ap.add_argument("--backward", action="store_true",
                     help="time a training step (forward keeping its state, then the backward pass)")
+    ap.add_argument("--block", action="store_true",
+                    help="time one reversible block (attention sublayer + chunked feed-forward)")
+    ap.add_argument("--chunk-rows", type=int, default=16384, help="feed-forward row chunk of --block")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device-to-device copy of this many MiB "
                          "(a reference kernel of known traffic for hardware byte counters)")
@@ -139,6 +165,8 @@ def main():
     from lsh_attention_amd import binding as bd
     from lsh_attention_amd import inputs as I
 
+    if args.block:
+        return bench_block(args)
     inp = I.make_inputs(args.workload, n_hashes=args.n_hashes)
     w = inp.workload
     B, H, L, D = inp.qk.values.shape
@@ -262,6 +290,87 @@ def main():
     if not args.no_cpu_baseline and args.attend == "none" and not args.backward:
         log("timing the oracle on the host (cpu_baseline leg)")
         result["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(result), flush=True)
+
+
+def bench_block(args):
+    import numpy as np
+    import torch
+
+    from lsh_attention_amd import binding as bd
+    from lsh_attention_amd import inputs as I
+
+    bi = I.make_block_inputs(args.workload, n_hashes=args.n_hashes)
+    w = bi.workload
+    B, L, dim = bi.x1.values.shape
+    H, n_h, n_b = dim // 64, bi.n_hashes, w.n_buckets
+    log(f"block {w.name}: B{B} L{L} dim{dim} heads{H} n_b{n_b} n_h{n_h} causal={w.causal} bf16 "
+        f"chunk_rows={args.chunk_rows}")
+
+    def dev(t):
+        if t is None:
+            return None
+        return torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    x1, x2, rot = dev(bi.x1), dev(bi.x2), dev(bi.rot)
+    P = {k: dev(t) for k, t in bi.params.items()}
+    y1, y2 = torch.empty_like(x1), torch.empty_like(x2)
+    ws = torch.empty(bd.block_workspace_bytes(B, L, H, n_b, n_h, 64, args.chunk_rows), dtype=torch.uint8,
+                     device="cuda")
+
+    def step(ev=None):
+        bd.reformer_block_fwd(x1, x2, rot, P, n_b, n_h, w.causal, chunk_rows=args.chunk_rows, y1=y1, y2=y2,
+                              workspace=ws, stage_events=ev)
+
+    for _ in range(args.warmup):
+        step()
+    events = [bd.EventSet(bd.BLOCK_N_EVENTS) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per = np.array([e.durations_ms() for e in events])
+    for e in events:
+        e.close()
+    ms = elapsed * 1e3 / args.steps
+    log(f"{args.steps} steps: {ms:.4f} ms/step wall")
+    work = block_work(B, L, H, n_b, n_h)
+    stages = {}
+    for i, name in enumerate(bd.BLOCK_STAGE_NAMES):
+        us = float(np.mean(per[:, i])) * 1e3
+        wk = work[name]
+        ent = {"us": round(us, 2)}
+        if wk["bytes"]:
+            ent["GBps"] = round(wk["bytes"] / (us * 1e-6) / 1e9, 1)
+            ent["hbm_frac"] = round(ent["GBps"] / HBM_PEAK_GBS, 4)
+        if wk["flops"]:
+            ent["TFLOPs"] = round(wk["flops"] / (us * 1e-6) / 1e12, 1)
+            ent["mfma_frac"] = round(ent["TFLOPs"] / BF16_PEAK_TFLOPS, 4)
+        stages[name] = ent
+        log(f"  {name:10s} {us:9.2f} us  {json.dumps({k: x for k, x in ent.items() if k != 'us'})}")
+    dom = max(stages, key=lambda k: stages[k]["us"])
+    wk, d_us = work[dom], stages[dom]["us"]
+    if wk["flops"] / (BF16_PEAK_TFLOPS * 1e12) > wk["bytes"] / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": round(wk["flops"] / (d_us * 1e-6) / 1e12, 2),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(wk["bytes"] / (d_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["kernel"] = dom
+    roof["traffic"] = None
+    result = {
+        "metric": "Reformer block fwd (LSH attention + chunked FFN) tokens/sec at L=64K, 8 hashes",
+        "value": round(B * L / (elapsed / args.steps), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "pass": "block", "batch": B, "seq_len": L, "dim": dim, "heads": H,
+                   "n_buckets": n_b, "n_hashes": n_h, "chunk_len": 64, "causal": w.causal,
+                   "ffn_chunk_rows": args.chunk_rows},
+        "roofline": roof, "stages": stages,
+    }
     print(json.dumps(result), flush=True)
 
 

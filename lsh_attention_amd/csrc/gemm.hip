@@ -85,14 +85,23 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint16_t* __restrict
   // loaded while stage k is computed and stage k+1 waits in the other set, so a
   // load has two stages of MFMA work to arrive.
   uint4 ra0[4], rw0[4], ra1[4], rw1[4];  // the two register sets (compile-time selected)
+  // A element offsets of this thread's 4 rows at k = 8 (p & 7); per stage only
+  // k0 (a multiple of 64) is added: + k0 in the rows layout, + (k0 / 64) L 64 in
+  // the head-major one.  Rows past M (a partial last row tile) read row M - 1:
+  // they only feed output rows that are never stored, and the loads stay
+  // unconditional.
+  size_t abase[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = tid + 256 * i;
+    abase[i] = ofs<AMODE>(min(m0 + (p >> 3), M - 1), 8 * (p & 7), K, L, H);
+  }
+  const size_t astep = AMODE == kLayoutRows ? (size_t)kTK : (size_t)L * 64;  // per stage of 64 columns
   auto load = [&](auto set, int k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int p = tid + 256 * i, r = p >> 3, pc = p & 7;
-      // rows past M (a partial last row tile) read row M - 1: they only feed
-      // output rows that are never stored, and the loads stay unconditional
-      const int m = min(m0 + r, M - 1);
-      const uint4 va = *(const uint4*)(A + ofs<AMODE>(m, k0 + 8 * pc, K, L, H));
+      const uint4 va = *(const uint4*)(A + abase[i] + (size_t)(k0 / kTK) * astep);
       const uint4 vw = *(const uint4*)(W + (size_t)(n0 + r) * K + k0 + 8 * pc);
       if constexpr (decltype(set)::value == 0) {
         ra0[i] = va;
