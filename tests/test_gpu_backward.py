@@ -139,3 +139,27 @@ def test_backward_full_size(gpu_lib, name, n_h):
     rel_check(gdx[toks], ref_x, tol, f"dqk sampled b{b} h{h}")
     rel_check(gdv[toks], ref_v, tol, f"dv sampled b{b} h{h}")
     say(f"  tokens {toks} within tolerance")
+
+
+def test_backward_is_deterministic_and_train_forward_matches(gpu_lib):
+    """No atomics: repeated backward calls give identical bits.  The training
+    forward returns the plain fused forward's output and lse, and the staged
+    calls' permutation and per-round lse, exactly."""
+    inp = I.make_inputs("causal_lm_4k", n_hashes=4, B=2, H=2, L=1024)
+    w = inp.workload
+    qk, v, rot = upload(inp)
+    out_t, lse_t, sidx, undo, l_s = bd.reformer_lsh_attn_fwd_train(qk, v, rot, w.n_buckets, 4, 64, w.causal)
+    out_f, lse_f = bd.reformer_lsh_attn_fwd(qk, v, rot, w.n_buckets, 4, 64, w.causal)
+    s_sidx, s_undo, s_ls, _, _ = gpu_forward(qk, v, rot, w.n_buckets, 4, w.causal)
+    torch.cuda.synchronize()
+    assert torch.equal(out_t, out_f) and torch.equal(lse_t, lse_f)
+    assert torch.equal(sidx, s_sidx) and torch.equal(undo, s_undo)
+    # the staged attention computes its own key scales from the rows: same to rounding
+    rel_check(f64(l_s), f64(s_ls), 1e-5, "per-round lse, fused vs staged")
+    dout_t, dlse_t = grads_inputs(123, tuple(qk.shape), w.dtype)
+    dout, dlse = to_device(dout_t), to_device(dlse_t)
+    first = bd.lsh_attn_bwd(qk, v, sidx, undo, l_s, out_t, dout, dlse, 4, 64, w.causal)
+    for _ in range(3):
+        again = bd.lsh_attn_bwd(qk, v, sidx, undo, l_s, out_t, dout, dlse, 4, 64, w.causal)
+        torch.cuda.synchronize()
+        assert torch.equal(first[0], again[0]) and torch.equal(first[1], again[1])
