@@ -14,7 +14,7 @@
 //
 // gfx950 design (one block of 4 waves walks a run of 8 consecutive chunks of
 // one (batch, head); wave w owns queries 16w..16w+15 of the current chunk; 128
-// VGPRs and 38 KiB of LDS per block, so 4 blocks share a CU):
+// VGPRs and 35 KiB of LDS per block, so 4 blocks share a CU):
 //  * Gathers are software-pipelined: the 64 x rows and 64 v rows of chunk c+1
 //    (128-byte rows addressed through sorted_idx) are loaded into registers
 //    while chunk c is computed, then written to LDS.  The previous chunk's
@@ -22,9 +22,11 @@
 //    block.  The block's slice of sorted_idx is staged in LDS up front.
 //  * V is stored transposed in LDS for the P.V product, with its keys permuted
 //    into the order the P.V operand consumes them, so each lane reads its 8
-//    keys as one 16-byte, bank-conflict-free LDS read.  Each thread gathers one
-//    4-byte word (two dims) from each of 8 rows and writes two 16-byte V^T
-//    pieces, so the transpose costs 2 LDS writes per thread per chunk.
+//    keys as one 16-byte LDS read.  Each thread gathers one 4-byte word (two
+//    dims) from each of 8 rows and writes two 16-byte V^T pieces, so the
+//    transpose costs 2 LDS writes per thread per chunk.  The bf16 tiles use
+//    unpadded rows with XOR-swizzled 16-byte pieces (xoff / voff below), the
+//    layout that lets both the operand reads and these writes run at full rate.
 //  * S^T = K Q^T on MFMA (keys are MFMA rows, queries MFMA columns), so each
 //    lane holds one query's logits for 4 consecutive keys per 16-key tile.
 //  * O^T = V^T P^T on MFMA: the P^T operand is exactly the lane's own
@@ -57,8 +59,8 @@ struct AttnTraits;
 template <>
 struct AttnTraits<true> {
   using T = uint16_t;
-  static constexpr int kXRow = 72;   // x rows in LDS: 64 dims + 8 pad (144 B)
-  static constexpr int kVRow = 136;  // V^T rows in LDS: 128 keys + 8 pad (272 B)
+  static constexpr int kXRow = 64;   // x rows in LDS: 64 dims, 16-byte pieces swizzled (xoff)
+  static constexpr int kVRow = 128;  // V^T rows in LDS: 2 slots x 64 keys, pieces swizzled (voff)
   static constexpr int kXLoads = 2;  // 16-byte loads per thread for its 16 dims of an x row
   static constexpr int kVWords = 8;  // 4-byte V words per thread (2 dims x 8 rows)
 };
@@ -74,6 +76,14 @@ struct AttnTraits<false> {
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+
+// bf16 LDS tiles keep rows unpadded and store 16-byte piece q of row r at
+// piece q ^ (r mod pieces-per-row).  The MFMA operand reads (16 lanes on 16
+// rows, the 4 lane groups on 4 pieces) and the staging writes then run at the
+// full LDS rate on gfx950; padded rows of 144 or 272 bytes measured 1.6x slower
+// for those reads.  Element offsets:
+__device__ inline int xoff(int row, int piece) { return row * 64 + 8 * (piece ^ (row & 7)); }    // x rows
+__device__ inline int voff(int row, int piece) { return row * 128 + 8 * (piece ^ (row & 15)); }  // V^T rows
 
 // ATTEND: 0 = the method as described; bit 0 = same-bucket keys only, bit 1 =
 // set union over the rounds (each distinct key once).  The variants take the
@@ -209,8 +219,12 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
   };
   auto commit = [&](int slot) {
 #pragma unroll
-    for (int i = 0; i < kXLoads; ++i)
-      *(uint4*)(&sX[slot][xrow * kXRow + 16 * xq4 + i * (16 / kXLoads)]) = xr[i];
+    for (int i = 0; i < kXLoads; ++i) {
+      if constexpr (BF16)
+        *(uint4*)(&sX[slot][xoff(xrow, 2 * xq4 + i)]) = xr[i];
+      else
+        *(uint4*)(&sX[slot][xrow * kXRow + 16 * xq4 + i * (16 / kXLoads)]) = xr[i];
+    }
     if (tsq != nullptr) {
       if (tid < 64) {
         sKs[slot][tid] = tsc.x;
@@ -244,8 +258,10 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
     if constexpr (BF16) {
       // V^T columns are keys in the order of the P.V operand: column 32h + 8g + 4b + e holds
       // chunk row 32h + 16b + 4g + e.  This thread holds rows 32h + 4g + e and 32h + 16 + 4g + e
-      // (h, g from its index), i.e. columns 32h + 8g + 0..7.
-      const int p = tid & 31, j = tid >> 5, r0 = 32 * (j >> 2) + 8 * (j & 3);
+      // (h, g from its index), i.e. columns 32h + 8g + 0..7: piece j of the slot.  V^T rows
+      // are dims in the order 0, 2, .., 62, 1, 3, .., 63 (row p = dim 2p, row 32 + p =
+      // dim 2p + 1), so the 32 lanes of a half-wave write 32 consecutive rows.
+      const int p = tid & 31, j = tid >> 5;
       // low halves = dim 2p, high halves = dim 2p+1, of the 8 rows in column order
       uint4 lo, hi;
       lo.x = __builtin_amdgcn_perm(vw[1], vw[0], 0x05040100u);
@@ -256,8 +272,8 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
       hi.y = __builtin_amdgcn_perm(vw[3], vw[2], 0x07060302u);
       hi.z = __builtin_amdgcn_perm(vw[5], vw[4], 0x07060302u);
       hi.w = __builtin_amdgcn_perm(vw[7], vw[6], 0x07060302u);
-      *(uint4*)(&sVT[(2 * p) * kVRow + 64 * slot + r0]) = lo;
-      *(uint4*)(&sVT[(2 * p + 1) * kVRow + 64 * slot + r0]) = hi;
+      *(uint4*)(&sVT[voff(p, 8 * slot + j)]) = lo;
+      *(uint4*)(&sVT[voff(32 + p, 8 * slot + j)]) = hi;
     } else {
       const int p = tid & 63, r0 = 16 * (tid >> 6);
 #pragma unroll
@@ -300,13 +316,14 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
     // ---- S^T = K Q^T : 8 key tiles of 16 (tiles 0-3 previous chunk, 4-7 current) ----
     auto scores = [&](f32x4 (&acc)[8]) {
       if constexpr (BF16) {
-        const bf16x8 bq0 = *(const bf16x8*)(&sX[cur][qrow * kXRow + 8 * grp]);
-        const bf16x8 bq1 = *(const bf16x8*)(&sX[cur][qrow * kXRow + 32 + 8 * grp]);
+        const bf16x8 bq0 = *(const bf16x8*)(&sX[cur][xoff(qrow, grp)]);
+        const bf16x8 bq1 = *(const bf16x8*)(&sX[cur][xoff(qrow, 4 + grp)]);
 #pragma unroll
         for (int kt = 0; kt < 8; ++kt) {
-          const T* kr = &sX[kt < 4 ? prv : cur][(16 * (kt & 3) + col) * kXRow];
-          const bf16x8 a0 = *(const bf16x8*)(kr + 8 * grp);
-          const bf16x8 a1 = *(const bf16x8*)(kr + 32 + 8 * grp);
+          const T* kx = sX[kt < 4 ? prv : cur];
+          const int krow = 16 * (kt & 3) + col;
+          const bf16x8 a0 = *(const bf16x8*)(kx + xoff(krow, grp));
+          const bf16x8 a1 = *(const bf16x8*)(kx + xoff(krow, 4 + grp));
           f32x4 z = {0.f, 0.f, 0.f, 0.f};
           z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bq0, z, 0, 0, 0);
           acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bq1, z, 0, 0, 0);
@@ -354,10 +371,10 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
           const bf16x8 bp = __builtin_shufflevector(blo, bhi, 0, 1, 2, 3, 4, 5, 6, 7);
           const int slot = ks < 2 ? prv : cur;
           // keys of tiles 2ks and 2ks+1 seen by lane group grp: V^T columns 32 (ks & 1) + 8 grp + 0..7
-          const int vcol = 64 * slot + 32 * (ks & 1) + 8 * grp;
+          const int vpiece = 8 * slot + 4 * (ks & 1) + grp;
 #pragma unroll
           for (int dt = 0; dt < 4; ++dt) {
-            const bf16x8 a = *(const bf16x8*)(&sVT[(16 * dt + col) * kVRow + vcol]);
+            const bf16x8 a = *(const bf16x8*)(&sVT[voff(16 * dt + col, vpiece)]);
             oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bp, oacc[dt], 0, 0, 0);
           }
         }
@@ -532,21 +549,29 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
       pv(p, oacc);
     }
 
-    // ---- normalise and store: lane holds dims 16 dt + 4 grp + 0..3 of its query ----
+    // ---- normalise and store ----
     const float rs = __builtin_amdgcn_rcpf(sum);
     const size_t row_g = (size_t)c * kChunk + qrow;
     T* orow = obase + row_g * kD;
+    if constexpr (BF16) {
+      // O^T row r is V^T row r: dim 2r for r < 32, dim 2(r - 32) + 1 above.  The
+      // lane's tiles 0 and 2 hold dims 8 grp + 0..7 (even, odd interleaved), tiles
+      // 1 and 3 dims 32 + 8 grp + 0..7: two 16-byte stores.
+      uint32_t w[2][4];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const float o0 = oacc[dt][0] * rs, o1 = oacc[dt][1] * rs, o2 = oacc[dt][2] * rs, o3 = oacc[dt][3] * rs;
-      if constexpr (BF16) {
-        const bf16x2 w0 = __builtin_convertvector(f32x2{o0, o1}, bf16x2);
-        const bf16x2 w1 = __builtin_convertvector(f32x2{o2, o3}, bf16x2);
-        *(uint2*)(orow + 16 * dt + 4 * grp) =
-            make_uint2(__builtin_bit_cast(uint32_t, w0), __builtin_bit_cast(uint32_t, w1));
-      } else {
-        *(float4*)(orow + 16 * dt + 4 * grp) = make_float4(o0, o1, o2, o3);
-      }
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[h][e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                                                     f32x2{oacc[h][e] * rs, oacc[h + 2][e] * rs}, bf16x2));
+      *(uint4*)(orow + 8 * grp) = make_uint4(w[0][0], w[0][1], w[0][2], w[0][3]);
+      *(uint4*)(orow + 32 + 8 * grp) = make_uint4(w[1][0], w[1][1], w[1][2], w[1][3]);
+    } else {
+      // lane holds dims 16 dt + 4 grp + 0..3 of its query
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        *(float4*)(orow + 16 * dt + 4 * grp) =
+            make_float4(oacc[dt][0] * rs, oacc[dt][1] * rs, oacc[dt][2] * rs, oacc[dt][3] * rs);
     }
     if (grp == 0) lbase[row_g] = (off + __builtin_amdgcn_logf(sum)) * kLn2;
 
