@@ -45,8 +45,12 @@
 //   dS kn is written to LDS (bf16) and the key-owning waves of the current
 //   chunk form dQ^T = Xk^T (dS kn)^T over all 128 keys for their 16 queries,
 //   whose layout equals their own key accumulators.  The dS tile reuses the
-//   dO row and dO^T buffers (a barrier separates the uses).  fp32 inputs take
-//   the fp32 MFMA and read the transposed operands from the row copies.
+//   dO row and dO^T buffers (a barrier separates the uses).  The transposed
+//   tiles list the dims as 0, 2, .., 62, 1, 3, .., 63, so each thread writes
+//   two 16-byte pieces of consecutive rows and each lane's finished dx and dv
+//   are two contiguous 16-byte pieces.  The bf16 tiles use unpadded rows with
+//   XOR-swizzled 16-byte pieces (xoff / voff).  fp32 inputs take the fp32 MFMA
+//   and read the transposed operands from the row copies.
 #include "lsh_bwd.h"
 
 namespace lsh {
@@ -71,10 +75,10 @@ struct BwdTraits;
 template <>
 struct BwdTraits<true> {
   using T = uint16_t;
-  static constexpr int kXRow = 72;    // row copies: 64 dims + 8 pad (144 B)
-  static constexpr int kTRow = 136;   // transposed x: 2 slots x 64 + 8 pad
-  static constexpr int kQRow = 72;    // transposed dO: 64 queries + 8 pad
-  static constexpr int kSRow = 136;   // dS kn: 128 keys + 8 pad
+  static constexpr int kXRow = 64;    // row copies: 64 dims (pieces swizzled, xoff)
+  static constexpr int kTRow = 128;   // transposed x: 2 slots x 64 (pieces swizzled, voff)
+  static constexpr int kQRow = 64;    // transposed dO: 64 queries (xoff)
+  static constexpr int kSRow = 128;   // dS kn: 2 slots x 64 keys (voff)
   static constexpr int kXLoads = 2;
 };
 template <>
@@ -96,6 +100,14 @@ __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF000
 __device__ inline uint16_t to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
+
+// bf16 LDS tiles keep rows unpadded and store 16-byte piece q of row r at
+// piece q ^ (r mod pieces-per-row): the MFMA operand reads (16 lanes on 16
+// rows, the 4 lane groups on 4 pieces) and the staging writes then run at the
+// full LDS rate on gfx950 (padded 144- or 272-byte rows measured 1.6x slower
+// for those reads).  Element offsets for 128-byte and 256-byte rows:
+__device__ inline int xoff(int row, int piece) { return row * 64 + 8 * (piece ^ (row & 7)); }
+__device__ inline int voff(int row, int piece) { return row * 128 + 8 * (piece ^ (row & 15)); }
 
 // Column of chunk row r in the transposed operand layout: column 32h + 8g + 4b + e
 // holds row 32h + 16b + 4g + e.
@@ -190,6 +202,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
 
   __shared__ __attribute__((aligned(16))) T sX[2][64 * kXRow];   // x rows per ring slot
   __shared__ __attribute__((aligned(16))) T sV[2][64 * kXRow];   // v rows per ring slot
+  // transposed tiles (bf16): rows are dims in the order 0, 2, .., 62, 1, 3, .., 63
   __shared__ __attribute__((aligned(16))) T sXT[BF16 ? 64 * kTRow : 1];  // [dim][64 slot + permcol(row)]
   // dO rows + dO^T (bf16), or dO rows (fp32); the bf16 dS kn tile reuses the space.
   constexpr int kDoElems = 64 * kXRow + (BF16 ? 64 * kQRow : 0);
@@ -236,14 +249,16 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
 
   // ---- gathers (registers) and commits (LDS) ----
   // rows: thread t holds 16-byte pieces (t & 7) * kLoads + i of row t >> 3.
-  // transposed (bf16): dims 2p, 2p+1 (p = t & 31) of rows 32h + 16b + 4g + 0..3,
-  // (h, g, b) from j = t >> 5, which land in columns 32h + 8g + 4b + 0..3.
+  // transposed (bf16): threads 0-255 transpose x, threads 256-511 dO.  Thread
+  // (p, j) = (t & 31, (t >> 5) & 7) holds dims 2p, 2p+1 of rows 32h + 16b + 4g +
+  // 0..3 (h = j >> 2, g = j & 3, b = 0, 1): columns 32h + 8g + 0..7, piece j of
+  // the 64 columns; it writes them to rows p (dim 2p) and 32 + p (dim 2p + 1).
   const int prow = tid >> 3, ppc = (tid & 7) * kLoads;
-  const int tp = tid & 31, tj = tid >> 5;
-  const int trow = 32 * (tj >> 3) + 16 * (tj & 1) + 4 * ((tj >> 1) & 3);
-  const int tcol = 32 * (tj >> 3) + 8 * ((tj >> 1) & 3) + 4 * (tj & 1);
+  const int tp = tid & 31, tj = (tid >> 5) & 7;
+  const int trow = 32 * (tj >> 2) + 4 * (tj & 3);
+  const char* const tsrc = tid < 256 ? xq : dq_in;  // wave-uniform
   uint4 xr[kLoads], vr[kLoads], dr[kLoads];
-  uint32_t xw[BF16 ? 4 : 1], dw[BF16 ? 4 : 1];
+  uint32_t tw[BF16 ? 8 : 1];
   float2 ksc = make_float2(0.f, 0.f), qsw = make_float2(0.f, 0.f);
   float qlse = 0.f;
   auto gather = [&](int k) {  // entry k: its keys, and (for every entry but the first) its queries
@@ -258,11 +273,8 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
     }
     if constexpr (BF16) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t o = (uint32_t)pos[trow + e] * kRowBytes + 4u * tp;
-        xw[e] = *(const uint32_t*)(xq + o);
-        dw[e] = *(const uint32_t*)(dq_in + o);
-      }
+      for (int i = 0; i < 8; ++i)
+        tw[i] = *(const uint32_t*)(tsrc + ((uint32_t)pos[trow + (i & 3) + 16 * (i >> 2)] * kRowBytes + 4u * tp));
     }
     if (tid < 64) {
       ksc = tsb[pos[tid]];
@@ -270,32 +282,48 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
       qsw = twb[(size_t)pos[tid] * n_h + chunk / cpr];
     }
   };
-  auto commit_t = [&](T* dst, int rowlen, int base, const uint32_t (&w)[BF16 ? 4 : 1]) {
-    if constexpr (BF16) {
-      uint2 lo, hi;
-      lo.x = __builtin_amdgcn_perm(w[1], w[0], 0x05040100u);
-      lo.y = __builtin_amdgcn_perm(w[3], w[2], 0x05040100u);
-      hi.x = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);
-      hi.y = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
-      *(uint2*)(&dst[(2 * tp) * rowlen + base + tcol]) = lo;
-      *(uint2*)(&dst[(2 * tp + 1) * rowlen + base + tcol]) = hi;
-    }
-  };
   auto commit = [&](int slot, bool queries) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      *(uint4*)(&sX[slot][prow * kXRow + (ppc + i) * (16 / sizeof(T))]) = xr[i];
-      *(uint4*)(&sV[slot][prow * kXRow + (ppc + i) * (16 / sizeof(T))]) = vr[i];
+      if constexpr (BF16) {
+        *(uint4*)(&sX[slot][xoff(prow, ppc)]) = xr[i];
+        *(uint4*)(&sV[slot][xoff(prow, ppc)]) = vr[i];
+      } else {
+        *(uint4*)(&sX[slot][prow * kXRow + (ppc + i) * 4]) = xr[i];
+        *(uint4*)(&sV[slot][prow * kXRow + (ppc + i) * 4]) = vr[i];
+      }
     }
     if (tid < 64) {
       sKs2[slot][tid] = ksc.x;
       sKn[slot][tid] = ksc.y;
     }
-    if constexpr (BF16) commit_t(sXT, kTRow, 64 * slot, xw);
+    if constexpr (BF16) {
+      // low halves: dim 2p of the 8 rows in column order; high halves: dim 2p + 1
+      uint4 lo, hi;
+      lo.x = __builtin_amdgcn_perm(tw[1], tw[0], 0x05040100u);
+      lo.y = __builtin_amdgcn_perm(tw[3], tw[2], 0x05040100u);
+      lo.z = __builtin_amdgcn_perm(tw[5], tw[4], 0x05040100u);
+      lo.w = __builtin_amdgcn_perm(tw[7], tw[6], 0x05040100u);
+      hi.x = __builtin_amdgcn_perm(tw[1], tw[0], 0x07060302u);
+      hi.y = __builtin_amdgcn_perm(tw[3], tw[2], 0x07060302u);
+      hi.z = __builtin_amdgcn_perm(tw[5], tw[4], 0x07060302u);
+      hi.w = __builtin_amdgcn_perm(tw[7], tw[6], 0x07060302u);
+      if (tid < 256) {
+        *(uint4*)(&sXT[voff(tp, 8 * slot + tj)]) = lo;
+        *(uint4*)(&sXT[voff(32 + tp, 8 * slot + tj)]) = hi;
+      } else if (queries) {
+        *(uint4*)(&sDOT[xoff(tp, tj)]) = lo;
+        *(uint4*)(&sDOT[xoff(32 + tp, tj)]) = hi;
+      }
+    }
     if (queries) {
 #pragma unroll
-      for (int i = 0; i < kLoads; ++i) *(uint4*)(&sDO[prow * kXRow + (ppc + i) * (16 / sizeof(T))]) = dr[i];
-      if constexpr (BF16) commit_t(sDOT, kQRow, 0, dw);
+      for (int i = 0; i < kLoads; ++i) {
+        if constexpr (BF16)
+          *(uint4*)(&sDO[xoff(prow, ppc)]) = dr[i];
+        else
+          *(uint4*)(&sDO[prow * kXRow + (ppc + i) * 4]) = dr[i];
+      }
       if (tid < 64) {
         sLse2[tid] = qlse * kLog2e;
         sW[tid] = qsw.x;
@@ -326,6 +354,14 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
   zero_acc();
 
   for (int c = c0; c <= c1; ++c) {
+    // The lane's tile coordinates, re-derived each step from an opaque copy of the
+    // lane id: the swizzled LDS addresses built from them are then computed inside
+    // the step instead of being hoisted out of the loop, where they would hold
+    // registers across it (the kernel is at the VGPR limit).
+    int lane_v = lane;
+    asm volatile("" : "+v"(lane_v));
+    const int col = lane_v & 15, grp = lane_v >> 4;
+    const int kr = 16 * kt + col;
     const int cur = c & 1, prv = cur ^ 1;
     const int ec = c - c0 + 1;  // sPos entry of step c
     if (c < c1) gather(ec + 1);  // next step's rows, in flight during this step
@@ -381,10 +417,10 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
         }
       };
       if constexpr (BF16) {
-        const bf16x8 k0 = *(const bf16x8*)(&sX[sw][kr * kXRow + 8 * grp]);
-        const bf16x8 k1 = *(const bf16x8*)(&sX[sw][kr * kXRow + 32 + 8 * grp]);
-        const bf16x8 v0 = *(const bf16x8*)(&sV[sw][kr * kXRow + 8 * grp]);
-        const bf16x8 v1 = *(const bf16x8*)(&sV[sw][kr * kXRow + 32 + 8 * grp]);
+        const bf16x8 k0 = *(const bf16x8*)(&sX[sw][xoff(kr, grp)]);
+        const bf16x8 k1 = *(const bf16x8*)(&sX[sw][xoff(kr, 4 + grp)]);
+        const bf16x8 v0 = *(const bf16x8*)(&sV[sw][xoff(kr, grp)]);
+        const bf16x8 v1 = *(const bf16x8*)(&sV[sw][xoff(kr, 4 + grp)]);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           bf16x4 bp4[2], bs4[2];
@@ -392,10 +428,10 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
           for (int h = 0; h < 2; ++h) {
             const int qt = 2 * ks + h;
             const int qr = 16 * qt + col;
-            const bf16x8 q0 = *(const bf16x8*)(&sX[cur][qr * kXRow + 8 * grp]);
-            const bf16x8 q1 = *(const bf16x8*)(&sX[cur][qr * kXRow + 32 + 8 * grp]);
-            const bf16x8 d0 = *(const bf16x8*)(&sDO[qr * kXRow + 8 * grp]);
-            const bf16x8 d1 = *(const bf16x8*)(&sDO[qr * kXRow + 32 + 8 * grp]);
+            const bf16x8 q0 = *(const bf16x8*)(&sX[cur][xoff(qr, grp)]);
+            const bf16x8 q1 = *(const bf16x8*)(&sX[cur][xoff(qr, 4 + grp)]);
+            const bf16x8 d0 = *(const bf16x8*)(&sDO[xoff(qr, grp)]);
+            const bf16x8 d1 = *(const bf16x8*)(&sDO[xoff(qr, 4 + grp)]);
             f32x4 z = {0.f, 0.f, 0.f, 0.f};
             z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q0, k0, z, 0, 0, 0);
             const f32x4 S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q1, k1, z, 0, 0, 0);
@@ -411,13 +447,14 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
             dsk16[2 * qt] = u.x;
             dsk16[2 * qt + 1] = u.y;
           }
-          // ---- dV^T += dO^T Pw, A^T += Xq^T dS (K = queries 32 ks .. 32 ks + 31, permuted) ----
+          // ---- dV^T += dO^T Pw, A^T += Xq^T dS (K = queries 32 ks .. 32 ks + 31, permuted;
+          // rows = dims in the transposed tiles' order) ----
           const bf16x8 bp = __builtin_shufflevector(bp4[0], bp4[1], 0, 1, 2, 3, 4, 5, 6, 7);
           const bf16x8 bs = __builtin_shufflevector(bs4[0], bs4[1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
           for (int dt = 0; dt < 4; ++dt) {
-            const bf16x8 ad = *(const bf16x8*)(&sDOT[(16 * dt + col) * kQRow + 32 * ks + 8 * grp]);
-            const bf16x8 ax = *(const bf16x8*)(&sXT[(16 * dt + col) * kTRow + 64 * cur + 32 * ks + 8 * grp]);
+            const bf16x8 ad = *(const bf16x8*)(&sDOT[xoff(16 * dt + col, 4 * ks + grp)]);
+            const bf16x8 ax = *(const bf16x8*)(&sXT[voff(16 * dt + col, 8 * cur + 4 * ks + grp)]);
             acc_v[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad, bp, acc_v[dt], 0, 0, 0);
             acc_a[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bs, acc_a[dt], 0, 0, 0);
           }
@@ -485,7 +522,8 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
             const int q = 16 * qt + 4 * grp + e;
             if constexpr (BF16) {
               const uint32_t wv = dsk16[2 * qt + (e >> 1)];
-              sDS16[q * kSRow + 64 * sw + permcol(kr)] = (uint16_t)((e & 1) ? (wv >> 16) : (wv & 0xFFFFu));
+              const int kc = 64 * sw + permcol(kr);
+              sDS16[voff(q, kc >> 3) + (kc & 7)] = (uint16_t)((e & 1) ? (wv >> 16) : (wv & 0xFFFFu));
             } else {
               sDsF[q * kSRow + 64 * sw + kr] = dskf[4 * qt + e];
             }
@@ -497,11 +535,11 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
         if constexpr (BF16) {
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
-            const int kcol = 64 * (ks < 2 ? prv : cur) + 32 * (ks & 1) + 8 * grp;
-            const bf16x8 bq = *(const bf16x8*)(&sDS16[kr * kSRow + kcol]);
+            const int kp = 8 * (ks < 2 ? prv : cur) + 4 * (ks & 1) + grp;  // piece: columns 8 kp .. 8 kp + 7
+            const bf16x8 bq = *(const bf16x8*)(&sDS16[voff(kr, kp)]);
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
-              const bf16x8 a = *(const bf16x8*)(&sXT[(16 * dt + col) * kTRow + kcol]);
+              const bf16x8 a = *(const bf16x8*)(&sXT[voff(16 * dt + col, kp)]);
               acc_q[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq, acc_q[dt], 0, 0, 0);
             }
           }
@@ -527,13 +565,25 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
       const int chunk = (c - 1 + n_chunks) % n_chunks;
       const float kn = sKn[sw][kr];
       const bool tiny = kn > 0.12e12f;  // |x| at the 1e-12 floor: khat = x / 1e-12, no projection
+      // bf16: accumulator row 16 dt + 4 grp + e is dim 2 (16 dt + 4 grp + e) for dt < 2 and
+      // 2 (16 (dt - 2) + 4 grp + e) + 1 above, so tiles dt and dt + 2 hold dims 32 dt + 8 grp
+      // + 2e and + 2e + 1 (dt = 0, 1): pieces grp and 4 + grp of the key's row.  fp32: tile
+      // dt holds dims 16 dt + 4 grp + e.
       float xv[4][4];
+      if constexpr (BF16) {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        if constexpr (BF16) {
-          const uint2 r = *(const uint2*)(&sX[sw][kr * kXRow + 16 * dt + 4 * grp]);
-          xv[dt][0] = bf_lo(r.x); xv[dt][1] = bf_hi(r.x); xv[dt][2] = bf_lo(r.y); xv[dt][3] = bf_hi(r.y);
-        } else {
+        for (int h = 0; h < 2; ++h) {
+          const uint4 r = *(const uint4*)(&sX[sw][xoff(kr, 4 * h + grp)]);
+          const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xv[h][e] = bf_lo(rw[e]);
+            xv[h + 2][e] = bf_hi(rw[e]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
           const float4 r = *(const float4*)(&sX[sw][kr * kXRow + 16 * dt + 4 * grp]);
           xv[dt][0] = r.x; xv[dt][1] = r.y; xv[dt][2] = r.z; xv[dt][3] = r.w;
         }
@@ -554,46 +604,23 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
       const float proj = tiny ? 0.f : 64.f * kn * kn * dot;
       const size_t row = (size_t)chunk * kChunk + kr;
       if constexpr (BF16) {
-        // bf16 pairs: rx[dt][h] / rv[dt][h] hold dims 16 dt + 4 grp + 2h, +1
-        uint32_t rx[4][2], rv[4][2];
+        // word e of piece h: dims 32 h + 8 grp + 2e, + 1 (tiles h and h + 2)
+        uint32_t rx[2][4], rv[2][4];
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const float x0 = acc_q[dt][2 * h] + kn * (acc_a[dt][2 * h] - proj * xv[dt][2 * h]);
-            const float x1 = acc_q[dt][2 * h + 1] + kn * (acc_a[dt][2 * h + 1] - proj * xv[dt][2 * h + 1]);
-            rx[dt][h] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
-            rv[dt][h] = __builtin_bit_cast(
-                uint32_t, __builtin_convertvector(f32x2{acc_v[dt][2 * h], acc_v[dt][2 * h + 1]}, bf16x2));
+          for (int e = 0; e < 4; ++e) {
+            const float x0 = acc_q[h][e] + kn * (acc_a[h][e] - proj * xv[h][e]);
+            const float x1 = acc_q[h + 2][e] + kn * (acc_a[h + 2][e] - proj * xv[h + 2][e]);
+            rx[h][e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+            rv[h][e] = __builtin_bit_cast(uint32_t,
+                                          __builtin_convertvector(f32x2{acc_v[h][e], acc_v[h + 2][e]}, bf16x2));
           }
-        // 4 x 4 transpose over the lanes holding this key (lane groups g) and dt:
-        // afterwards lane group g holds, in slot j, dims 16 g + 4 j .. +3, so it
-        // stores 32 contiguous bytes and one instruction writes whole rows.
-        auto transpose = [](uint32_t (&r)[4][2]) {
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int d = 0; d < 2; ++d) {  // lane groups 2,3 of r[d] <-> lane groups 0,1 of r[d + 2]
-              const auto t = __builtin_amdgcn_permlane32_swap(r[d][h], r[d + 2][h], false, false);
-              r[d][h] = t[0];
-              r[d + 2][h] = t[1];
-            }
-#pragma unroll
-            for (int d = 0; d < 4; d += 2) {  // odd lane groups of r[d] <-> even lane groups of r[d + 1]
-              const auto t = __builtin_amdgcn_permlane16_swap(r[d][h], r[d + 1][h], false, false);
-              r[d][h] = t[0];
-              r[d + 1][h] = t[1];
-            }
-          }
-        };
-        transpose(rx);
-        transpose(rv);
-        T* px = dxb + row * kD + 16 * grp;
-        T* pv = dvb + row * kD + 16 * grp;
-        *(uint4*)px = make_uint4(rx[0][0], rx[0][1], rx[1][0], rx[1][1]);
-        *(uint4*)(px + 8) = make_uint4(rx[2][0], rx[2][1], rx[3][0], rx[3][1]);
-        *(uint4*)pv = make_uint4(rv[0][0], rv[0][1], rv[1][0], rv[1][1]);
-        *(uint4*)(pv + 8) = make_uint4(rv[2][0], rv[2][1], rv[3][0], rv[3][1]);
+        for (int h = 0; h < 2; ++h) {
+          *(uint4*)(dxb + row * kD + 32 * h + 8 * grp) = make_uint4(rx[h][0], rx[h][1], rx[h][2], rx[h][3]);
+          *(uint4*)(dvb + row * kD + 32 * h + 8 * grp) = make_uint4(rv[h][0], rv[h][1], rv[h][2], rv[h][3]);
+        }
       } else {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {

@@ -38,6 +38,8 @@ namespace lsh {
 
 namespace {
 
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
 __device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ inline double to_f64(uint16_t b) { return (double)bf16_to_f32(b); }
 __device__ inline double to_f64(float f) { return (double)f; }
@@ -314,7 +316,7 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
     float rho = 0.f;  // largest column norm of this round's rotation
     for (int k = 0; k < nblk; ++k) rho = fmaxf(rho, colmax[r * nblk + k]);
     const float eps_scale = 65.0f * 0x1p-23f * rho;
-    int32_t result[2];
+    int jstar[2];
     bool certified[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -326,29 +328,52 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
       const int win_h = m1[q] > pm1 ? hb : (m1[q] < pm1 ? (hb ^ 1) : 0);
       const uint32_t u = lowmask - (M1 & lowmask);  // 16 tg + e
       const int tg = (int)(u >> 4), e = (int)(u & 15);
-      const int jstar = 32 * tg + 8 * (e >> 2) + 4 * win_h + (e & 3);
+      jstar[q] = 32 * tg + 8 * (e >> 2) + 4 * win_h + (e & 3);
       const float t1 = __uint_as_float(M1 & kmask), t2 = __uint_as_float(M2 & kmask);
       const float eps = eps_scale * (sqrtf(nrm2[q]) * 1.000001f);
       const int ebits = (int)((M1 >> 23) & 0xFFu) - 23 + ibits;
       const float delta = ebits >= 1 ? __uint_as_float((uint32_t)ebits << 23) : 0x1p-126f;
       certified[q] = (t1 - t2) > 2.0f * eps + delta;
-      // Sign of the winner: its score recomputed from this lane's half of the
-      // token (the MFMA operand registers) and the partner lane's half.  When the
-      // decision is certified |score| > 2 eps, so the fp32 sign is exact.
-      const T* rr = rot_t + ((size_t)r * halfp + jstar) * kD;
-      float dp = 0.f;
-      if constexpr (BF16) {
+    }
+    // Sign of each winner: its score recomputed from this lane's half of the
+    // token (the MFMA operand registers) and the partner lane's half.  When the
+    // decision is certified |score| > 2 eps, so the fp32 sign is exact.  The
+    // rotation rows of both groups are loaded before either is used, so the
+    // round end waits for one round trip to memory, not one per load.
+    int32_t result[2];
+    if constexpr (BF16) {
+      u32x4 w[2][4];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const T* rr = rot_t + ((size_t)r * halfp + jstar[q]) * kD + 8 * hb;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) w[q][s] = *(const u32x4*)(rr + 16 * s);
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        // v_dot2c_f32_bf16: two exact bf16 products added to the fp32 sum with one
+        // rounding per step (measured), within the same error bound as the MFMA sum.
+        float dp = 0.f;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const u32x4 w = *(const u32x4*)(rr + 16 * s + 8 * hb);
           const u32x4 xb = __builtin_bit_cast(u32x4, bq16[q][s]);
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            dp = fmaf(__uint_as_float(w[k] << 16), __uint_as_float(xb[k] << 16), dp);
-            dp = fmaf(__uint_as_float(w[k] & 0xFFFF0000u), __uint_as_float(xb[k] & 0xFFFF0000u), dp);
+            // (elements copied to scalars first: a bit_cast applied directly to a
+            // vector element is lowered as element 0 by this compiler)
+            const uint32_t wk = w[q][s][k], xk = xb[k];
+            dp = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wk), __builtin_bit_cast(bf16x2, xk),
+                                                 dp, false);
           }
         }
-      } else {
+        dp += __shfl_xor(dp, 32);
+        result[q] = dp > 0.f ? jstar[q] : jstar[q] + half;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const T* rr = rot_t + ((size_t)r * halfp + jstar[q]) * kD;
+        float dp = 0.f;
 #pragma unroll
         for (int s4 = 0; s4 < 8; ++s4) {
           const float4 a4 = *(const float4*)(rr + 32 * hb + 4 * s4);
@@ -357,9 +382,9 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
           dp = fmaf(a4.z, bq32[q][4 * s4 + 2], dp);
           dp = fmaf(a4.w, bq32[q][4 * s4 + 3], dp);
         }
+        dp += __shfl_xor(dp, 32);
+        result[q] = dp > 0.f ? jstar[q] : jstar[q] + half;
       }
-      dp += __shfl_xor(dp, 32);
-      result[q] = dp > 0.f ? jstar : jstar + half;
     }
     if (wave_valid) {
       // Lanes 0-31 store group 0, lanes 32-63 group 1: 64 consecutive tokens.
