@@ -104,7 +104,7 @@ struct HashTraits;
 template <>
 struct HashTraits<true> {
   using T = uint16_t;
-  static constexpr int kRow = 72;  // LDS row stride in elements (144 B: the 32-row operand reads run at full rate)
+  static constexpr int kRow = 72;  // LDS row stride in elements (144 B, conflict-free b128 reads)
 };
 template <>
 struct HashTraits<false> {
