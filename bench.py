@@ -242,6 +242,11 @@ def main():
     tokens = B * L
     value = tokens / (elapsed / args.steps)
     log(f"{args.steps} steps: {ms_per_step:.4f} ms/step wall, {gpu_ms:.4f} ms/step between first and last event")
+    # near-ties of the hash argmax in the last step: decisions fp32 could not
+    # certify, re-decided from float64 sums
+    uncertified = bd.hash_uncertified(ws, B, H, L, n_b, n_h, qk.dtype)
+    n_decisions = B * H * n_h * L
+    log(f"hash: {uncertified} of {n_decisions} token-rounds re-decided in float64 ({uncertified / n_decisions:.2e})")
 
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
@@ -288,6 +293,7 @@ def main():
                    "n_hashes": n_h, "chunk_len": 64, "causal": w.causal},
         "roofline": roof,
         "kernels": kernels,
+        "hash_uncertified": {"token_rounds": uncertified, "of": n_decisions},
     }
     if args.attend != "none":
         result["config"]["attend"] = args.attend

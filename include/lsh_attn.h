@@ -77,6 +77,22 @@ int lsh_hash_workspace_bytes(int B, int H, int L, int D, int n_b, int n_h, lsh_d
 int lsh_hash(const void* qk, const void* rot, int32_t* buckets, int B, int H, int L, int D,
              int n_b, int n_h, lsh_dtype dt, void* ws, size_t ws_bytes, void* stream);
 
+/* How many token-rounds the last hashing on this workspace could not certify in
+ * fp32 and re-decided from float64 sums: the near-ties of the argmax, counted
+ * by the GPU (same decision rule as lsh_hash above).
+ *   ws      the workspace of the last lsh_hash or reformer_lsh_attn_fwd /
+ *           _fwd_ex / _fwd_train call (the hashing part sits at the start of
+ *           both layouts), called with the same B, H, L, n_b, n_h and dt;
+ *           ws_bytes its size.
+ *   count   out (host memory): the count; 0 when n_b == 1 or the problem is
+ *           empty.
+ * Waits for the work queued on stream, then copies one int from the device.
+ * Errors: LSH_ERR_NULL (count NULL), the shape / bucket / dtype errors of
+ * lsh_hash, LSH_ERR_WORKSPACE (ws NULL or smaller than the hashing part),
+ * LSH_ERR_HIP (the copy failed). */
+int lsh_hash_uncertified(const void* ws, size_t ws_bytes, int B, int H, int L, int n_b, int n_h,
+                         lsh_dtype dt, int* count, void* stream);
+
 /* Step 2, sort by (round, bucket, position) (explainer page: sort by bucket).
  *   buckets    [B, H, n_h, L]  input, values in [0, n_b) (not checked on device).
  *   sorted_idx [B, H, n_h*L]   out: slot g = r*L + k holds the original position

@@ -32,6 +32,7 @@ _SIGS = {
     "lsh_status_string": (ctypes.c_char_p, [_c_int]),
     "lsh_hash_workspace_bytes": (_c_int, [_c_int] * 7 + [ctypes.POINTER(_c_size)]),
     "lsh_hash": (_c_int, [_vp, _vp, _vp] + [_c_int] * 7 + [_vp, _c_size, _vp]),
+    "lsh_hash_uncertified": (_c_int, [_vp, _c_size] + [_c_int] * 6 + [ctypes.POINTER(_c_int), _vp]),
     "lsh_sort_workspace_bytes": (_c_int, [_c_int] * 5 + [ctypes.POINTER(_c_size)]),
     "lsh_sort": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [_vp, _c_size, _vp]),
     "lsh_chunk_attn": (_c_int, [_vp] * 5 + [_c_int] * 8 + [_vp]),
@@ -91,12 +92,16 @@ def _check(fn: str, status: int):
         raise LshError(fn, status)
 
 
-def _dtype_code(t: torch.Tensor) -> int:
-    if t.dtype == torch.bfloat16:
+def _dtype_code_of(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
         return LSH_BF16
-    if t.dtype == torch.float32:
+    if dtype == torch.float32:
         return LSH_F32
-    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    raise TypeError(f"unsupported dtype {dtype} (float32 or bfloat16)")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    return _dtype_code_of(t.dtype)
 
 
 def _dev(*ts):
@@ -142,19 +147,34 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 
 
 def lsh_hash(qk: torch.Tensor, rot: torch.Tensor | None, n_buckets: int, n_hashes: int,
-             buckets: torch.Tensor | None = None) -> torch.Tensor:
-    """qk [B,H,L,D], rot [n_h,D,n_b/2] (or None when n_b == 1) -> buckets int32 [B,H,n_h,L]."""
-    _dev(qk, rot, buckets)
+             buckets: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """qk [B,H,L,D], rot [n_h,D,n_b/2] (or None when n_b == 1) -> buckets int32 [B,H,n_h,L].
+    `workspace` (uint8, at least hash_workspace_bytes) may be passed in, e.g. to read
+    hash_uncertified afterwards."""
+    _dev(qk, rot, buckets, workspace)
     B, H, L, D = qk.shape
     dt = _dtype_code(qk)
     if rot is not None and rot.dtype != qk.dtype:
         raise TypeError("rot must have the dtype of qk")
     if buckets is None:
         buckets = torch.empty((B, H, n_hashes, L), dtype=torch.int32, device=qk.device)
-    ws = _workspace(hash_workspace_bytes(B, H, L, D, n_buckets, n_hashes, dt), qk.device)
+    ws = workspace if workspace is not None else _workspace(
+        hash_workspace_bytes(B, H, L, D, n_buckets, n_hashes, dt), qk.device)
     _check("lsh_hash", lib().lsh_hash(qk.data_ptr(), _ptr(rot), buckets.data_ptr(), B, H, L, D, n_buckets, n_hashes,
                                       dt, ws.data_ptr(), ws.numel(), _stream(qk.device)))
     return buckets
+
+
+def hash_uncertified(workspace: torch.Tensor, B: int, H: int, L: int, n_buckets: int, n_hashes: int,
+                     dtype: torch.dtype) -> int:
+    """Token-rounds the last hashing on `workspace` (of lsh_hash or the fused forward,
+    same shapes) re-decided from float64 sums because fp32 could not certify them."""
+    _dev(workspace)
+    n = _c_int(0)
+    _check("lsh_hash_uncertified", lib().lsh_hash_uncertified(
+        workspace.data_ptr(), workspace.numel(), B, H, L, n_buckets, n_hashes, _dtype_code_of(dtype), ctypes.byref(n),
+        _stream(workspace.device)))
+    return int(n.value)
 
 
 def lsh_sort(buckets: torch.Tensor, n_buckets: int):

@@ -82,7 +82,7 @@ FwdWs fwd_ws(int BH, int L, int n_b, int n_h, lsh_dtype dt) {
   FwdWs w;
   const size_t slots = (size_t)BH * n_h * L;
   w.hash = hash_ws(BH, L, n_b, n_h, dt);
-  w.hash_base = c.take(w.hash.total);
+  w.hash_base = c.take(w.hash.total);  // first: lsh_hash_uncertified reads it at offset 0
   w.sort_base = c.take(sort_ws_bytes(BH, L, n_b, n_h));
   w.buckets = c.take(slots * sizeof(int32_t));
   w.sorted_idx = c.take(slots * sizeof(int32_t));
@@ -237,6 +237,26 @@ int lsh_hash(const void* qk, const void* rot, int32_t* buckets, int B, int H, in
   int k = 0;
   return hip_status(enqueue_hash(qk, rot, buckets, nullptr, (char*)ws, w, BH, L, n_b, n_h, dt,
                                  (hipStream_t)stream, nullptr, &k));
+}
+
+int lsh_hash_uncertified(const void* ws, size_t ws_bytes, int B, int H, int L, int n_b, int n_h, lsh_dtype dt,
+                         int* count, void* stream) {
+  if (count == nullptr) return LSH_ERR_NULL;
+  int st = check_problem(B, H, L, kD, n_h);
+  if (st == LSH_OK) st = check_buckets(n_b, L);
+  if (st == LSH_OK && !dtype_ok(dt)) st = LSH_ERR_UNSUPPORTED;
+  if (st != LSH_OK) return st;
+  *count = 0;
+  if (is_empty(B, H, L) || n_b == 1) return LSH_OK;
+  const HashWs w = hash_ws(B * H, L, n_b, n_h, dt);  // at offset 0 of the hash and forward workspaces
+  if (ws == nullptr || ws_bytes < w.total) return LSH_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  int v = 0;
+  if (hipMemcpyAsync(&v, (const char*)ws + w.fix_count, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return LSH_ERR_HIP;
+  *count = v;
+  return LSH_OK;
 }
 
 int lsh_sort_workspace_bytes(int B, int H, int L, int n_b, int n_h, size_t* bytes) {

@@ -117,6 +117,26 @@ def test_stage_calls_reject_before_launch(L):
     assert L.lsh_event_elapsed_ms(None, None, None) == NULL
 
 
+def test_uncertified_count_rejects_before_copy(L):
+    n = ctypes.c_int(7)
+    st, hws = _ws("lsh_hash_workspace_bytes", 1, 1, 256, 64, 16, 2, BF16)
+    assert st == OK
+    assert L.lsh_hash_uncertified(P1, hws, 1, 1, 256, 16, 2, BF16, None, None) == NULL
+    assert L.lsh_hash_uncertified(P1, hws - 1, 1, 1, 256, 16, 2, BF16, ctypes.byref(n), None) == WORKSPACE
+    assert L.lsh_hash_uncertified(None, hws, 1, 1, 256, 16, 2, BF16, ctypes.byref(n), None) == WORKSPACE
+    assert L.lsh_hash_uncertified(P1, hws, 1, 1, 256, 15, 2, BF16, ctypes.byref(n), None) == BUCKETS
+    assert L.lsh_hash_uncertified(P1, hws, 1, 1, 256, 16, 0, BF16, ctypes.byref(n), None) == SHAPE
+    assert L.lsh_hash_uncertified(P1, hws, 1, 1, 256, 16, 2, 9, ctypes.byref(n), None) == UNSUPPORTED
+    # nothing is hashed for one bucket or an empty problem: the count is 0 and no
+    # workspace is read
+    assert L.lsh_hash_uncertified(None, 0, 1, 1, 256, 1, 2, BF16, ctypes.byref(n), None) == OK and n.value == 0
+    n.value = 7
+    assert L.lsh_hash_uncertified(None, 0, 0, 1, 256, 16, 2, BF16, ctypes.byref(n), None) == OK and n.value == 0
+    # the forward workspace starts with the hashing part, so it always suffices
+    st, fws = _ws("lsh_fwd_workspace_bytes", 1, 1, 256, 64, 16, 2, 64, BF16)
+    assert st == OK and fws >= hws
+
+
 @pytest.mark.parametrize("B,H,n", [(0, 1, 64), (1, 0, 64), (1, 1, 0), (0, 0, 0)])
 def test_empty_problems_are_no_ops(L, B, H, n):
     # Zero-sized problems succeed without touching any pointer (all NULL here)

@@ -151,6 +151,78 @@ def test_every_token_needs_the_exact_path(gpu_lib):
     assert np.all(got % 2 == 0)  # the lower index of each identical pair
 
 
+def _uncertified_bracket(x64, rot64):
+    """Bounds on the number of token-rounds the GPU cannot certify, from exact
+    (float64) scores of one problem.  The kernel certifies a decision when its
+    fp32 top-two gap of truncated keys exceeds 2 eps + delta, eps = 65 2^-23 |x|
+    max_j |r_j| bounding a 64-term fp32 sum's error and delta = 2^(e - 23 +
+    ibits) the key's truncation step (e = exponent of the top score, 2^ibits >=
+    columns per lane).  The computed gap lies within 2 eps + delta of the exact
+    one, so an exact tie is never certified and an exact gap above 4 eps +
+    2 delta always is."""
+    n_h, _, half = rot64.shape
+    halfp = -(-half // 64) * 64
+    ibits = 0
+    while (1 << ibits) < halfp // 2:
+        ibits += 1
+    xn = np.linalg.norm(x64, axis=1)
+    lo = hi = 0
+    for r in range(n_h):
+        a = np.zeros((x64.shape[0], max(halfp, 2)))
+        a[:, :half] = np.abs(x64 @ rot64[r])        # padded columns score 0
+        top = np.sort(a, axis=1)[:, -2:]
+        t1, gap = top[:, 1], top[:, 1] - top[:, 0]
+        eps = 65 * 2.0**-23 * xn * np.max(np.linalg.norm(rot64[r], axis=0)) * 1.0001
+        with np.errstate(divide="ignore"):
+            e = np.floor(np.log2(t1 + eps))
+        delta = np.where(t1 + eps > 0, 2.0 ** (e - 23 + ibits), 2.0**-126)
+        lo += int(np.sum(gap == 0))
+        hi += int(np.sum(gap <= 4 * eps + 2 * delta))
+    return lo, hi
+
+
+@pytest.mark.parametrize("name,shape,n_h", REDUCED, ids=[f"{n}-h{h}" for n, _, h in REDUCED])
+def test_uncertified_count_is_bracketed(gpu_lib, name, shape, n_h):
+    """The GPU's count of float64 re-decisions (lsh_hash_uncertified) lies between
+    the exact ties and the exact gaps within the certification band, and the
+    fused forward counts the same decisions as the staged hash."""
+    inp = I.make_inputs(name, n_hashes=n_h, **shape)
+    w = inp.workload
+    B, H, L, D = inp.qk.values.shape
+    qk, v, rot = upload(inp)
+    say(f"case {name} B{B} H{H} L{L} n_b{w.n_buckets} n_h{n_h}")
+    dt = bd.LSH_BF16 if qk.dtype == torch.bfloat16 else bd.LSH_F32
+    ws = torch.empty(bd.hash_workspace_bytes(B, H, L, D, w.n_buckets, n_h, dt), dtype=torch.uint8, device="cuda")
+    bd.lsh_hash(qk, rot, w.n_buckets, n_h, workspace=ws)
+    got = bd.hash_uncertified(ws, B, H, L, w.n_buckets, n_h, qk.dtype)
+    lo = hi = 0
+    rot64 = inp.rot.values.astype(np.float64)
+    for b in range(B):
+        for h in range(H):
+            l, u = _uncertified_bracket(inp.qk.values[b, h].astype(np.float64), rot64)
+            lo, hi = lo + l, hi + u
+    say(f"  uncertified {got} of {B * H * n_h * L} token-rounds; exact bracket [{lo}, {hi}]")
+    assert lo <= got <= hi
+    fws = torch.empty(bd.fwd_workspace_bytes(B, H, L, D, w.n_buckets, n_h, 64, dt), dtype=torch.uint8,
+                      device="cuda")
+    bd.reformer_lsh_attn_fwd(qk, v, rot, w.n_buckets, n_h, 64, w.causal, workspace=fws)
+    assert bd.hash_uncertified(fws, B, H, L, w.n_buckets, n_h, qk.dtype) == got
+
+
+def test_all_tied_rounds_are_all_counted(gpu_lib):
+    """With every rotation column duplicated, no decision can be certified: the
+    count is every token-round."""
+    rng = np.random.default_rng(8)
+    half, n_h, B, H, L = 64, 2, 2, 2, 576
+    rot = np.repeat(rng.standard_normal((n_h, 64, half // 2)).astype(np.float32), 2, axis=2)
+    rt = I.Tensor(I.f32_from_bf16_bits(I.bf16_bits_from_f32(rot)), I.bf16_bits_from_f32(rot))
+    xt = I.gaussian(9, (B, H, L, 64), "bf16")
+    ws = torch.empty(bd.hash_workspace_bytes(B, H, L, 64, 2 * half, n_h, bd.LSH_BF16), dtype=torch.uint8,
+                     device="cuda")
+    bd.lsh_hash(to_device(xt), to_device(rt), 2 * half, n_h, workspace=ws)
+    assert bd.hash_uncertified(ws, B, H, L, 2 * half, n_h, torch.bfloat16) == B * H * n_h * L
+
+
 @pytest.mark.parametrize("n_b,n_h,L", [(2, 1, 64), (4096, 2, 4096), (8, 16, 128), (64, 1, 64)])
 def test_extreme_bucket_and_round_counts(gpu_lib, n_b, n_h, L):
     say(f"case extremes n_b{n_b} n_h{n_h} L{L}")
