@@ -77,3 +77,36 @@ def test_full_size(gpu_lib, name, n_h):
         rel_check(f64(out_f[b, h, ti]), ref_o, tol, f"fused out b{b} h{h}")
         lse_check(f64(lse_f[b, h, ti]), ref_l, f"fused lse b{b} h{h}")
     say("  sampled chunks and tokens within tolerance")
+
+
+def test_peaked_recall_from_the_gpu_permutation(gpu_lib):
+    """The peaked-attention workload at full size (B4 H8 L16384, 256 vMF clusters,
+    n_b 256) with 2 and 8 rounds: recall of each sampled query's 16 nearest keys
+    and the share of its exact (full) attention weight that fall inside the
+    windows the GPU's permutation gives it.  Both are printed; the windows of 8
+    rounds must catch at least as much as those of 2 (the 8-round rotations do
+    not extend the 2-round ones, so this is compared on the means over the
+    sampled problems and queries, with a small allowance).  The workload's points
+    lie on the unit sphere, so every logit is within 1/8 of 0 and the exact
+    attention is nearly uniform: the mass share is about the windows' share of
+    the keys."""
+    res = {}
+    for n_h in (2, 8):
+        inp = I.make_inputs("peaked_vmf_16k", n_hashes=n_h)
+        w = inp.workload
+        B, H, L, D = inp.qk.values.shape
+        say(f"recall case peaked_vmf_16k n_h{n_h} B{B} H{H} L{L} n_b{w.n_buckets}")
+        qk, v, rot = upload(inp)
+        sidx, undo = bd.lsh_sort(bd.lsh_hash(qk, rot, w.n_buckets, n_h), w.n_buckets)
+        torch.cuda.synchronize()
+        gs, gu = sidx.cpu().numpy().astype(np.int64), undo.cpu().numpy().astype(np.int64)
+        r_k, r_m = [], []
+        for b, h in [(0, 0), (1, 3), (3, 7)]:
+            x64 = inp.qk.values[b, h].astype(np.float64)
+            q = np.random.default_rng(1000 + 10 * b + h).choice(L, 64, replace=False)
+            r_k.append(O.recall_at_k(x64, gs[b, h], gu[b, h], 64, q, 16))
+            r_m.append(O.attention_mass_recall(x64, gs[b, h], gu[b, h], 64, q))
+        res[n_h] = (float(np.mean(r_k)), float(np.mean(r_m)))
+        say(f"  n_h {n_h}: recall@16 {res[n_h][0]:.3f}, attention mass in the windows {res[n_h][1]:.3f}")
+    assert 0.0 < res[2][0] <= 1.0 and 0.0 < res[8][0] <= 1.0
+    assert res[8][0] >= res[2][0] - 0.02 and res[8][1] >= res[2][1] - 0.02
