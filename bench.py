@@ -112,6 +112,24 @@ def measured_traffic(workload: str, kernel: str, attend: str = "none"):
     return rec["traffic_bytes"]
 
 
+def hbm_copy_gbs(nbytes: int = 1 << 30, reps: int = 5) -> float:
+    """Achievable HBM bandwidth: read + write bytes of a plain 1 GiB device copy
+    per second (reported beside the datasheet peak, not instead of it)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    del src, dst
+    return 2.0 * nbytes * reps / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(inp, min_seconds: float = 10.0):
     """The oracle, untouched, on a bounded sample: whole (batch, head) problems
     of the same workload at full length, one after another until at least
@@ -254,6 +272,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    copy_gbs = hbm_copy_gbs()
+    log(f"plain device copy: {copy_gbs:.0f} GB/s (read + write), {copy_gbs / HBM_PEAK_GBS:.3f} of the HBM peak")
 
     work = algorithmic_work(B, H, L, D, n_b, n_h, es, same_bucket, dedup)
     peak_flops = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
@@ -294,6 +314,8 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "hash_uncertified": {"token_rounds": uncertified, "of": n_decisions},
+        "hbm_copy": {"GBps": round(copy_gbs, 1), "frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
+                     "what": "1 GiB device-to-device copy, read + write bytes"},
     }
     if args.attend != "none":
         result["config"]["attend"] = args.attend
