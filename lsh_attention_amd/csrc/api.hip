@@ -170,7 +170,7 @@ hipError_t enqueue_hash(const void* qk, const void* rot, int32_t* buckets, float
       hipSuccess)
     return e;
   if ((e = mark()) != hipSuccess) return e;
-  if ((e = launch_fixup(qk, rot_t, buckets, queue, count, L, n_b, n_h, dt, s)) != hipSuccess) return e;
+  if ((e = launch_fixup(qk, rot_t, colmax, buckets, queue, count, L, n_b, n_h, dt, s)) != hipSuccess) return e;
   return mark();
 }
 

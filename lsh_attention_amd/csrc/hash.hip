@@ -406,23 +406,60 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
 
 
 // ---------------------------------------------------------------------------
-// Float64 re-decision of queued tokens: one wave per token-round, lane l scores
-// the rotation columns l, l + 64, ... as float64 sums of exact products (from
-// the transposed rotation, one contiguous row per column), then a wave argmax
-// with the lowest index on ties.  Grid-stride over the queue.
+// Float64 re-decision of queued tokens, one wave per token-round (grid-stride
+// over the queue), in two phases.
+//  1. fp32 scores of every column, within the certification's eps of the exact
+//     ones.  The wave reads the round's transposed rotation front to back with
+//     each load instruction covering whole rows: lane l holds 16-byte piece
+//     l % P of row (64 / P) i + l / P (P pieces per row), so an instruction
+//     touches 64 / P cache lines, not 64 as a column per lane would.  A batch of
+//     P instructions covers 64 rows; a reduce-scatter over the P lanes of a row
+//     finishes the sums, leaving lane l row (64 / P)(l % P) + l / P of the batch.
+//  2. The exact argmax lies among the columns whose fp32 score is within 2 eps
+//     (plus a denormal allowance) of the best one: each is scored as a float64
+//     sum of exact products by the whole wave (lane d holds element d), lowest
+//     index on equal values.  More candidates than kMaxCand (tied or
+//     degenerate inputs): every column in float64, lane-parallel.
 // ---------------------------------------------------------------------------
+constexpr int kMaxCand = 8;
+constexpr int kFixWaves = 4;
+constexpr int kMaxHalfp = 2048;
+static_assert(kMaxHalfp >= kMaxBuckets / 2 && kMaxHalfp % 64 == 0, "score slots for the largest n_b");
+
+// fp32 dot product of one 16-byte piece of x and of a rotation row.
+__device__ inline float piece_dot(const uint4& a, const uint4& b, uint16_t) {
+  const uint32_t xa[4] = {a.x, a.y, a.z, a.w}, ra[4] = {b.x, b.y, b.z, b.w};
+  float acc = 0.f;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const uint32_t xw = xa[h], rw = ra[h];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xw), __builtin_bit_cast(bf16x2, rw), acc, false);
+  }
+  return acc;
+}
+__device__ inline float piece_dot(const uint4& a, const uint4& b, float) {
+  float acc = __uint_as_float(a.x) * __uint_as_float(b.x);
+  acc = fmaf(__uint_as_float(a.y), __uint_as_float(b.y), acc);
+  acc = fmaf(__uint_as_float(a.z), __uint_as_float(b.z), acc);
+  return fmaf(__uint_as_float(a.w), __uint_as_float(b.w), acc);
+}
+
 template <typename T>
-__global__ __launch_bounds__(256) void fixup_kernel(const T* __restrict__ qk, const T* __restrict__ rot_t,
-                                                    int32_t* __restrict__ buckets,
-                                                    const int* __restrict__ fix_queue,
-                                                    const int* __restrict__ fix_count, int L, int n_h,
-                                                    int half, int halfp) {
-  constexpr int kPer = 16 / sizeof(T);   // elements per 16-byte load
-  constexpr int kLoads = kD / kPer;      // 16-byte loads per 64-element row
+__global__ __launch_bounds__(kFixWaves * 64) void fixup_kernel(const T* __restrict__ qk,
+                                                               const T* __restrict__ rot_t,
+                                                               const float* __restrict__ colmax,
+                                                               int32_t* __restrict__ buckets,
+                                                               const int* __restrict__ fix_queue,
+                                                               const int* __restrict__ fix_count, int L, int n_h,
+                                                               int half, int halfp) {
+  constexpr int P = kD * (int)sizeof(T) / 16;  // 16-byte pieces per row
+  __shared__ float ssc[kFixWaves][kMaxHalfp];  // |fp32 score|, slot 64 g + lane of batch g
   const int lane = threadIdx.x & 63;
+  float* sc = ssc[threadIdx.x >> 6];
   const int gw = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int nw = (gridDim.x * blockDim.x) >> 6;
   const int count = *fix_count;
+  const int nbatch = halfp >> 6;  // also the 64-column blocks of colmax
   for (int it = gw; it < count; it += nw) {
     const int idx = fix_queue[it];
     const int tok = idx % L;
@@ -430,34 +467,107 @@ __global__ __launch_bounds__(256) void fixup_kernel(const T* __restrict__ qk, co
     const int r = br % n_h;
     const int bh = br / n_h;
     const T* x = qk + ((size_t)bh * L + tok) * kD;
-    uint4 xr[kLoads];
-    for (int k = 0; k < kLoads; ++k) xr[k] = *(const uint4*)(x + k * kPer);
-    const T* xe = (const T*)xr;
+    const uint4 xp = ((const uint4*)x)[lane % P];
+    const double xd = to_f64(x[lane]);
+    const uint4* R4 = (const uint4*)(rot_t + (size_t)r * halfp * kD);
+    float rho = 0.f;  // largest column norm of the round (rounded up)
+    for (int k = 0; k < nbatch; ++k) rho = fmaxf(rho, colmax[r * nbatch + k]);
+    // Phase 1.
+    float m = 0.f;
+    for (int g = 0; g < nbatch; ++g) {
+      uint4 rw[P];
+#pragma unroll
+      for (int i = 0; i < P; ++i) rw[i] = R4[(size_t)64 * (P * g + i) + lane];
+      float V[P];
+#pragma unroll
+      for (int i = 0; i < P; ++i) V[i] = piece_dot(xp, rw[i], T());
+#pragma unroll
+      for (int h = P / 2; h >= 1; h >>= 1) {
+        const bool up = (lane & h) != 0;  // keep the upper half of the batch's rows
+#pragma unroll
+        for (int i = 0; i < h; ++i) {
+          const float send = up ? V[i] : V[i + h], keep = up ? V[i + h] : V[i];
+          V[i] = keep + __shfl_xor(send, h);
+        }
+      }
+      const int row = 64 * g + (64 / P) * (lane % P) + lane / P;
+      const float a = fabsf(V[0]);
+      sc[64 * g + lane] = row < half ? a : -INFINITY;
+      m = row < half ? fmaxf(m, a) : m;
+    }
+    float n2 = piece_dot(xp, xp, T());
+#pragma unroll
+    for (int h = 1; h < P; h <<= 1) n2 += __shfl_xor(n2, h);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    // Each fp32 score passes through at most 8 roundings (4 in the piece, up to
+    // 4 in the reduction): far inside eps.  A flushed denormal product errs by at
+    // most 2^-126, 64 of them by 2^-120, for each of the two scores compared.
+    const float eps = 65.0f * 0x1p-23f * rho * (sqrtf(n2) * 1.00001f);
+    const double thr64 = (double)m - (2.0 * (double)eps + 0x1p-118);
+    float thr = (float)thr64;
+    if ((double)thr > thr64) thr = nextafterf(thr, -INFINITY);
+    uint32_t mask = 0;  // bit g: this lane's row of batch g is a candidate
+    for (int g = 0; g < nbatch; ++g) mask |= (sc[64 * g + lane] >= thr ? 1u : 0u) << g;
+    // Phase 2.
+    int cj[kMaxCand];
+#pragma unroll
+    for (int c = 0; c < kMaxCand; ++c) {
+      const uint64_t bal = __ballot(mask != 0);
+      if (bal == 0) {
+        cj[c] = -1;
+        continue;
+      }
+      const int src = __builtin_ctzll(bal);
+      const uint32_t ms = __shfl(mask, src);
+      cj[c] = 64 * __builtin_ctz(ms) + (64 / P) * (src % P) + src / P;
+      if (lane == src) mask &= mask - 1u;
+    }
+    const bool overflow = __ballot(mask != 0) != 0;
     double best_v = -1.0;
     int best_i = 0x7FFFFFFF;
-    for (int j = lane; j < half; j += 64) {
-      const T* rr = rot_t + ((size_t)r * halfp + j) * kD;
-      uint4 rw[kLoads];
-      for (int k = 0; k < kLoads; ++k) rw[k] = *(const uint4*)(rr + k * kPer);
-      const T* re = (const T*)rw;
-      double p = 0.0;
-      for (int d = 0; d < kD; ++d) p = fma(to_f64(xe[d]), to_f64(re[d]), p);
-      const double v = fabs(p);
-      const int i = p < 0.0 ? j + half : j;  // the larger of +p (index j) and -p (index j + half)
-      if (v > best_v || (v == best_v && i < best_i)) {
-        best_v = v;
-        best_i = i;
+    if (!overflow) {
+      T rv[kMaxCand];
+#pragma unroll
+      for (int c = 0; c < kMaxCand; ++c) rv[c] = cj[c] >= 0 ? rot_t[((size_t)r * halfp + cj[c]) * kD + lane] : T(0);
+#pragma unroll
+      for (int c = 0; c < kMaxCand; ++c) {
+        if (cj[c] < 0) break;
+        double p = xd * to_f64(rv[c]);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) p += __shfl_xor(p, off);
+        const double v = fabs(p);
+        const int i = p < 0.0 ? cj[c] + half : cj[c];  // the larger of +p (index j) and -p (index j + half)
+        if (v > best_v || (v == best_v && i < best_i)) {
+          best_v = v;
+          best_i = i;
+        }
+      }
+    } else {
+      // x re-read from memory (cached) to keep this rare path's registers low
+      for (int j = lane; j < half; j += 64) {
+        const T* rr = rot_t + ((size_t)r * halfp + j) * kD;
+        double p = 0.0;
+        for (int d = 0; d < kD; ++d) p = fma(to_f64(x[d]), to_f64(rr[d]), p);
+        const double v = fabs(p);
+        const int i = p < 0.0 ? j + half : j;
+        if (v > best_v || (v == best_v && i < best_i)) {
+          best_v = v;
+          best_i = i;
+        }
+      }
+      for (int off = 32; off >= 1; off >>= 1) {
+        const double ov = __shfl_xor(best_v, off);
+        const int oi = __shfl_xor(best_i, off);
+        if (ov > best_v || (ov == best_v && oi < best_i)) {
+          best_v = ov;
+          best_i = oi;
+        }
       }
     }
-    for (int off = 32; off >= 1; off >>= 1) {
-      const double ov = __shfl_xor(best_v, off);
-      const int oi = __shfl_xor(best_i, off);
-      if (ov > best_v || (ov == best_v && oi < best_i)) {
-        best_v = ov;
-        best_i = oi;
-      }
-    }
-    if (lane == 0) buckets[idx] = best_i;
+    // With finite inputs the best fp32 score is always a candidate; non-finite
+    // ones leave the first pass's decision in place.
+    if (lane == 0 && best_i != 0x7FFFFFFF) buckets[idx] = best_i;
   }
 }
 
@@ -498,15 +608,17 @@ hipError_t launch_hash(const void* qk, const void* rot_t, const float* colmax, i
   return hipGetLastError();
 }
 
-hipError_t launch_fixup(const void* qk, const void* rot_t, int32_t* buckets, const int* fix_queue,
-                        const int* fix_count, int L, int n_b, int n_h, lsh_dtype dt, hipStream_t s) {
+hipError_t launch_fixup(const void* qk, const void* rot_t, const float* colmax, int32_t* buckets,
+                        const int* fix_queue, const int* fix_count, int L, int n_b, int n_h, lsh_dtype dt,
+                        hipStream_t s) {
   const int half = n_b / 2, halfp = padded_half(n_b);
+  if (halfp > kMaxHalfp) return hipErrorInvalidValue;
   if (dt == LSH_BF16)
-    fixup_kernel<uint16_t><<<512, 256, 0, s>>>((const uint16_t*)qk, (const uint16_t*)rot_t, buckets, fix_queue,
-                                               fix_count, L, n_h, half, halfp);
+    fixup_kernel<uint16_t><<<1024, kFixWaves * 64, 0, s>>>((const uint16_t*)qk, (const uint16_t*)rot_t, colmax,
+                                                          buckets, fix_queue, fix_count, L, n_h, half, halfp);
   else
-    fixup_kernel<float><<<512, 256, 0, s>>>((const float*)qk, (const float*)rot_t, buckets, fix_queue, fix_count,
-                                            L, n_h, half, halfp);
+    fixup_kernel<float><<<1024, kFixWaves * 64, 0, s>>>((const float*)qk, (const float*)rot_t, colmax, buckets,
+                                                       fix_queue, fix_count, L, n_h, half, halfp);
   return hipGetLastError();
 }
 

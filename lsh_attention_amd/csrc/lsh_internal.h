@@ -67,8 +67,8 @@ hipError_t launch_prep(const void* rot, void* rot_t, float* colmax, int* fix_cou
 hipError_t launch_hash(const void* qk, const void* rot_t, const float* colmax, int32_t* buckets,
                        int* fix_queue, int* fix_count, float2* token_scales, int BH, int L, int n_b,
                        int n_h, lsh_dtype dt, hipStream_t s);
-hipError_t launch_fixup(const void* qk, const void* rot_t, int32_t* buckets, const int* fix_queue,
-                        const int* fix_count, int L, int n_b, int n_h, lsh_dtype dt,
+hipError_t launch_fixup(const void* qk, const void* rot_t, const float* colmax, int32_t* buckets,
+                        const int* fix_queue, const int* fix_count, int L, int n_b, int n_h, lsh_dtype dt,
                         hipStream_t s);
 hipError_t launch_fill_zero(int32_t* p, size_t n, hipStream_t s);
 
