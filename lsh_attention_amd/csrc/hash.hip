@@ -62,30 +62,54 @@ template <typename T>
 __global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ rot, T* __restrict__ rot_t,
                                                    float* __restrict__ colmax, int* __restrict__ fix_count,
                                                    int half, int halfp, int nblk) {
+  constexpr int kPer = 16 / sizeof(T);  // elements per 16-byte piece
+  constexpr int kPieces = kD / kPer;    // pieces per transposed row
   __shared__ T tile[kD][65];
   __shared__ double red[4];
+  const int tid = threadIdx.x;
   const int r = blockIdx.x / nblk, blk = blockIdx.x % nblk, j0 = blk * 64;
   const T* R = rot + (size_t)r * kD * half;
-  for (int idx = threadIdx.x; idx < kD * 64; idx += blockDim.x) {
-    const int d = idx >> 6, jj = idx & 63;
-    tile[d][jj] = (j0 + jj < half) ? R[(size_t)d * half + j0 + jj] : T(0);
-  }
+  // 64 x 64 elements, 16 per thread (column tid % 64, rows tid / 64 + 4 k), all
+  // loads issued before the first is used.
+  const int jj = tid & 63, d0 = tid >> 6;
+  const bool in = j0 + jj < half;
+  T v[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) v[k] = in ? R[(size_t)(d0 + 4 * k) * half + j0 + jj] : T(0);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) tile[d0 + 4 * k][jj] = v[k];
   __syncthreads();
+  // Transposed rows written as 16-byte pieces, consecutive threads on
+  // consecutive pieces.
   T* RT = rot_t + ((size_t)r * halfp + j0) * kD;
-  for (int idx = threadIdx.x; idx < kD * 64; idx += blockDim.x) {
-    const int jj = idx >> 6, d = idx & 63;
-    if (j0 + jj < halfp) RT[(size_t)jj * kD + d] = tile[d][jj];
+#pragma unroll
+  for (int k = 0; k < 64 * kPieces / 256; ++k) {
+    const int q = tid + 256 * k, row = q / kPieces, pc = q % kPieces;
+    union {
+      T e[kPer];
+      uint4 u;
+    } piece;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) piece.e[i] = tile[kPer * pc + i][row];
+    if (j0 + row < halfp) *(uint4*)(RT + (size_t)row * kD + kPer * pc) = piece.u;
   }
-  double nrm = 0.0;
-  if (threadIdx.x < 64)
-    for (int d = 0; d < kD; ++d) {
-      const double f = to_f64(tile[d][threadIdx.x]);
-      nrm = fma(f, f, nrm);
-    }
-  for (int off = 32; off >= 1; off >>= 1) nrm = fmax(nrm, __shfl_xor(nrm, off));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = nrm;
+  // Column norms in float64, four threads per column (16 rows each), then the
+  // block's largest.
+  const int c = tid >> 2, q4 = tid & 3;
+  double na = 0.0, nb = 0.0;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    const double f = to_f64(tile[16 * q4 + i][c]), g = to_f64(tile[16 * q4 + i + 1][c]);
+    na = fma(f, f, na);
+    nb = fma(g, g, nb);
+  }
+  double nrm = na + nb;
+  nrm += __shfl_xor(nrm, 1);
+  nrm += __shfl_xor(nrm, 2);
+  for (int off = 4; off <= 32; off <<= 1) nrm = fmax(nrm, __shfl_xor(nrm, off));
+  if ((tid & 63) == 0) red[tid >> 6] = nrm;
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     // Rounded up, so it bounds every column norm of the block.
     colmax[blockIdx.x] = (float)(sqrt(fmax(fmax(red[0], red[1]), fmax(red[2], red[3]))) * (1.0 + 1e-6));
     if (blockIdx.x == 0) *fix_count = 0;

@@ -63,8 +63,17 @@ __global__ __launch_bounds__(1024) void sort_scatter_kernel(const int32_t* __res
   for (int b = threadIdx.x; b < waves * n_b; b += blockDim.x) sh[b] = 0;
   __syncthreads();
   const int32_t* bk = buckets + (size_t)bhr * L;
-  // 1. per-wave counts of its sub-tile
-  for (int i = w0 + lane; i < w1; i += 64) atomicAdd(&cnt[clamp_bucket(bk[i], n_b)], 1);
+  // 1. per-wave counts of its sub-tile; the buckets stay in registers for step 3
+  constexpr int kPer = kSortWaveTokens / 64;
+  int bv[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int i = w0 + lane + 64 * k;
+    bv[k] = i < w1 ? clamp_bucket(bk[i], n_b) : -1;
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k)
+    if (bv[k] >= 0) atomicAdd(&cnt[bv[k]], 1);
   __syncthreads();
   // 2. first slot of (bucket, wave) in the round's output: the totals of all
   //    smaller buckets, plus this bucket's counts in earlier tiles, plus its
@@ -75,9 +84,18 @@ __global__ __launch_bounds__(1024) void sort_scatter_kernel(const int32_t* __res
   const int nthr = (int)blockDim.x;
   const int per = (n_b + nthr - 1) / nthr;
   const int bb0 = min(n_b, (int)threadIdx.x * per), bb1 = min(n_b, bb0 + per);
-  int mine = 0;
-  for (int b = bb0; b < bb1; ++b)
-    for (int t = 0; t < n_tiles; ++t) mine += hp[(size_t)t * n_b + b];
+  int mine = 0, before1 = 0;  // per == 1: the one bucket's total and its count in earlier tiles
+  if (per == 1) {
+    if (bb0 < bb1)
+      for (int t = 0; t < n_tiles; ++t) {
+        const int c = hp[(size_t)t * n_b + bb0];
+        before1 += t < tile ? c : 0;
+        mine += c;
+      }
+  } else {
+    for (int b = bb0; b < bb1; ++b)
+      for (int t = 0; t < n_tiles; ++t) mine += hp[(size_t)t * n_b + b];
+  }
   // exclusive scan of `mine` over the threads of the block
   int incl = mine;
   for (int off = 1; off < 64; off <<= 1) {
@@ -89,11 +107,14 @@ __global__ __launch_bounds__(1024) void sort_scatter_kernel(const int32_t* __res
   int run = incl - mine;
   for (int w = 0; w < wave; ++w) run += wtot[w];
   for (int b = bb0; b < bb1; ++b) {
-    int before = 0, total = 0;
-    for (int t = 0; t < n_tiles; ++t) {
-      const int c = hp[(size_t)t * n_b + b];
-      before += t < tile ? c : 0;
-      total += c;
+    int before = before1, total = mine;
+    if (per != 1) {
+      before = total = 0;
+      for (int t = 0; t < n_tiles; ++t) {
+        const int c = hp[(size_t)t * n_b + b];
+        before += t < tile ? c : 0;
+        total += c;
+      }
     }
     int slot = run + before;
     for (int w = 0; w < waves; ++w) {
@@ -108,10 +129,11 @@ __global__ __launch_bounds__(1024) void sort_scatter_kernel(const int32_t* __res
   const int r = bhr % n_h, bh = bhr / n_h;
   int32_t* sidx = sorted_idx + (size_t)bh * n_h * L;
   int32_t* uidx = undo_idx + (size_t)bhr * L;
-  for (int i0 = w0; i0 < w1; i0 += 64) {
-    const int i = i0 + lane;
-    const bool act = i < w1;
-    const int b = act ? clamp_bucket(bk[i], n_b) : 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int i = w0 + 64 * k + lane;
+    const bool act = bv[k] >= 0;  // i < w1
+    const int b = act ? bv[k] : 0;
     uint64_t match = __ballot(act);
     for (int k = 0; k < nbits; ++k) {
       const bool bit = (b >> k) & 1;
