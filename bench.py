@@ -177,7 +177,8 @@ def main():
     ap.add_argument("--chunk-rows", type=int, default=16384, help="feed-forward row chunk of --block")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device-to-device copy of this many MiB "
-                         "(a reference kernel of known traffic for hardware byte counters)")
+                         "(a reference kernel of known traffic for hardware byte counters; the run then "
+                         "skips its own bandwidth copy)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the forward pass is not sharded across GPUs in this build "
@@ -272,8 +273,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    copy_gbs = hbm_copy_gbs()
-    log(f"plain device copy: {copy_gbs:.0f} GB/s (read + write), {copy_gbs / HBM_PEAK_GBS:.3f} of the HBM peak")
+    # A counter run's copy probe must be the run's only device copy.
+    copy_gbs = None if args.copy_probe_mib else hbm_copy_gbs()
+    if copy_gbs is not None:
+        log(f"plain device copy: {copy_gbs:.0f} GB/s (read + write), {copy_gbs / HBM_PEAK_GBS:.3f} of the HBM peak")
 
     work = algorithmic_work(B, H, L, D, n_b, n_h, es, same_bucket, dedup)
     peak_flops = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
@@ -314,8 +317,9 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "hash_uncertified": {"token_rounds": uncertified, "of": n_decisions},
-        "hbm_copy": {"GBps": round(copy_gbs, 1), "frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
-                     "what": "1 GiB device-to-device copy, read + write bytes"},
+        "hbm_copy": None if copy_gbs is None else {
+            "GBps": round(copy_gbs, 1), "frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
+            "what": "1 GiB device-to-device copy, read + write bytes"},
     }
     if args.attend != "none":
         result["config"]["attend"] = args.attend

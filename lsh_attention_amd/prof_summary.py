@@ -67,6 +67,9 @@ def counters(d: str):
             k = kernel_key(r["Kernel_Name"])
             per[k][r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
     out = {k: {c: sum(v.values()) / len(v) for c, v in cs.items()} for k, cs in per.items()}
+    # The probe is the run's largest copy (small read-backs use the same blit kernel).
+    if "copy" in per:
+        out["copy"] = {c: max(v.values()) for c, v in per["copy"].items()}
     return out
 
 

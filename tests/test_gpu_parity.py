@@ -151,6 +151,38 @@ def test_every_token_needs_the_exact_path(gpu_lib):
     assert np.all(got % 2 == 0)  # the lower index of each identical pair
 
 
+def test_near_ties_only_float64_separates(gpu_lib):
+    """fp32 rotation columns in pairs that differ by one ulp in coordinate 0: the
+    pair's two scores differ by |x_0| ulp(r_0), far inside the fp32 error bound,
+    so which of the two wins is decided by the float64 re-scoring of the
+    candidates, and depends on the sign of x_0 (both members must occur).
+    |x_0| >= 0.5 and |r_0| >= 0.25 keep each pair's gap at or above 2^-26; the
+    smallest top-two gap in these inputs is 7.6e-10, both far outside the float64
+    sums' rounding (about 1e-13 here), so the exact order is the oracle's."""
+    say("case one-ulp column pairs, fp32")
+    rng = np.random.default_rng(12)
+    half, n_h = 64, 2
+
+    def away_from_zero(a, m):
+        return (np.where(a >= 0, 1, -1) * np.maximum(np.abs(a), m)).astype(np.float32)
+
+    base = rng.standard_normal((n_h, 64, half // 2)).astype(np.float32)
+    base[:, 0, :] = away_from_zero(base[:, 0, :], 0.25)
+    rot = np.repeat(base, 2, axis=2)
+    rot[:, 0, 1::2] = np.nextafter(rot[:, 0, 1::2], np.float32(np.inf))
+    rt = I.Tensor(rot)
+    xv = I.gaussian(13, (2, 2, 576, 64), "f32").values.copy()
+    xv[..., 0] = away_from_zero(xv[..., 0], 0.5)
+    xt = I.Tensor(xv)
+    got = bd.lsh_hash(to_device(xt), to_device(rt), 2 * half, n_h).cpu().numpy()
+    for b in range(2):
+        for h in range(2):
+            ref, _ = O.hash_buckets(xt.values[b, h].astype(np.float64), rot.astype(np.float64), 2 * half)
+            np.testing.assert_array_equal(got[b, h], ref)
+    col = got % half
+    assert np.any(col % 2 == 0) and np.any(col % 2 == 1)
+
+
 def _uncertified_bracket(x64, rot64):
     """Bounds on the number of token-rounds the GPU cannot certify, from exact
     (float64) scores of one problem.  The kernel certifies a decision when its
