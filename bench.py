@@ -35,6 +35,7 @@ METRIC_TRAIN = "LSH-attn fwd+bwd (training step) tokens/sec at L=64K, 8 hashes; 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3    # MI355X fp32 MFMA / packed vector
+TOP_CLOCK_MHZ = 2400         # MI355X top engine clock (the published peaks' clock)
 
 
 def log(*a):
@@ -277,6 +278,11 @@ def main():
     copy_gbs = None if args.copy_probe_mib else hbm_copy_gbs()
     if copy_gbs is not None:
         log(f"plain device copy: {copy_gbs:.0f} GB/s (read + write), {copy_gbs / HBM_PEAK_GBS:.3f} of the HBM peak")
+    # The shader clock under load, beside fractions that use the published peaks
+    # (which assume the 2400 MHz top clock).
+    clock_mhz = None if args.copy_probe_mib else bd.measure_clock_mhz(200)
+    if clock_mhz is not None:
+        log(f"shader clock under a full-chip FMA spin: {clock_mhz:.0f} MHz (top {TOP_CLOCK_MHZ})")
 
     work = algorithmic_work(B, H, L, D, n_b, n_h, es, same_bucket, dedup)
     peak_flops = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
@@ -316,7 +322,11 @@ def main():
                    "n_hashes": n_h, "chunk_len": 64, "causal": w.causal},
         "roofline": roof,
         "kernels": kernels,
+        "token_head_rounds_per_s": round(n_decisions / (elapsed / args.steps), 1),
         "hash_uncertified": {"token_rounds": uncertified, "of": n_decisions},
+        "clock": None if clock_mhz is None else {
+            "mhz": round(clock_mhz, 1), "top_mhz": TOP_CLOCK_MHZ,
+            "what": "shader cycles per real-time tick over a 200 us full-chip FMA spin right after the timed steps"},
         "hbm_copy": None if copy_gbs is None else {
             "GBps": round(copy_gbs, 1), "frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
             "what": "1 GiB device-to-device copy, read + write bytes"},

@@ -312,6 +312,21 @@ int lsh_event_destroy(void* event);
 int lsh_event_record(void* event, void* stream);
 int lsh_event_elapsed_ms(void* start, void* end, float* ms);
 
+/* Measured shader clock, for reporting beside roofline fractions (which use
+ * the published peaks).  Every CU runs a dependent-FMA spin of about spin_us
+ * microseconds (2048 blocks of 256 threads); each block counts shader-clock
+ * cycles (s_memtime) against the constant-rate real-time counter
+ * (s_memrealtime, whose rate is hipDeviceAttributeWallClockRate).
+ *   ticks    device memory, LSH_CLOCK_TICKS_BYTES, caller-owned scratch
+ *            (overwritten: per block the two counter deltas);
+ *   spin_us  1 .. 100000;
+ *   mhz      out (host): mean over the blocks of cycles / real time, in MHz;
+ *   stream   HIP stream (NULL: the null stream); the call synchronises it.
+ * Errors: LSH_ERR_NULL (ticks or mhz NULL), LSH_ERR_SHAPE (spin_us out of
+ * range), LSH_ERR_HIP (attribute query, launch or copy failed). */
+#define LSH_CLOCK_TICKS_BYTES (2 * 2048 * 8)
+int lsh_measure_clock(void* ticks, int spin_us, double* mhz, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -53,6 +53,7 @@ _SIGS = {
     "lsh_event_destroy": (_c_int, [_vp]),
     "lsh_event_record": (_c_int, [_vp, _vp]),
     "lsh_event_elapsed_ms": (_c_int, [_vp, _vp, ctypes.POINTER(ctypes.c_float)]),
+    "lsh_measure_clock": (_c_int, [_vp, _c_int, ctypes.POINTER(ctypes.c_double), _vp]),
 }
 
 
@@ -175,6 +176,19 @@ def hash_uncertified(workspace: torch.Tensor, B: int, H: int, L: int, n_buckets:
         workspace.data_ptr(), workspace.numel(), B, H, L, n_buckets, n_hashes, _dtype_code_of(dtype), ctypes.byref(n),
         _stream(workspace.device)))
     return int(n.value)
+
+
+CLOCK_TICKS_BYTES = 2 * 2048 * 8  # LSH_CLOCK_TICKS_BYTES
+
+
+def measure_clock_mhz(spin_us: int = 200, device="cuda") -> float:
+    """Shader clock in MHz under a full-chip FMA spin of about spin_us microseconds
+    (shader-cycle counter against the constant-rate real-time counter)."""
+    ticks = torch.empty(CLOCK_TICKS_BYTES, dtype=torch.uint8, device=device)
+    mhz = ctypes.c_double(0.0)
+    _check("lsh_measure_clock", lib().lsh_measure_clock(ticks.data_ptr(), spin_us, ctypes.byref(mhz),
+                                                        _stream(ticks.device)))
+    return float(mhz.value)
 
 
 def lsh_sort(buckets: torch.Tensor, n_buckets: int):

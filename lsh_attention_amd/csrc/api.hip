@@ -2,6 +2,7 @@
 // workspace carving and the stream-ordered launch sequence.  Validation runs
 // entirely on the host and returns before anything is enqueued.
 #include <string.h>
+#include <vector>
 
 #include "lsh_block.h"
 #include "lsh_bwd.h"
@@ -190,6 +191,33 @@ hipError_t enqueue_sort(const int32_t* buckets, int32_t* sorted_idx, int32_t* un
 }
 
 }  // namespace
+
+namespace lsh {
+namespace {
+// Dependent FMAs between two reads of the shader-cycle and real-time counters.
+__global__ __launch_bounds__(256) void clock_spin_kernel(unsigned long long* __restrict__ ticks, int iters) {
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+  float a = (float)threadIdx.x * 1e-3f, b = 1.0001f;
+  for (int i = 0; i < iters; ++i) {
+    a = fmaf(a, b, 1e-7f);
+    b = fmaf(b, 0.99999f, 1e-6f);
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    ticks[2 * blockIdx.x] = t1 - t0;
+    ticks[2 * blockIdx.x + 1] = r1 - r0;
+  }
+  if (a < 0.f) ticks[2 * blockIdx.x] = 0;  // a stays positive; the test keeps the chain live
+}
+}  // namespace
+
+constexpr int kClockBlocks = LSH_CLOCK_TICKS_BYTES / 16;
+
+hipError_t launch_clock_spin(unsigned long long* ticks, int blocks, int iters, hipStream_t s) {
+  clock_spin_kernel<<<blocks, 256, 0, s>>>(ticks, iters);
+  return hipGetLastError();
+}
+}  // namespace lsh
 
 extern "C" {
 
@@ -713,6 +741,31 @@ int lsh_event_elapsed_ms(void* start, void* end, float* ms) {
   if (start == nullptr || end == nullptr || ms == nullptr) return LSH_ERR_NULL;
   if (hipEventSynchronize((hipEvent_t)end) != hipSuccess) return LSH_ERR_HIP;
   return hip_status(hipEventElapsedTime(ms, (hipEvent_t)start, (hipEvent_t)end));
+}
+
+int lsh_measure_clock(void* ticks, int spin_us, double* mhz, void* stream) {
+  if (ticks == nullptr || mhz == nullptr) return LSH_ERR_NULL;
+  if (spin_us < 1 || spin_us > 100000) return LSH_ERR_SHAPE;
+  int dev = 0, wall_khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || wall_khz <= 0)
+    return LSH_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  // about 24 iterations per microsecond at 8 waves per SIMD
+  if (lsh::launch_clock_spin((unsigned long long*)ticks, lsh::kClockBlocks, 24 * spin_us, s) != hipSuccess)
+    return LSH_ERR_HIP;
+  std::vector<unsigned long long> h(2 * lsh::kClockBlocks);
+  if (hipMemcpyAsync(h.data(), ticks, h.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost, s) !=
+          hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return LSH_ERR_HIP;
+  double cycles = 0.0, real = 0.0;
+  for (int b = 0; b < lsh::kClockBlocks; ++b) {
+    cycles += (double)h[2 * b];
+    real += (double)h[2 * b + 1];
+  }
+  *mhz = real > 0.0 ? cycles / real * (double)wall_khz / 1e3 : 0.0;
+  return LSH_OK;
 }
 
 }  // extern "C"

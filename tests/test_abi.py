@@ -137,6 +137,15 @@ def test_uncertified_count_rejects_before_copy(L):
     assert st == OK and fws >= hws
 
 
+def test_clock_measurement_rejects_before_launch(L):
+    mhz = ctypes.c_double(0.0)
+    assert L.lsh_measure_clock(None, 100, ctypes.byref(mhz), None) == NULL
+    assert L.lsh_measure_clock(P1, 100, None, None) == NULL
+    assert L.lsh_measure_clock(P1, 0, ctypes.byref(mhz), None) == SHAPE
+    assert L.lsh_measure_clock(P1, 100001, ctypes.byref(mhz), None) == SHAPE
+    assert bd.CLOCK_TICKS_BYTES == 2 * 2048 * 8
+
+
 @pytest.mark.parametrize("B,H,n", [(0, 1, 64), (1, 0, 64), (1, 1, 0), (0, 0, 0)])
 def test_empty_problems_are_no_ops(L, B, H, n):
     # Zero-sized problems succeed without touching any pointer (all NULL here)
