@@ -154,8 +154,14 @@ def cpu_baseline(inp, min_seconds: float = 10.0):
             break
     t = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {"value": round(B * L * done / (B * H * t), 1), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu,
             "sample": f"{done} of {B * H} (batch, head) problems at full L={L}, all {inp.n_hashes} rounds, "
                       f"float64 numpy, {t:.2f} s; tokens/s = B*L*problems / (B*H*t)",
             "seconds": round(t, 3)}
