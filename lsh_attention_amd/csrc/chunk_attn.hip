@@ -308,6 +308,7 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
     const int cur = c & 1, prv = cur ^ 1;
     const int kc = c - c0 + 1;  // sPos entry of chunk c
     if (c + 1 < c1) gather(kc + 1);
+    __builtin_amdgcn_s_setprio(0);
 
     const int qrow = 16 * wave + col;  // this lane's query row in the current chunk
     const int qpos = sPos[kc][qrow];
@@ -575,12 +576,18 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
     }
     if (grp == 0) lbase[row_g] = (off + __builtin_amdgcn_logf(sum)) * kLn2;
 
+    // From here through the issue of the next iteration's gather the wave runs
+    // at raised priority: the block's critical path (the barriers, the commit
+    // to LDS, the next loads) goes ahead of the other blocks' vector work on
+    // the SIMD (measured: about 2 us of 324 at long_seq_64k).
+    __builtin_amdgcn_s_setprio(2);
     __syncthreads();  // every wave is done with slot prv
     if (c + 1 < c1) {
       commit(prv);
       __syncthreads();
     }
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // Token-major record of the set-union variant: rec[bh][i][r] = (bucket of i in
