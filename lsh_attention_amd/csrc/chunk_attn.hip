@@ -49,6 +49,7 @@ namespace lsh {
 namespace {
 
 constexpr int kChunksPerBlock = 8;
+constexpr size_t kAttnFillBlocks = 1024;  // 4 blocks on each of 256 CUs
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSelf2 = -1.0e5f * kLog2e;        // self logit, base 2
@@ -109,8 +110,8 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
     const typename AttnTraits<BF16>::T* __restrict__ qk, const typename AttnTraits<BF16>::T* __restrict__ v,
     const int32_t* __restrict__ sorted_idx, typename AttnTraits<BF16>::T* __restrict__ o_out,
     float* __restrict__ lse_out, const float2* __restrict__ token_scales, const int32_t* __restrict__ buckets,
-    const int32_t* __restrict__ tok_rec, int L, int n_h, int n_slots, int n_chunks, int blocks_per_bh) {
-  constexpr int kCPB = chunks_per_block<ATTEND>();
+    const int32_t* __restrict__ tok_rec, int L, int n_h, int n_slots, int n_chunks, int blocks_per_bh, int cpb) {
+  constexpr int kCPB = chunks_per_block<ATTEND>();  // the longest run (cpb <= kCPB)
   constexpr bool kSB = (ATTEND & 1) != 0, kDD = (ATTEND & 2) != 0;
   using T = typename AttnTraits<BF16>::T;
   constexpr int kXRow = AttnTraits<BF16>::kXRow;
@@ -131,8 +132,8 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
   int* const sFirst = sLast + (kDD ? (kCPB + 1) * 64 : 0);
 
   const int bh = blockIdx.x / blocks_per_bh;
-  const int c0 = (blockIdx.x % blocks_per_bh) * kCPB;
-  const int c1 = min(n_chunks, c0 + kCPB);
+  const int c0 = (blockIdx.x % blocks_per_bh) * cpb;
+  const int c1 = min(n_chunks, c0 + cpb);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15;  // query (column) of the MFMA tiles
@@ -621,17 +622,22 @@ hipError_t launch_attn_t(const void* qk, const void* v, const int32_t* sorted_id
   constexpr int kCPB = chunks_per_block<ATTEND>();
   const int n_slots = n_h * L;
   const int n_chunks = n_slots / kChunk;
-  const int blocks_per_bh = (n_chunks + kCPB - 1) / kCPB;
+  // Runs of kCPB chunks, halved while the launch would not give every CU four
+  // blocks (small problems: more, shorter runs, each re-gathering its look-back
+  // chunk, instead of a few long serial walks).
+  int cpb = kCPB;
+  while (cpb > 1 && (size_t)BH * (size_t)((n_chunks + cpb - 1) / cpb) < kAttnFillBlocks) cpb >>= 1;
+  const int blocks_per_bh = (n_chunks + cpb - 1) / cpb;
   const unsigned grid = (unsigned)blocks_per_bh * (unsigned)BH;
   const size_t dyn = variant_lds_bytes(ATTEND, n_h);
   if (causal)
     chunk_attn_kernel<BF16, true, ATTEND><<<grid, 256, dyn, s>>>(
         (const T*)qk, (const T*)v, sorted_idx, (T*)o_out, lse_out, token_scales, buckets, tok_rec, L, n_h,
-        n_slots, n_chunks, blocks_per_bh);
+        n_slots, n_chunks, blocks_per_bh, cpb);
   else
     chunk_attn_kernel<BF16, false, ATTEND><<<grid, 256, dyn, s>>>(
         (const T*)qk, (const T*)v, sorted_idx, (T*)o_out, lse_out, token_scales, buckets, tok_rec, L, n_h,
-        n_slots, n_chunks, blocks_per_bh);
+        n_slots, n_chunks, blocks_per_bh, cpb);
   return hipGetLastError();
 }
 
