@@ -188,8 +188,8 @@ def main():
                          "skips its own bandwidth copy)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the forward pass is not sharded across GPUs in this build "
-              "(run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library runs each problem on one GPU and has no "
+              "multi-GPU sharding (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
