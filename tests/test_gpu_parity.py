@@ -183,6 +183,36 @@ def test_near_ties_only_float64_separates(gpu_lib):
     assert np.any(col % 2 == 0) and np.any(col % 2 == 1)
 
 
+@pytest.mark.parametrize("copies", [8, 9])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_candidate_limit_boundary(gpu_lib, dtype, copies):
+    """A rotation whose column 3 appears `copies` times (at 3, 5, 7, ...): a token
+    whose best column is one of them has that many exactly tied candidates.  8
+    fit the float64 candidate path (unless another column also comes within the
+    bound), 9 exceed it and take the all-column float64 loop; either way the
+    lowest index wins, as in the oracle."""
+    say(f"case {copies} tied copies, {dtype}")
+    rng = np.random.default_rng(40 + copies)
+    half, n_h = 32, 2
+    rot = rng.standard_normal((n_h, 64, half)).astype(np.float32)
+    dup = [3 + 2 * k for k in range(copies)]
+    rot[:, :, dup] = rot[:, :, 3:4]
+    if dtype == "bf16":
+        rt = I.Tensor(I.f32_from_bf16_bits(I.bf16_bits_from_f32(rot)), I.bf16_bits_from_f32(rot))
+    else:
+        rt = I.Tensor(rot)
+    xt = I.gaussian(41 + copies, (2, 2, 576, 64), dtype)
+    got = bd.lsh_hash(to_device(xt), to_device(rt), 2 * half, n_h).cpu().numpy()
+    hits = 0
+    for b in range(2):
+        for h in range(2):
+            ref, _ = O.hash_buckets(xt.values[b, h].astype(np.float64), rt.values.astype(np.float64), 2 * half)
+            np.testing.assert_array_equal(got[b, h], ref)
+            hits += int(np.sum(np.isin(ref % half, dup)))
+    # the tied column wins often, and always as its lowest copy
+    assert hits > 0 and not np.any(np.isin(got % half, dup[1:]))
+
+
 def _uncertified_bracket(x64, rot64):
     """Bounds on the number of token-rounds the GPU cannot certify, from exact
     (float64) scores of one problem.  The kernel certifies a decision when its
