@@ -131,14 +131,20 @@ def hbm_copy_gbs(nbytes: int = 1 << 30, reps: int = 5) -> float:
     return 2.0 * nbytes * reps / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(inp, min_seconds: float = 10.0):
+SMALL_WORKLOADS = ("single_head_fp32", "mlm_small_512", "causal_lm_4k")
+
+
+def cpu_baseline(inp, min_seconds: float = 10.0, one_thread: bool = False):
     """The oracle, untouched, on a bounded sample: whole (batch, head) problems
     of the same workload at full length, one after another until at least
     `min_seconds` have passed (or all are done); tokens/s scaled to the batch."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle as O
+    if one_thread:
+        with threadpool_limits(limits=1):
+            return cpu_baseline(inp, min_seconds, False)
     w = inp.workload
     B, H, L, _ = inp.qk.values.shape
     rot = None if inp.rot is None else inp.rot.values.astype(np.float64)
@@ -345,6 +351,9 @@ def main():
     if not args.no_cpu_baseline and args.attend == "none" and not args.backward:
         log("timing the oracle on the host (cpu_baseline leg)")
         result["cpu_baseline"] = cpu_baseline(inp)
+        if w.name in SMALL_WORKLOADS:
+            one = cpu_baseline(inp, 5.0, one_thread=True)
+            result["cpu_baseline"]["one_thread"] = {k: one[k] for k in ("value", "cores", "sample", "seconds")}
     print(json.dumps(result), flush=True)
 
 
