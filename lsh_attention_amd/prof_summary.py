@@ -92,9 +92,32 @@ def traffic(d: str, workload: str, out_json: str, copy_mib: int = 256):
     return res
 
 
+def counter_table(d: str, kernels=("hash", "fixup", "sort_scatter", "chunk_attn", "combine")) -> str:
+    """Markdown table of SQ counters per dispatch (mean over the kernel's
+    dispatches) from --pmc runs under `d`, with ratios of like units only."""
+    c = counters(d)
+    names = sorted({k for v in c.values() for k in v})
+    out = ["| kernel | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
+    for k in kernels:
+        if k in c:
+            out.append(f"| {k} | " + " | ".join(f"{c[k].get(n, float('nan')):.4g}" for n in names) + " |")
+    out += ["", "| kernel | VALU insts per MFMA inst | MFMA-busy cycles with VALU co-executing | "
+            "LDS bank-conflict cycles per LDS inst | transcendental share of VALU |", "|---|---|---|---|---|"]
+    for k in kernels:
+        v = c.get(k, {})
+        def ratio(a, b):
+            return f"{v[a] / v[b]:.3g}" if v.get(a) is not None and v.get(b) else "-"
+        out.append(f"| {k} | {ratio('SQ_INSTS_VALU', 'SQ_INSTS_MFMA')} | "
+                   f"{ratio('SQ_VALU_MFMA_COEXEC_CYCLES', 'SQ_VALU_MFMA_BUSY_CYCLES')} | "
+                   f"{ratio('SQ_LDS_BANK_CONFLICT', 'SQ_INSTS_LDS')} | {ratio('SQ_INSTS_VALU_TRANS_F32', 'SQ_INSTS_VALU')} |")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         print(stats_table(sys.argv[2]))
+    elif sys.argv[1] == "counters":
+        print(counter_table(sys.argv[2]))
     elif sys.argv[1] == "traffic":
         print(json.dumps(traffic(sys.argv[2], sys.argv[3], sys.argv[4]), indent=1))
     else:
