@@ -371,6 +371,138 @@ def test_combine_equals_softmax_over_the_multiset_union(causal):
 
 
 # ----------------------------------------------------------------- recall --
+# Recall is what the explainer's nearest-neighbour reading of attention and its
+# multi-round sentence are about: the share of a query's true nearest keys that
+# its hashed windows (union over rounds) contain.  The pins below fix the
+# neighbour order, the windows and the expected fractions by hand.
+
+def _circle_tokens():
+    """Eight tokens in the plane of the first two dims (D = 64, the rest zero):
+    token i at angle 2^i - 1 degrees (0, 1, 3, 7, 15, 31, 63, 127) with norm 2^i.
+    All angles lie in [0, 127], so the angular distance of i and j is
+    |2^i - 2^j| degrees, and these are distinct for distinct pairs; by cosine
+    (keys normalised) the neighbours of query i are i-1, i-2, ..., 0 (distances
+    2^i - 2^j < 2^i), then i+1, ..., 7 (distances >= 2^i).  The norms grow with
+    i, so a key left unnormalised would reorder them."""
+    deg = np.array([2.0 ** i - 1 for i in range(8)])
+    rho = np.array([2.0 ** i for i in range(8)])
+    x = np.zeros((8, 64))
+    x[:, 0] = rho * np.cos(np.radians(deg))
+    x[:, 1] = rho * np.sin(np.radians(deg))
+    return x
+
+
+# One round, chunk_len 2: sorted order 0 1 | 4 5 | 2 3 | 6 7, so the windows
+# (previous chunk, cyclic, and the own chunk) are
+#   tokens 0, 1: {6, 7, 0, 1}   tokens 4, 5: {0, 1, 4, 5}
+#   tokens 2, 3: {4, 5, 2, 3}   tokens 6, 7: {2, 3, 6, 7}
+_S1 = np.array([0, 1, 4, 5, 2, 3, 6, 7])
+_U1 = np.array([[0, 1, 4, 5, 2, 3, 6, 7]])
+# A second round in position order (slots 8..15: 0 1 | 2 3 | 4 5 | 6 7); its first
+# chunk looks back at round 0's last chunk {6, 7}, and round 0's first chunk now
+# looks back at round 1's last chunk, again {6, 7}.  Unions over both rounds:
+#   tokens 0, 1: {0, 1, 6, 7}   tokens 2..5: {0, ..., 5}   tokens 6, 7: {2, ..., 7}
+_S2 = np.array([0, 1, 4, 5, 2, 3, 6, 7, 0, 1, 2, 3, 4, 5, 6, 7])
+_U2 = np.array([[0, 1, 4, 5, 2, 3, 6, 7], list(range(8, 16))])
+
+
+def test_hand_windows_of_the_recall_pins():
+    assert O.attended_positions(_S1, _U1, 2, 0) == {0, 1, 6, 7}
+    assert O.attended_positions(_S1, _U1, 2, 4) == {0, 1, 4, 5}
+    assert O.attended_positions(_S1, _U1, 2, 3) == {2, 3, 4, 5}
+    assert O.attended_positions(_S1, _U1, 2, 7) == {2, 3, 6, 7}
+    assert O.attended_positions(_S2, _U2, 2, 1) == {0, 1, 6, 7}
+    assert O.attended_positions(_S2, _U2, 2, 4) == {0, 1, 2, 3, 4, 5}
+    assert O.attended_positions(_S2, _U2, 2, 6) == {2, 3, 4, 5, 6, 7}
+
+
+def test_recall_at_k_hand_counts_one_round():
+    """Nearest neighbours (first three) of each query, and whether the query's
+    window holds them:
+      q0: 1 2 3 -> 1 in, 2 3 out        q4: 3 2 1 -> 3 2 out, 1 in
+      q1: 0 2 3 -> 0 in                 q5: 4 3 2 -> 4 in
+      q2: 1 0 3 -> 1 0 out, 3 in        q6: 5 4 3 -> 5 4 out, 3 in
+      q3: 2 1 0 -> 2 in                 q7: 6 5 4 -> 6 in
+    R@1 = 5/8 (q0 q1 q3 q5 q7); R@2 = 5/16; R@3 = 8/24.  A query counted as its
+    own neighbour gives R@1 = 1; the smallest logits, or keys left unnormalised,
+    give other counts."""
+    x = _circle_tokens()
+    assert O.recall_at_k(x, _S1, _U1, 2, range(8), 1) == 5 / 8
+    assert O.recall_at_k(x, _S1, _U1, 2, range(8), 2) == 5 / 16
+    assert O.recall_at_k(x, _S1, _U1, 2, range(8), 3) == 8 / 24
+    # the mean is over the queries given
+    assert O.recall_at_k(x, _S1, _U1, 2, [2, 4, 6], 1) == 0.0
+    assert O.recall_at_k(x, _S1, _U1, 2, [0, 1], 2) == 2 / 4
+
+
+def test_recall_at_k_hand_counts_two_rounds():
+    """Over the union of both rounds' windows every nearest neighbour is in
+    (R@1 = 1); second neighbours miss for q0 (2) and q1 (2) only: R@2 = 14/16;
+    third neighbours miss for q0 (3) and q1 (3) only: R@3 = 20/24.  The union
+    contains the first round's windows, so recall cannot drop."""
+    x = _circle_tokens()
+    assert O.recall_at_k(x, _S2, _U2, 2, range(8), 1) == 1.0
+    assert O.recall_at_k(x, _S2, _U2, 2, range(8), 2) == 14 / 16
+    assert O.recall_at_k(x, _S2, _U2, 2, range(8), 3) == 20 / 24
+
+
+def test_recall_at_k_equals_a_full_sort_on_random_problems():
+    """Second definition: the k best keys by a full stable sort of the cosine
+    (ties impossible on Gaussian data), the window membership by enumerating
+    every round's window slots, per query."""
+    rng = np.random.default_rng(31)
+    for L, n_h, C, k in ((64, 2, 8, 1), (96, 3, 16, 5), (128, 1, 32, 16)):
+        x = rng.standard_normal((L, 64))
+        s, u = O.sort_by_bucket(rng.integers(0, 4, (n_h, L)))
+        q = rng.choice(L, 20, replace=False)
+        hits = 0
+        for i in q:
+            cos = [float(x[j] @ x[i]) / float(np.linalg.norm(x[j])) if j != i else -math.inf for j in range(L)]
+            best = sorted(range(L), key=lambda j: -cos[j])[:k]
+            win = set()
+            for r in range(n_h):
+                c = int(u[r, i]) // C
+                prev = (c - 1) % (n_h * L // C)
+                win |= {int(s[g]) for g in range(prev * C, prev * C + C)} | {int(s[g]) for g in range(c * C, c * C + C)}
+            hits += sum(1 for j in best if j in win)
+        assert O.recall_at_k(x, s, u, C, q, k) == hits / (k * len(q))
+
+
+def test_attention_mass_recall_uniform_logits():
+    """All tokens along one direction with distinct norms: with keys normalised
+    every logit j != i equals |x_i| / 8, so the exact weights are uniform over
+    the L - 1 other tokens and the mass inside a window set W (which holds the
+    query itself, at weight 0) is (|W| - 1) / (L - 1).  One round: |W| = 4 for
+    every query -> 3/7.  Two rounds: |W| = 4 for q0, q1 and 6 for the others ->
+    (2 * 3/7 + 6 * 5/7) / 8 = 9/14."""
+    x = np.zeros((8, 64))
+    x[:, 5] = np.arange(1, 9, dtype=np.float64)
+    assert abs(O.attention_mass_recall(x, _S1, _U1, 2, range(8)) - 3 / 7) < 1e-14
+    assert abs(O.attention_mass_recall(x, _S2, _U2, 2, range(8)) - 9 / 14) < 1e-14
+
+
+def test_attention_mass_recall_two_directions():
+    """Tokens 0-3 at +e1 (norm 1), tokens 4-7 at -2 e1 (norm 2); scale 1/8, keys
+    normalised.  A query in the first group sees logit +1/8 on the three others
+    of its group and -1/8 on the second group; a query in the second group sees
+    +1/4 on its group and -1/4 on the first.  One-round windows:
+      q0..q3 (W holds 1 other of its group, 2 of the other):
+          (e^{1/8} + 2 e^{-1/8}) / (3 e^{1/8} + 4 e^{-1/8})
+      q4..q7 (W holds 1 other of its group, 2 of the other):
+          (e^{1/4} + 2 e^{-1/4}) / (3 e^{1/4} + 4 e^{-1/4})
+    The mean is the average of the two.  Negated logits, another scale or a
+    query weighting its own key give other values."""
+    x = np.zeros((8, 64))
+    x[:4, 0] = 1.0
+    x[4:, 0] = -2.0
+    a = math.exp(1 / 8)
+    b = math.exp(1 / 4)
+    first = (a + 2 / a) / (3 * a + 4 / a)
+    second = (b + 2 / b) / (3 * b + 4 / b)
+    assert abs(O.attention_mass_recall(x, _S1, _U1, 2, range(4)) - first) < 1e-14
+    assert abs(O.attention_mass_recall(x, _S1, _U1, 2, range(4, 8)) - second) < 1e-14
+    assert abs(O.attention_mass_recall(x, _S1, _U1, 2, range(8)) - (first + second) / 2) < 1e-14
+
 
 def test_recall_is_one_when_every_key_is_in_the_window():
     x, _, _ = _problem(14, 32, 1, 1)
