@@ -46,8 +46,9 @@ ATTEND = {"none": (False, False), "same_bucket": (True, False), "dedup": (False,
 
 
 def algorithmic_work(B, H, L, D, n_b, n_h, es, same_bucket=False, dedup=False):
-    """Per-launch algorithmic bytes and flops of each kernel (see the design
-    notes): what the method must read and write, not what a kernel happens to."""
+    """Per-launch algorithmic bytes and flops of each kernel: what the method
+    must read and write (each input once, each output once), not what a kernel
+    happens to move."""
     th = B * H * L            # token-heads
     tr = th * n_h             # token-rounds
     # variants: the slot's bucket (same-bucket), every round's unsort index (set union)
@@ -55,15 +56,20 @@ def algorithmic_work(B, H, L, D, n_b, n_h, es, same_bucket=False, dedup=False):
     half = n_b // 2
     return {
         "prep": {"bytes": 2 * n_h * D * half * es, "flops": 0},
+        # per token-head: its row read, one bucket id per round written; D * n_b * n_h flop
+        # (the n_b/2 dot products of [xR; -xR], 2 flop per multiply-add)
         "hash": {"bytes": th * (D * es + 4 * n_h), "flops": 2 * th * D * half * n_h},
         "fixup": {"bytes": 0, "flops": 0},
+        # the sort as a whole reads each bucket id and writes the sorted and unsort
+        # indices: 12 B per token-round, split as the two launches touch them
         "sort_hist": {"bytes": tr * 4, "flops": 0},
-        # scatter: read each bucket id, write its sorted index and unsort index
-        "sort_scatter": {"bytes": tr * 12, "flops": 0},
-        # per token-round (slot of the sorted order): its index, its gathered QK and V
-        # rows, its output row and lse.  Each round's chunks read their rows in that
-        # round's order, so every row is gathered once per round.
-        "chunk_attn": {"bytes": tr * (4 + 3 * D * es + 4) + extra, "flops": tr * 4 * D * 128},
+        "sort_scatter": {"bytes": tr * 8, "flops": 0},
+        # per token-round: its sorted index, its output row and lse; the QK and V rows
+        # are compulsory once per token-head (2 D es / n_h per token-round).  A kernel
+        # whose rounds each gather their rows from beyond the caches moves
+        # 2 D es per token-round instead (gathered_bytes below).
+        "chunk_attn": {"bytes": tr * (4 + D * es + 4) + th * 2 * D * es + extra, "flops": tr * 4 * D * 128,
+                       "gathered_bytes": tr * (4 + 3 * D * es + 4) + extra},
         # per token-head: n_h rows + lse + undo index read, one output row + LSE written
         "combine": {"bytes": th * (n_h * (D * es + 8) + D * es + 4), "flops": 0},
         # backward: per token x, out, dout rows and dLSE read, key scales written; per slot
@@ -134,43 +140,93 @@ def hbm_copy_gbs(nbytes: int = 1 << 30, reps: int = 5) -> float:
 SMALL_WORKLOADS = ("single_head_fp32", "mlm_small_512", "causal_lm_4k")
 
 
-def cpu_baseline(inp, min_seconds: float = 10.0, one_thread: bool = False):
-    """The oracle, untouched, on a bounded sample: whole (batch, head) problems
-    of the same workload at full length, one after another until at least
-    `min_seconds` have passed (or all are done); tokens/s scaled to the batch."""
-    import numpy as np
-    from threadpoolctl import threadpool_info, threadpool_limits
+def _oracle_problem(args):
+    """One (batch, head) problem through the oracle, in a worker process with a
+    one-thread BLAS (so that the worker count is the core count)."""
+    from threadpoolctl import threadpool_limits
 
     import oracle as O
-    if one_thread:
-        with threadpool_limits(limits=1):
-            return cpu_baseline(inp, min_seconds, False)
+    x, v, rot, n_b, n_h, C, causal = args
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        O.forward_problem(x, v, rot, n_b, n_h, C, causal)
+        return time.perf_counter() - t0
+
+
+def _warm_worker(_):
+    """Imports the oracle in a worker and holds it briefly, so that every worker
+    has started and imported before the timed run."""
+    import oracle  # noqa: F401
+    time.sleep(0.5)
+    return 0
+
+
+def _one_thread_env():
+    for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[k] = "1"
+
+
+def cpu_baseline(inp, min_seconds: float = 10.0, max_workers: int = 16):
+    """The oracle, untouched, timed on the host: whole (batch, head) problems of
+    the workload at full length, spread over worker processes (one problem per
+    worker at a time, one BLAS thread each), submitted until at least
+    `min_seconds` of wall time have passed or every problem is done.  A run
+    that finishes within 10 s is repeated three times and the median taken.
+    tokens/s = B*L * problems_done / (B*H * wall)."""
+    from concurrent.futures import FIRST_COMPLETED, ProcessPoolExecutor, wait
+    from multiprocessing import get_context
+
+    import numpy as np
     w = inp.workload
     B, H, L, _ = inp.qk.values.shape
     rot = None if inp.rot is None else inp.rot.values.astype(np.float64)
-    t0 = time.perf_counter()
-    done = 0
-    for k in range(B * H):
+    n_prob = B * H
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    workers = max(1, min(max_workers, avail, n_prob))
+
+    def job(k):
         b, h = divmod(k, H)
-        x = inp.qk.values[b, h].astype(np.float64)
-        v = inp.v.values[b, h].astype(np.float64)
-        O.forward_problem(x, v, rot, w.n_buckets, inp.n_hashes, w.chunk_len, w.causal)
-        done += 1
-        if time.perf_counter() - t0 >= min_seconds:
-            break
-    t = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        return (inp.qk.values[b, h].astype(np.float64), inp.v.values[b, h].astype(np.float64), rot,
+                w.n_buckets, inp.n_hashes, w.chunk_len, w.causal)
+
+    runs = []
+    with ProcessPoolExecutor(workers, mp_context=get_context("spawn"), initializer=_one_thread_env) as ex:
+        list(ex.map(_warm_worker, range(workers)))  # every worker started and importing before timing
+        while True:
+            t0 = time.perf_counter()
+            pending, nxt, done = set(), 0, 0
+            while nxt < n_prob and len(pending) < workers:
+                pending.add(ex.submit(_oracle_problem, job(nxt)))
+                nxt += 1
+            while pending:
+                fin, pending = wait(pending, return_when=FIRST_COMPLETED)
+                done += len(fin)
+                if nxt < n_prob and time.perf_counter() - t0 < min_seconds:
+                    for _ in fin:
+                        if nxt < n_prob:
+                            pending.add(ex.submit(_oracle_problem, job(nxt)))
+                            nxt += 1
+            runs.append((time.perf_counter() - t0, done))
+            if len(runs) == 3 or runs[0][0] > min_seconds:
+                break
+    rates = sorted(B * L * d / (n_prob * t) for t, d in runs)
+    med = rates[len(rates) // 2]
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
             cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
     except OSError:
         pass
-    return {"value": round(B * L * done / (B * H * t), 1), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle", "cpu_model": cpu,
-            "sample": f"{done} of {B * H} (batch, head) problems at full L={L}, all {inp.n_hashes} rounds, "
-                      f"float64 numpy, {t:.2f} s; tokens/s = B*L*problems / (B*H*t)",
-            "seconds": round(t, 3)}
+    t_med, d_med = next((t, d) for t, d in runs if B * L * d / (n_prob * t) == med)
+    return {"value": round(med, 1), "unit": "tokens/s", "cores": workers, "kind": "oracle", "cpu_model": cpu,
+            "sample": f"{d_med} of {n_prob} (batch, head) problems at full L={L}, all {inp.n_hashes} rounds, "
+                      f"float64 numpy oracle in {workers} worker processes with one BLAS thread each, "
+                      f"{t_med:.2f} s wall; median of {len(runs)} run(s); "
+                      f"tokens/s = B*L*problems / (B*H*wall)",
+            "seconds": round(t_med, 3), "runs": [round(B * L * d / (n_prob * t), 1) for t, d in runs]}
 
 
 def main():
@@ -298,24 +354,36 @@ def main():
 
     work = algorithmic_work(B, H, L, D, n_b, n_h, es, same_bucket, dedup)
     peak_flops = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
-    kernels = {}
-    for i, name in enumerate(names):
-        us = float(np.mean(per_kernel[:, i])) * 1e3
-        wk = work[name]
+
+    def rates(wk, us):
         ent = {"us": round(us, 2)}
         if us > 0 and wk["bytes"]:
             ent["GBps"] = round(wk["bytes"] / (us * 1e-6) / 1e9, 1)
             ent["hbm_frac"] = round(ent["GBps"] / HBM_PEAK_GBS, 4)
+        if us > 0 and wk.get("gathered_bytes"):
+            ent["gathered_GBps"] = round(wk["gathered_bytes"] / (us * 1e-6) / 1e9, 1)
         if us > 0 and wk["flops"]:
             ent["TFLOPs"] = round(wk["flops"] / (us * 1e-6) / 1e12, 1)
             ent["mfma_frac"] = round(ent["TFLOPs"] / peak_flops, 4)
-        kernels[name] = ent
-        log(f"  {name:13s} {us:9.2f} us  {json.dumps({k: x for k, x in ent.items() if k != 'us'})}")
+        return ent
+
+    kernels = {}
+    for i, name in enumerate(names):
+        kernels[name] = rates(work[name], float(np.mean(per_kernel[:, i])) * 1e3)
+        log(f"  {name:13s} {kernels[name]['us']:9.2f} us  "
+            f"{json.dumps({k: x for k, x in kernels[name].items() if k != 'us'})}")
+    # the sort as one step (its launches together): 12 B per token-round
+    if "sort_hist" in kernels and "sort_scatter" in kernels:
+        sort_wk = {"bytes": work["sort_hist"]["bytes"] + work["sort_scatter"]["bytes"], "flops": 0}
+        sort_ent = rates(sort_wk, kernels["sort_hist"]["us"] + kernels["sort_scatter"]["us"])
+        log(f"  {'sort (both)':13s} {sort_ent['us']:9.2f} us  {json.dumps({k: x for k, x in sort_ent.items() if k != 'us'})}")
+    else:
+        sort_ent = None
     dom = max(kernels, key=lambda k: kernels[k]["us"])
     d_us = kernels[dom]["us"]
     wk = work[dom]
     # The binding roofline of the dominant kernel: compute if its flops take longer
-    # at peak than its bytes at peak bandwidth.
+    # at peak than its algorithmic bytes at peak bandwidth.
     if wk["flops"] / (peak_flops * 1e12) > wk["bytes"] / (HBM_PEAK_GBS * 1e9):
         roof = {"bound": "mfma", "achieved": round(wk["flops"] / (d_us * 1e-6) / 1e12, 2), "peak": peak_flops,
                 "unit": "TFLOP/s"}
@@ -325,6 +393,34 @@ def main():
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["kernel"] = dom
     roof["traffic"] = measured_traffic(w.name, dom, "train" if args.backward else args.attend)
+    roof["algorithmic_bytes"] = wk["bytes"]
+    if roof["traffic"] is not None:
+        roof["traffic_over_algorithmic"] = round(roof["traffic"] / wk["bytes"], 3)
+    if "hbm_frac" in kernels[dom]:
+        roof["hbm_frac"] = kernels[dom]["hbm_frac"]
+    if "mfma_frac" in kernels[dom]:
+        roof["mfma_frac"] = kernels[dom]["mfma_frac"]
+
+    # Each step against the roofline its target is stated on: chunk attention
+    # against bf16 (fp32) MFMA peak, sort and unsort+combine against HBM peak,
+    # the hash against whichever of MFMA and HBM binds its algorithmic work.
+    stage_roof = {}
+    if not args.backward:
+        hk, hw = kernels.get("hash"), work["hash"]
+        if hk:
+            hb = "mfma" if hw["flops"] / (peak_flops * 1e12) > hw["bytes"] / (HBM_PEAK_GBS * 1e9) else "hbm"
+            stage_roof["hash"] = {"measure": hb, "frac": hk["mfma_frac" if hb == "mfma" else "hbm_frac"],
+                                  "hbm_frac": hk.get("hbm_frac"), "target": None if hb == "mfma" else 0.5}
+        if sort_ent:
+            stage_roof["sort"] = {"measure": "hbm", "frac": sort_ent.get("hbm_frac"), "us": sort_ent["us"],
+                                  "target": 0.5}
+        if "chunk_attn" in kernels:
+            ck = kernels["chunk_attn"]
+            stage_roof["chunk_attn"] = {"measure": "mfma", "frac": ck.get("mfma_frac"),
+                                        "hbm_frac": ck.get("hbm_frac"), "target": 0.4}
+        if "combine" in kernels:
+            stage_roof["unsort_combine"] = {"measure": "hbm", "frac": kernels["combine"].get("hbm_frac"),
+                                            "target": 0.5}
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -333,6 +429,7 @@ def main():
         "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": L, "d_head": D, "n_buckets": n_b,
                    "n_hashes": n_h, "chunk_len": 64, "causal": w.causal},
         "roofline": roof,
+        "stage_roofline": stage_roof,
         "kernels": kernels,
         "token_head_rounds_per_s": round(n_decisions / (elapsed / args.steps), 1),
         "hash_uncertified": {"token_rounds": uncertified, "of": n_decisions},
@@ -351,9 +448,7 @@ def main():
     if not args.no_cpu_baseline and args.attend == "none" and not args.backward:
         log("timing the oracle on the host (cpu_baseline leg)")
         result["cpu_baseline"] = cpu_baseline(inp)
-        if w.name in SMALL_WORKLOADS:
-            one = cpu_baseline(inp, 5.0, one_thread=True)
-            result["cpu_baseline"]["one_thread"] = {k: one[k] for k in ("value", "cores", "sample", "seconds")}
+        log(f"  oracle: {result['cpu_baseline']['value']} tokens/s on {result['cpu_baseline']['cores']} cores")
     print(json.dumps(result), flush=True)
 
 
