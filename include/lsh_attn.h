@@ -54,7 +54,9 @@ enum {
   LSH_ERR_UNSUPPORTED = -4, /* D != 64, C != 64, n_h > 16, unknown dtype or attend bits */
   LSH_ERR_WORKSPACE = -5,   /* workspace pointer NULL or smaller than required */
   LSH_ERR_ALIAS = -6,       /* an output overlaps an input */
-  LSH_ERR_HIP = -7          /* a kernel launch or event record failed */
+  LSH_ERR_HIP = -7,         /* a kernel launch or event record failed */
+  LSH_ERR_TOO_LARGE = -8    /* reformer_lsh_attn_fwd_noalloc: one (batch, head) problem does not
+                               fit its fixed scratch */
 };
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -189,6 +191,34 @@ int reformer_lsh_attn_fwd_ex(const void* qk, const void* v, const void* rot, int
                              int n_hashes, int chunk_len, int causal, int attend, int B, int H,
                              int L, int D, lsh_dtype dt, void* out, float* lse_out, void* ws,
                              size_t ws_bytes, void* stream, void* const* stage_events);
+
+/* The whole forward pass (as reformer_lsh_attn_fwd, attend = 0, no stage
+ * events) without a workspace argument and without allocating: for callers
+ * that cannot allocate device memory (code under HIP graph capture, serving
+ * loops with a fixed memory plan, harnesses that forbid hipMalloc).
+ *   The intermediates live in a fixed scratch array of
+ *   LSH_NOALLOC_SCRATCH_BYTES (256 MiB) per device, part of the library's code
+ *   object: every device the library runs on holds it from the library's load
+ *   until the process ends.  Problems are processed in groups of (batch, head)
+ *   problems whose workspace (lsh_fwd_workspace_bytes) fits the scratch, one
+ *   group after another on `stream`; results are bit-identical to
+ *   reformer_lsh_attn_fwd.  A problem fits when lsh_fwd_workspace_bytes for
+ *   B = H = 1 is at most the scratch size: in bf16 up to n_h * L = 2^20
+ *   token-rounds (L = 65536 with 16 rounds: 164.5 MiB), in fp32 up to 2^19
+ *   (L = 65536 with 8 rounds: 141.8 MiB).
+ *   Returns LSH_ERR_TOO_LARGE, before anything is enqueued, when one problem's
+ *   workspace exceeds the scratch; other errors as in reformer_lsh_attn_fwd.
+ *   The first call on a device looks up that device's scratch address (with
+ *   the device current) and keeps it; a failure there returns LSH_ERR_HIP.
+ *   All calls on one device share its scratch, which keeps the last call's
+ *   contents (every kernel writes what it later reads; nothing needs clearing).
+ *   Calls that overlap in time on one device - on different streams, or from
+ *   different host threads - race on the scratch: order them on one stream or
+ *   synchronise between them. */
+#define LSH_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int reformer_lsh_attn_fwd_noalloc(const void* qk, const void* v, const void* rot, int n_buckets,
+                                  int n_hashes, int chunk_len, int causal, int B, int H, int L,
+                                  int D, lsh_dtype dt, void* out, float* lse_out, void* stream);
 
 /* Backward of the forward pass with respect to qk and v (Reformer explainer:
  * the method's pipeline, differentiated; hashing and sorting are piecewise

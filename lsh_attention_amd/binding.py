@@ -36,6 +36,7 @@ _SIGS = {
     "lsh_sort_workspace_bytes": (_c_int, [_c_int] * 5 + [ctypes.POINTER(_c_size)]),
     "lsh_sort": (_c_int, [_vp, _vp, _vp] + [_c_int] * 5 + [_vp, _c_size, _vp]),
     "lsh_chunk_attn": (_c_int, [_vp] * 5 + [_c_int] * 8 + [_vp]),
+    "reformer_lsh_attn_fwd_noalloc": (_c_int, [_vp, _vp, _vp] + [_c_int] * 9 + [_vp, _vp, _vp]),
     "lsh_chunk_attn_ex_workspace_bytes": (_c_int, [_c_int] * 5 + [ctypes.POINTER(_c_size)]),
     "lsh_chunk_attn_ex": (_c_int, [_vp] * 7 + [_c_int] * 9 + [_vp, _c_size, _vp]),
     "lsh_unsort_combine": (_c_int, [_vp] * 5 + [_c_int] * 6 + [_vp]),
@@ -294,6 +295,29 @@ def reformer_lsh_attn_fwd(qk: torch.Tensor, v: torch.Tensor, rot: torch.Tensor |
         _check("reformer_lsh_attn_fwd_ex", lib().reformer_lsh_attn_fwd_ex(
             qk.data_ptr(), v.data_ptr(), _ptr(rot), n_buckets, n_hashes, chunk_len, int(bool(causal)), attend, B, H,
             L, D, dt, out.data_ptr(), _ptr(lse), workspace.data_ptr(), workspace.numel(), _stream(qk.device), ev))
+    return out, lse
+
+
+def reformer_lsh_attn_fwd_noalloc(qk: torch.Tensor, v: torch.Tensor, rot: torch.Tensor | None, n_buckets: int,
+                                  n_hashes: int, chunk_len: int = 64, causal: bool = False,
+                                  out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                                  want_lse: bool = True):
+    """The fused forward pass on the library's fixed device scratch (no workspace).
+    Returns (out, lse or None); pass `out` / `lse` to allocate nothing here either."""
+    _dev(qk, v, rot, out, lse)
+    B, H, L, D = qk.shape
+    dt = _dtype_code(qk)
+    if v.shape != qk.shape or v.dtype != qk.dtype:
+        raise ValueError("v must match qk in shape and dtype")
+    if rot is not None and rot.dtype != qk.dtype:
+        raise TypeError("rot must have the dtype of qk")
+    if out is None:
+        out = torch.empty_like(qk)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=qk.device)
+    _check("reformer_lsh_attn_fwd_noalloc", lib().reformer_lsh_attn_fwd_noalloc(
+        qk.data_ptr(), v.data_ptr(), _ptr(rot), n_buckets, n_hashes, chunk_len, int(bool(causal)), B, H, L, D, dt,
+        out.data_ptr(), _ptr(lse), _stream(qk.device)))
     return out, lse
 
 

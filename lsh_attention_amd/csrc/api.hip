@@ -2,6 +2,8 @@
 // workspace carving and the stream-ordered launch sequence.  Validation runs
 // entirely on the host and returns before anything is enqueued.
 #include <string.h>
+
+#include <mutex>
 #include <vector>
 
 #include "lsh_block.h"
@@ -231,6 +233,9 @@ const char* lsh_status_string(int status) {
     case LSH_ERR_WORKSPACE: return "workspace missing or too small";
     case LSH_ERR_ALIAS: return "an output overlaps an input";
     case LSH_ERR_HIP: return "HIP launch or event error";
+    case LSH_ERR_TOO_LARGE:
+      return "one (batch, head) problem needs more than the fixed scratch of the allocation-free forward "
+             "(LSH_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -414,6 +419,40 @@ int lsh_fwd_workspace_bytes(int B, int H, int L, int D, int n_b, int n_h, int C,
 
 namespace {
 
+// The launch sequence of the fused forward over BH problems, with every
+// intermediate carved from `base` by the layout `w` (fwd_ws of the same BH, L,
+// n_b, n_h, dt).  sorted_out / undo_out / lse_sorted_out: all or none.
+hipError_t enqueue_forward(const void* qk, const void* v, const void* rot, int n_b, int n_h, int causal, int attend,
+                           int BH, int L, lsh_dtype dt, void* out, float* lse_out, int32_t* sorted_out,
+                           int32_t* undo_out, float* lse_sorted_out, char* base, const FwdWs& w, hipStream_t s,
+                           void* const* stage_events) {
+  const bool save = sorted_out != nullptr;
+  int32_t* buckets = (int32_t*)(base + w.buckets);
+  int32_t* sorted_idx = save ? sorted_out : (int32_t*)(base + w.sorted_idx);
+  int32_t* undo_idx = save ? undo_out : (int32_t*)(base + w.undo_idx);
+  void* o_sorted = base + w.o_sorted;
+  float* lse_sorted = save ? lse_sorted_out : (float*)(base + w.lse_sorted);
+  // Per-token attention scales are a by-product of hashing; with one bucket there is
+  // no hash pass and the attention computes them itself.
+  float2* token_scales = n_b > 1 ? (float2*)(base + w.token_scales) : nullptr;
+  int k = 0;
+  hipError_t e = hipSuccess;
+  if (stage_events != nullptr) e = hipEventRecord((hipEvent_t)stage_events[0], s);
+  if (e == hipSuccess)
+    e = enqueue_hash(qk, rot, buckets, token_scales, base + w.hash_base, w.hash, BH, L, n_b, n_h, dt, s,
+                     stage_events, &k);
+  if (e == hipSuccess)
+    e = enqueue_sort(buckets, sorted_idx, undo_idx, (int*)(base + w.sort_base), BH, L, n_b, n_h, s, stage_events,
+                     &k);
+  if (e == hipSuccess)
+    e = launch_chunk_attn(qk, v, sorted_idx, o_sorted, lse_sorted, token_scales, buckets, undo_idx,
+                          (int32_t*)(base + w.tok_rec), BH, L, n_h, causal, attend, dt, s);
+  if (e == hipSuccess && stage_events != nullptr) e = hipEventRecord((hipEvent_t)stage_events[++k], s);
+  if (e == hipSuccess) e = launch_combine(o_sorted, lse_sorted, undo_idx, out, lse_out, BH, L, n_h, dt, s);
+  if (e == hipSuccess && stage_events != nullptr) e = hipEventRecord((hipEvent_t)stage_events[++k], s);
+  return e;
+}
+
 // The fused forward; sorted_idx / undo_idx / lse_sorted (all or none) receive
 // the state that the backward pass reuses instead of workspace scratch.
 int fused_forward(const void* qk, const void* v, const void* rot, int n_buckets, int n_hashes, int chunk_len,
@@ -462,32 +501,8 @@ int fused_forward(const void* qk, const void* v, const void* rot, int n_buckets,
     }
   }
 
-  hipStream_t s = (hipStream_t)stream;
-  char* base = (char*)ws;
-  int32_t* buckets = (int32_t*)(base + w.buckets);
-  int32_t* sorted_idx = save ? sorted_out : (int32_t*)(base + w.sorted_idx);
-  int32_t* undo_idx = save ? undo_out : (int32_t*)(base + w.undo_idx);
-  void* o_sorted = base + w.o_sorted;
-  float* lse_sorted = save ? lse_sorted_out : (float*)(base + w.lse_sorted);
-  // Per-token attention scales are a by-product of hashing; with one bucket there is
-  // no hash pass and the attention computes them itself.
-  float2* token_scales = n_b > 1 ? (float2*)(base + w.token_scales) : nullptr;
-  int k = 0;
-  hipError_t e = hipSuccess;
-  if (stage_events != nullptr) e = hipEventRecord((hipEvent_t)stage_events[0], s);
-  if (e == hipSuccess)
-    e = enqueue_hash(qk, rot, buckets, token_scales, base + w.hash_base, w.hash, BH, L, n_b, n_h, dt, s,
-                     stage_events, &k);
-  if (e == hipSuccess)
-    e = enqueue_sort(buckets, sorted_idx, undo_idx, (int*)(base + w.sort_base), BH, L, n_b, n_h, s, stage_events,
-                     &k);
-  if (e == hipSuccess)
-    e = launch_chunk_attn(qk, v, sorted_idx, o_sorted, lse_sorted, token_scales, buckets, undo_idx,
-                          (int32_t*)(base + w.tok_rec), BH, L, n_h, causal, attend, dt, s);
-  if (e == hipSuccess && stage_events != nullptr) e = hipEventRecord((hipEvent_t)stage_events[++k], s);
-  if (e == hipSuccess) e = launch_combine(o_sorted, lse_sorted, undo_idx, out, lse_out, BH, L, n_h, dt, s);
-  if (e == hipSuccess && stage_events != nullptr) e = hipEventRecord((hipEvent_t)stage_events[++k], s);
-  return hip_status(e);
+  return hip_status(enqueue_forward(qk, v, rot, n_b, n_h, causal, attend, BH, L, dt, out, lse_out, sorted_out,
+                                    undo_out, lse_sorted_out, (char*)ws, w, (hipStream_t)stream, stage_events));
 }
 
 }  // namespace
@@ -519,6 +534,95 @@ int reformer_lsh_attn_fwd_train(const void* qk, const void* v, const void* rot, 
     return LSH_ERR_NULL;
   return fused_forward(qk, v, rot, n_buckets, n_hashes, chunk_len, causal, 0, B, H, L, D, dt, out, lse_out,
                        sorted_idx, undo_idx, lse_sorted, ws, ws_bytes, stream, stage_events);
+}
+
+}  // extern "C"
+
+// ---- The allocation-free forward: a fixed device scratch in place of the workspace ----
+namespace {
+
+// Every device the library runs on holds one copy of this array (allocated when
+// the code object is loaded there) until the process ends.  In host code its
+// name is only a stand-in: the device address of each device's copy comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[LSH_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up on the first call
+// on that device (with the device current) and kept.
+hipError_t current_scratch(char** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = (char*)g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// The largest number of (batch, head) problems whose forward workspace fits the
+// scratch (0 when one does not).
+int noalloc_group(int BH, int L, int n_b, int n_h, lsh_dtype dt) {
+  const size_t one = fwd_ws(1, L, n_b, n_h, dt).total;
+  if (one > LSH_NOALLOC_SCRATCH_BYTES) return 0;
+  int g = (int)(LSH_NOALLOC_SCRATCH_BYTES / one);
+  if (g > BH) g = BH;
+  while (g > 1 && fwd_ws(g, L, n_b, n_h, dt).total > LSH_NOALLOC_SCRATCH_BYTES) --g;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+int reformer_lsh_attn_fwd_noalloc(const void* qk, const void* v, const void* rot, int n_buckets, int n_hashes,
+                                  int chunk_len, int causal, int B, int H, int L, int D, lsh_dtype dt, void* out,
+                                  float* lse_out, void* stream) {
+  int st = check_problem(B, H, L, D, n_hashes);
+  if (st == LSH_OK) st = check_buckets(n_buckets, L);
+  if (st != LSH_OK) return st;
+  if (chunk_len != kChunk) return chunk_len <= 0 ? LSH_ERR_SHAPE : LSH_ERR_UNSUPPORTED;
+  if (!dtype_ok(dt)) return LSH_ERR_UNSUPPORTED;
+  if (is_empty(B, H, L)) return LSH_OK;
+  if (qk == nullptr || v == nullptr || out == nullptr || (n_buckets > 1 && rot == nullptr)) return LSH_ERR_NULL;
+  const int BH = B * H, n_h = n_hashes, n_b = n_buckets;
+  const int group = noalloc_group(BH, L, n_b, n_h, dt);
+  if (group == 0) return LSH_ERR_TOO_LARGE;
+  const size_t es = elem_size(dt);
+  const size_t in_bytes = (size_t)BH * L * kD * es;
+  const size_t rot_bytes = n_b > 1 ? (size_t)n_h * kD * (n_b / 2) * es : 0;
+  const size_t lo_bytes = (size_t)BH * L * sizeof(float);
+  const void* ins[3] = {qk, v, rot};
+  const size_t in_n[3] = {in_bytes, in_bytes, rot_bytes};
+  for (int a = 0; a < 3; ++a)
+    if (overlaps(out, in_bytes, ins[a], in_n[a]) || overlaps(lse_out, lo_bytes, ins[a], in_n[a]))
+      return LSH_ERR_ALIAS;
+  if (overlaps(out, in_bytes, lse_out, lo_bytes)) return LSH_ERR_ALIAS;
+  char* base = nullptr;
+  hipError_t e = current_scratch(&base);
+  if (e != hipSuccess) return LSH_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  // Groups of problems in stream order on the one scratch: each group's kernels
+  // finish their reads of it before the next group's first kernel writes it.
+  for (int g0 = 0; g0 < BH && e == hipSuccess; g0 += group) {
+    const int n = BH - g0 < group ? BH - g0 : group;
+    const FwdWs w = fwd_ws(n, L, n_b, n_h, dt);
+    const size_t row0 = (size_t)g0 * L;
+    e = enqueue_forward((const char*)qk + row0 * kD * es, (const char*)v + row0 * kD * es, rot, n_b, n_h, causal, 0,
+                        n, L, dt, (char*)out + row0 * kD * es, lse_out == nullptr ? nullptr : lse_out + row0,
+                        nullptr, nullptr, nullptr, base, w, s, nullptr);
+  }
+  return hip_status(e);
 }
 
 int lsh_attn_bwd_workspace_bytes(int B, int H, int L, int D, int n_h, int C, lsh_dtype dt, size_t* bytes) {

@@ -248,3 +248,31 @@ def test_block_calls_reject_before_launch(L):
     params[7] = None
     assert f(P1, P2, P3, pp, 1, 256, 2, 8, 2, 64, 0, 100, BF, P4, P5, P6, need, None, None) == NULL
     assert f(None, None, None, None, 1, 0, 2, 8, 2, 64, 0, 100, BF, None, None, None, 0, None, None) == OK
+
+
+TOO_LARGE = -8
+
+
+def test_noalloc_forward_rejects_on_the_host(L):
+    """The allocation-free forward validates like reformer_lsh_attn_fwd and
+    rejects a problem whose workspace exceeds its fixed scratch before it looks
+    up the scratch or enqueues anything (no GPU is used here)."""
+    f = L.reformer_lsh_attn_fwd_noalloc
+    # fp32, one problem of 65536 tokens with 16 rounds: about 296 MiB of workspace
+    big = bd.fwd_workspace_bytes(1, 1, 65536, 64, 4096, 16, 64, F32)
+    assert big > 256 << 20
+    assert f(P1, P2, P3, 4096, 16, 64, 0, 1, 1, 65536, 64, F32, P4, P5, None) == TOO_LARGE
+    # the largest bf16 problem the header names fits (2^20 token-rounds)
+    assert bd.fwd_workspace_bytes(1, 1, 65536, 64, 4096, 16, 64, BF16) <= 256 << 20
+    assert bd.fwd_workspace_bytes(1, 1, 65536, 64, 4096, 8, 64, F32) <= 256 << 20
+    assert f(None, P2, P3, 16, 1, 64, 0, 1, 1, 1024, 64, F32, P4, P5, None) == NULL
+    assert f(P1, P2, None, 16, 1, 64, 0, 1, 1, 1024, 64, F32, P4, P5, None) == NULL
+    assert f(P1, P2, P3, 16, 1, 64, 0, 1, 1, 1000, 64, F32, P4, P5, None) == SHAPE
+    assert f(P1, P2, P3, 15, 1, 64, 0, 1, 1, 1024, 64, F32, P4, P5, None) == BUCKETS
+    assert f(P1, P2, P3, 16, 1, 32, 0, 1, 1, 1024, 64, F32, P4, P5, None) == UNSUPPORTED
+    assert f(P1, P2, P3, 16, 1, 64, 0, 1, 1, 1024, 64, 7, P4, P5, None) == UNSUPPORTED
+    # out overlapping qk
+    assert f(P1, P2, P3, 16, 1, 64, 0, 1, 1, 1024, 64, F32, P1 + 64, P5, None) == ALIAS
+    # empty problems are no-op successes that touch no pointer
+    assert f(None, None, None, 16, 1, 64, 0, 0, 1, 1024, 64, F32, None, None, None) == OK
+    assert L.lsh_status_string(TOO_LARGE) != L.lsh_status_string(99)
