@@ -13,6 +13,12 @@ def problem_recall(args):
     query's window union, and per query the bracket test of the mass; plus the
     number of queries whose 2-round windows are contained in their 8-round
     windows (all but those in round 0's first chunk, whose look-back differs)."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):  # one BLAS thread per worker process
+        return _problem_recall(args)
+
+
+def _problem_recall(args):
     x, q, perms, C = args
     L = x.shape[0]
     out = {}

@@ -126,8 +126,19 @@ def test_peaked_recall_from_the_gpu_permutation(gpu_lib):
                      {n_h: (perms[n_h][0][b, h], perms[n_h][1][b, h]) for n_h in (2, 8)}, 64))
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
     say(f"  oracle recall on {len(jobs)} problems x 2048 queries, {workers} CPU worker processes")
-    with ProcessPoolExecutor(workers, mp_context=get_context("spawn")) as ex:
-        res = list(ex.map(_recall_pool.problem_recall, jobs))
+    # the workers start with one BLAS thread each (their numpy reads these at import)
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    try:
+        for k in saved:
+            os.environ[k] = "1"
+        with ProcessPoolExecutor(workers, mp_context=get_context("spawn")) as ex:
+            res = list(ex.map(_recall_pool.problem_recall, jobs))
+    finally:
+        for k, val in saved.items():
+            if val is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = val
     mean = {n_h: {k: float(np.mean([r[n_h][k] for r in res])) for k in ("r1", "r16", "mass", "chance")}
             for n_h in (2, 8)}
     for (b, h), r in zip(problems, res):
