@@ -123,6 +123,7 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
   __shared__ __attribute__((aligned(16))) float sKs[2][64];   // key scale: log2(e) / (8 |x_j|)
   __shared__ __attribute__((aligned(16))) float sM[2][64];    // query bound: log2(e) |x_i| / 8
   __shared__ __attribute__((aligned(16))) int sPos[kCPB + 1][64];
+  __shared__ __attribute__((aligned(16))) float sPf[kCPB + 1][64];  // 2 * position (exact below 2^23)
   // Variant tables (dynamic LDS, [entry][row] each, rounds inner for sChk):
   // sCode, sChk[entry][round][row], sLast, sFirst.
   extern __shared__ __attribute__((aligned(16))) int sVar[];
@@ -134,6 +135,7 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
   const int bh = blockIdx.x / blocks_per_bh;
   const int c0 = (blockIdx.x % blocks_per_bh) * cpb;
   const int c1 = min(n_chunks, c0 + cpb);
+  const int cpr = L / kChunk;  // chunks per round
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15;  // query (column) of the MFMA tiles
@@ -153,7 +155,9 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
   for (int e = tid; e < (c1 - c0 + 1) * 64; e += 256) {
     const int k = e >> 6, r = e & 63;
     const int c = (k == 0) ? (c0 - 1 + n_chunks) % n_chunks : c0 - 1 + k;
-    sPos[k][r] = (int)min((uint32_t)sidx[(size_t)c * kChunk + r], (uint32_t)(L - 1));
+    const int pos = (int)min((uint32_t)sidx[(size_t)c * kChunk + r], (uint32_t)(L - 1));
+    sPos[k][r] = pos;
+    sPf[k][r] = 2.0f * (float)pos;
   }
   __syncthreads();
   if constexpr (ATTEND != 0) {
@@ -403,27 +407,55 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
     float sum = 0.f;
     f32x4 oacc[4];
     float off = M2;
+    bool self_only = false, patch = false;
     if constexpr (ATTEND == 0) {
     // ---- fast path: probabilities offset by the a-priori bound M2, masks as zeroes ----
+    // The causal mask is a median: y = 2 (query position - key position) is >= 2
+    // for a key that is kept and <= 0 for one at or after the query, and the
+    // probability is at most 1 + 2^-20, so med3(p, 0, y) is p or 0 (no
+    // compare/select pair, whose mask register costs wait states between the two).
+      const float qf2 = sPf[kc][qrow];
 #pragma unroll
       for (int kt = 0; kt < 8; ++kt) {
         const int slot = kt < 4 ? prv : cur;
         const int kr0 = 16 * (kt & 3) + 4 * grp;
         const float4 ks = *(const float4*)(&sKs[slot][kr0]);
-        const int4 kp = *(const int4*)(&sPos[kt < 4 ? kc - 1 : kc][kr0]);
         const float ksv[4] = {ks.x, ks.y, ks.z, ks.w};
-        const int kpos[4] = {kp.x, kp.y, kp.z, kp.w};
+        if constexpr (CAUSAL) {
+          const float4 kf = *(const float4*)(&sPf[kt < 4 ? kc - 1 : kc][kr0]);
+          const float kfv[4] = {kf.x, kf.y, kf.z, kf.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float q = __builtin_amdgcn_exp2f(fmaf(acc[kt][e], ksv[e], -M2));
-          const bool drop = CAUSAL ? (kpos[e] >= qpos) : (kpos[e] == qpos);
-          p[kt][e] = drop ? 0.f : q;
-          sum += p[kt][e];
+          for (int e = 0; e < 4; ++e) {
+            const float q = __builtin_amdgcn_exp2f(fmaf(acc[kt][e], ksv[e], -M2));
+            p[kt][e] = __builtin_amdgcn_fmed3f(q, 0.f, qf2 - kfv[e]);
+            sum += p[kt][e];
+          }
+        } else {
+          // only the self key is masked
+          const int4 kp = *(const int4*)(&sPos[kt < 4 ? kc - 1 : kc][kr0]);
+          const int kpos[4] = {kp.x, kp.y, kp.z, kp.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float q = __builtin_amdgcn_exp2f(fmaf(acc[kt][e], ksv[e], -M2));
+            p[kt][e] = kpos[e] == qpos ? 0.f : q;
+            sum += p[kt][e];
+          }
         }
       }
       sum = qsum(sum);
       pv(p, oacc);
-      if (__builtin_expect(__ballot(!(sum >= kMinSum)) != 0ull, 0)) {
+      // A row whose sum is not usable.  With M2 < 60 every kept key has probability
+      // at least 2^-120, so a zero sum means that every key but the self was masked.
+      // In a chunk that is not the first of its round the look-back chunk belongs
+      // to the same round, so the self key occurs once and the exact result is
+      // o = v_self, lse = -1e5: such rows are patched after the normalisation (the
+      // common rare case: causal queries early in the sequence).  Anything else (a
+      // self key that may occur twice, a tiny non-zero sum) takes the exact path.
+      const bool z = !(sum >= kMinSum);
+      self_only = z && sum == 0.f && M2 < 60.f;
+      if (__builtin_expect(__ballot(z) != 0ull, 0))
+        patch = (c % cpr) != 0 && __ballot(z && !self_only) == 0ull;
+      if (__builtin_expect(__ballot(z && !patch) != 0ull, 0)) {
         // Exact path for the wave (rare): logits with the -1e5 self value and the
         // row maximum, recomputed from the LDS tiles.  The clobber makes this path
         // reload its LDS operands instead of keeping the fast path's loads live.
@@ -555,27 +587,47 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
     const float rs = __builtin_amdgcn_rcpf(sum);
     const size_t row_g = (size_t)c * kChunk + qrow;
     T* orow = obase + row_g * kD;
+    const bool own = patch && self_only;  // o = v_self, lse = -1e5
+    uint32_t ow[BF16 ? 8 : 16];           // the lane's pieces of the output row
+    const char* vself = vq + (uint32_t)qpos * kRowBytes;
     if constexpr (BF16) {
       // O^T row r is V^T row r: dim 2r for r < 32, dim 2(r - 32) + 1 above.  The
       // lane's tiles 0 and 2 hold dims 8 grp + 0..7 (even, odd interleaved), tiles
-      // 1 and 3 dims 32 + 8 grp + 0..7: two 16-byte stores.
-      uint32_t w[2][4];
+      // 1 and 3 dims 32 + 8 grp + 0..7: two 16-byte pieces of the output row.
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          w[h][e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
-                                                     f32x2{oacc[h][e] * rs, oacc[h + 2][e] * rs}, bf16x2));
-      *(uint4*)(orow + 8 * grp) = make_uint4(w[0][0], w[0][1], w[0][2], w[0][3]);
-      *(uint4*)(orow + 32 + 8 * grp) = make_uint4(w[1][0], w[1][1], w[1][2], w[1][3]);
+          ow[4 * h + e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                                                           f32x2{oacc[h][e] * rs, oacc[h + 2][e] * rs}, bf16x2));
+      if (__builtin_expect(own, 0)) {
+        const uint4 a = *(const uint4*)(vself + 16u * grp), b = *(const uint4*)(vself + 64u + 16u * grp);
+        ow[0] = a.x; ow[1] = a.y; ow[2] = a.z; ow[3] = a.w;
+        ow[4] = b.x; ow[5] = b.y; ow[6] = b.z; ow[7] = b.w;
+      }
     } else {
       // lane holds dims 16 dt + 4 grp + 0..3 of its query
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
-        *(float4*)(orow + 16 * dt + 4 * grp) =
-            make_float4(oacc[dt][0] * rs, oacc[dt][1] * rs, oacc[dt][2] * rs, oacc[dt][3] * rs);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ow[4 * dt + e] = __float_as_uint(oacc[dt][e] * rs);
+      if (__builtin_expect(own, 0)) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const uint4 a = *(const uint4*)(vself + 4u * (16 * dt + 4 * grp));
+          ow[4 * dt] = a.x; ow[4 * dt + 1] = a.y; ow[4 * dt + 2] = a.z; ow[4 * dt + 3] = a.w;
+        }
+      }
     }
-    if (grp == 0) lbase[row_g] = (off + __builtin_amdgcn_logf(sum)) * kLn2;
+    if constexpr (BF16) {
+      *(uint4*)(orow + 8 * grp) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+      *(uint4*)(orow + 32 + 8 * grp) = make_uint4(ow[4], ow[5], ow[6], ow[7]);
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        *(uint4*)(orow + 16 * dt + 4 * grp) = make_uint4(ow[4 * dt], ow[4 * dt + 1], ow[4 * dt + 2], ow[4 * dt + 3]);
+    }
+    if (grp == 0) lbase[row_g] = own ? kSelf2 * kLn2 : (off + __builtin_amdgcn_logf(sum)) * kLn2;
 
     // From here through the issue of the next iteration's gather the wave runs
     // at raised priority: the block's critical path (the barriers, the commit
