@@ -71,16 +71,18 @@ const char* lsh_status_string(int status);
  *                             the index of the largest entry of
  *                             [x R_r ; -x R_r], lowest index on exact ties.
  *   ws      workspace of at least lsh_hash_workspace_bytes(...) bytes.
- * The decision is exact: fp32 MFMA scores are certified against a rigorous
- * rounding bound, and any token whose top two scores are closer than that
- * bound is re-decided from float64 sums. */
+ * The decision is exact for finite inputs: fp32 MFMA scores are certified
+ * against a rigorous rounding bound; a token whose top two scores are closer
+ * than that bound is re-scored in float64 against a bound of its own, and the
+ * columns still inside it (and a winner's sign within it of zero) are decided
+ * by exact summation of the float64 products. */
 int lsh_hash_workspace_bytes(int B, int H, int L, int D, int n_b, int n_h, lsh_dtype dt,
                              size_t* bytes);
 int lsh_hash(const void* qk, const void* rot, int32_t* buckets, int B, int H, int L, int D,
              int n_b, int n_h, lsh_dtype dt, void* ws, size_t ws_bytes, void* stream);
 
 /* How many token-rounds the last hashing on this workspace could not certify in
- * fp32 and re-decided from float64 sums: the near-ties of the argmax, counted
+ * fp32 and re-decided in the fixup pass: the near-ties of the argmax, counted
  * by the GPU (same decision rule as lsh_hash above).
  *   ws      the workspace of the last lsh_hash or reformer_lsh_attn_fwd /
  *           _fwd_ex / _fwd_train call (the hashing part sits at the start of
@@ -167,7 +169,7 @@ int lsh_unsort_combine(const void* o_sorted, const float* lse_sorted, const int3
  * LSH_FWD_KERNEL_* list, for per-kernel timing. */
 #define LSH_FWD_KERNEL_PREP 0      /* rotation transpose + norms */
 #define LSH_FWD_KERNEL_HASH 1      /* MFMA projection + certified argmax */
-#define LSH_FWD_KERNEL_FIXUP 2     /* float64 re-decision of uncertified tokens */
+#define LSH_FWD_KERNEL_FIXUP 2     /* float64/exact re-decision of uncertified tokens */
 #define LSH_FWD_KERNEL_HIST 3      /* per-tile bucket histograms */
 #define LSH_FWD_KERNEL_SCATTER 4   /* histogram scan + stable in-tile ranking + scatter */
 #define LSH_FWD_KERNEL_ATTN 5      /* chunked attention */

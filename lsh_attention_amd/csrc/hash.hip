@@ -20,9 +20,13 @@
 //  * The decision is certified: an fp32 sum of 64 exact bf16 products (or
 //    rounded fp32 products) is within eps = 65 * 2^-23 * |x| * max_j |r_j| of
 //    the exact value, and the key truncation adds at most one key-grid step
-//    delta.  If the top-2 gap is not above 2 eps + delta the token is queued and
-//    re-decided from float64 sums by `fixup_kernel`, so the result equals the
-//    exact-arithmetic argmax.
+//    delta.  If the top-2 gap is not above 2 eps + delta the token is queued
+//    for `fixup_kernel`, which re-scores the columns that may win in float64
+//    (each product exact) with a rounding bound of its own, and decides the
+//    ones that bound cannot separate, and the sign of a winner whose sum lies
+//    within it of zero, by exact summation of the products (floating-point
+//    expansions).  The result is the exact-arithmetic argmax for all finite
+//    inputs whose products stay within float64's range.
 //  * The rotation is shared by every (batch, head): it is transposed once per
 //    call into [n_h][n_b/2 padded to 64][D] so a workgroup stages it into LDS
 //    in 64-column blocks with 16-byte row loads (block k+2 is loaded into
@@ -32,6 +36,7 @@
 //    tile t+1 are issued before the vector top-2 selection of tile t, so the
 //    matrix and vector work of a wave overlap (they hardly overlap across
 //    waves on gfx950).
+#include "exact_sum.h"
 #include "lsh_internal.h"
 
 namespace lsh {
@@ -477,7 +482,7 @@ __global__ __launch_bounds__(kFixWaves * 64) void fixup_kernel(const T* __restri
                                                                const int* __restrict__ fix_count, int L, int n_h,
                                                                int half, int halfp) {
   constexpr int P = kD * (int)sizeof(T) / 16;  // 16-byte pieces per row
-  __shared__ float ssc[kFixWaves][kMaxHalfp];  // |fp32 score|, slot 64 g + lane of batch g
+  __shared__ __attribute__((aligned(16))) float ssc[kFixWaves][kMaxHalfp];  // |fp32 score|, slot 64 g + lane of batch g
   const int lane = threadIdx.x & 63;
   float* sc = ssc[threadIdx.x >> 6];
   const int gw = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
@@ -548,46 +553,172 @@ __global__ __launch_bounds__(kFixWaves * 64) void fixup_kernel(const T* __restri
       if (lane == src) mask &= mask - 1u;
     }
     const bool overflow = __ballot(mask != 0) != 0;
-    double best_v = -1.0;
+    // Each candidate's float64 sum is certified against its rounding: the exact
+    // sum S and the computed one differ by at most err * sum|x_d r_d| (err =
+    // 8 * 2^-53 for the 6-level butterfly below, 72 * 2^-53 for a serial fma
+    // chain of 64 terms; sum|x_d r_d| itself computed the same way).  The winner
+    // is decided in float64 when its interval lies strictly above every other
+    // candidate's and away from zero (so its sign, which picks column j or
+    // j + half, is exact); otherwise every candidate that may win is compared
+    // exactly (exact_abs_compare), lowest index on equal values.
+    constexpr double kErrTree = 0x1p-50, kErrSerial = 72.0 * 0x1p-53;
+    double* ex = (double*)sc;  // the wave's LDS area, free after phase 1: 1024 doubles
+    double* pa = ex;           // products of the current best column
+    double* pb = ex + 64;      // products of the column it is compared with
+    double* e1 = ex + 128;     // expansions: 64 + 64 + 128
+    double* e2 = ex + 192;
+    double* e3 = ex + 256;
+    const T* rrow = rot_t + (size_t)r * halfp * kD;  // this round's transposed rotation
     int best_i = 0x7FFFFFFF;
+    int best_j = -1;            // column of a float64 winner that could not be certified
+    uint32_t cmask = 0;         // this lane's columns j = lane + 64 k that may beat it (bit k)
+    uint32_t cand8 = 0;         // or: candidates c of the short list that may (bit c)
     if (!overflow) {
       T rv[kMaxCand];
 #pragma unroll
-      for (int c = 0; c < kMaxCand; ++c) rv[c] = cj[c] >= 0 ? rot_t[((size_t)r * halfp + cj[c]) * kD + lane] : T(0);
+      for (int c = 0; c < kMaxCand; ++c) rv[c] = cj[c] >= 0 ? rrow[(size_t)cj[c] * kD + lane] : T(0);
+      double S[kMaxCand], A[kMaxCand];
+#pragma unroll
+      for (int c = 0; c < kMaxCand; ++c) {
+        double p = cj[c] >= 0 ? xd * to_f64(rv[c]) : 0.0, q = fabs(p);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+          p += __shfl_xor(p, off);
+          q += __shfl_xor(q, off);
+        }
+        S[c] = p;
+        A[c] = q;
+      }
+      int bc = 0;
+      double bv = -1.0;
 #pragma unroll
       for (int c = 0; c < kMaxCand; ++c) {
         if (cj[c] < 0) break;
-        double p = xd * to_f64(rv[c]);
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) p += __shfl_xor(p, off);
-        const double v = fabs(p);
-        const int i = p < 0.0 ? cj[c] + half : cj[c];  // the larger of +p (index j) and -p (index j + half)
-        if (v > best_v || (v == best_v && i < best_i)) {
-          best_v = v;
+        const double v = fabs(S[c]);
+        const int i = S[c] < 0.0 ? cj[c] + half : cj[c];  // the larger of +p (index j) and -p (index j + half)
+        if (v > bv || (v == bv && i < best_i)) {
+          bv = v;
           best_i = i;
+          bc = c;
         }
       }
+      const double eb = kErrTree * A[bc];
+      bool ok = bv > eb || A[bc] == 0.0;
+#pragma unroll
+      for (int c = 0; c < kMaxCand; ++c)
+        if (cj[c] >= 0 && c != bc && !(bv - eb > fabs(S[c]) + kErrTree * A[c])) {
+          ok = false;
+          cand8 |= 1u << c;
+        }
+      if (!ok) {
+        best_j = cj[bc];
+        best_i = 0x7FFFFFFF;
+      }
     } else {
-      // x re-read from memory (cached) to keep this rare path's registers low
+      // Every column in float64, lane-parallel (x re-read from memory, cached, to
+      // keep this rare path's registers low).
+      double bv = -1.0, be = 0.0;
+      int bj = -1;
       for (int j = lane; j < half; j += 64) {
-        const T* rr = rot_t + ((size_t)r * halfp + j) * kD;
-        double p = 0.0;
-        for (int d = 0; d < kD; ++d) p = fma(to_f64(x[d]), to_f64(rr[d]), p);
+        const T* rr = rrow + (size_t)j * kD;
+        double p = 0.0, q = 0.0;
+        for (int d = 0; d < kD; ++d) {
+          const double t = to_f64(x[d]) * to_f64(rr[d]);
+          p += t;
+          q += fabs(t);
+        }
         const double v = fabs(p);
         const int i = p < 0.0 ? j + half : j;
-        if (v > best_v || (v == best_v && i < best_i)) {
-          best_v = v;
+        if (v > bv || (v == bv && i < best_i)) {
+          bv = v;
           best_i = i;
+          bj = j;
+          be = kErrSerial * q;
         }
       }
       for (int off = 32; off >= 1; off >>= 1) {
-        const double ov = __shfl_xor(best_v, off);
-        const int oi = __shfl_xor(best_i, off);
-        if (ov > best_v || (ov == best_v && oi < best_i)) {
-          best_v = ov;
+        const double ov = __shfl_xor(bv, off), oe = __shfl_xor(be, off);
+        const int oi = __shfl_xor(best_i, off), oj = __shfl_xor(bj, off);
+        if (ov > bv || (ov == bv && oi < best_i)) {
+          bv = ov;
           best_i = oi;
+          bj = oj;
+          be = oe;
         }
       }
+      // Columns whose interval reaches the winner's.
+      for (int j = lane, k = 0; j < half; j += 64, ++k) {
+        if (j == bj) continue;
+        const T* rr = rrow + (size_t)j * kD;
+        double p = 0.0, q = 0.0;
+        for (int d = 0; d < kD; ++d) {
+          const double t = to_f64(x[d]) * to_f64(rr[d]);
+          p += t;
+          q += fabs(t);
+        }
+        if (!(bv - be > fabs(p) + kErrSerial * q)) cmask |= 1u << k;
+      }
+      const bool sign_ok = bv > be || be == 0.0;
+      if (!sign_ok || __ballot(cmask != 0) != 0) {
+        best_j = bj;
+        best_i = 0x7FFFFFFF;
+      }
+    }
+    if (best_j >= 0) {
+      // Exact decision among the winner and the columns that may beat it.  Lane d
+      // writes product d; lane 0 runs the expansions.  (One wave's LDS
+      // operations execute in order, so lane 0 reads what every lane wrote.)
+      pa[lane] = xd * to_f64(rrow[(size_t)best_j * kD + lane]);
+      __builtin_amdgcn_wave_barrier();
+      int sbest = 2;  // sign of the best column's sum once known
+      auto challenge = [&](int j) {
+        const T rj = rrow[(size_t)j * kD + lane], rb = rrow[(size_t)best_j * kD + lane];
+        if (__ballot(rj != rb) == 0ull) {
+          // identical columns: equal sums and signs, so the lower column wins
+          if (j < best_j) best_j = j;
+          return;
+        }
+        pb[lane] = xd * to_f64(rj);
+        __builtin_amdgcn_wave_barrier();
+        int cmp = 0, sa = 0, sbj = 0;
+        if (lane == 0) cmp = exact_abs_compare(pa, pb, kD, e1, e2, e3, sa, sbj);
+        cmp = __shfl(cmp, 0);
+        sa = __shfl(sa, 0);
+        sbj = __shfl(sbj, 0);
+        const int ia = sa < 0 ? best_j + half : best_j, ib = sbj < 0 ? j + half : j;
+        if (cmp < 0 || (cmp == 0 && ib < ia)) {
+          best_j = j;
+          sbest = sbj;
+          pa[lane] = pb[lane];
+          __builtin_amdgcn_wave_barrier();
+        } else {
+          sbest = sa;
+        }
+      };
+      if (!overflow) {
+#pragma unroll
+        for (int c = 0; c < kMaxCand; ++c)
+          if (cand8 & (1u << c)) challenge(cj[c]);
+      } else {
+        for (uint64_t bal = __ballot(cmask != 0); bal != 0ull; bal = __ballot(cmask != 0)) {
+          const int src = __builtin_ctzll(bal);
+          const int k = __builtin_ctz(__shfl(cmask, src));
+          if (lane == src) cmask &= cmask - 1u;
+          challenge(src + 64 * k);
+        }
+      }
+      if (sbest == 2) {
+        // no exact comparison was made (identical columns, or only the winner's
+        // sign was uncertain): the sign of its sum, exactly
+        int sg = 0;
+        if (lane == 0) {
+          int n = 0;
+          for (int k = 0; k < kD; ++k) n = grow_expansion(e1, n, pa[k]);
+          sg = expansion_sign(e1, n);
+        }
+        sbest = __shfl(sg, 0);
+      }
+      best_i = sbest < 0 ? best_j + half : best_j;
     }
     // With finite inputs the best fp32 score is always a candidate; non-finite
     // ones leave the first pass's decision in place.

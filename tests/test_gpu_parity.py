@@ -213,6 +213,83 @@ def test_candidate_limit_boundary(gpu_lib, dtype, copies):
     assert hits > 0 and not np.any(np.isin(got % half, dup[1:]))
 
 
+def _dtype_tensor(a, dtype):
+    """Values rounded to the dtype (round to nearest even for bf16)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if dtype == "bf16":
+        bits = I.bf16_bits_from_f32(a)
+        return I.Tensor(I.f32_from_bf16_bits(bits), bits)
+    return I.Tensor(a)
+
+
+# Crafted tokens (coordinates 0, 1, 2, 6, 34; every other coordinate 0), and
+# their buckets for the two rotations of test_gaps_below_float64_resolution.
+_T = 2.0**-70
+_SUBDOUBLE_TOKENS = [  # (name, {coordinate: value}, bucket with 4 columns, bucket with 16 columns)
+    ("+1,+t", {0: 1.0, 1: _T}, 1, 9),
+    ("+1,-t", {0: 1.0, 1: -_T}, 0, 0),
+    ("-1,+t", {0: -1.0, 1: _T}, 4, 16),
+    ("-1,-t", {0: -1.0, 1: -_T}, 5, 25),
+    ("+1,0 tie", {0: 1.0}, 0, 0),
+    ("-1,0 tie", {0: -1.0}, 4, 16),
+    ("sign +", {2: 1.0, 34: _T, 6: -1.0}, 2, 10),
+    ("sign -", {2: 1.0, 34: -_T, 6: -1.0}, 6, 26),
+    ("sign 0", {2: 1.0, 6: -1.0}, 0, 0),
+    ("zero", {}, 0, 0),
+]
+
+
+@pytest.mark.parametrize("half", [4, 16])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gaps_below_float64_resolution(gpu_lib, dtype, half):
+    """Top-two gaps far below float64's resolution of the scores, so float64 sums
+    tie or even get the sign wrong and only exact summation decides.
+
+    Columns: c0 = e0 and c1 = e0 + e1 (half 4), or c_j = e0 + j 2^-60 e1 for
+    j < 10 (half 16); then c = e2 + e6 + e34 (column 2, resp. 10); the rest are
+    small random columns on coordinates 8..31.  A token (+-1, +-2^-70) scores
+    1 + 2^-70 (or 1 + j 2^-130) against 1 on its rivals: in float64 they are
+    equal.  A token (e2 - e6 +- 2^-70 e34) scores +-2^-70 on the sum column,
+    which a float64 pairwise sum (1 + 2^-70 first, then - 1) gives as 0.  The
+    4-column rotation takes the fixup's candidate short list, the 16-column one
+    (10 or more tied candidates) its all-column loop.  Expected buckets are
+    worked by hand and also the oracle's (exact rationals)."""
+    say(f"case sub-double gaps {dtype} half {half}")
+    rng = np.random.default_rng(70 + half)
+    rot = np.zeros((1, 64, half), dtype=np.float64)
+    n_near = 2 if half == 4 else 10
+    for j in range(n_near):
+        rot[0, 0, j] = 1.0
+        rot[0, 1, j] = 1.0 if half == 4 and j == 1 else j * 2.0**-60
+    rot[0, [2, 6, 34], n_near] = 1.0
+    rot[0, 8:32, n_near + 1:] = rng.standard_normal((24, half - n_near - 1)) * 2.0**-12
+    L = 256
+    x = np.zeros((1, 2, L, 64))
+    x[0, 1] = rng.standard_normal((L, 64))       # head 1: random tokens, mostly near-tied on c_j
+    pos = rng.permutation(L)
+    expect = {}
+    for k, (name, coords, b4, b16) in enumerate(_SUBDOUBLE_TOKENS):
+        for i in pos[k::len(_SUBDOUBLE_TOKENS)]:
+            for c, val in coords.items():
+                x[0, 0, i, c] = val
+            expect[int(i)] = (name, b4 if half == 4 else b16)
+    xt = _dtype_tensor(x, dtype)
+    rt = _dtype_tensor(rot, dtype)
+    assert np.array_equal(xt.values[0, 0], x[0, 0]) and np.array_equal(rt.values[0, :8], rot[0, :8])  # exact
+    n_b = 2 * half
+    ws = torch.empty(bd.hash_workspace_bytes(1, 2, L, 64, n_b, 1, bd.LSH_BF16 if dtype == "bf16" else bd.LSH_F32),
+                     dtype=torch.uint8, device="cuda")
+    got = bd.lsh_hash(to_device(xt), to_device(rt), n_b, 1, workspace=ws).cpu().numpy()
+    for i, (name, b) in sorted(expect.items()):
+        assert got[0, 0, 0, i] == b, f"token {i} ({name}): bucket {got[0, 0, 0, i]}, expected {b}"
+    for h in range(2):
+        ref, _ = O.hash_buckets(xt.values[0, h].astype(np.float64), rt.values.astype(np.float64), n_b)
+        np.testing.assert_array_equal(got[0, h], ref, err_msg=f"head {h}")
+    unc = bd.hash_uncertified(ws, 1, 2, L, n_b, 1, torch.bfloat16 if dtype == "bf16" else torch.float32)
+    say(f"  hand-worked buckets and the oracle agree; {unc} of {2 * L} token-rounds uncertified in fp32")
+    assert unc >= L  # every crafted token is a near-tie
+
+
 def _uncertified_bracket(x64, rot64):
     """Bounds on the number of token-rounds the GPU cannot certify, from exact
     (float64) scores of one problem.  The kernel certifies a decision when its
