@@ -31,6 +31,9 @@
 //    lane holds one query's logits for 4 consecutive keys per 16-key tile.
 //  * O^T = V^T P^T on MFMA: the P^T operand is exactly the lane's own
 //    probabilities (the K index is permuted to match).
+//  * bf16 fast path: S MFMAs, softmax and P.V MFMAs of a chunk run as one
+//    interleaved stream per wave (stage kt: tile kt+1's S, tile kt's
+//    probabilities, an earlier key pair's P.V), not as three serial phases.
 //  * Per-row key scale and query bound come from the hash pass in the fused
 //    forward (token_scales); the standalone call computes them from the rows.
 //  * A query's 128 logits sit in 4 lanes (l, l^16, l^32, l^48); their sums and
@@ -402,7 +405,6 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
     };
 
     f32x4 acc[8];
-    scores(acc);
     float p[8][4];
     float sum = 0.f;
     f32x4 oacc[4];
@@ -415,6 +417,101 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
     // probability is at most 1 + 2^-20, so med3(p, 0, y) is p or 0 (no
     // compare/select pair, whose mask register costs wait states between the two).
       const float qf2 = sPf[kc][qrow];
+      if constexpr (BF16) {
+        // One stream per wave: the offset M2 is known before any logit, so key
+        // tile kt's probabilities need nothing from other tiles and the three
+        // phases interleave.  Stage kt issues the two S MFMAs of tile kt+1 and
+        // two P.V MFMAs of an earlier key pair next to the logits of tile kt
+        // (exp, mask, sum); sched_group_barrier asks for six VALU instructions
+        // after each MFMA and leaves their choice to the scheduler (pinning one
+        // logit per MFMA serialises each exp chain and measured 30 % slower).
+        // The LDS operands of tile kt+2 and of the next pair's V^T are read a
+        // stage ahead.  The sums and the P.V accumulation keep the order of the
+        // phase-by-phase form, so the results are the same bits.
+        const bf16x8 bq0 = *(const bf16x8*)(&sX[cur][xoff(qrow, grp)]);
+        const bf16x8 bq1 = *(const bf16x8*)(&sX[cur][xoff(qrow, 4 + grp)]);
+        bf16x8 ka0[8], ka1[8], va[4][4], bp[4];
+        float ksv[8][4], kfv[8][4];
+        int kpv[8][4];
+        auto loads = [&](int kt) {
+          const int slot = kt < 4 ? prv : cur;
+          const T* kx = sX[slot];
+          const int krow = 16 * (kt & 3) + col, kr0 = 16 * (kt & 3) + 4 * grp;
+          ka0[kt] = *(const bf16x8*)(kx + xoff(krow, grp));
+          ka1[kt] = *(const bf16x8*)(kx + xoff(krow, 4 + grp));
+          const float4 ks = *(const float4*)(&sKs[slot][kr0]);
+          ksv[kt][0] = ks.x; ksv[kt][1] = ks.y; ksv[kt][2] = ks.z; ksv[kt][3] = ks.w;
+          if constexpr (CAUSAL) {
+            const float4 kf = *(const float4*)(&sPf[kt < 4 ? kc - 1 : kc][kr0]);
+            kfv[kt][0] = kf.x; kfv[kt][1] = kf.y; kfv[kt][2] = kf.z; kfv[kt][3] = kf.w;
+          } else {
+            const int4 kp = *(const int4*)(&sPos[kt < 4 ? kc - 1 : kc][kr0]);
+            kpv[kt][0] = kp.x; kpv[kt][1] = kp.y; kpv[kt][2] = kp.z; kpv[kt][3] = kp.w;
+          }
+        };
+        auto vloads = [&](int ks) {
+          const int vpiece = 8 * (ks < 2 ? prv : cur) + 4 * (ks & 1) + grp;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) va[ks][dt] = *(const bf16x8*)(&sVT[voff(16 * dt + col, vpiece)]);
+        };
+        auto smfma = [&](int kt, int h) {
+          if (h == 0)
+            acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0[kt], bq0, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          else
+            acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1[kt], bq1, acc[kt], 0, 0, 0);
+        };
+        auto pvm = [&](int ks, int dt) {
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[ks][dt], bp[ks], oacc[dt], 0, 0, 0);
+        };
+        auto soft = [&](int kt, int e) {
+          const float q = __builtin_amdgcn_exp2f(fmaf(acc[kt][e], ksv[kt][e], -M2));
+          if constexpr (CAUSAL)
+            p[kt][e] = __builtin_amdgcn_fmed3f(q, 0.f, qf2 - kfv[kt][e]);
+          else
+            p[kt][e] = kpv[kt][e] == qpos ? 0.f : q;
+          sum += p[kt][e];
+        };
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        loads(0);
+        loads(1);
+        smfma(0, 0);
+        smfma(0, 1);
+        loads(2);
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) {
+          // P.V of key pair (kt - 2) / 2, dims 2 (kt & 1) + 0, 1: its probabilities
+          // were packed and its V^T operands read in stage kt - 1 or earlier.
+          const bool pv_here = kt >= 2;
+          const int ks = (kt - 2) >> 1, dt0 = 2 * (kt & 1);
+          if (kt + 1 < 8) smfma(kt + 1, 0);
+          soft(kt, 0);
+          if (pv_here) pvm(ks, dt0);
+          soft(kt, 1);
+          if (kt + 1 < 8) smfma(kt + 1, 1);
+          soft(kt, 2);
+          if (pv_here) pvm(ks, dt0 + 1);
+          soft(kt, 3);
+          if (kt + 2 < 8) loads(kt + 2);
+          if (kt & 1) {
+            // K index (grp, e): e < 4 -> key 4 grp + e of tile kt - 1; e >= 4 -> of tile kt.
+            const f32x4 lo = {p[kt - 1][0], p[kt - 1][1], p[kt - 1][2], p[kt - 1][3]};
+            const f32x4 hi = {p[kt][0], p[kt][1], p[kt][2], p[kt][3]};
+            bp[kt >> 1] = __builtin_shufflevector(__builtin_convertvector(lo, bf16x4),
+                                                  __builtin_convertvector(hi, bf16x4), 0, 1, 2, 3, 4, 5, 6, 7);
+            vloads(kt >> 1);
+          }
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+          }
+        }
+        sum = qsum(sum);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) pvm(3, dt);
+      } else {
+      scores(acc);
 #pragma unroll
       for (int kt = 0; kt < 8; ++kt) {
         const int slot = kt < 4 ? prv : cur;
@@ -444,6 +541,7 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
       }
       sum = qsum(sum);
       pv(p, oacc);
+      }
       // A row whose sum is not usable.  With M2 < 60 every kept key has probability
       // at least 2^-120, so a zero sum means that every key but the self was masked.
       // In a chunk that is not the first of its round the look-back chunk belongs
@@ -494,6 +592,7 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
       }
     } else {
       // ---- attended-set variants: exact path (row maximum) for every chunk ----
+      scores(acc);
       // same-bucket: keys with another (round, bucket) code than the query are
       // dropped.  set union: each kept logit, the self's included, gets
       // -log2 N, N = the number of (query occurrence, key occurrence) pairs of
