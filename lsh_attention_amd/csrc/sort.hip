@@ -14,8 +14,9 @@
 //             an exclusive scan over buckets, the counts of earlier tiles and
 //             waves); then each wave ranks its sub-tile's tokens in order: the
 //             lanes holding the same bucket are found with one ballot per key
-//             bit, their rank is a popcount below the lane, and a per-wave LDS
-//             counter per bucket carries the running offset.
+//             bit (4 vector instructions per bit), their rank is the count of
+//             those lanes below this one (mbcnt), and a per-wave LDS counter per
+//             bucket carries the running offset.
 // Bucket values outside [0, n_b) are clamped to n_b - 1 (callers must not
 // pass them; clamping only keeps every write in bounds).
 #include "lsh_internal.h"
@@ -134,16 +135,20 @@ __global__ __launch_bounds__(1024) void sort_scatter_kernel(const int32_t* __res
     const int i = w0 + 64 * k + lane;
     const bool act = bv[k] >= 0;  // i < w1
     const int b = act ? bv[k] : 0;
-    uint64_t match = __ballot(act);
-    for (int k = 0; k < nbits; ++k) {
-      const bool bit = (b >> k) & 1;
-      const uint64_t bal = __ballot(bit);
-      match &= bit ? bal : ~bal;
+    // Lanes holding the same bucket: the active lanes whose ballot of every key
+    // bit agrees with this lane's bit.  s = bit t of b as 0 or all ones, so each
+    // half of the mask takes one three-input bitwise instruction per bit.
+    const uint64_t am = __ballot(act);
+    uint32_t mlo = (uint32_t)am, mhi = (uint32_t)(am >> 32);
+    for (int t = 0; t < nbits; ++t) {
+      const uint32_t s = (uint32_t)__builtin_amdgcn_sbfe(b, (uint32_t)t, 1u);
+      const uint64_t bal = __ballot(s != 0u);
+      mlo &= ~((uint32_t)bal ^ s);
+      mhi &= ~((uint32_t)(bal >> 32) ^ s);
     }
-    const uint64_t below = match & ((1ull << lane) - 1ull);
-    const int rank = __popcll(below);
+    const int rank = (int)__builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));  // same-bucket lanes below
     const int first = act ? cnt[b] : 0;
-    if (act && below == 0ull) cnt[b] = first + __popcll(match);
+    if (act && rank == 0) cnt[b] = first + __popc(mlo) + __popc(mhi);
     if (act) {
       const int g = r * L + first + rank;
       sidx[g] = i;
