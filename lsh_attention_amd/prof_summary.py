@@ -32,6 +32,13 @@ KERNEL_SOURCES = {
 }
 
 
+N_XCDS = 8      # GRBM_GUI_ACTIVE counts shader cycles on each of the 8 XCDs
+N_SIMDS = 1024  # 256 CUs x 4 SIMDs; SQ counters are device totals
+# Cycles one MFMA occupies its SIMD's matrix pipe: v_mfma_f32_32x32x16_bf16 (hash)
+# and v_mfma_f32_16x16x32_bf16 (chunk attention) at 512 and 256 MACs per cycle.
+MFMA_CYCLES = {"hash": 32, "chunk_attn": 16}
+
+
 def kernel_key(name: str) -> str:
     m = re.search(r"(\w+)_kernel\b", name)
     if m:
@@ -59,14 +66,24 @@ def stats_table(d: str) -> str:
 
 
 def counters(d: str):
-    """{kernel: {counter: mean over dispatches of the per-dispatch value}} plus the copy kernel's bytes."""
+    """{kernel: {counter: mean over dispatches of the per-dispatch value}} plus the copy kernel's bytes.
+    Each kernel also gets "_dur_ns" (mean dispatch duration) and, when GRBM_GUI_ACTIVE was
+    collected, "_clock_ghz" (mean over dispatches of that counter / 8 XCDs / duration)."""
     per = collections.defaultdict(lambda: collections.defaultdict(lambda: collections.defaultdict(float)))
-    copy_bytes = {}
+    dur = collections.defaultdict(dict)
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
             k = kernel_key(r["Kernel_Name"])
-            per[k][r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+            key = f"{f}:{r['Dispatch_Id']}"
+            per[k][r["Counter_Name"]][key] += float(r["Counter_Value"])
+            dur[k][key] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     out = {k: {c: sum(v.values()) / len(v) for c, v in cs.items()} for k, cs in per.items()}
+    for k in out:
+        out[k]["_dur_ns"] = sum(dur[k].values()) / len(dur[k])
+        g = per[k].get("GRBM_GUI_ACTIVE")
+        if g:
+            clocks = [g[x] / N_XCDS / dur[k][x] for x in g if dur[k].get(x)]
+            out[k]["_clock_ghz"] = sum(clocks) / len(clocks)
     # The probe is the run's largest copy (small read-backs use the same blit kernel).
     if "copy" in per:
         out["copy"] = {c: max(v.values()) for c, v in per["copy"].items()}
@@ -110,6 +127,26 @@ def counter_table(d: str, kernels=("hash", "fixup", "sort_scatter", "chunk_attn"
         out.append(f"| {k} | {ratio('SQ_INSTS_VALU', 'SQ_INSTS_MFMA')} | "
                    f"{ratio('SQ_VALU_MFMA_COEXEC_CYCLES', 'SQ_VALU_MFMA_BUSY_CYCLES')} | "
                    f"{ratio('SQ_LDS_BANK_CONFLICT', 'SQ_INSTS_LDS')} | {ratio('SQ_INSTS_VALU_TRANS_F32', 'SQ_INSTS_VALU')} |")
+    out += ["", "| kernel | dispatch (us) | shader clock (GHz) | MFMA pipe busy | MFMA busy from instruction count "
+            "| VALU issue (non-MFMA) | wave-cycles waiting on dependencies | wave-cycles waiting to issue |",
+            "|---|---|---|---|---|---|---|---|"]
+    for k in kernels:
+        v = c.get(k, {})
+        ghz = v.get("_clock_ghz")
+        cyc = v["_dur_ns"] * ghz if ghz else None  # shader cycles per dispatch
+
+        def frac(x):
+            return "-" if x is None else f"{x:.3f}"
+        busy = v["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMDS * cyc) if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in v else None
+        by_count = (v["SQ_INSTS_MFMA"] * MFMA_CYCLES[k] / (N_SIMDS * cyc)
+                    if cyc and k in MFMA_CYCLES and "SQ_INSTS_MFMA" in v else None)
+        valu = ((v["SQ_INSTS_VALU"] - v.get("SQ_INSTS_MFMA", 0.0)) * 4 / (N_SIMDS * cyc)
+                if cyc and "SQ_INSTS_VALU" in v else None)
+        wc = v.get("SQ_WAVE_CYCLES")
+        w_dep = v["SQ_WAIT_ANY"] / wc if wc and "SQ_WAIT_ANY" in v else None
+        w_iss = v["SQ_WAIT_INST_ANY"] / wc if wc and "SQ_WAIT_INST_ANY" in v else None
+        out.append(f"| {k} | {v['_dur_ns'] / 1e3:.1f} | {frac(ghz)} | {frac(busy)} | {frac(by_count)} | "
+                   f"{frac(valu)} | {frac(w_dep)} | {frac(w_iss)} |")
     return "\n".join(out)
 
 
