@@ -113,7 +113,8 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
     const typename AttnTraits<BF16>::T* __restrict__ qk, const typename AttnTraits<BF16>::T* __restrict__ v,
     const int32_t* __restrict__ sorted_idx, typename AttnTraits<BF16>::T* __restrict__ o_out,
     float* __restrict__ lse_out, const float2* __restrict__ token_scales, const int32_t* __restrict__ buckets,
-    const int32_t* __restrict__ tok_rec, int L, int n_h, int n_slots, int n_chunks, int blocks_per_bh, int cpb) {
+    const int32_t* __restrict__ tok_rec, int L, int n_h, int n_slots, int n_chunks, int blocks_per_bh, int cpb,
+    int n_bh, bool xcd_local) {
   constexpr int kCPB = chunks_per_block<ATTEND>();  // the longest run (cpb <= kCPB)
   constexpr bool kSB = (ATTEND & 1) != 0, kDD = (ATTEND & 2) != 0;
   using T = typename AttnTraits<BF16>::T;
@@ -135,8 +136,14 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
   int* const sLast = sChk + (kDD ? (kCPB + 1) * n_h * 64 : 0);
   int* const sFirst = sLast + (kDD ? (kCPB + 1) * 64 : 0);
 
-  const int bh = blockIdx.x / blocks_per_bh;
-  const int c0 = (blockIdx.x % blocks_per_bh) * cpb;
+  // xcd_local: the runs of one (batch, head) share an XCD (consecutive items on
+  // one XCD), so its gathered rows meet in one L2 instead of all eight.
+  // Otherwise blocks go round-robin over the XCDs in item order, so all XCDs
+  // work on the same few heads at a time.
+  const unsigned item = xcd_local ? xcd_item(blockIdx.x, gridDim.x) : blockIdx.x;
+  if (item >= (unsigned)blocks_per_bh * (unsigned)n_bh) return;
+  const int bh = (int)item / blocks_per_bh;
+  const int c0 = ((int)item % blocks_per_bh) * cpb;
   const int c1 = min(n_chunks, c0 + cpb);
   const int cpr = L / kChunk;  // chunks per round
   const int tid = threadIdx.x;
@@ -779,16 +786,24 @@ hipError_t launch_attn_t(const void* qk, const void* v, const int32_t* sorted_id
   int cpb = kCPB;
   while (cpb > 1 && (size_t)BH * (size_t)((n_chunks + cpb - 1) / cpb) < kAttnFillBlocks) cpb >>= 1;
   const int blocks_per_bh = (n_chunks + cpb - 1) / cpb;
-  const unsigned grid = (unsigned)blocks_per_bh * (unsigned)BH;
+  // A (batch, head)'s QK and V rows are gathered again in every round.  When
+  // they fit one XCD's L2 (4 MiB), keeping each head's runs on one XCD turns
+  // those re-gathers into L2 hits (causal_lm_4k 79 -> 73 us, peaked_vmf_16k
+  // 278 -> 265 us); when they do not (16.8 MB per head at L 65536), spreading
+  // the blocks in order keeps all XCDs on the same heads, which the shared
+  // last-level cache serves better (284 -> 278 us).
+  const bool xcd_local = 2ull * (unsigned long long)L * kD * sizeof(T) <= (4ull << 20);
+  const unsigned n_items = (unsigned)blocks_per_bh * (unsigned)BH;
+  const unsigned grid = xcd_local ? xcd_grid(n_items) : n_items;
   const size_t dyn = variant_lds_bytes(ATTEND, n_h);
   if (causal)
     chunk_attn_kernel<BF16, true, ATTEND><<<grid, 256, dyn, s>>>(
         (const T*)qk, (const T*)v, sorted_idx, (T*)o_out, lse_out, token_scales, buckets, tok_rec, L, n_h,
-        n_slots, n_chunks, blocks_per_bh, cpb);
+        n_slots, n_chunks, blocks_per_bh, cpb, BH, xcd_local);
   else
     chunk_attn_kernel<BF16, false, ATTEND><<<grid, 256, dyn, s>>>(
         (const T*)qk, (const T*)v, sorted_idx, (T*)o_out, lse_out, token_scales, buckets, tok_rec, L, n_h,
-        n_slots, n_chunks, blocks_per_bh, cpb);
+        n_slots, n_chunks, blocks_per_bh, cpb, BH, xcd_local);
   return hipGetLastError();
 }
 
