@@ -341,9 +341,11 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
 
     // End of round r: merge with the partner lane (same tokens, the other 16 rows
     // of each tile), decode the winner, certify, take the sign.
-    const int nblk = (halfp + 63) / 64;
-    float rho = 0.f;  // largest column norm of this round's rotation
-    for (int k = 0; k < nblk; ++k) rho = fmaxf(rho, colmax[r * nblk + k]);
+    // largest column norm of this round's rotation: one load per lane
+    const int nblk = (halfp + 63) / 64;  // <= 32
+    float rho = lane < nblk ? colmax[r * nblk + lane] : 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) rho = fmaxf(rho, __shfl_xor(rho, off));
     const float eps_scale = 65.0f * 0x1p-23f * rho;
     int jstar[2];
     bool certified[2];
@@ -540,6 +542,7 @@ __global__ __launch_bounds__(kFixWaves * 64) void fixup_kernel(const T* __restri
     for (int g = 0; g < nbatch; ++g) mask |= (sc[64 * g + lane] >= thr ? 1u : 0u) << g;
     // Phase 2.
     int cj[kMaxCand];
+    int ncand = 0;  // candidates found (the first ncand entries of cj; wave-uniform)
 #pragma unroll
     for (int c = 0; c < kMaxCand; ++c) {
       const uint64_t bal = __ballot(mask != 0);
@@ -547,6 +550,7 @@ __global__ __launch_bounds__(kFixWaves * 64) void fixup_kernel(const T* __restri
         cj[c] = -1;
         continue;
       }
+      ++ncand;
       const int src = __builtin_ctzll(bal);
       const uint32_t ms = __shfl(mask, src);
       cj[c] = 64 * __builtin_ctz(ms) + (64 / P) * (src % P) + src / P;
@@ -578,9 +582,12 @@ __global__ __launch_bounds__(kFixWaves * 64) void fixup_kernel(const T* __restri
 #pragma unroll
       for (int c = 0; c < kMaxCand; ++c) rv[c] = cj[c] >= 0 ? rrow[(size_t)cj[c] * kD + lane] : T(0);
       double S[kMaxCand], A[kMaxCand];
+      const int nc = __builtin_amdgcn_readfirstlane(ncand);
 #pragma unroll
       for (int c = 0; c < kMaxCand; ++c) {
-        double p = cj[c] >= 0 ? xd * to_f64(rv[c]) : 0.0, q = fabs(p);
+        S[c] = A[c] = 0.0;
+        if (c >= nc) continue;  // empty slots skip the two float64 butterflies
+        double p = xd * to_f64(rv[c]), q = fabs(p);
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
           p += __shfl_xor(p, off);
