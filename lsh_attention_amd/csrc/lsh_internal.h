@@ -44,14 +44,21 @@ __device__ inline unsigned xcd_item(unsigned b, unsigned grid) { return (b % kXc
 // Columns of the transposed rotation, padded to whole 64-column staging blocks
 // (two 32-column MFMA tiles).
 inline int padded_half(int n_b) { return n_b == 1 ? 0 : (int)align_up((size_t)(n_b / 2), 64); }
-// Waves per sort tile: as many as the per-wave LDS counters allow (4 * n_b bytes
-// each, 64 KiB per block) and the sequence needs, 1..16.  Larger tiles give
-// longer runs of consecutive output slots per bucket (fewer partial-line writes).
+// LDS of one sort-scatter block of w waves: per-wave 16-bit bucket counters
+// (two waves per word), two ints per bucket (the tile's first sorted position of
+// the bucket and its offset to the global slot), and the tile's staged order
+// (16-bit token offsets).
+inline size_t sort_scatter_lds(int w, int n_b) {
+  return (size_t)((w + 1) / 2) * n_b * 4 + (size_t)n_b * 8 + (size_t)w * kSortWaveTokens * 2;
+}
+// Waves per sort tile: as many as the sequence needs, at most 16, and no more
+// than fit the scatter block's LDS in 63.5 KiB.  Larger tiles give longer runs
+// of consecutive output slots per bucket (fewer partial-line writes).
 inline int sort_waves(int L, int n_b) {
-  int w = 16384 / (n_b < 1 ? 1 : n_b);
   const int need = (L + kSortWaveTokens - 1) / kSortWaveTokens;
-  if (w > need) w = need;
-  return w < 1 ? 1 : (w > 16 ? 16 : w);
+  int w = need < 16 ? (need < 1 ? 1 : need) : 16;
+  while (w > 1 && sort_scatter_lds(w, n_b) > 65024) --w;
+  return w;
 }
 inline int sort_tile(int L, int n_b) { return kSortWaveTokens * sort_waves(L, n_b); }
 inline int sort_tiles(int L, int n_b) { return (L + sort_tile(L, n_b) - 1) / sort_tile(L, n_b); }

@@ -10,13 +10,17 @@
 //   hist    - per (problem, round, tile of sort_tile() tokens) bucket histogram
 //             in LDS, stored hist[bhr][tile][bucket] (coalesced rows);
 //   scatter - each block first turns its problem's tile histograms into the
-//             first output slot of every (bucket, tile, wave) (bucket totals,
-//             an exclusive scan over buckets, the counts of earlier tiles and
-//             waves); then each wave ranks its sub-tile's tokens in order: the
-//             lanes holding the same bucket are found with one ballot per key
-//             bit (4 vector instructions per bit), their rank is the count of
-//             those lanes below this one (mbcnt), and a per-wave LDS counter per
-//             bucket carries the running offset.
+//             first output slot of every (bucket, tile) (bucket totals, an
+//             exclusive scan over buckets, the counts of earlier tiles) and the
+//             tile's own order (a scan of its counts, each wave's offset within
+//             a bucket's run); then each wave ranks its sub-tile's tokens in
+//             order: the lanes holding the same bucket are found with one ballot
+//             per key bit (4 vector instructions per bit), their rank is the
+//             count of those lanes below this one (mbcnt), and a per-wave 16-bit
+//             LDS counter per bucket carries the running offset.  The unsort
+//             index is written from the walk (coalesced); the sorted index too,
+//             or, with 256 buckets or more, the tile's sorted order is staged in
+//             LDS and written afterwards as whole bucket runs.
 // Bucket values outside [0, n_b) are clamped to n_b - 1 (callers must not
 // pass them; clamping only keeps every write in bounds).
 #include "lsh_internal.h"
@@ -44,27 +48,41 @@ __global__ __launch_bounds__(1024) void sort_hist_kernel(const int32_t* __restri
   for (int b = threadIdx.x; b < n_b; b += blockDim.x) out[b] = sh[b];
 }
 
+template <bool STAGE>
 __global__ __launch_bounds__(1024) void sort_scatter_kernel(const int32_t* __restrict__ buckets,
                                                             const int* __restrict__ hist,
                                                             int32_t* __restrict__ sorted_idx,
                                                             int32_t* __restrict__ undo_idx, int L, int n_b,
                                                             int n_h, int n_tiles, int nbits, int n_items) {
-  extern __shared__ int sh[];  // waves x n_b running offsets
-  __shared__ int wtot[16];      // per-wave sums of the bucket scan
+  extern __shared__ int sh[];
+  __shared__ int wtot[2][16];  // per-wave sums of the two bucket scans
   const int waves = blockDim.x >> 6;
-  // The tiles of one problem share an XCD, so the scattered writes of one
-  // problem's sorted index meet in one L2 and leave it as whole lines.
+  const int npair = (waves + 1) >> 1;
+  const int tile_len = waves * kSortWaveTokens;
+  // Dynamic LDS (sort_scatter_lds): cw[npair][n_b] holds waves 2p (low half) and
+  // 2p+1 (high half) of each bucket's count, later its running offset within
+  // the tile's run of the bucket; tpos[b] = the tile's first sorted position of
+  // bucket b; goff[b] = global slot minus tile position for bucket b; stage[t] =
+  // the tile's t-th token in sorted order, as an offset from t0 (< 8192).
+  uint32_t* cw = (uint32_t*)sh;
+  int* tpos = sh + npair * n_b;
+  int* goff = tpos + n_b;
+  uint16_t* stage = (uint16_t*)(goff + n_b);
+  // The tiles of one problem share an XCD, so the sorted-index writes of one
+  // problem meet in one L2.
   const unsigned item = xcd_item(blockIdx.x, gridDim.x);
   if (item >= (unsigned)n_items) return;
   const int bhr = (int)item / n_tiles, tile = (int)item % n_tiles;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = tile * waves * kSortWaveTokens, t1 = min(L, t0 + waves * kSortWaveTokens);
+  const int t0 = tile * tile_len, t1 = min(L, t0 + tile_len);
   const int w0 = t0 + wave * kSortWaveTokens, w1 = min(t1, w0 + kSortWaveTokens);
-  int* cnt = sh + wave * n_b;
-  for (int b = threadIdx.x; b < waves * n_b; b += blockDim.x) sh[b] = 0;
+  const int shift = 16 * (wave & 1);
+  uint32_t* mycw = cw + (wave >> 1) * n_b;
+  for (int b = threadIdx.x; b < npair * n_b; b += blockDim.x) cw[b] = 0u;
   __syncthreads();
   const int32_t* bk = buckets + (size_t)bhr * L;
-  // 1. per-wave counts of its sub-tile; the buckets stay in registers for step 3
+  // 1. per-wave counts of its sub-tile (at most 512, so a 16-bit field); the
+  //    buckets stay in registers for step 3
   constexpr int kPer = kSortWaveTokens / 64;
   int bv[kPer];
 #pragma unroll
@@ -74,60 +92,68 @@ __global__ __launch_bounds__(1024) void sort_scatter_kernel(const int32_t* __res
   }
 #pragma unroll
   for (int k = 0; k < kPer; ++k)
-    if (bv[k] >= 0) atomicAdd(&cnt[bv[k]], 1);
+    if (bv[k] >= 0) atomicAdd(&mycw[bv[k]], 1u << shift);
   __syncthreads();
-  // 2. first slot of (bucket, wave) in the round's output: the totals of all
-  //    smaller buckets, plus this bucket's counts in earlier tiles, plus its
-  //    counts in the earlier waves of this tile.  Each block scans the problem's
-  //    tile histograms itself (the same scan in every tile of the problem).
+  // 2. Two exclusive scans over the buckets: of each bucket's total in the
+  //    problem-round (its first output slot, plus its counts in earlier tiles)
+  //    and of its count in this tile (its first position in the tile's sorted
+  //    order); then each wave's offset within the tile's run of the bucket.
   //    Thread t owns the contiguous buckets [t*per, (t+1)*per).
   const int* hp = hist + (size_t)bhr * n_tiles * n_b;  // [tile][bucket] counts
   const int nthr = (int)blockDim.x;
   const int per = (n_b + nthr - 1) / nthr;
   const int bb0 = min(n_b, (int)threadIdx.x * per), bb1 = min(n_b, bb0 + per);
-  int mine = 0, before1 = 0;  // per == 1: the one bucket's total and its count in earlier tiles
-  if (per == 1) {
-    if (bb0 < bb1)
-      for (int t = 0; t < n_tiles; ++t) {
-        const int c = hp[(size_t)t * n_b + bb0];
-        before1 += t < tile ? c : 0;
-        mine += c;
-      }
-  } else {
-    for (int b = bb0; b < bb1; ++b)
-      for (int t = 0; t < n_tiles; ++t) mine += hp[(size_t)t * n_b + b];
-  }
-  // exclusive scan of `mine` over the threads of the block
-  int incl = mine;
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) wtot[wave] = incl;
-  __syncthreads();
-  int run = incl - mine;
-  for (int w = 0; w < wave; ++w) run += wtot[w];
+  int gmine = 0, tmine = 0;
   for (int b = bb0; b < bb1; ++b) {
-    int before = before1, total = mine;
-    if (per != 1) {
-      before = total = 0;
-      for (int t = 0; t < n_tiles; ++t) {
-        const int c = hp[(size_t)t * n_b + b];
-        before += t < tile ? c : 0;
-        total += c;
-      }
+    for (int t = 0; t < n_tiles; ++t) gmine += hp[(size_t)t * n_b + b];
+    for (int q = 0; q < npair; ++q) {
+      const uint32_t w = cw[q * n_b + b];
+      tmine += (int)(w & 0xFFFFu) + (int)(w >> 16);
     }
-    int slot = run + before;
-    for (int w = 0; w < waves; ++w) {
-      const int c = sh[w * n_b + b];
-      sh[w * n_b + b] = slot;
-      slot += c;
+  }
+  int gin = gmine, tin = tmine;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int yg = __shfl_up(gin, off), yt = __shfl_up(tin, off);
+    if (lane >= off) {
+      gin += yg;
+      tin += yt;
     }
-    run += total;
+  }
+  if (lane == 63) {
+    wtot[0][wave] = gin;
+    wtot[1][wave] = tin;
   }
   __syncthreads();
-  // 3. ordered walk, 64 tokens at a time.
+  int grun = gin - gmine, trun = tin - tmine;
+  for (int w = 0; w < wave; ++w) {
+    grun += wtot[0][w];
+    trun += wtot[1][w];
+  }
   const int r = bhr % n_h, bh = bhr / n_h;
+  for (int b = bb0; b < bb1; ++b) {
+    int before = 0, total = 0;
+    for (int t = 0; t < n_tiles; ++t) {
+      const int c = hp[(size_t)t * n_b + b];
+      before += t < tile ? c : 0;
+      total += c;
+    }
+    tpos[b] = trun;
+    goff[b] = r * L + grun + before - trun;
+    int o = 0;  // waves' offsets within the tile's run of bucket b, in wave order
+    for (int q = 0; q < npair; ++q) {
+      const uint32_t w = cw[q * n_b + b];
+      const int lo = (int)(w & 0xFFFFu), hi = (int)(w >> 16);
+      cw[q * n_b + b] = (uint32_t)o | ((uint32_t)(o + lo) << 16);
+      o += lo + hi;
+    }
+    grun += total;
+    trun += o;
+  }
+  __syncthreads();
+  // 3. Ordered walk, 64 tokens at a time: each token's position in the tile's
+  //    sorted order and its global slot; the unsort index is written here
+  //    (coalesced), the sorted index either here too (STAGE false) or, staged
+  //    in LDS, after the walk.
   int32_t* sidx = sorted_idx + (size_t)bh * n_h * L;
   int32_t* uidx = undo_idx + (size_t)bhr * L;
 #pragma unroll
@@ -147,13 +173,29 @@ __global__ __launch_bounds__(1024) void sort_scatter_kernel(const int32_t* __res
       mhi &= ~((uint32_t)(bal >> 32) ^ s);
     }
     const int rank = (int)__builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));  // same-bucket lanes below
-    const int first = act ? cnt[b] : 0;
-    if (act && rank == 0) cnt[b] = first + __popc(mlo) + __popc(mhi);
+    // this wave's running offset in the bucket's run (its own half of the word;
+    // the other wave of the pair only adds to the other half, without carry)
+    const int first = act ? (int)((mycw[b] >> shift) & 0xFFFFu) : 0;
+    if (act && rank == 0) atomicAdd(&mycw[b], (uint32_t)(__popc(mlo) + __popc(mhi)) << shift);
     if (act) {
-      const int g = r * L + first + rank;
-      sidx[g] = i;
+      const int t = tpos[b] + first + rank;
+      const int g = goff[b] + t;
       uidx[i] = g;
+      if constexpr (STAGE)
+        stage[t] = (uint16_t)(i - t0);
+      else
+        sidx[g] = i;
     }
+  }
+  if constexpr (!STAGE) return;
+  __syncthreads();
+  // 4. The sorted index of the tile, written in sorted order: consecutive threads
+  //    write consecutive slots within each bucket's run (the token's bucket is
+  //    read again from the bucket array, which this block just read).
+  const int cnt = t1 - t0;
+  for (int t = (int)threadIdx.x; t < cnt; t += (int)blockDim.x) {
+    const int i = t0 + (int)stage[t];
+    sidx[goff[clamp_bucket(bk[i], n_b)] + t] = i;
   }
 }
 
@@ -172,8 +214,18 @@ hipError_t launch_sort_scatter(const int32_t* buckets, const int* hist, int32_t*
   const int nt = sort_tiles(L, n_b), waves = sort_waves(L, n_b);
   int nbits = 0;
   while ((1 << nbits) < n_b) ++nbits;
-  sort_scatter_kernel<<<xcd_grid(nt * BHR), 64 * waves, waves * n_b * sizeof(int), s>>>(
-      buckets, hist, sorted_idx, undo_idx, L, n_b, n_h, nt, nbits, nt * BHR);
+  // With 256 buckets or more, the lanes of a 64-token step hold different
+  // buckets, so writing the sorted index from the walk touches a line per lane;
+  // staging the tile's order and writing whole bucket runs then pays
+  // (long_seq_64k 33.5 -> 30.6 us, peaked_vmf_16k 29.2 -> 23.6 us).  With fewer
+  // buckets the walk's writes already share lines and the extra phase costs more
+  // (causal_lm_4k 11.7 -> 13.3 us).
+  if (n_b >= 256)
+    sort_scatter_kernel<true><<<xcd_grid(nt * BHR), 64 * waves, sort_scatter_lds(waves, n_b), s>>>(
+        buckets, hist, sorted_idx, undo_idx, L, n_b, n_h, nt, nbits, nt * BHR);
+  else
+    sort_scatter_kernel<false><<<xcd_grid(nt * BHR), 64 * waves, sort_scatter_lds(waves, n_b), s>>>(
+        buckets, hist, sorted_idx, undo_idx, L, n_b, n_h, nt, nbits, nt * BHR);
   return hipGetLastError();
 }
 
