@@ -121,6 +121,43 @@ def test_linear_epilogues_and_layouts(gpu_lib, epi):
                   "heads -> rows")
 
 
+@pytest.mark.parametrize("epi", ["plain", "bias_gelu", "resid", "bias_resid"])
+def test_linear_large_tiles(gpu_lib, epi):
+    """The GEMM at a long shape: M = 32832 rows (257 row tiles, the last one
+    partial), K = 192 (three K-stages), N = 512; every element against float64,
+    every epilogue, and both head-major layouts."""
+    rng = np.random.default_rng(7)
+    B, L, K, N = 1, 32832, 192, 512
+    say(f"case long linear {epi} M{L} K{K} N{N}")
+
+    def bf(a):
+        return to_device(I._store(np.asarray(a, dtype=np.float32), "bf16"))
+
+    a = bf(rng.standard_normal((B, L, K)))
+    wt = bf(rng.standard_normal((N, K)) / np.sqrt(K))
+    bias = bf(rng.standard_normal(N))
+    res = bf(rng.standard_normal((B, L, N)))
+    A, W, BI, R = f64(a), f64(wt), f64(bias), f64(res)
+    kw = {}
+    ref = A @ W.T
+    if epi in ("bias_gelu", "bias_resid"):
+        kw["bias"] = bias
+        ref = ref + BI
+    if epi == "bias_gelu":
+        kw["gelu"] = True
+        ref = OBk.gelu(ref)
+    if epi in ("resid", "bias_resid"):
+        kw["resid"] = res
+        ref = ref + R
+    rel_check(f64(bd.lsh_linear(a, wt, **kw)), ref, TOLB, f"large tiles rows -> rows {epi}")
+    if epi == "plain":
+        hm = bd.lsh_linear_heads(a, wt)  # [B, H, L, 64]
+        rel_check(heads_to_rows(f64(hm)), A @ W.T, TOLB, "large tiles rows -> heads")
+        w2 = bf(rng.standard_normal((N, N)) / np.sqrt(N))
+        rel_check(f64(bd.lsh_linear(hm, w2, a_heads=True)), heads_to_rows(f64(hm)) @ f64(w2).T, TOLB,
+                  "large tiles heads -> rows")
+
+
 @pytest.mark.parametrize("dim", [128, 512, 1024])
 def test_layer_norm(gpu_lib, dim):
     rng = np.random.default_rng(dim)
