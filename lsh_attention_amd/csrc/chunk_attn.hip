@@ -45,6 +45,8 @@
 //    If a row's sum falls below 2^-60 (only a self-only row, or keys far from
 //    the query's direction at huge norms), the wave recomputes that chunk with
 //    the row maximum and the explicit -1e5 self logit.
+#include <type_traits>
+
 #include "lsh_internal.h"
 
 namespace lsh {
@@ -435,88 +437,106 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
         // The LDS operands of tile kt+2 and of the next pair's V^T are read a
         // stage ahead.  The sums and the P.V accumulation keep the order of the
         // phase-by-phase form, so the results are the same bits.
-        const bf16x8 bq0 = *(const bf16x8*)(&sX[cur][xoff(qrow, grp)]);
-        const bf16x8 bq1 = *(const bf16x8*)(&sX[cur][xoff(qrow, 4 + grp)]);
-        bf16x8 ka0[8], ka1[8], va[4][4], bp[4];
-        float ksv[8][4], kfv[8][4];
-        int kpv[8][4];
-        auto loads = [&](int kt) {
-          const int slot = kt < 4 ? prv : cur;
-          const T* kx = sX[slot];
-          const int krow = 16 * (kt & 3) + col, kr0 = 16 * (kt & 3) + 4 * grp;
-          ka0[kt] = *(const bf16x8*)(kx + xoff(krow, grp));
-          ka1[kt] = *(const bf16x8*)(kx + xoff(krow, 4 + grp));
-          const float4 ks = *(const float4*)(&sKs[slot][kr0]);
-          ksv[kt][0] = ks.x; ksv[kt][1] = ks.y; ksv[kt][2] = ks.z; ksv[kt][3] = ks.w;
-          if constexpr (CAUSAL) {
-            const float4 kf = *(const float4*)(&sPf[kt < 4 ? kc - 1 : kc][kr0]);
-            kfv[kt][0] = kf.x; kfv[kt][1] = kf.y; kfv[kt][2] = kf.z; kfv[kt][3] = kf.w;
-          } else {
-            const int4 kp = *(const int4*)(&sPos[kt < 4 ? kc - 1 : kc][kr0]);
-            kpv[kt][0] = kp.x; kpv[kt][1] = kp.y; kpv[kt][2] = kp.z; kpv[kt][3] = kp.w;
+        // Without the causal mask only the self key is masked.  In the current chunk
+        // the query's token occurs once, at the query's own slot (tile 4 + wave,
+        // key col of it), so that mask is static; the look-back chunk can hold
+        // the token only when it is the previous round's last chunk (the query's
+        // chunk is a round's first, c % cpr == 0, which includes a single chunk
+        // looking back at itself): only then are positions compared (kLB).
+        auto run_stream = [&](auto kLB) {
+          const bf16x8 bq0 = *(const bf16x8*)(&sX[cur][xoff(qrow, grp)]);
+          const bf16x8 bq1 = *(const bf16x8*)(&sX[cur][xoff(qrow, 4 + grp)]);
+          bf16x8 ka0[8], ka1[8], va[4][4], bp[4];
+          float ksv[8][4], kfv[8][4];
+          int kpv[8][4];
+          auto loads = [&](int kt) {
+            const int slot = kt < 4 ? prv : cur;
+            const T* kx = sX[slot];
+            const int krow = 16 * (kt & 3) + col, kr0 = 16 * (kt & 3) + 4 * grp;
+            ka0[kt] = *(const bf16x8*)(kx + xoff(krow, grp));
+            ka1[kt] = *(const bf16x8*)(kx + xoff(krow, 4 + grp));
+            const float4 ks = *(const float4*)(&sKs[slot][kr0]);
+            ksv[kt][0] = ks.x; ksv[kt][1] = ks.y; ksv[kt][2] = ks.z; ksv[kt][3] = ks.w;
+            if constexpr (CAUSAL) {
+              const float4 kf = *(const float4*)(&sPf[kt < 4 ? kc - 1 : kc][kr0]);
+              kfv[kt][0] = kf.x; kfv[kt][1] = kf.y; kfv[kt][2] = kf.z; kfv[kt][3] = kf.w;
+            } else if (decltype(kLB)::value && kt < 4) {
+              const int4 kp = *(const int4*)(&sPos[kc - 1][kr0]);
+              kpv[kt][0] = kp.x; kpv[kt][1] = kp.y; kpv[kt][2] = kp.z; kpv[kt][3] = kp.w;
+            }
+          };
+          auto vloads = [&](int ks) {
+            const int vpiece = 8 * (ks < 2 ? prv : cur) + 4 * (ks & 1) + grp;
+  #pragma unroll
+            for (int dt = 0; dt < 4; ++dt) va[ks][dt] = *(const bf16x8*)(&sVT[voff(16 * dt + col, vpiece)]);
+          };
+          auto smfma = [&](int kt, int h) {
+            if (h == 0)
+              acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0[kt], bq0, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            else
+              acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1[kt], bq1, acc[kt], 0, 0, 0);
+          };
+          auto pvm = [&](int ks, int dt) {
+            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[ks][dt], bp[ks], oacc[dt], 0, 0, 0);
+          };
+          auto soft = [&](int kt, int e) {
+            const float q = __builtin_amdgcn_exp2f(fmaf(acc[kt][e], ksv[kt][e], -M2));
+            if constexpr (CAUSAL)
+              p[kt][e] = __builtin_amdgcn_fmed3f(q, 0.f, qf2 - kfv[kt][e]);
+            else if (kt >= 4)  // the current chunk holds the token once: its own slot
+              p[kt][e] = (kt - 4 == wave && 4 * grp + e == col) ? 0.f : q;
+            else if constexpr (decltype(kLB)::value)
+              p[kt][e] = kpv[kt][e] == qpos ? 0.f : q;
+            else
+              p[kt][e] = q;
+            sum += p[kt][e];
+          };
+  #pragma unroll
+          for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          loads(0);
+          loads(1);
+          smfma(0, 0);
+          smfma(0, 1);
+          loads(2);
+  #pragma unroll
+          for (int kt = 0; kt < 8; ++kt) {
+            // P.V of key pair (kt - 2) / 2, dims 2 (kt & 1) + 0, 1: its probabilities
+            // were packed and its V^T operands read in stage kt - 1 or earlier.
+            const bool pv_here = kt >= 2;
+            const int ks = (kt - 2) >> 1, dt0 = 2 * (kt & 1);
+            if (kt + 1 < 8) smfma(kt + 1, 0);
+            soft(kt, 0);
+            if (pv_here) pvm(ks, dt0);
+            soft(kt, 1);
+            if (kt + 1 < 8) smfma(kt + 1, 1);
+            soft(kt, 2);
+            if (pv_here) pvm(ks, dt0 + 1);
+            soft(kt, 3);
+            if (kt + 2 < 8) loads(kt + 2);
+            if (kt & 1) {
+              // K index (grp, e): e < 4 -> key 4 grp + e of tile kt - 1; e >= 4 -> of tile kt.
+              const f32x4 lo = {p[kt - 1][0], p[kt - 1][1], p[kt - 1][2], p[kt - 1][3]};
+              const f32x4 hi = {p[kt][0], p[kt][1], p[kt][2], p[kt][3]};
+              bp[kt >> 1] = __builtin_shufflevector(__builtin_convertvector(lo, bf16x4),
+                                                    __builtin_convertvector(hi, bf16x4), 0, 1, 2, 3, 4, 5, 6, 7);
+              vloads(kt >> 1);
+            }
+  #pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            }
           }
+          sum = qsum(sum);
+  #pragma unroll
+          for (int dt = 0; dt < 4; ++dt) pvm(3, dt);
         };
-        auto vloads = [&](int ks) {
-          const int vpiece = 8 * (ks < 2 ? prv : cur) + 4 * (ks & 1) + grp;
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) va[ks][dt] = *(const bf16x8*)(&sVT[voff(16 * dt + col, vpiece)]);
-        };
-        auto smfma = [&](int kt, int h) {
-          if (h == 0)
-            acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0[kt], bq0, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-          else
-            acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1[kt], bq1, acc[kt], 0, 0, 0);
-        };
-        auto pvm = [&](int ks, int dt) {
-          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[ks][dt], bp[ks], oacc[dt], 0, 0, 0);
-        };
-        auto soft = [&](int kt, int e) {
-          const float q = __builtin_amdgcn_exp2f(fmaf(acc[kt][e], ksv[kt][e], -M2));
-          if constexpr (CAUSAL)
-            p[kt][e] = __builtin_amdgcn_fmed3f(q, 0.f, qf2 - kfv[kt][e]);
-          else
-            p[kt][e] = kpv[kt][e] == qpos ? 0.f : q;
-          sum += p[kt][e];
-        };
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        loads(0);
-        loads(1);
-        smfma(0, 0);
-        smfma(0, 1);
-        loads(2);
-#pragma unroll
-        for (int kt = 0; kt < 8; ++kt) {
-          // P.V of key pair (kt - 2) / 2, dims 2 (kt & 1) + 0, 1: its probabilities
-          // were packed and its V^T operands read in stage kt - 1 or earlier.
-          const bool pv_here = kt >= 2;
-          const int ks = (kt - 2) >> 1, dt0 = 2 * (kt & 1);
-          if (kt + 1 < 8) smfma(kt + 1, 0);
-          soft(kt, 0);
-          if (pv_here) pvm(ks, dt0);
-          soft(kt, 1);
-          if (kt + 1 < 8) smfma(kt + 1, 1);
-          soft(kt, 2);
-          if (pv_here) pvm(ks, dt0 + 1);
-          soft(kt, 3);
-          if (kt + 2 < 8) loads(kt + 2);
-          if (kt & 1) {
-            // K index (grp, e): e < 4 -> key 4 grp + e of tile kt - 1; e >= 4 -> of tile kt.
-            const f32x4 lo = {p[kt - 1][0], p[kt - 1][1], p[kt - 1][2], p[kt - 1][3]};
-            const f32x4 hi = {p[kt][0], p[kt][1], p[kt][2], p[kt][3]};
-            bp[kt >> 1] = __builtin_shufflevector(__builtin_convertvector(lo, bf16x4),
-                                                  __builtin_convertvector(hi, bf16x4), 0, 1, 2, 3, 4, 5, 6, 7);
-            vloads(kt >> 1);
-          }
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-          }
-        }
-        sum = qsum(sum);
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) pvm(3, dt);
+        if constexpr (CAUSAL)
+          run_stream(std::false_type{});
+        else if (c % cpr == 0)
+          run_stream(std::true_type{});
+        else
+          run_stream(std::false_type{});
       } else {
       scores(acc);
 #pragma unroll
