@@ -166,7 +166,10 @@ int lsh_unsort_combine(const void* o_sorted, const float* lse_sorted, const int3
  * Arguments as above.  `stage_events` is optional: NULL, or an array of
  * LSH_FWD_N_EVENTS hipEvent_t (as void*) that are recorded on `stream` before
  * the first and after every kernel launch, in the order of the
- * LSH_FWD_KERNEL_* list, for per-kernel timing. */
+ * LSH_FWD_KERNEL_* list, for per-kernel timing.  A NULL entry is skipped, so
+ * a caller can time one kernel (entries k and k+1) without the cost of the
+ * other records (each adds a few microseconds between kernels).  The same holds
+ * for every stage_events array below. */
 #define LSH_FWD_KERNEL_PREP 0      /* rotation transpose + norms */
 #define LSH_FWD_KERNEL_HASH 1      /* MFMA projection + certified argmax */
 #define LSH_FWD_KERNEL_FIXUP 2     /* float64/exact re-decision of uncertified tokens */

@@ -476,11 +476,15 @@ def reformer_block_fwd(x1: torch.Tensor, x2: torch.Tensor, rot, params: dict, n_
 
 class EventSet:
     """N_EVENTS hipEvents created by the library, recorded by the fused call
-    around each kernel; `durations_ms()` gives the per-kernel times."""
+    around each kernel; `durations_ms()` gives the per-kernel times.  With
+    `only`, just those indices get an event (the others stay NULL and are not
+    recorded): `only=(k, k + 1)` times kernel k alone."""
 
-    def __init__(self, n: int = N_EVENTS):
+    def __init__(self, n: int = N_EVENTS, only=None):
         self._ev = (_vp * n)()
-        for i in range(n):
+        for i in (range(n) if only is None else only):
+            if not 0 <= i < n:
+                raise ValueError(f"event index {i} outside 0..{n - 1}")
             h = _vp()
             _check("lsh_event_create", lib().lsh_event_create(ctypes.byref(h)))
             self._ev[i] = h

@@ -147,6 +147,11 @@ int check_block(int B, int L, int heads, int n_b, int n_h, int chunk_len, int ch
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LSH_OK : LSH_ERR_HIP; }
 
+// Records stage event k of `ev` on s; a NULL array or a NULL entry records nothing.
+hipError_t record_stage(void* const* ev, int k, hipStream_t s) {
+  return ev == nullptr || ev[k] == nullptr ? hipSuccess : hipEventRecord((hipEvent_t)ev[k], s);
+}
+
 // Enqueue hashing (prep, MFMA hash, fixup) into the given scratch regions.
 hipError_t enqueue_hash(const void* qk, const void* rot, int32_t* buckets, float2* token_scales, char* ws,
                         const HashWs& w, int BH, int L, int n_b, int n_h, lsh_dtype dt, hipStream_t s,
@@ -154,7 +159,7 @@ hipError_t enqueue_hash(const void* qk, const void* rot, int32_t* buckets, float
   auto mark = [&](void) -> hipError_t {
     if (ev == nullptr) return hipSuccess;
     ++*k;
-    return hipEventRecord((hipEvent_t)ev[*k], s);
+    return record_stage(ev, *k, s);
   };
   hipError_t e;
   if (n_b == 1) {
@@ -182,7 +187,7 @@ hipError_t enqueue_sort(const int32_t* buckets, int32_t* sorted_idx, int32_t* un
   auto mark = [&](void) -> hipError_t {
     if (ev == nullptr) return hipSuccess;
     ++*k;
-    return hipEventRecord((hipEvent_t)ev[*k], s);
+    return record_stage(ev, *k, s);
   };
   const int BHR = BH * n_h;
   hipError_t e;
@@ -437,7 +442,7 @@ hipError_t enqueue_forward(const void* qk, const void* v, const void* rot, int n
   float2* token_scales = n_b > 1 ? (float2*)(base + w.token_scales) : nullptr;
   int k = 0;
   hipError_t e = hipSuccess;
-  if (stage_events != nullptr) e = hipEventRecord((hipEvent_t)stage_events[0], s);
+  e = record_stage(stage_events, 0, s);
   if (e == hipSuccess)
     e = enqueue_hash(qk, rot, buckets, token_scales, base + w.hash_base, w.hash, BH, L, n_b, n_h, dt, s,
                      stage_events, &k);
@@ -447,9 +452,9 @@ hipError_t enqueue_forward(const void* qk, const void* v, const void* rot, int n
   if (e == hipSuccess)
     e = launch_chunk_attn(qk, v, sorted_idx, o_sorted, lse_sorted, token_scales, buckets, undo_idx,
                           (int32_t*)(base + w.tok_rec), BH, L, n_h, causal, attend, dt, s);
-  if (e == hipSuccess && stage_events != nullptr) e = hipEventRecord((hipEvent_t)stage_events[++k], s);
+  if (e == hipSuccess && stage_events != nullptr) e = record_stage(stage_events, ++k, s);
   if (e == hipSuccess) e = launch_combine(o_sorted, lse_sorted, undo_idx, out, lse_out, BH, L, n_h, dt, s);
-  if (e == hipSuccess && stage_events != nullptr) e = hipEventRecord((hipEvent_t)stage_events[++k], s);
+  if (e == hipSuccess && stage_events != nullptr) e = record_stage(stage_events, ++k, s);
   return e;
 }
 
@@ -468,7 +473,7 @@ int fused_forward(const void* qk, const void* v, const void* rot, int n_buckets,
     // Nothing to compute; the stage events are still recorded, back to back.
     if (stage_events != nullptr)
       for (int k = 0; k < LSH_FWD_N_EVENTS; ++k)
-        if (hipEventRecord((hipEvent_t)stage_events[k], (hipStream_t)stream) != hipSuccess) return LSH_ERR_HIP;
+        if (record_stage(stage_events, k, (hipStream_t)stream) != hipSuccess) return LSH_ERR_HIP;
     return LSH_OK;
   }
   if (qk == nullptr || v == nullptr || out == nullptr || (n_buckets > 1 && rot == nullptr)) return LSH_ERR_NULL;
@@ -646,7 +651,7 @@ int lsh_attn_bwd(const void* qk, const void* v, const int32_t* sorted_idx, const
   if (is_empty(B, H, L)) {
     if (stage_events != nullptr)
       for (int k = 0; k < LSH_BWD_N_EVENTS; ++k)
-        if (hipEventRecord((hipEvent_t)stage_events[k], (hipStream_t)stream) != hipSuccess) return LSH_ERR_HIP;
+        if (record_stage(stage_events, k, (hipStream_t)stream) != hipSuccess) return LSH_ERR_HIP;
     return LSH_OK;
   }
   if (qk == nullptr || v == nullptr || sorted_idx == nullptr || undo_idx == nullptr || lse_sorted == nullptr ||
@@ -674,7 +679,7 @@ int lsh_attn_bwd(const void* qk, const void* v, const int32_t* sorted_idx, const
   void* dv_slot = base + w.dv_slot;
   int k = 0;
   auto mark = [&](void) -> hipError_t {
-    return stage_events == nullptr ? hipSuccess : hipEventRecord((hipEvent_t)stage_events[k++], s);
+    return record_stage(stage_events, k++, s);
   };
   hipError_t e = mark();
   if (e == hipSuccess)
@@ -745,7 +750,7 @@ int reformer_block_fwd(const void* x1, const void* x2, const void* rot, const vo
   if (is_empty(B, heads, L)) {
     if (stage_events != nullptr)
       for (int k = 0; k < LSH_BLOCK_N_EVENTS; ++k)
-        if (hipEventRecord((hipEvent_t)stage_events[k], s) != hipSuccess) return LSH_ERR_HIP;
+        if (record_stage(stage_events, k, s) != hipSuccess) return LSH_ERR_HIP;
     return LSH_OK;
   }
   if (x1 == nullptr || x2 == nullptr || params == nullptr || y1 == nullptr || y2 == nullptr ||
@@ -785,7 +790,7 @@ int reformer_block_fwd(const void* x1, const void* x2, const void* rot, const vo
   void* hid = base + w.hid;
   int k = 0;
   auto mark = [&](void) -> hipError_t {
-    return stage_events == nullptr ? hipSuccess : hipEventRecord((hipEvent_t)stage_events[k++], s);
+    return record_stage(stage_events, k++, s);
   };
   const void* const* p = params;
   hipError_t e = mark();

@@ -79,7 +79,6 @@ struct BwdTraits<true> {
   static constexpr int kTRow = 128;   // transposed x: 2 slots x 64 (pieces swizzled, voff)
   static constexpr int kQRow = 64;    // transposed dO: 64 queries (xoff)
   static constexpr int kSRow = 128;   // dS kn: 2 slots x 64 keys (voff)
-  static constexpr int kXLoads = 2;
 };
 template <>
 struct BwdTraits<false> {
@@ -88,7 +87,6 @@ struct BwdTraits<false> {
   static constexpr int kTRow = 4;     // unused
   static constexpr int kQRow = 4;     // unused
   static constexpr int kSRow = 132;
-  static constexpr int kXLoads = 4;
 };
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
@@ -97,9 +95,6 @@ typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 
 __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-__device__ inline uint16_t to_bf16(float f) {
-  return __builtin_bit_cast(uint16_t, (__bf16)f);
-}
 
 // bf16 LDS tiles keep rows unpadded and store 16-byte piece q of row r at
 // piece q ^ (r mod pieces-per-row): the MFMA operand reads (16 lanes on 16
@@ -223,9 +218,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
   const int c1 = min(n_chunks, c0 + kCPB);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15, grp = lane >> 4;
   const int sw = wave >> 2, kt = wave & 3;  // owned keys: rows 16 kt .. 16 kt + 15 of ring slot sw
-  const int kr = 16 * kt + col;             // this lane's key row
 
   constexpr uint32_t kRowBytes = kD * sizeof(T);
   const char* xq = (const char*)(qk + (size_t)bh * L * kD);
