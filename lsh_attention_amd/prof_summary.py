@@ -1,8 +1,9 @@
 """Summaries of rocprofv3 output for the fused LSH-attention forward pass.
 
-  python -m lsh_attention_amd.prof_summary stats <rocprofv3 output dir>
+  python -m lsh_attention_amd.prof_summary stats <rocprofv3 output dir> [K]
       Markdown table of the --kernel-trace --stats run (average duration per
-      kernel, per launch).
+      kernel, per launch); with K, also each kernel's average over its last K
+      launches from the kernel trace (bench.py's K timed steps come last).
   python -m lsh_attention_amd.prof_summary traffic <pmc dir> <workload> <out.json>
       From --pmc runs of FETCH_SIZE and WRITE_SIZE (one sub-directory per
       pass, each holding *_counter_collection.csv) over a benchmark run that
@@ -53,15 +54,28 @@ def source_sha256(key: str) -> str:
     return h.hexdigest()
 
 
-def stats_table(d: str) -> str:
+def last_launches_us(d: str, k: int) -> dict:
+    """{kernel name: mean duration (us) of its last k launches} from the kernel trace."""
+    f = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)[0]
+    per = collections.defaultdict(list)
+    for r in csv.DictReader(open(f)):
+        per[r["Kernel_Name"]].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    return {name: sum(e - s for s, e in sorted(v)[-k:]) / min(k, len(v)) / 1e3 for name, v in per.items()}
+
+
+def stats_table(d: str, last: int = 0) -> str:
     f = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)[0]
     rows = list(csv.DictReader(open(f)))
-    out = ["| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
-           "|---|---|---|---|---|---|"]
+    tail = last_launches_us(d, last) if last else {}
+    extra = f" average of the last {last} (us) |" if last else ""
+    out = ["| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |" + extra,
+           "|---|---|---|---|---|---|" + ("---|" if last else "")]
     for r in rows:
+        t = tail.get(r["Name"])
         out.append(f"| {kernel_key(r['Name'])} (`{r['Name'][:70]}`) | {r['Calls']} | "
                    f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
-                   f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} % |")
+                   f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} % |" +
+                   ((f" {t:.2f} |" if t is not None else " - |") if last else ""))
     return "\n".join(out)
 
 
@@ -152,7 +166,7 @@ def counter_table(d: str, kernels=("hash", "fixup", "sort_scatter", "chunk_attn"
 
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
-        print(stats_table(sys.argv[2]))
+        print(stats_table(sys.argv[2], int(sys.argv[3]) if len(sys.argv) > 3 else 0))
     elif sys.argv[1] == "counters":
         print(counter_table(sys.argv[2]))
     elif sys.argv[1] == "traffic":
