@@ -242,16 +242,15 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
 
   // ---- gathers (registers) and commits (LDS) ----
   // rows: thread t holds 16-byte pieces (t & 7) * kLoads + i of row t >> 3.
-  // transposed (bf16): threads 0-255 transpose x, threads 256-511 dO.  Thread
-  // (p, j) = (t & 31, (t >> 5) & 7) holds dims 2p, 2p+1 of rows 32h + 16b + 4g +
-  // 0..3 (h = j >> 2, g = j & 3, b = 0, 1): columns 32h + 8g + 0..7, piece j of
-  // the 64 columns; it writes them to rows p (dim 2p) and 32 + p (dim 2p + 1).
+  // transposed (bf16), built from the row copies once they are in LDS: threads
+  // 0-255 transpose x, threads 256-511 dO.  Thread (p, j) = (t & 31, (t >> 5) & 7)
+  // reads dims 2p, 2p+1 of rows 32h + 16b + 4g + 0..3 (h = j >> 2, g = j & 3,
+  // b = 0, 1): columns 32h + 8g + 0..7, piece j of the 64 columns; it writes them
+  // to rows p (dim 2p) and 32 + p (dim 2p + 1).
   const int prow = tid >> 3, ppc = (tid & 7) * kLoads;
   const int tp = tid & 31, tj = (tid >> 5) & 7;
   const int trow = 32 * (tj >> 2) + 4 * (tj & 3);
-  const char* const tsrc = tid < 256 ? xq : dq_in;  // wave-uniform
   uint4 xr[kLoads], vr[kLoads], dr[kLoads];
-  uint32_t tw[BF16 ? 8 : 1];
   float2 ksc = make_float2(0.f, 0.f), qsw = make_float2(0.f, 0.f);
   float qlse = 0.f;
   auto gather = [&](int k) {  // entry k: its keys, and (for every entry but the first) its queries
@@ -263,11 +262,6 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
       xr[i] = *(const uint4*)(xq + off + 16u * i);
       vr[i] = *(const uint4*)(vq + off + 16u * i);
       dr[i] = *(const uint4*)(dq_in + off + 16u * i);
-    }
-    if constexpr (BF16) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        tw[i] = *(const uint32_t*)(tsrc + ((uint32_t)pos[trow + (i & 3) + 16 * (i >> 2)] * kRowBytes + 4u * tp));
     }
     if (tid < 64) {
       ksc = tsb[pos[tid]];
@@ -290,25 +284,6 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
       sKs2[slot][tid] = ksc.x;
       sKn[slot][tid] = ksc.y;
     }
-    if constexpr (BF16) {
-      // low halves: dim 2p of the 8 rows in column order; high halves: dim 2p + 1
-      uint4 lo, hi;
-      lo.x = __builtin_amdgcn_perm(tw[1], tw[0], 0x05040100u);
-      lo.y = __builtin_amdgcn_perm(tw[3], tw[2], 0x05040100u);
-      lo.z = __builtin_amdgcn_perm(tw[5], tw[4], 0x05040100u);
-      lo.w = __builtin_amdgcn_perm(tw[7], tw[6], 0x05040100u);
-      hi.x = __builtin_amdgcn_perm(tw[1], tw[0], 0x07060302u);
-      hi.y = __builtin_amdgcn_perm(tw[3], tw[2], 0x07060302u);
-      hi.z = __builtin_amdgcn_perm(tw[5], tw[4], 0x07060302u);
-      hi.w = __builtin_amdgcn_perm(tw[7], tw[6], 0x07060302u);
-      if (tid < 256) {
-        *(uint4*)(&sXT[voff(tp, 8 * slot + tj)]) = lo;
-        *(uint4*)(&sXT[voff(32 + tp, 8 * slot + tj)]) = hi;
-      } else if (queries) {
-        *(uint4*)(&sDOT[xoff(tp, tj)]) = lo;
-        *(uint4*)(&sDOT[xoff(32 + tp, tj)]) = hi;
-      }
-    }
     if (queries) {
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
@@ -323,6 +298,35 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
         sWc[tid] = qsw.y;
         const uint64_t so = __ballot(qlse < kSelfOnlyLse);  // wave 0: the chunk's 64 queries
         if (tid == 0) sSelfOnly = so != 0ull ? 1 : 0;
+      }
+    }
+    if constexpr (BF16) {
+      __syncthreads();  // the row copies are in LDS
+      if (tid < 256 || queries) {
+        const T* src = tid < 256 ? sX[slot] : sDO;  // wave-uniform
+        uint32_t tw[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = trow + (i & 3) + 16 * (i >> 2);
+          tw[i] = *(const uint32_t*)(src + xoff(r, tp >> 2) + 2 * (tp & 3));
+        }
+        // low halves: dim 2p of the 8 rows in column order; high halves: dim 2p + 1
+        uint4 lo, hi;
+        lo.x = __builtin_amdgcn_perm(tw[1], tw[0], 0x05040100u);
+        lo.y = __builtin_amdgcn_perm(tw[3], tw[2], 0x05040100u);
+        lo.z = __builtin_amdgcn_perm(tw[5], tw[4], 0x05040100u);
+        lo.w = __builtin_amdgcn_perm(tw[7], tw[6], 0x05040100u);
+        hi.x = __builtin_amdgcn_perm(tw[1], tw[0], 0x07060302u);
+        hi.y = __builtin_amdgcn_perm(tw[3], tw[2], 0x07060302u);
+        hi.z = __builtin_amdgcn_perm(tw[5], tw[4], 0x07060302u);
+        hi.w = __builtin_amdgcn_perm(tw[7], tw[6], 0x07060302u);
+        if (tid < 256) {
+          *(uint4*)(&sXT[voff(tp, 8 * slot + tj)]) = lo;
+          *(uint4*)(&sXT[voff(32 + tp, 8 * slot + tj)]) = hi;
+        } else {
+          *(uint4*)(&sDOT[xoff(tp, tj)]) = lo;
+          *(uint4*)(&sDOT[xoff(32 + tp, tj)]) = hi;
+        }
       }
     }
   };
