@@ -314,7 +314,7 @@ def token_output(x, v, sorted_idx, undo_idx, chunk_len: int, causal: bool, i: in
 
 # --------------------------------------------------------------------------
 # Exact attention and recall (explainer page: attention as nearest-neighbour
-# search; used to judge how much the hashed windows recover)
+# search; it measures how much the hashed windows recover)
 # --------------------------------------------------------------------------
 
 def full_attention(x, v, causal: bool):

@@ -4,7 +4,7 @@ vs the float64 block oracle, through the C ABI.
 Each stage of a staged GPU run (LayerNorm, projections, LSH attention, output
 projection, LayerNorm, feed-forward) is checked against the oracle applied to
 the GPU's own previous stage, so that a bucket decision taken on the GPU's
-bf16 projections is judged on the same values; the fused block call must
+bf16 projections is checked on the same values; the fused block call must
 equal the staged run bit for bit (same kernels, row chunking included)."""
 import numpy as np
 import pytest

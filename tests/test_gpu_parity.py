@@ -3,7 +3,7 @@
 Integer results (buckets, permutations) must match bit for bit; the hash is
 decided exactly on both sides, and oracle near-ties (margin < 1e-6 on the unit
 vector) are counted and printed.  Each floating-point stage is fed the GPU's
-own upstream results, so a stage is judged on its own; the fused call is also
+own upstream results, so a stage is checked on its own; the fused call is also
 checked end to end against the oracle's own forward pass.
 """
 import numpy as np

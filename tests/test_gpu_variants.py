@@ -2,7 +2,7 @@
 HIP path vs the CPU oracle, through the C ABI.
 
 The attention stage is fed the GPU's own hash and sort results, so it is
-judged on its own against the oracle's chunk attention with the variant's
+checked on its own against the oracle's chunk attention with the variant's
 slot codes and pair multiplicities; the fused call is checked against the
 staged calls and end to end against the oracle's forward pass with the same
 variant flags.
