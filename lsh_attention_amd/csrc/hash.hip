@@ -152,6 +152,7 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
   using T = typename HashTraits<BF16>::T;
   constexpr int kRow = HashTraits<BF16>::kRow;
   __shared__ __attribute__((aligned(16))) T sR[2][kHashCB * kRow];
+  __shared__ uint32_t sRho[kMaxHashes];  // per round: largest column norm (fp32 bits, >= 0)
 
   const int blocks_per_bh = (L + kHashTok - 1) / kHashTok;
   const int bh = blockIdx.x / blocks_per_bh;
@@ -205,6 +206,21 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
   }
   if (token_scales != nullptr && wave_valid)  // lanes 0-31: group 0, lanes 32-63: group 1
     token_scales[(size_t)bh * L + tok_base + 32 * hb + n] = token_scale(hb ? nrm2[1] : nrm2[0]);
+  // |x| rounded up, for the certification bound of every round
+  const float xnorm[2] = {sqrtf(nrm2[0]) * 1.000001f, sqrtf(nrm2[1]) * 1.000001f};
+
+  // Largest column norm of each round, from the per-block bounds, into LDS once,
+  // so that a round end reads it without a load and a reduction (NaN bounds are
+  // skipped, as fmaxf would).
+  if (threadIdx.x < kMaxHashes) sRho[threadIdx.x] = 0u;
+  __syncthreads();
+  {
+    const int nblk = (halfp + 63) / 64;
+    for (int i = (int)threadIdx.x; i < n_h * nblk; i += 256) {
+      const float v = colmax[i];
+      if (v == v) atomicMax(&sRho[i / nblk], __float_as_uint(v));
+    }
+  }
 
   // Rotation blocks of kHashCB columns, over all rounds in order.  halfp is a
   // multiple of kHashCB and rot_t is [n_h][halfp][D], so block k is the k-th
@@ -341,27 +357,26 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
 
     // End of round r: merge with the partner lane (same tokens, the other 16 rows
     // of each tile), decode the winner, certify, take the sign.
-    // largest column norm of this round's rotation: one load per lane
-    const int nblk = (halfp + 63) / 64;  // <= 32
-    float rho = lane < nblk ? colmax[r * nblk + lane] : 0.f;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) rho = fmaxf(rho, __shfl_xor(rho, off));
-    const float eps_scale = 65.0f * 0x1p-23f * rho;
+    // largest column norm of this round's rotation
+    const float eps_scale = 65.0f * 0x1p-23f * __uint_as_float(sRho[r]);
     int jstar[2];
     bool certified[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const uint32_t pm1 = __shfl_xor(m1[q], 32), pm2 = __shfl_xor(m2[q], 32);
-      const uint32_t M1 = max(m1[q], pm1);
-      const uint32_t M2 = max(min(m1[q], pm1), max(m2[q], pm2));
+      // lanes l and l + 32 hold the same tokens: both see (lower lane's, upper
+      // lane's) key through one swap of the wave's halves
+      const auto k1 = __builtin_amdgcn_permlane32_swap(m1[q], m1[q], false, false);
+      const auto k2 = __builtin_amdgcn_permlane32_swap(m2[q], m2[q], false, false);
+      const uint32_t M1 = max(k1[0], k1[1]);
+      const uint32_t M2 = max(min(k1[0], k1[1]), max(k2[0], k2[1]));
       // Half of the tile the winner's row lies in (ties of identical keys are
       // equal-value ties, which are never certified, so any choice works).
-      const int win_h = m1[q] > pm1 ? hb : (m1[q] < pm1 ? (hb ^ 1) : 0);
+      const int win_h = k1[0] < k1[1] ? 1 : 0;
       const uint32_t u = lowmask - (M1 & lowmask);  // 16 tg + e
       const int tg = (int)(u >> 4), e = (int)(u & 15);
       jstar[q] = 32 * tg + 8 * (e >> 2) + 4 * win_h + (e & 3);
       const float t1 = __uint_as_float(M1 & kmask), t2 = __uint_as_float(M2 & kmask);
-      const float eps = eps_scale * (sqrtf(nrm2[q]) * 1.000001f);
+      const float eps = eps_scale * xnorm[q];
       const int ebits = (int)((M1 >> 23) & 0xFFu) - 23 + ibits;
       const float delta = ebits >= 1 ? __uint_as_float((uint32_t)ebits << 23) : 0x1p-126f;
       certified[q] = (t1 - t2) > 2.0f * eps + delta;
@@ -397,7 +412,8 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
                                                  dp, false);
           }
         }
-        dp += __shfl_xor(dp, 32);
+        const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(dp), __float_as_uint(dp), false, false);
+        dp = __uint_as_float(h[0]) + __uint_as_float(h[1]);
         result[q] = dp > 0.f ? jstar[q] : jstar[q] + half;
       }
     } else {
@@ -413,7 +429,8 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
           dp = fmaf(a4.z, bq32[q][4 * s4 + 2], dp);
           dp = fmaf(a4.w, bq32[q][4 * s4 + 3], dp);
         }
-        dp += __shfl_xor(dp, 32);
+        const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(dp), __float_as_uint(dp), false, false);
+        dp = __uint_as_float(h[0]) + __uint_as_float(h[1]);
         result[q] = dp > 0.f ? jstar[q] : jstar[q] + half;
       }
     }
