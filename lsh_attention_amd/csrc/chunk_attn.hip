@@ -110,7 +110,8 @@ inline size_t variant_lds_bytes(int attend, int n_h) {
   return (size_t)(chunks_per_block<1>() + 1) * 64 * per_row * sizeof(int);
 }
 
-template <bool BF16, bool CAUSAL, int ATTEND>
+// NT: the output rows are written with non-temporal stores (stream_slot_rows).
+template <bool BF16, bool CAUSAL, int ATTEND, bool NT = false>
 __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn_kernel(
     const typename AttnTraits<BF16>::T* __restrict__ qk, const typename AttnTraits<BF16>::T* __restrict__ v,
     const int32_t* __restrict__ sorted_idx, typename AttnTraits<BF16>::T* __restrict__ o_out,
@@ -745,13 +746,18 @@ __global__ __launch_bounds__(256, (BF16 && ATTEND == 0) ? 4 : 2) void chunk_attn
         }
       }
     }
-    if constexpr (BF16) {
-      *(uint4*)(orow + 8 * grp) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-      *(uint4*)(orow + 32 + 8 * grp) = make_uint4(ow[4], ow[5], ow[6], ow[7]);
-    } else {
+    {
+      // the lane's 16-byte pieces: BF16 two (dims 8 grp.. and 32 + 8 grp..), fp32 four
+      constexpr int kPc = BF16 ? 2 : 4;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        *(uint4*)(orow + 16 * dt + 4 * grp) = make_uint4(ow[4 * dt], ow[4 * dt + 1], ow[4 * dt + 2], ow[4 * dt + 3]);
+      for (int h = 0; h < kPc; ++h) {
+        const u32x4 piece = {ow[4 * h], ow[4 * h + 1], ow[4 * h + 2], ow[4 * h + 3]};
+        u32x4* dst = (u32x4*)(orow + (BF16 ? 32 * h + 8 * grp : 16 * h + 4 * grp));
+        if constexpr (NT)
+          __builtin_nontemporal_store(piece, dst);
+        else
+          *dst = piece;
+      }
     }
     if (grp == 0) lbase[row_g] = own ? kSelf2 * kLn2 : (off + __builtin_amdgcn_logf(sum)) * kLn2;
 
@@ -816,14 +822,26 @@ hipError_t launch_attn_t(const void* qk, const void* v, const int32_t* sorted_id
   const unsigned n_items = (unsigned)blocks_per_bh * (unsigned)BH;
   const unsigned grid = xcd_local ? xcd_grid(n_items) : n_items;
   const size_t dyn = variant_lds_bytes(ATTEND, n_h);
-  if (causal)
-    chunk_attn_kernel<BF16, true, ATTEND><<<grid, 256, dyn, s>>>(
+  // the base bf16 kernel streams large outputs past the last-level cache
+  const bool nt = BF16 && ATTEND == 0 && stream_slot_rows(BH, L, n_h, BF16 ? LSH_BF16 : LSH_F32);
+  auto go = [&](auto causal_tag, auto nt_tag) {
+    chunk_attn_kernel<BF16, decltype(causal_tag)::value, ATTEND, decltype(nt_tag)::value><<<grid, 256, dyn, s>>>(
         (const T*)qk, (const T*)v, sorted_idx, (T*)o_out, lse_out, token_scales, buckets, tok_rec, L, n_h,
         n_slots, n_chunks, blocks_per_bh, cpb, BH, xcd_local);
-  else
-    chunk_attn_kernel<BF16, false, ATTEND><<<grid, 256, dyn, s>>>(
-        (const T*)qk, (const T*)v, sorted_idx, (T*)o_out, lse_out, token_scales, buckets, tok_rec, L, n_h,
-        n_slots, n_chunks, blocks_per_bh, cpb, BH, xcd_local);
+  };
+  using True = std::true_type;
+  using False = std::false_type;
+  if constexpr (BF16 && ATTEND == 0) {
+    if (causal)
+      nt ? go(True{}, True{}) : go(True{}, False{});
+    else
+      nt ? go(False{}, True{}) : go(False{}, False{});
+  } else {
+    if (causal)
+      go(True{}, False{});
+    else
+      go(False{}, False{});
+  }
   return hipGetLastError();
 }
 

@@ -22,7 +22,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ o
                                                       const float* __restrict__ lse_sorted,
                                                       const int32_t* __restrict__ undo_idx,
                                                       void* __restrict__ out_v, float* __restrict__ lse_out,
-                                                      int L, int n_h_rt, size_t n_tokens) {
+                                                      int L, int n_h_rt, size_t n_tokens, bool nt_in) {
   constexpr int kLanesPerTok = BF16 ? 8 : 16;
   constexpr int kMaxH = NH > 0 ? NH : kMaxHashes;
   const int n_h = NH > 0 ? NH : n_h_rt;
@@ -48,7 +48,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ o
   for (int r = 0; r < kMaxH; ++r)
     if (r < n_h) {
       const char* row = (const char*)o_sorted_v + ((bh * n_slots + g[r]) * kD) * (BF16 ? 2 : 4);
-      raw[r] = *(const uint4*)(row + 16 * sub);
+      if (nt_in) {
+        const u32x4 t = __builtin_nontemporal_load((const u32x4*)(row + 16 * sub));
+        raw[r] = make_uint4(t[0], t[1], t[2], t[3]);
+      } else {
+        raw[r] = *(const uint4*)(row + 16 * sub);
+      }
     }
   float m = -INFINITY;
 #pragma unroll
@@ -103,10 +108,11 @@ hipError_t launch_combine_t(const void* o_sorted, const float* lse_sorted, const
   const size_t n_tokens = (size_t)BH * L;
   const size_t threads = n_tokens * (BF16 ? 8 : 16);
   const unsigned grid = (unsigned)((threads + 255) / 256);
+  const bool nt = stream_slot_rows(BH, L, n_h, BF16 ? LSH_BF16 : LSH_F32);  // as the attention wrote them
 #define LSH_COMBINE_CASE(NHV)                                                                              \
   case NHV:                                                                                                \
     combine_kernel<BF16, NHV><<<grid, 256, 0, s>>>(o_sorted, lse_sorted, undo_idx, out, lse_out, L, n_h,   \
-                                                   n_tokens);                                              \
+                                                   n_tokens, nt);                                          \
     break;
   switch (n_h) {
     LSH_COMBINE_CASE(1)
@@ -116,7 +122,7 @@ hipError_t launch_combine_t(const void* o_sorted, const float* lse_sorted, const
     LSH_COMBINE_CASE(8)
     default:
       combine_kernel<BF16, 0><<<grid, 256, 0, s>>>(o_sorted, lse_sorted, undo_idx, out, lse_out, L, n_h,
-                                                   n_tokens);
+                                                   n_tokens, nt);
   }
 #undef LSH_COMBINE_CASE
   return hipGetLastError();

@@ -85,6 +85,14 @@ hipError_t launch_sort_scatter(const int32_t* buckets, const int* hist, int32_t*
                                int32_t* undo_idx, int BHR, int L, int n_b, int n_h,
                                hipStream_t s);
 
+// The per-slot attention rows are written once and read once, by the combine.
+// When they outgrow the chip's 256 MiB last-level cache they are written and
+// read with non-temporal accesses, which keeps them from evicting the QK and V
+// rows that the attention gathers again in every round.
+inline bool stream_slot_rows(int BH, int L, int n_h, lsh_dtype dt) {
+  return (size_t)BH * n_h * L * kD * (dt == LSH_BF16 ? 2 : 4) >= (256ull << 20);
+}
+
 // Outputs per sorted slot ([BH][n_h*L][64], [BH][n_h*L]).  token_scales (nullable): per
 // token (key scale, query bound) from the hash pass.  attend: 0, or the
 // LSH_ATTEND_* bits; buckets ([BH][n_h][L]) are read with LSH_ATTEND_SAME_BUCKET,
