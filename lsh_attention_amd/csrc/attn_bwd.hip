@@ -180,7 +180,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const void* __restrict__ 
 // ---------------------------------------------------------------------------
 // attn_bwd
 // ---------------------------------------------------------------------------
-template <bool BF16, bool CAUSAL>
+// NT: the per-slot dx and dv rows are written with non-temporal stores
+// (stream_slot_rows: large, written once, read once by bwd_reduce).
+template <bool BF16, bool CAUSAL, bool NT>
 __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
     const typename BwdTraits<BF16>::T* __restrict__ qk, const typename BwdTraits<BF16>::T* __restrict__ v,
     const typename BwdTraits<BF16>::T* __restrict__ dout, const int32_t* __restrict__ sorted_idx,
@@ -615,8 +617,16 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
           }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          *(uint4*)(dxb + row * kD + 32 * h + 8 * grp) = make_uint4(rx[h][0], rx[h][1], rx[h][2], rx[h][3]);
-          *(uint4*)(dvb + row * kD + 32 * h + 8 * grp) = make_uint4(rv[h][0], rv[h][1], rv[h][2], rv[h][3]);
+          const u32x4 px = {rx[h][0], rx[h][1], rx[h][2], rx[h][3]}, pv = {rv[h][0], rv[h][1], rv[h][2], rv[h][3]};
+          u32x4* const qx = (u32x4*)(dxb + row * kD + 32 * h + 8 * grp);
+          u32x4* const qv = (u32x4*)(dvb + row * kD + 32 * h + 8 * grp);
+          if constexpr (NT) {
+            __builtin_nontemporal_store(px, qx);
+            __builtin_nontemporal_store(pv, qv);
+          } else {
+            *qx = px;
+            *qv = pv;
+          }
         }
       } else {
 #pragma unroll
@@ -627,8 +637,16 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
             ox[e] = acc_q[dt][e] + kn * (acc_a[dt][e] - proj * xv[dt][e]);
             ov[e] = acc_v[dt][e];
           }
-          *(float4*)(dxb + row * kD + 16 * dt + 4 * grp) = make_float4(ox[0], ox[1], ox[2], ox[3]);
-          *(float4*)(dvb + row * kD + 16 * dt + 4 * grp) = make_float4(ov[0], ov[1], ov[2], ov[3]);
+          const f32x4 px = {ox[0], ox[1], ox[2], ox[3]}, pv = {ov[0], ov[1], ov[2], ov[3]};
+          f32x4* const qx = (f32x4*)(dxb + row * kD + 16 * dt + 4 * grp);
+          f32x4* const qv = (f32x4*)(dvb + row * kD + 16 * dt + 4 * grp);
+          if constexpr (NT) {
+            __builtin_nontemporal_store(px, qx);
+            __builtin_nontemporal_store(pv, qv);
+          } else {
+            *qx = px;
+            *qv = pv;
+          }
         }
       }
       zero_acc();
@@ -650,7 +668,8 @@ template <bool BF16>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const void* __restrict__ dx_slot,
                                                          const void* __restrict__ dv_slot,
                                                          const int32_t* __restrict__ undo_idx, void* __restrict__ dx,
-                                                         void* __restrict__ dv, int L, int n_h, size_t n_tokens) {
+                                                         void* __restrict__ dv, int L, int n_h, size_t n_tokens,
+                                                         bool nt_in) {
   constexpr int kLanesPerTok = BF16 ? 8 : 16;
   constexpr int kE = BF16 ? 8 : 4;
   constexpr size_t kEs = BF16 ? 2 : 4;
@@ -671,8 +690,15 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const void* __restrict_
   for (int r = 0; r < kMaxHashes; ++r)
     if (r < n_h) {
       const size_t off = ((bh * n_slots + g[r]) * kD) * kEs + 16 * sub;
-      rx[r] = *(const uint4*)((const char*)dx_slot + off);
-      rv[r] = *(const uint4*)((const char*)dv_slot + off);
+      if (nt_in) {  // rows the attention backward streamed past the last-level cache
+        const u32x4 tx = __builtin_nontemporal_load((const u32x4*)((const char*)dx_slot + off));
+        const u32x4 tv = __builtin_nontemporal_load((const u32x4*)((const char*)dv_slot + off));
+        rx[r] = make_uint4(tx[0], tx[1], tx[2], tx[3]);
+        rv[r] = make_uint4(tv[0], tv[1], tv[2], tv[3]);
+      } else {
+        rx[r] = *(const uint4*)((const char*)dx_slot + off);
+        rv[r] = *(const uint4*)((const char*)dv_slot + off);
+      }
     }
   float ax[kE], av[kE];
 #pragma unroll
@@ -737,8 +763,9 @@ hipError_t launch_attn_bwd(const void* qk, const void* v, const void* dout, cons
   const int n_chunks = n_slots / kChunk;
   const int blocks_per_bh = (n_chunks + kBwdChunksPerBlock - 1) / kBwdChunksPerBlock;
   const unsigned grid = (unsigned)blocks_per_bh * (unsigned)BH;
+  const bool nt = stream_slot_rows(BH, L, n_h, dt);
 #define LSH_BWD_LAUNCH(B16, CA)                                                                               \
-  attn_bwd_kernel<B16, CA><<<grid, 512, 0, s>>>(                                                              \
+  (nt ? attn_bwd_kernel<B16, CA, true> : attn_bwd_kernel<B16, CA, false>)<<<grid, 512, 0, s>>>(              \
       (const typename BwdTraits<B16>::T*)qk, (const typename BwdTraits<B16>::T*)v,                           \
       (const typename BwdTraits<B16>::T*)dout, sorted_idx, lse_sorted, tok_w, tok_scale,                     \
       (typename BwdTraits<B16>::T*)dx_slot, (typename BwdTraits<B16>::T*)dv_slot, L, n_h, n_slots, n_chunks, \
@@ -759,10 +786,11 @@ hipError_t launch_bwd_reduce(const void* dx_slot, const void* dv_slot, const int
   const size_t n_tok = (size_t)BH * L;
   const int lanes = dt == LSH_BF16 ? 8 : 16;
   const unsigned grid = (unsigned)((n_tok * lanes + 255) / 256);
+  const bool nt = stream_slot_rows(BH, L, n_h, dt);  // as attn_bwd wrote them
   if (dt == LSH_BF16)
-    bwd_reduce_kernel<true><<<grid, 256, 0, s>>>(dx_slot, dv_slot, undo_idx, dx, dv, L, n_h, n_tok);
+    bwd_reduce_kernel<true><<<grid, 256, 0, s>>>(dx_slot, dv_slot, undo_idx, dx, dv, L, n_h, n_tok, nt);
   else
-    bwd_reduce_kernel<false><<<grid, 256, 0, s>>>(dx_slot, dv_slot, undo_idx, dx, dv, L, n_h, n_tok);
+    bwd_reduce_kernel<false><<<grid, 256, 0, s>>>(dx_slot, dv_slot, undo_idx, dx, dv, L, n_h, n_tok, nt);
   return hipGetLastError();
 }
 
