@@ -22,11 +22,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ o
                                                       const float* __restrict__ lse_sorted,
                                                       const int32_t* __restrict__ undo_idx,
                                                       void* __restrict__ out_v, float* __restrict__ lse_out,
-                                                      int L, int n_h_rt, size_t n_tokens, bool nt_in) {
+                                                      int L, int n_h_rt, size_t n_tokens, bool nt_in,
+                                                      bool xcd_order) {
   constexpr int kLanesPerTok = BF16 ? 8 : 16;
   constexpr int kMaxH = NH > 0 ? NH : kMaxHashes;
   const int n_h = NH > 0 ? NH : n_h_rt;
-  const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t blk = xcd_order ? xcd_item(blockIdx.x, gridDim.x) : blockIdx.x;
+  const size_t gid = blk * blockDim.x + threadIdx.x;
   const size_t tok = gid / kLanesPerTok;
   const int sub = (int)(gid % kLanesPerTok);
   if (tok >= n_tokens) return;
@@ -107,12 +109,17 @@ hipError_t launch_combine_t(const void* o_sorted, const float* lse_sorted, const
                             float* lse_out, int BH, int L, int n_h, hipStream_t s) {
   const size_t n_tokens = (size_t)BH * L;
   const size_t threads = n_tokens * (BF16 ? 8 : 16);
-  const unsigned grid = (unsigned)((threads + 255) / 256);
   const bool nt = stream_slot_rows(BH, L, n_h, BF16 ? LSH_BF16 : LSH_F32);  // as the attention wrote them
+  // Rows that stay in the last-level cache between the two kernels: each XCD
+  // takes a contiguous range of tokens (causal_lm_4k 31.8 -> 27.1 us); streamed
+  // rows keep the plain order.
+  const bool xo = !nt;
+  const unsigned n_blk = (unsigned)((threads + 255) / 256);
+  const unsigned grid = xo ? xcd_grid(n_blk) : n_blk;
 #define LSH_COMBINE_CASE(NHV)                                                                              \
   case NHV:                                                                                                \
     combine_kernel<BF16, NHV><<<grid, 256, 0, s>>>(o_sorted, lse_sorted, undo_idx, out, lse_out, L, n_h,   \
-                                                   n_tokens, nt);                                          \
+                                                   n_tokens, nt, xo);                                          \
     break;
   switch (n_h) {
     LSH_COMBINE_CASE(1)
@@ -122,7 +129,7 @@ hipError_t launch_combine_t(const void* o_sorted, const float* lse_sorted, const
     LSH_COMBINE_CASE(8)
     default:
       combine_kernel<BF16, 0><<<grid, 256, 0, s>>>(o_sorted, lse_sorted, undo_idx, out, lse_out, L, n_h,
-                                                   n_tokens, nt);
+                                                   n_tokens, nt, xo);
   }
 #undef LSH_COMBINE_CASE
   return hipGetLastError();
