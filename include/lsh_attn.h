@@ -341,7 +341,10 @@ int reformer_block_fwd(const void* x1, const void* x2, const void* rot, const vo
 
 /* Timing helpers for callers that have no HIP runtime binding of their own:
  * create/destroy a hipEvent_t (returned as void*), and the elapsed time in
- * milliseconds between two recorded events (synchronises on `end`). */
+ * milliseconds between two recorded events (synchronises on `end`).  The
+ * events are for timing only (created with hipEventDisableSystemFence): their
+ * completion does not make device writes visible to the host, so synchronise
+ * the stream or the device before reading results on the host. */
 int lsh_event_create(void** event);
 int lsh_event_destroy(void* event);
 int lsh_event_record(void* event, void* stream);
