@@ -40,17 +40,18 @@
 // ring slot w >> 2):
 //   S = Q K^T and dP = dO V^T on MFMA with queries as rows, so each lane holds
 //   4 consecutive queries of one key;  dV^T += dO^T Pw and A^T += Xq^T dS take
-//   the lane's own Pw / dS as the B operand, the A operand from LDS copies of
-//   dO and x stored transposed with the queries permuted into operand order;
-//   dS kn is written to LDS (bf16) and the key-owning waves of the current
-//   chunk form dQ^T = Xk^T (dS kn)^T over all 128 keys for their 16 queries,
-//   whose layout equals their own key accumulators.  The dS tile reuses the
-//   dO row and dO^T buffers (a barrier separates the uses).  The transposed
-//   tiles list the dims as 0, 2, .., 62, 1, 3, .., 63, so each thread writes
-//   two 16-byte pieces of consecutive rows and each lane's finished dx and dv
-//   are two contiguous 16-byte pieces.  The bf16 tiles use unpadded rows with
-//   XOR-swizzled 16-byte pieces (xoff / voff).  fp32 inputs take the fp32 MFMA
-//   and read the transposed operands from the row copies.
+//   the lane's own Pw / dS as the B operand, the A operand straight from the
+//   LDS row copies of dO and x through the gfx950 transposing LDS read
+//   (ds_read_b64_tr_b16, tr_operand), with the queries in the order of the B
+//   operand; dS kn is written to LDS (bf16) and the key-owning waves of the
+//   current chunk form dQ^T = Xk^T (dS kn)^T over all 128 keys for their 16
+//   queries, whose layout equals their own key accumulators.  The dS tile
+//   reuses the dO row buffer (a barrier separates the uses).  The transposed
+//   operands put dims 8g + 4h + e (h = 0, 1) of each 32-dim half in the rows
+//   of lane group g, so each lane's finished dx and dv are two contiguous
+//   16-byte pieces.  The bf16 tiles use unpadded rows with XOR-swizzled 16-byte
+//   pieces (xoff / voff).  fp32 inputs take the fp32 MFMA and read the
+//   operands element by element from the row copies.
 #include "lsh_bwd.h"
 
 namespace lsh {
@@ -76,16 +77,12 @@ template <>
 struct BwdTraits<true> {
   using T = uint16_t;
   static constexpr int kXRow = 64;    // row copies: 64 dims (pieces swizzled, xoff)
-  static constexpr int kTRow = 128;   // transposed x: 2 slots x 64 (pieces swizzled, voff)
-  static constexpr int kQRow = 64;    // transposed dO: 64 queries (xoff)
   static constexpr int kSRow = 128;   // dS kn: 2 slots x 64 keys (voff)
 };
 template <>
 struct BwdTraits<false> {
   using T = float;
   static constexpr int kXRow = 68;
-  static constexpr int kTRow = 4;     // unused
-  static constexpr int kQRow = 4;     // unused
   static constexpr int kSRow = 132;
 };
 
@@ -108,6 +105,36 @@ __device__ inline int voff(int row, int piece) { return row * 128 + 8 * (piece ^
 // holds row 32h + 16b + 4g + e.
 __device__ inline int permcol(int r) {
   return (r & ~31) | (((r >> 2) & 3) << 3) | (((r >> 4) & 1) << 2) | (r & 3);
+}
+
+// The value of the lane with index (this lane xor 1), resp. xor 2, within its
+// quad of lanes (DPP quad permutations [1, 0, 3, 2] and [2, 3, 0, 1]).
+__device__ inline uint32_t quad_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+}
+__device__ inline uint32_t quad_xor2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// A operand (16 dims x 32 rows of a bf16 row tile) of v_mfma_f32_16x16x32_bf16,
+// read transposed from the row-major tile by ds_read_b64_tr_b16.  Within each
+// 16-lane group, that instruction hands lane i element j of the 8-byte read of
+// lane 4j + (i >> 2), element i & 3 (checked on the device).  Here lane
+// 16g + 4j + r of the group reads row r0 + 4g + j (and r0 + 16 + 4g + j) at dims
+// D(r) .. D(r) + 3, D(r) = 32 (dt >> 1) + 8r + 4 (dt & 1), so operand row i holds
+// dim 32 (dt >> 1) + 8 (i >> 2) + 4 (dt & 1) + (i & 3) and lane group g the K
+// indices 8g + b * 4 + e <-> tile rows r0 + 16b + 4g + e: the order of the
+// lane's own probabilities as the B operand (permcol).
+__device__ inline bf16x8 tr_operand(const uint16_t* tile, int r0, int dt, int lane) {
+  const int g = lane >> 4, j = (lane >> 2) & 3, r = lane & 3;
+  const int piece = 4 * (dt >> 1) + r, sub = 4 * (dt & 1);
+  const int ra = r0 + 4 * g + j;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + xoff(ra, piece) + sub));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + xoff(ra + 16, piece) + sub));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // ---------------------------------------------------------------------------
@@ -191,18 +218,14 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
     int n_h, int n_slots, int n_chunks, int blocks_per_bh) {
   using T = typename BwdTraits<BF16>::T;
   constexpr int kXRow = BwdTraits<BF16>::kXRow;
-  constexpr int kTRow = BwdTraits<BF16>::kTRow;
-  constexpr int kQRow = BwdTraits<BF16>::kQRow;
   constexpr int kSRow = BwdTraits<BF16>::kSRow;
   constexpr int kCPB = kBwdChunksPerBlock;
   constexpr int kLoads = BF16 ? 1 : 2;  // 16-byte row pieces per thread (8 per bf16 row, 16 per fp32 row)
 
   __shared__ __attribute__((aligned(16))) T sX[2][64 * kXRow];   // x rows per ring slot
   __shared__ __attribute__((aligned(16))) T sV[2][64 * kXRow];   // v rows per ring slot
-  // transposed tiles (bf16): rows are dims in the order 0, 2, .., 62, 1, 3, .., 63
-  __shared__ __attribute__((aligned(16))) T sXT[BF16 ? 64 * kTRow : 1];  // [dim][64 slot + permcol(row)]
-  // dO rows + dO^T (bf16), or dO rows (fp32); the bf16 dS kn tile reuses the space.
-  constexpr int kDoElems = 64 * kXRow + (BF16 ? 64 * kQRow : 0);
+  // dO rows; the bf16 dS kn tile reuses the space.
+  constexpr int kDoElems = 64 * kXRow;
   constexpr int kSElems = 64 * kSRow;
   constexpr int kUnion = BF16 ? (kDoElems > kSElems ? kDoElems : kSElems) : kDoElems;
   __shared__ __attribute__((aligned(16))) T sDoBuf[kUnion];
@@ -212,7 +235,6 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
   __shared__ __attribute__((aligned(16))) int sPos[kCPB + 2][64];
   __shared__ int sSelfOnly;  // the current chunk has a self-only query row
   T* const sDO = sDoBuf;                      // [query][dim]
-  T* const sDOT = sDoBuf + 64 * kXRow;        // [dim][permcol(query)] (bf16)
   uint16_t* const sDS16 = (uint16_t*)sDoBuf;  // [query][64 slot + permcol(key)] (bf16)
 
   const int bh = blockIdx.x / blocks_per_bh;
@@ -244,14 +266,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
 
   // ---- gathers (registers) and commits (LDS) ----
   // rows: thread t holds 16-byte pieces (t & 7) * kLoads + i of row t >> 3.
-  // transposed (bf16), built from the row copies once they are in LDS: threads
-  // 0-255 transpose x, threads 256-511 dO.  Thread (p, j) = (t & 31, (t >> 5) & 7)
-  // reads dims 2p, 2p+1 of rows 32h + 16b + 4g + 0..3 (h = j >> 2, g = j & 3,
-  // b = 0, 1): columns 32h + 8g + 0..7, piece j of the 64 columns; it writes them
-  // to rows p (dim 2p) and 32 + p (dim 2p + 1).
   const int prow = tid >> 3, ppc = (tid & 7) * kLoads;
-  const int tp = tid & 31, tj = (tid >> 5) & 7;
-  const int trow = 32 * (tj >> 2) + 4 * (tj & 3);
   uint4 xr[kLoads], vr[kLoads], dr[kLoads];
   float2 ksc = make_float2(0.f, 0.f), qsw = make_float2(0.f, 0.f);
   float qlse = 0.f;
@@ -300,35 +315,6 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
         sWc[tid] = qsw.y;
         const uint64_t so = __ballot(qlse < kSelfOnlyLse);  // wave 0: the chunk's 64 queries
         if (tid == 0) sSelfOnly = so != 0ull ? 1 : 0;
-      }
-    }
-    if constexpr (BF16) {
-      __syncthreads();  // the row copies are in LDS
-      if (tid < 256 || queries) {
-        const T* src = tid < 256 ? sX[slot] : sDO;  // wave-uniform
-        uint32_t tw[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int r = trow + (i & 3) + 16 * (i >> 2);
-          tw[i] = *(const uint32_t*)(src + xoff(r, tp >> 2) + 2 * (tp & 3));
-        }
-        // low halves: dim 2p of the 8 rows in column order; high halves: dim 2p + 1
-        uint4 lo, hi;
-        lo.x = __builtin_amdgcn_perm(tw[1], tw[0], 0x05040100u);
-        lo.y = __builtin_amdgcn_perm(tw[3], tw[2], 0x05040100u);
-        lo.z = __builtin_amdgcn_perm(tw[5], tw[4], 0x05040100u);
-        lo.w = __builtin_amdgcn_perm(tw[7], tw[6], 0x05040100u);
-        hi.x = __builtin_amdgcn_perm(tw[1], tw[0], 0x07060302u);
-        hi.y = __builtin_amdgcn_perm(tw[3], tw[2], 0x07060302u);
-        hi.z = __builtin_amdgcn_perm(tw[5], tw[4], 0x07060302u);
-        hi.w = __builtin_amdgcn_perm(tw[7], tw[6], 0x07060302u);
-        if (tid < 256) {
-          *(uint4*)(&sXT[voff(tp, 8 * slot + tj)]) = lo;
-          *(uint4*)(&sXT[voff(32 + tp, 8 * slot + tj)]) = hi;
-        } else {
-          *(uint4*)(&sDOT[xoff(tp, tj)]) = lo;
-          *(uint4*)(&sDOT[xoff(32 + tp, tj)]) = hi;
-        }
       }
     }
   };
@@ -447,13 +433,13 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
             dsk16[2 * qt + 1] = u.y;
           }
           // ---- dV^T += dO^T Pw, A^T += Xq^T dS (K = queries 32 ks .. 32 ks + 31, permuted;
-          // rows = dims in the transposed tiles' order) ----
+          // rows = dims in tr_operand's order) ----
           const bf16x8 bp = __builtin_shufflevector(bp4[0], bp4[1], 0, 1, 2, 3, 4, 5, 6, 7);
           const bf16x8 bs = __builtin_shufflevector(bs4[0], bs4[1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
           for (int dt = 0; dt < 4; ++dt) {
-            const bf16x8 ad = *(const bf16x8*)(&sDOT[xoff(16 * dt + col, 4 * ks + grp)]);
-            const bf16x8 ax = *(const bf16x8*)(&sXT[voff(16 * dt + col, 8 * cur + 4 * ks + grp)]);
+            const bf16x8 ad = tr_operand(sDO, 32 * ks, dt, lane_v);
+            const bf16x8 ax = tr_operand(sX[cur], 32 * ks, dt, lane_v);
             acc_v[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ad, bp, acc_v[dt], 0, 0, 0);
             acc_a[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bs, acc_a[dt], 0, 0, 0);
           }
@@ -514,19 +500,35 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
     if (do_ds) {
       __syncthreads();  // every wave is done reading dO (the bf16 dS tile reuses its space)
       if (active) {
+        if constexpr (BF16) {
+          // The four lanes of a quad hold keys 4i .. 4i + 3, whose tile columns are
+          // consecutive (permcol keeps a key's low two bits), for the same four
+          // queries of each query tile.  A 4 x 4 transpose of their 16-bit values
+          // inside the quad gives lane j the four keys of query j, written as one
+          // 8-byte piece instead of four 2-byte stores to one word.
+          const int j = lane_v & 3;
+          const int kc0 = 64 * sw + (permcol(kr) & ~3);
+          const uint32_t sel = (j & 1) ? 0x03020706u : 0x05040100u;
 #pragma unroll
-        for (int qt = 0; qt < 4; ++qt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int q = 16 * qt + 4 * grp + e;
-            if constexpr (BF16) {
-              const uint32_t wv = dsk16[2 * qt + (e >> 1)];
-              const int kc = 64 * sw + permcol(kr);
-              sDS16[voff(q, kc >> 3) + (kc & 7)] = (uint16_t)((e & 1) ? (wv >> 16) : (wv & 0xFFFFu));
-            } else {
-              sDsF[q * kSRow + 64 * sw + kr] = dskf[4 * qt + e];
-            }
+          for (int qt = 0; qt < 4; ++qt) {
+            const uint32_t d0 = dsk16[2 * qt], d1 = dsk16[2 * qt + 1];  // queries (0, 1), (2, 3) of key j
+            // with lane j ^ 2: lanes 0, 1 keep queries 0-1 of keys j, j + 2; lanes 2, 3 queries 2-3
+            const uint32_t got = quad_xor2((j & 2) ? d0 : d1);
+            const uint32_t a = (j & 2) ? got : d0;  // key j & 1
+            const uint32_t b = (j & 2) ? d1 : got;  // key (j & 1) + 2
+            // with lane j ^ 1: the halves of query j of keys 0, 1 and of keys 2, 3
+            const uint32_t a1 = quad_xor1(a), b1 = quad_xor1(b);
+            uint2 w;
+            w.x = __builtin_amdgcn_perm(a1, a, sel);
+            w.y = __builtin_amdgcn_perm(b1, b, sel);
+            *(uint2*)(&sDS16[voff(16 * qt + 4 * grp + j, kc0 >> 3) + (kc0 & 7)]) = w;
           }
+        } else {
+#pragma unroll
+          for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sDsF[(16 * qt + 4 * grp + e) * kSRow + 64 * sw + kr] = dskf[4 * qt + e];
+        }
       }
       __syncthreads();
       if (mine_cur) {
@@ -538,7 +540,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
             const bf16x8 bq = *(const bf16x8*)(&sDS16[voff(kr, kp)]);
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
-              const bf16x8 a = *(const bf16x8*)(&sXT[voff(16 * dt + col, kp)]);
+              const bf16x8 a = tr_operand(sX[ks < 2 ? prv : cur], 32 * (ks & 1), dt, lane_v);
               acc_q[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq, acc_q[dt], 0, 0, 0);
             }
           }
@@ -564,10 +566,10 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
       const int chunk = (c - 1 + n_chunks) % n_chunks;
       const float kn = sKn[sw][kr];
       const bool tiny = kn > 0.12e12f;  // |x| at the 1e-12 floor: khat = x / 1e-12, no projection
-      // bf16: accumulator row 16 dt + 4 grp + e is dim 2 (16 dt + 4 grp + e) for dt < 2 and
-      // 2 (16 (dt - 2) + 4 grp + e) + 1 above, so tiles dt and dt + 2 hold dims 32 dt + 8 grp
-      // + 2e and + 2e + 1 (dt = 0, 1): pieces grp and 4 + grp of the key's row.  fp32: tile
-      // dt holds dims 16 dt + 4 grp + e.
+      // bf16: accumulator row 4 grp + e of tile dt is dim 32 (dt >> 1) + 8 grp + 4 (dt & 1) + e
+      // (tr_operand), so tiles 2h and 2h + 1 hold piece 4h + grp of the key's row: its dim
+      // 32 h + 8 grp + u is element u & 3 of tile 2h + (u >> 2).  fp32: tile dt holds dims
+      // 16 dt + 4 grp + e.
       float xv[4][4];
       if constexpr (BF16) {
 #pragma unroll
@@ -576,8 +578,8 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
           const uint32_t rw[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            xv[h][e] = bf_lo(rw[e]);
-            xv[h + 2][e] = bf_hi(rw[e]);
+            xv[2 * h + (e >> 1)][2 * (e & 1)] = bf_lo(rw[e]);
+            xv[2 * h + (e >> 1)][2 * (e & 1) + 1] = bf_hi(rw[e]);
           }
         }
       } else {
@@ -587,11 +589,17 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
           xv[dt][0] = r.x; xv[dt][1] = r.y; xv[dt][2] = r.z; xv[dt][3] = r.w;
         }
       }
+      // x . a over the lane's 16 dims; bf16 in the order 8 grp + 2e, 32 + 8 grp + 2e,
+      // 8 grp + 2e + 1, 32 + 8 grp + 2e + 1 (e = 0..3), fp32 tile by tile
       float dot = 0.f;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int s2 = 0; s2 < 4; ++s2)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dot = fmaf(xv[dt][e], acc_a[dt][e], dot);
+        for (int e = 0; e < 4; ++e) {
+          const int t = BF16 ? 2 * (s2 & 1) + (e >> 1) : s2;
+          const int u = BF16 ? 2 * (e & 1) + (s2 >> 1) : e;
+          dot = fmaf(xv[t][u], acc_a[t][u], dot);
+        }
       // sum over the 4 lanes holding this key (lanes l, l^16, l^32, l^48)
       {
         auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(dot), __float_as_uint(dot), false, false);
@@ -603,17 +611,18 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_kernel(
       const float proj = tiny ? 0.f : 64.f * kn * kn * dot;
       const size_t row = (size_t)chunk * kChunk + kr;
       if constexpr (BF16) {
-        // word e of piece h: dims 32 h + 8 grp + 2e, + 1 (tiles h and h + 2)
+        // word e of piece h: dims 32 h + 8 grp + 2e, + 1: elements 2 (e & 1), + 1 of tile 2h + (e >> 1)
         uint32_t rx[2][4], rv[2][4];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float x0 = acc_q[h][e] + kn * (acc_a[h][e] - proj * xv[h][e]);
-            const float x1 = acc_q[h + 2][e] + kn * (acc_a[h + 2][e] - proj * xv[h + 2][e]);
+            const int t = 2 * h + (e >> 1), u = 2 * (e & 1);
+            const float x0 = acc_q[t][u] + kn * (acc_a[t][u] - proj * xv[t][u]);
+            const float x1 = acc_q[t][u + 1] + kn * (acc_a[t][u + 1] - proj * xv[t][u + 1]);
             rx[h][e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
             rv[h][e] = __builtin_bit_cast(uint32_t,
-                                          __builtin_convertvector(f32x2{acc_v[h][e], acc_v[h + 2][e]}, bf16x2));
+                                          __builtin_convertvector(f32x2{acc_v[t][u], acc_v[t][u + 1]}, bf16x2));
           }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
