@@ -5,12 +5,22 @@ and the angular-sector picture of the Reformer explainer page
 (akshathtiwari.co.in/blog/reformer), closed forms worked by hand, exact
 invariants, and brute force on tiny inputs.
 """
+import json
 import math
+import os
 
 import numpy as np
 import pytest
 
 import oracle as O
+
+_GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    """A hand-worked fixture of tests/golden (each states its source and derivation)."""
+    with open(os.path.join(_GOLDEN, name)) as f:
+        return json.load(f)
 
 
 def _unit(v):
@@ -233,53 +243,34 @@ def test_one_bucket_one_chunk_is_full_attention(n_h, causal):
 
 
 def test_hand_worked_logits_scale_and_key_normalisation():
-    """Four tokens, one bucket, one chunk (the window is the chunk twice).
-    Keys are normalised, queries are not, the scale is 1/sqrt(64) = 1/8:
-      x0 = 2 e0, x1 = 3 e0 + 4 e1 (|x1| = 5), x2 = -e1, x3 = e2 / 2.
-    Logits worked by hand (self excluded):
-      q0: k1 = 2*3/5/8 = 0.15, k2 = 0, k3 = 0
-      q1: k0 = 3/8, k2 = -4/8, k3 = 0
-      q2: k0 = 0, k1 = -0.8/8, k3 = 0
-      q3: all 0.
-    With one-hot values, out_i is the weight vector."""
+    """Four tokens, one bucket, one chunk (the window is the chunk twice), logits
+    worked by hand in tests/golden/hand_logits.json: keys normalised, queries
+    not, scale 1/sqrt(64) = 1/8, self excluded.  With one-hot values, out_i is
+    the weight vector."""
+    g = _golden("hand_logits.json")
     D = 64
     x = np.zeros((4, D))
-    x[0, 0] = 2
-    x[1, 0], x[1, 1] = 3, 4
-    x[2, 1] = -1
-    x[3, 2] = 0.5
+    for i, d, val in g["x_nonzero"]:
+        x[i, d] = val
     v = np.eye(4, D)
-    e = math.exp
+    w = [[0.0 if lg is None else math.exp(lg) for lg in row] for row in g["logits"]]
     expect = np.zeros((4, D))
-    w = [[0, e(0.15), 1, 1], [e(0.375), 0, e(-0.5), 1], [1, e(-0.1), 0, 1], [1, 1, 1, 0]]
     for i in range(4):
         expect[i, :4] = np.array(w[i]) / sum(w[i])
     r = O.forward_problem(x, v, None, 1, 1, 4, False)
     np.testing.assert_allclose(r["out"], expect, rtol=0, atol=1e-14)
-    np.testing.assert_allclose(r["lse"], [math.log(2 * sum(wi)) for wi in w], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(r["lse"], [math.log(g["window_multiplicity"] * sum(wi)) for wi in w], rtol=0,
+                               atol=1e-14)
 
 
 # Two buckets, two rounds, x_i = +e0 for even i and -e0 for odd i; round 0's
-# single rotation column is +e0 and round 1's is -e0.  Round 0 therefore sorts
-# the even positions (bucket 0) before the odd ones, round 1 the reverse.
-# Chunks of 4 over the 32 round-major slots, worked by hand:
-#   ch0 [0,2,4,6]    ch1 [8,10,12,14]  ch2 [1,3,5,7]   ch3 [9,11,13,15]
-#   ch4 [1,3,5,7]    ch5 [9,11,13,15]  ch6 [0,2,4,6]   ch7 [8,10,12,14]
-# and the window of chunk c is chunk c-1 (cyclic over all 8) plus chunk c:
-HAND_WINDOWS = {
-    0: {8, 10, 12, 14, 0, 2, 4, 6},
-    1: {0, 2, 4, 6, 8, 10, 12, 14},
-    2: {8, 10, 12, 14, 1, 3, 5, 7},
-    3: {1, 3, 5, 7, 9, 11, 13, 15},
-    4: {9, 11, 13, 15, 1, 3, 5, 7},
-    5: {1, 3, 5, 7, 9, 11, 13, 15},
-    6: {9, 11, 13, 15, 0, 2, 4, 6},
-    7: {0, 2, 4, 6, 8, 10, 12, 14},
-}
-HAND_CHUNK_OF = {  # (round, position) -> chunk
-    **{(0, p): c for c, ps in {0: [0, 2, 4, 6], 1: [8, 10, 12, 14], 2: [1, 3, 5, 7], 3: [9, 11, 13, 15]}.items() for p in ps},
-    **{(1, p): c for c, ps in {4: [1, 3, 5, 7], 5: [9, 11, 13, 15], 6: [0, 2, 4, 6], 7: [8, 10, 12, 14]}.items() for p in ps},
-}
+# single rotation column is +e0 and round 1's is -e0.  The chunks of the sorted
+# slots and each chunk's window (previous chunk, cyclic over all rounds, plus
+# itself) are worked by hand in tests/golden/windows_two_rounds.json.
+_WIN = _golden("windows_two_rounds.json")
+HAND_WINDOWS = {int(c): set(w) for c, w in _WIN["windows"].items()}
+_CPR = _WIN["L"] // _WIN["chunk_len"]  # chunks per round
+HAND_CHUNK_OF = {(int(c) // _CPR, p): int(c) for c, ps in _WIN["chunks"].items() for p in ps}
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -289,14 +280,14 @@ def test_hand_enumerated_windows(causal):
     output is its weight vector, whose support must be the hand-enumerated
     window minus the token itself (keys after it dropped when causal; the
     token alone when nothing else is left)."""
-    L, D = 16, 64
+    L, D, n_h = _WIN["L"], 64, _WIN["n_hashes"]
     x = np.zeros((L, D))
-    x[:, 0] = [1.0 if i % 2 == 0 else -1.0 for i in range(L)]
-    rot = np.zeros((2, D, 1))
-    rot[0, 0, 0], rot[1, 0, 0] = 1.0, -1.0
+    x[:, 0] = _WIN["x_dim0"]
+    rot = np.zeros((n_h, D, _WIN["n_buckets"] // 2))
+    rot[:, 0, 0] = _WIN["rotation_dim0"]
     v = np.eye(L, D)
-    r = O.forward_problem(x, v, rot, 2, 2, 4, causal)
-    for rr in range(2):
+    r = O.forward_problem(x, v, rot, _WIN["n_buckets"], n_h, _WIN["chunk_len"], causal)
+    for rr in range(n_h):
         for i in range(L):
             win = HAND_WINDOWS[HAND_CHUNK_OF[(rr, i)]] - {i}
             if causal:
@@ -376,74 +367,66 @@ def test_combine_equals_softmax_over_the_multiset_union(causal):
 # its hashed windows (union over rounds) contain.  The pins below fix the
 # neighbour order, the windows and the expected fractions by hand.
 
+_REC = _golden("recall_circle.json")
+
+
 def _circle_tokens():
-    """Eight tokens in the plane of the first two dims (D = 64, the rest zero):
-    token i at angle 2^i - 1 degrees (0, 1, 3, 7, 15, 31, 63, 127) with norm 2^i.
-    All angles lie in [0, 127], so the angular distance of i and j is
-    |2^i - 2^j| degrees, and these are distinct for distinct pairs; by cosine
-    (keys normalised) the neighbours of query i are i-1, i-2, ..., 0 (distances
-    2^i - 2^j < 2^i), then i+1, ..., 7 (distances >= 2^i).  The norms grow with
-    i, so a key left unnormalised would reorder them."""
-    deg = np.array([2.0 ** i - 1 for i in range(8)])
-    rho = np.array([2.0 ** i for i in range(8)])
+    """Eight tokens in the plane of the first two dims (D = 64, the rest zero) at
+    the angles and norms of tests/golden/recall_circle.json (token i at 2^i - 1
+    degrees, norm 2^i): the neighbours of query i by cosine are i-1, ..., 0, then
+    i+1, ..., 7.  The norms grow with i, so a key left unnormalised would reorder
+    them."""
+    deg = np.array(_REC["angles_deg"], dtype=np.float64)
+    rho = np.array(_REC["norms"], dtype=np.float64)
     x = np.zeros((8, 64))
     x[:, 0] = rho * np.cos(np.radians(deg))
     x[:, 1] = rho * np.sin(np.radians(deg))
     return x
 
 
-# One round, chunk_len 2: sorted order 0 1 | 4 5 | 2 3 | 6 7, so the windows
-# (previous chunk, cyclic, and the own chunk) are
-#   tokens 0, 1: {6, 7, 0, 1}   tokens 4, 5: {0, 1, 4, 5}
-#   tokens 2, 3: {4, 5, 2, 3}   tokens 6, 7: {2, 3, 6, 7}
-_S1 = np.array([0, 1, 4, 5, 2, 3, 6, 7])
-_U1 = np.array([[0, 1, 4, 5, 2, 3, 6, 7]])
-# A second round in position order (slots 8..15: 0 1 | 2 3 | 4 5 | 6 7); its first
-# chunk looks back at round 0's last chunk {6, 7}, and round 0's first chunk now
-# looks back at round 1's last chunk, again {6, 7}.  Unions over both rounds:
-#   tokens 0, 1: {0, 1, 6, 7}   tokens 2..5: {0, ..., 5}   tokens 6, 7: {2, ..., 7}
-_S2 = np.array([0, 1, 4, 5, 2, 3, 6, 7, 0, 1, 2, 3, 4, 5, 6, 7])
-_U2 = np.array([[0, 1, 4, 5, 2, 3, 6, 7], list(range(8, 16))])
+# One round, chunk_len 2, sorted order 0 1 | 4 5 | 2 3 | 6 7; a second round in
+# position order, whose first chunk looks back at round 0's last chunk {6, 7}
+# (and round 0's first chunk at round 1's last, again {6, 7}).  Windows and
+# expected fractions: tests/golden/recall_circle.json.
+_C = _REC["chunk_len"]
+_S1 = np.array(_REC["one_round"]["sorted_idx"])
+_U1 = np.array(_REC["one_round"]["undo_idx"])
+_S2 = np.array(_REC["two_rounds"]["sorted_idx"])
+_U2 = np.array(_REC["two_rounds"]["undo_idx"])
+
+
+def _frac(nd):
+    return nd[0] / nd[1]
 
 
 def test_hand_windows_of_the_recall_pins():
-    assert O.attended_positions(_S1, _U1, 2, 0) == {0, 1, 6, 7}
-    assert O.attended_positions(_S1, _U1, 2, 4) == {0, 1, 4, 5}
-    assert O.attended_positions(_S1, _U1, 2, 3) == {2, 3, 4, 5}
-    assert O.attended_positions(_S1, _U1, 2, 7) == {2, 3, 6, 7}
-    assert O.attended_positions(_S2, _U2, 2, 1) == {0, 1, 6, 7}
-    assert O.attended_positions(_S2, _U2, 2, 4) == {0, 1, 2, 3, 4, 5}
-    assert O.attended_positions(_S2, _U2, 2, 6) == {2, 3, 4, 5, 6, 7}
+    for key, s, u in (("one_round", _S1, _U1), ("two_rounds", _S2, _U2)):
+        for i, w in _REC[key]["windows"].items():
+            assert O.attended_positions(s, u, _C, int(i)) == set(w), (key, i)
 
 
 def test_recall_at_k_hand_counts_one_round():
-    """Nearest neighbours (first three) of each query, and whether the query's
-    window holds them:
-      q0: 1 2 3 -> 1 in, 2 3 out        q4: 3 2 1 -> 3 2 out, 1 in
-      q1: 0 2 3 -> 0 in                 q5: 4 3 2 -> 4 in
-      q2: 1 0 3 -> 1 0 out, 3 in        q6: 5 4 3 -> 5 4 out, 3 in
-      q3: 2 1 0 -> 2 in                 q7: 6 5 4 -> 6 in
-    R@1 = 5/8 (q0 q1 q3 q5 q7); R@2 = 5/16; R@3 = 8/24.  A query counted as its
-    own neighbour gives R@1 = 1; the smallest logits, or keys left unnormalised,
-    give other counts."""
+    """Hand counts of the first three neighbours inside the one-round windows:
+    R@1 = 5/8, R@2 = 5/16, R@3 = 8/24.  A query counted as its own neighbour
+    gives R@1 = 1; the smallest logits, or keys left unnormalised, give other
+    counts."""
     x = _circle_tokens()
-    assert O.recall_at_k(x, _S1, _U1, 2, range(8), 1) == 5 / 8
-    assert O.recall_at_k(x, _S1, _U1, 2, range(8), 2) == 5 / 16
-    assert O.recall_at_k(x, _S1, _U1, 2, range(8), 3) == 8 / 24
+    g = _REC["one_round"]
+    for k, nd in g["recall_at_k"].items():
+        assert O.recall_at_k(x, _S1, _U1, _C, range(8), int(k)) == _frac(nd), k
     # the mean is over the queries given
-    assert O.recall_at_k(x, _S1, _U1, 2, [2, 4, 6], 1) == 0.0
-    assert O.recall_at_k(x, _S1, _U1, 2, [0, 1], 2) == 2 / 4
+    for sub in g["recall_subsets"]:
+        assert O.recall_at_k(x, _S1, _U1, _C, sub["queries"], sub["k"]) == _frac(sub["value"])
 
 
 def test_recall_at_k_hand_counts_two_rounds():
     """Over the union of both rounds' windows every nearest neighbour is in
-    (R@1 = 1); second neighbours miss for q0 (2) and q1 (2) only: R@2 = 14/16;
-    third neighbours miss for q0 (3) and q1 (3) only: R@3 = 20/24.  The union
-    contains the first round's windows, so recall cannot drop."""
+    (R@1 = 1); second neighbours miss for q0 and q1 only (R@2 = 14/16), third
+    ones too (R@3 = 20/24).  The union contains the first round's windows, so
+    recall cannot drop."""
     x = _circle_tokens()
-    assert O.recall_at_k(x, _S2, _U2, 2, range(8), 1) == 1.0
-    assert O.recall_at_k(x, _S2, _U2, 2, range(8), 2) == 14 / 16
-    assert O.recall_at_k(x, _S2, _U2, 2, range(8), 3) == 20 / 24
+    for k, nd in _REC["two_rounds"]["recall_at_k"].items():
+        assert O.recall_at_k(x, _S2, _U2, _C, range(8), int(k)) == _frac(nd), k
 
 
 def test_recall_at_k_equals_a_full_sort_on_random_problems():
@@ -477,8 +460,8 @@ def test_attention_mass_recall_uniform_logits():
     (2 * 3/7 + 6 * 5/7) / 8 = 9/14."""
     x = np.zeros((8, 64))
     x[:, 5] = np.arange(1, 9, dtype=np.float64)
-    assert abs(O.attention_mass_recall(x, _S1, _U1, 2, range(8)) - 3 / 7) < 1e-14
-    assert abs(O.attention_mass_recall(x, _S2, _U2, 2, range(8)) - 9 / 14) < 1e-14
+    assert abs(O.attention_mass_recall(x, _S1, _U1, _C, range(8)) - _frac(_REC["one_round"]["mass_uniform"])) < 1e-14
+    assert abs(O.attention_mass_recall(x, _S2, _U2, _C, range(8)) - _frac(_REC["two_rounds"]["mass_uniform"])) < 1e-14
 
 
 def test_attention_mass_recall_two_directions():
