@@ -29,9 +29,10 @@
 //    inputs whose products stay within float64's range.
 //  * The rotation is shared by every (batch, head): it is transposed once per
 //    call into [n_h][n_b/2 padded to 64][D] so a workgroup stages it into LDS
-//    in 64-column blocks with 16-byte row loads (block k+2 is loaded into
-//    registers while block k is used and block k+1 waits in the other LDS
-//    buffer), and read by all four waves.
+//    in blocks of 128 columns (64 where the padded width is not a multiple of
+//    128), double-buffered with one barrier per block, and read by all four
+//    waves.  The next block is moved in 64-column parts with 16-byte row loads,
+//    each part stored to the free buffer between two pipeline steps.
 //  * Each wave runs a software pipeline over 32-column tiles: the MFMAs of
 //    tile t+1 are issued before the vector top-2 selection of tile t, so the
 //    matrix and vector work of a wave overlap (they hardly overlap across
@@ -126,7 +127,6 @@ __global__ __launch_bounds__(256) void prep_kernel(const T* __restrict__ rot, T*
 // groups), 256 tokens per block; grid = (ceil(L / 256), B*H).
 // ---------------------------------------------------------------------------
 constexpr int kHashTok = 256;
-constexpr int kHashCB = 64;  // rotation columns staged in LDS per pass
 
 template <bool BF16>
 struct HashTraits;
@@ -141,7 +141,9 @@ struct HashTraits<false> {
   static constexpr int kRow = 68;  // 272 B
 };
 
-template <bool BF16>
+// CB: rotation columns staged in LDS per pass (a multiple of 64: an even number
+// of 32-column tiles), one barrier per pass.
+template <bool BF16, int CB>
 __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<BF16>::T* __restrict__ qk,
                                                    const typename HashTraits<BF16>::T* __restrict__ rot_t,
                                                    const float* __restrict__ colmax,
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
                                                    int ibits) {
   using T = typename HashTraits<BF16>::T;
   constexpr int kRow = HashTraits<BF16>::kRow;
-  __shared__ __attribute__((aligned(16))) T sR[2][kHashCB * kRow];
+  __shared__ __attribute__((aligned(16))) T sR[2][CB * kRow];
   __shared__ uint32_t sRho[kMaxHashes];  // per round: largest column norm (fp32 bits, >= 0)
 
   const int blocks_per_bh = (L + kHashTok - 1) / kHashTok;
@@ -222,17 +224,23 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
     }
   }
 
-  // Rotation blocks of kHashCB columns, over all rounds in order.  halfp is a
-  // multiple of kHashCB and rot_t is [n_h][halfp][D], so block k is the k-th
-  // contiguous run of kHashCB rows: thread t moves the 16-byte pieces
-  // t + 256 i of it, at fixed offsets.  Block k+2 is loaded into registers
-  // while block k is used and block k+1 waits in the other LDS buffer.
+  // Rotation blocks of CB columns, over all rounds in order, moved in parts of
+  // 64 columns.  halfp is a multiple of CB and rot_t is [n_h][halfp][D], so part
+  // q is the q-th contiguous run of 64 rows (block q / kParts, LDS buffer
+  // (q / kParts) & 1): thread t moves the 16-byte pieces t + 256 i of it, at
+  // fixed offsets.  While block k is used, the parts of block k+1 are stored to
+  // the other buffer one after another, each as soon as it is in registers,
+  // and the next part is loaded in its place.
   constexpr int kPieces = BF16 ? 8 : 16;  // 16-byte pieces per 64-element row
   constexpr int kPer = BF16 ? 8 : 4;      // elements per piece
-  constexpr int kPF = kHashCB * kPieces / 256;
-  constexpr uint32_t kBlockBytes = kHashCB * kD * sizeof(T);
-  const int nbpr = halfp / kHashCB;  // blocks per round
+  constexpr int kPF = 64 * kPieces / 256;
+  constexpr uint32_t kPartBytes = 64 * kD * sizeof(T);
+  constexpr int kT = CB / 32;       // 32-column tiles per block
+  constexpr int kParts = CB / 64;   // parts per block
+  static_assert(CB % 64 == 0 && kT > kParts, "an even number of tiles, and a step before each part's store");
+  const int nbpr = halfp / CB;  // blocks per round
   const int total = n_h * nbpr;
+  const int tparts = total * kParts;
   int lds_off[kPF];
 #pragma unroll
   for (int i = 0; i < kPF; ++i) {
@@ -241,18 +249,18 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
   }
   const uint32_t piece_off = 16u * threadIdx.x;
   u32x4 pf[kPF];  // native vector type: HIP's uint4 struct copies defeat register promotion here
-  auto prefetch = [&](int k) {
-    const char* src = (const char*)rot_t + (size_t)k * kBlockBytes;  // wave-uniform
+  auto prefetch = [&](int q) {
+    const char* src = (const char*)rot_t + (size_t)q * kPartBytes;  // wave-uniform
 #pragma unroll
     for (int i = 0; i < kPF; ++i) pf[i] = *(const u32x4*)(src + (piece_off + 4096u * i));
   };
-  auto stage = [&](int k) {
-    T* dst = sR[k & 1];
+  auto stage = [&](int q) {
+    T* dst = sR[(q / kParts) & 1] + (q % kParts) * 64 * kRow;
 #pragma unroll
     for (int i = 0; i < kPF; ++i) *(u32x4*)(dst + lds_off[i]) = pf[i];
   };
 
-  // Software pipeline over the stream of 32-column tiles (two per staged block):
+  // Software pipeline over the stream of 32-column tiles (kT per staged block):
   // the MFMAs of the next tile are issued between the top-2 selection steps of
   // the current one, so matrix and vector work of one wave overlap.  Blocks are
   // double-buffered in LDS (block k in sR[k & 1]), one barrier per block.
@@ -334,24 +342,38 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
     }
   };
   f32x16 ea0, ea1, ob0, ob1;  // accumulators of the even / odd tile of a block
-  prefetch(0);
-  stage(0);
-  if (total > 1) prefetch(1);
+#pragma unroll
+  for (int h = 0; h < kParts; ++h) {
+    prefetch(h);
+    stage(h);
+  }
+  if (tparts > kParts) prefetch(kParts);
   __syncthreads();
   project0(ea0, ea1);
   int r = 0, cb = 0;  // round and first column of block it
   for (int it = 0; it < total; ++it) {
-    step(sR[it & 1], 1, ob0, ob1, cb >> 5, ea0, ea1);
-    if (it + 1 < total) {
-      // sR[(it + 1) & 1] was last read before the previous iteration's barrier.
-      stage(it + 1);
-      if (it + 2 < total) prefetch(it + 2);
+    // Tiles 1 .. kT-1 of block it (MFMAs of tile t, selection of tile t - 1),
+    // alternating between the two accumulator pairs.
+    // After step t <= kParts, part t - 1 of block it+1 (in registers since the
+    // previous store) goes to sR[(it + 1) & 1], which was last read before the
+    // previous iteration's barrier, and the next part is loaded.
+#pragma unroll
+    for (int t = 1; t < kT; ++t) {
+      if (t & 1)
+        step(sR[it & 1], t, ob0, ob1, (cb >> 5) + t - 1, ea0, ea1);
+      else
+        step(sR[it & 1], t, ea0, ea1, (cb >> 5) + t - 1, ob0, ob1);
+      const int q = (it + 1) * kParts + t - 1;
+      if (t <= kParts && q < tparts) {
+        stage(q);
+        if (q + 1 < tparts) prefetch(q + 1);
+      }
     }
     __syncthreads();
     // After the last block this reads the other (stale but in-bounds) buffer
     // and the result is unused: it keeps the step free of branches.
-    step(sR[(it + 1) & 1], 0, ea0, ea1, (cb >> 5) + 1, ob0, ob1);
-    cb += kHashCB;
+    step(sR[(it + 1) & 1], 0, ea0, ea1, (cb >> 5) + kT - 1, ob0, ob1);
+    cb += CB;
     if (cb < halfp) continue;
     cb = 0;
 
@@ -778,11 +800,17 @@ hipError_t launch_hash(const void* qk, const void* rot_t, const float* colmax, i
   while ((1 << ibits) < halfp / 2) ++ibits;
   const uint32_t lowmask = (1u << ibits) - 1u;
   const unsigned grid = (unsigned)((L + kHashTok - 1) / kHashTok) * (unsigned)BH;
-  if (dt == LSH_BF16)
-    hash_kernel<true><<<grid, 256, 0, s>>>((const uint16_t*)qk, (const uint16_t*)rot_t, colmax, buckets, fix_queue,
+  // bf16: 128-column passes (half the barriers) when the padded rotation splits
+  // into them, else 64.
+  if (dt == LSH_BF16 && halfp % 128 == 0)
+    hash_kernel<true, 128><<<grid, 256, 0, s>>>((const uint16_t*)qk, (const uint16_t*)rot_t, colmax, buckets,
+                                                fix_queue, fix_count, token_scales, L, n_h, half, halfp, lowmask,
+                                                ibits);
+  else if (dt == LSH_BF16)
+    hash_kernel<true, 64><<<grid, 256, 0, s>>>((const uint16_t*)qk, (const uint16_t*)rot_t, colmax, buckets, fix_queue,
                                            fix_count, token_scales, L, n_h, half, halfp, lowmask, ibits);
   else
-    hash_kernel<false><<<grid, 256, 0, s>>>((const float*)qk, (const float*)rot_t, colmax, buckets, fix_queue,
+    hash_kernel<false, 64><<<grid, 256, 0, s>>>((const float*)qk, (const float*)rot_t, colmax, buckets, fix_queue,
                                             fix_count, token_scales, L, n_h, half, halfp, lowmask, ibits);
   return hipGetLastError();
 }
