@@ -31,8 +31,11 @@
 //    call into [n_h][n_b/2 padded to 64][D] so a workgroup stages it into LDS
 //    in blocks of 128 columns (64 where the padded width is not a multiple of
 //    128), double-buffered with one barrier per block, and read by all four
-//    waves.  The next block is moved in 64-column parts with 16-byte row loads,
-//    each part stored to the free buffer between two pipeline steps.
+//    waves.  bf16: the next block goes from memory straight into the free
+//    buffer (global_load_lds, 16 bytes per lane, no registers) while the
+//    current one is used, into XOR-swizzled 128-byte rows.  fp32: it is moved
+//    in 64-column parts through registers, each part stored between two
+//    pipeline steps.
 //  * Each wave runs a software pipeline over 32-column tiles: the MFMAs of
 //    tile t+1 are issued before the vector top-2 selection of tile t, so the
 //    matrix and vector work of a wave overlap (they hardly overlap across
@@ -133,7 +136,9 @@ struct HashTraits;
 template <>
 struct HashTraits<true> {
   using T = uint16_t;
-  static constexpr int kRow = 72;  // LDS row stride in elements (144 B, conflict-free b128 reads)
+  // Unpadded 128-byte LDS rows whose 16-byte piece p of row r sits at p ^ (r & 7)
+  // (conflict-free b128 operand reads), written by direct global-to-LDS loads.
+  static constexpr int kRow = 64;
 };
 template <>
 struct HashTraits<false> {
@@ -153,7 +158,10 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
                                                    int ibits) {
   using T = typename HashTraits<BF16>::T;
   constexpr int kRow = HashTraits<BF16>::kRow;
-  __shared__ __attribute__((aligned(16))) T sR[2][CB * kRow];
+  // Double buffer of staged rotation blocks: two arrays, so that at every use
+  // the compiler knows which one a direct load writes and which one is read.
+  __shared__ __attribute__((aligned(16))) T sR0[CB * kRow];
+  __shared__ __attribute__((aligned(16))) T sR1[CB * kRow];
   __shared__ uint32_t sRho[kMaxHashes];  // per round: largest column norm (fp32 bits, >= 0)
 
   const int blocks_per_bh = (L + kHashTok - 1) / kHashTok;
@@ -255,15 +263,31 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
     for (int i = 0; i < kPF; ++i) pf[i] = *(const u32x4*)(src + (piece_off + 4096u * i));
   };
   auto stage = [&](int q) {
-    T* dst = sR[(q / kParts) & 1] + (q % kParts) * 64 * kRow;
+    T* dst = (((q / kParts) & 1) ? sR1 : sR0) + (q % kParts) * 64 * kRow;
 #pragma unroll
     for (int i = 0; i < kPF; ++i) *(u32x4*)(dst + lds_off[i]) = pf[i];
+  };
+  // bf16: block k goes straight from memory to dst (global_load_lds, no
+  // registers).  One wave instruction fills 8 rows: lane l writes the 16-byte
+  // slot l of them (row l / 8, position l % 8) with source piece
+  // (l % 8) ^ (l / 8), which is the swizzle since the 8 rows start at a
+  // multiple of 8.  Wave w fills the 8-row groups w, w + 4, ...
+  auto dma = [&](T* dst, int k) {
+    const char* src = (const char*)rot_t + (size_t)k * (CB * kD * sizeof(T));  // wave-uniform
+    const uint32_t soff = 128u * (uint32_t)(lane >> 3) + 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
+#pragma unroll
+    for (int i = 0; i < CB / 32; ++i) {
+      const int g = wave + 4 * i;
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src + 1024u * g + soff),
+                                       (__attribute__((address_space(3))) void*)(dst + 8 * g * kRow), 16, 0, 0);
+    }
   };
 
   // Software pipeline over the stream of 32-column tiles (kT per staged block):
   // the MFMAs of the next tile are issued between the top-2 selection steps of
   // the current one, so matrix and vector work of one wave overlap.  Blocks are
-  // double-buffered in LDS (block k in sR[k & 1]), one barrier per block.
+  // double-buffered in LDS (block k in sR0 for even k, sR1 for odd), one
+  // barrier per block.
   uint32_t m1[2] = {0u, 0u}, m2[2] = {0u, 0u};  // running top-2 keys per token group
   // One pipeline step: the MFMAs of tile t_next (from LDS buffer buf) into
   // (n0, n1), interleaved in issue order with the top-2 selection of the
@@ -288,7 +312,7 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
     if constexpr (BF16) {
       bf16x8 a[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) a[s] = *(const bf16x8*)(arow + 16 * s + 8 * hb);
+      for (int s = 0; s < 4; ++s) a[s] = *(const bf16x8*)(arow + 8 * ((2 * s + hb) ^ (n & 7)));
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], bq16[0][s], n0, 0, 0, 0);
@@ -320,11 +344,11 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
   auto project0 = [&](f32x16& n0, f32x16& n1) {
     n0 = f32x16{};
     n1 = f32x16{};
-    const T* arow = sR[0] + n * kRow;
+    const T* arow = sR0 + n * kRow;
     if constexpr (BF16) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8 a = *(const bf16x8*)(arow + 16 * s + 8 * hb);
+        const bf16x8 a = *(const bf16x8*)(arow + 8 * ((2 * s + hb) ^ (n & 7)));
         n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq16[0][s], n0, 0, 0, 0);
         n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq16[1][s], n1, 0, 0, 0);
       }
@@ -342,39 +366,51 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
     }
   };
   f32x16 ea0, ea1, ob0, ob1;  // accumulators of the even / odd tile of a block
+  if constexpr (BF16) {
+    dma(sR0, 0);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
+  } else {
 #pragma unroll
-  for (int h = 0; h < kParts; ++h) {
-    prefetch(h);
-    stage(h);
+    for (int h = 0; h < kParts; ++h) {
+      prefetch(h);
+      stage(h);
+    }
+    if (tparts > kParts) prefetch(kParts);
   }
-  if (tparts > kParts) prefetch(kParts);
   __syncthreads();
   project0(ea0, ea1);
   int r = 0, cb = 0;  // round and first column of block it
-  for (int it = 0; it < total; ++it) {
+  // One block: cur holds block it, nxt receives block it+1 (the other buffer,
+  // last read before the previous block's barrier).
+  auto block = [&](const T* cur, T* nxt, int it) {
+    // bf16: block it+1 is loaded straight into nxt while block it is used.
+    if constexpr (BF16)
+      if (it + 1 < total) dma(nxt, it + 1);
     // Tiles 1 .. kT-1 of block it (MFMAs of tile t, selection of tile t - 1),
-    // alternating between the two accumulator pairs.
-    // After step t <= kParts, part t - 1 of block it+1 (in registers since the
-    // previous store) goes to sR[(it + 1) & 1], which was last read before the
-    // previous iteration's barrier, and the next part is loaded.
+    // alternating between the two accumulator pairs.  fp32: after step
+    // t <= kParts, part t - 1 of block it+1 (in registers since the previous
+    // store) goes to nxt and the next part is loaded.
 #pragma unroll
     for (int t = 1; t < kT; ++t) {
       if (t & 1)
-        step(sR[it & 1], t, ob0, ob1, (cb >> 5) + t - 1, ea0, ea1);
+        step(cur, t, ob0, ob1, (cb >> 5) + t - 1, ea0, ea1);
       else
-        step(sR[it & 1], t, ea0, ea1, (cb >> 5) + t - 1, ob0, ob1);
-      const int q = (it + 1) * kParts + t - 1;
-      if (t <= kParts && q < tparts) {
-        stage(q);
-        if (q + 1 < tparts) prefetch(q + 1);
+        step(cur, t, ea0, ea1, (cb >> 5) + t - 1, ob0, ob1);
+      if constexpr (!BF16) {
+        const int q = (it + 1) * kParts + t - 1;
+        if (t <= kParts && q < tparts) {
+          stage(q);
+          if (q + 1 < tparts) prefetch(q + 1);
+        }
       }
     }
+    if constexpr (BF16) __builtin_amdgcn_s_waitcnt(0);  // this wave's part of block it+1 has landed
     __syncthreads();
     // After the last block this reads the other (stale but in-bounds) buffer
     // and the result is unused: it keeps the step free of branches.
-    step(sR[(it + 1) & 1], 0, ea0, ea1, (cb >> 5) + kT - 1, ob0, ob1);
+    step(nxt, 0, ea0, ea1, (cb >> 5) + kT - 1, ob0, ob1);
     cb += CB;
-    if (cb < halfp) continue;
+    if (cb < halfp) return;
     cb = 0;
 
     // End of round r: merge with the partner lane (same tokens, the other 16 rows
@@ -471,6 +507,15 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
     }
     m1[0] = m1[1] = m2[0] = m2[1] = 0u;
     ++r;
+  };
+  if constexpr (BF16) {
+    // unrolled by two, so that each call's buffers are fixed arrays
+    for (int it = 0; it < total; it += 2) {
+      block(sR0, sR1, it);
+      if (it + 1 < total) block(sR1, sR0, it + 1);
+    }
+  } else {
+    for (int it = 0; it < total; ++it) block((it & 1) ? sR1 : sR0, (it & 1) ? sR0 : sR1, it);
   }
 }
 
