@@ -136,8 +136,9 @@ struct HashTraits;
 template <>
 struct HashTraits<true> {
   using T = uint16_t;
-  // Unpadded 128-byte LDS rows whose 16-byte piece p of row r sits at p ^ (r & 7)
-  // (conflict-free b128 operand reads), written by direct global-to-LDS loads.
+  // Unpadded 128-byte LDS rows whose 16-byte piece p of row r sits at
+  // p ^ (r & 7) ^ ((r >> 3) & 1) (conflict-free b128 operand reads), written by
+  // direct global-to-LDS loads.
   static constexpr int kRow = 64;
 };
 template <>
@@ -268,16 +269,19 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
     for (int i = 0; i < kPF; ++i) *(u32x4*)(dst + lds_off[i]) = pf[i];
   };
   // bf16: block k goes straight from memory to dst (global_load_lds, no
-  // registers).  One wave instruction fills 8 rows: lane l writes the 16-byte
-  // slot l of them (row l / 8, position l % 8) with source piece
-  // (l % 8) ^ (l / 8), which is the swizzle since the 8 rows start at a
-  // multiple of 8.  Wave w fills the 8-row groups w, w + 4, ...
+  // registers).  Piece p of row r is stored at position p ^ (r & 7) ^ ((r >> 3) & 1):
+  // the 16 rows an operand read covers at a time (rows r and r + 8 included)
+  // then fall on distinct LDS banks.  One wave instruction fills 8 rows: lane
+  // l writes the 16-byte slot l of them (row l / 8, position l % 8), so it
+  // loads source piece (l % 8) ^ (l / 8) ^ (g & 1) of 8-row group g.  Wave w
+  // fills the groups w, w + 4, ...
   auto dma = [&](T* dst, int k) {
     const char* src = (const char*)rot_t + (size_t)k * (CB * kD * sizeof(T));  // wave-uniform
-    const uint32_t soff = 128u * (uint32_t)(lane >> 3) + 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
 #pragma unroll
     for (int i = 0; i < CB / 32; ++i) {
       const int g = wave + 4 * i;
+      const uint32_t soff =
+          128u * (uint32_t)(lane >> 3) + 16u * (uint32_t)((lane & 7) ^ (lane >> 3) ^ (g & 1));
       __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(src + 1024u * g + soff),
                                        (__attribute__((address_space(3))) void*)(dst + 8 * g * kRow), 16, 0, 0);
     }
@@ -312,7 +316,7 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
     if constexpr (BF16) {
       bf16x8 a[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) a[s] = *(const bf16x8*)(arow + 8 * ((2 * s + hb) ^ (n & 7)));
+      for (int s = 0; s < 4; ++s) a[s] = *(const bf16x8*)(arow + 8 * ((2 * s + hb) ^ (n & 7) ^ ((n >> 3) & 1)));
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s], bq16[0][s], n0, 0, 0, 0);
@@ -348,7 +352,7 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
     if constexpr (BF16) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8 a = *(const bf16x8*)(arow + 8 * ((2 * s + hb) ^ (n & 7)));
+        const bf16x8 a = *(const bf16x8*)(arow + 8 * ((2 * s + hb) ^ (n & 7) ^ ((n >> 3) & 1)));
         n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq16[0][s], n0, 0, 0, 0);
         n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq16[1][s], n1, 0, 0, 0);
       }

@@ -379,6 +379,25 @@ def test_extreme_bucket_and_round_counts(gpu_lib, n_b, n_h, L):
             lse_check(f64(lse)[0, h], ref["lse"], f"lse h{h}")
 
 
+# The hash stages the rotation in blocks of 128 columns when the padded width
+# n_b/2 (rounded up to 64) is a multiple of 128, else 64, two blocks per loop
+# trip.  These bucket counts give one block per round with padding (130, 256),
+# an odd number of blocks in all (256 with one round, 384 with three rounds: 3
+# blocks per round), 64-column blocks beyond one per round (640: 5) and
+# 128-column ones (1536: 6), in both dtypes.
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n_b,n_h", [(130, 2), (256, 1), (384, 3), (640, 2), (1536, 3)])
+def test_hash_staging_block_counts(gpu_lib, n_b, n_h, dtype):
+    L = 320  # two hash blocks, the second one ragged
+    say(f"case staging n_b{n_b} n_h{n_h} L{L} {dtype}")
+    qk_t = I.gaussian(41, (1, 2, L, 64), dtype)
+    rot_t = I.rotations(42, n_h, 64, n_b, dtype)
+    got = bd.lsh_hash(to_device(qk_t), to_device(rot_t), n_b, n_h).cpu().numpy()
+    for h in range(2):
+        ref, _ = O.hash_buckets(qk_t.values[0, h].astype(np.float64), rot_t.values.astype(np.float64), n_b)
+        np.testing.assert_array_equal(got[0, h], ref, err_msg=f"head {h}")
+
+
 def test_repeatable_bits(gpu_lib):
     inp = I.make_inputs("causal_lm_4k", B=2, H=2, L=1024)
     say("case determinism")
