@@ -233,13 +233,15 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
     }
   }
 
-  // Rotation blocks of CB columns, over all rounds in order, moved in parts of
-  // 64 columns.  halfp is a multiple of CB and rot_t is [n_h][halfp][D], so part
-  // q is the q-th contiguous run of 64 rows (block q / kParts, LDS buffer
-  // (q / kParts) & 1): thread t moves the 16-byte pieces t + 256 i of it, at
-  // fixed offsets.  While block k is used, the parts of block k+1 are stored to
-  // the other buffer one after another, each as soon as it is in registers,
-  // and the next part is loaded in its place.
+  // Rotation blocks of CB columns, over all rounds in order.  halfp is a multiple
+  // of CB and rot_t is [n_h][halfp][D], so block k is the k-th contiguous run of
+  // CB rows.  bf16 moves a block with direct loads (dma, below).  fp32 moves it
+  // through registers in parts of 64 columns: part q is the q-th contiguous run
+  // of 64 rows (block q / kParts, LDS buffer (q / kParts) & 1), and thread t
+  // moves its 16-byte pieces t + 256 i at fixed offsets.  While block k is
+  // used, the parts of block k+1 are stored to the other buffer one after
+  // another, each as soon as it is in registers, and the next part is loaded
+  // in its place.
   constexpr int kPieces = BF16 ? 8 : 16;  // 16-byte pieces per 64-element row
   constexpr int kPer = BF16 ? 8 : 4;      // elements per piece
   constexpr int kPF = 64 * kPieces / 256;
