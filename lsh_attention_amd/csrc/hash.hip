@@ -534,8 +534,8 @@ __global__ __launch_bounds__(256, 3) void hash_kernel(const typename HashTraits<
 //     each load instruction covering whole rows: lane l holds 16-byte piece
 //     l % P of row (64 / P) i + l / P (P pieces per row), so an instruction
 //     touches 64 / P cache lines, not 64 as a column per lane would.  A batch of
-//     P instructions covers 64 rows; a reduce-scatter over the P lanes of a row
-//     finishes the sums, leaving lane l row (64 / P)(l % P) + l / P of the batch.
+//     P instructions covers 64 rows; DPP adds over the P lanes of a row finish
+//     the sums, and lane l keeps row (64 / P)(l % P) + l / P of the batch.
 //  2. The exact argmax lies among the columns whose fp32 score is within 2 eps
 //     (plus a denormal allowance) of the best one: each is scored as a float64
 //     sum of exact products by the whole wave (lane d holds element d), lowest
@@ -546,6 +546,12 @@ constexpr int kMaxCand = 8;
 constexpr int kFixWaves = 4;
 constexpr int kMaxHalfp = 2048;
 static_assert(kMaxHalfp >= kMaxBuckets / 2 && kMaxHalfp % 64 == 0, "score slots for the largest n_b");
+
+// A lane's value moved by a DPP lane pattern (CTRL: the gfx9 dpp_ctrl code).
+template <int CTRL>
+__device__ inline float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
 
 // fp32 dot product of one 16-byte piece of x and of a rotation row.
 __device__ inline float piece_dot(const uint4& a, const uint4& b, uint16_t) {
@@ -591,8 +597,11 @@ __global__ __launch_bounds__(kFixWaves * 64) void fixup_kernel(const T* __restri
     const uint4 xp = ((const uint4*)x)[lane % P];
     const double xd = to_f64(x[lane]);
     const uint4* R4 = (const uint4*)(rot_t + (size_t)r * halfp * kD);
-    float rho = 0.f;  // largest column norm of the round (rounded up)
-    for (int k = 0; k < nbatch; ++k) rho = fmaxf(rho, colmax[r * nbatch + k]);
+    // largest column norm of the round (rounded up): one block bound per lane
+    // (nbatch <= 32), then a wave maximum
+    float rho = lane < nbatch ? colmax[r * nbatch + lane] : 0.f;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) rho = fmaxf(rho, __shfl_xor(rho, off));
     // Phase 1.
     float m = 0.f;
     for (int g = 0; g < nbatch; ++g) {
@@ -602,17 +611,24 @@ __global__ __launch_bounds__(kFixWaves * 64) void fixup_kernel(const T* __restri
       float V[P];
 #pragma unroll
       for (int i = 0; i < P; ++i) V[i] = piece_dot(xp, rw[i], T());
+      // Sum each row over the P lanes that hold its pieces (a group of P
+      // consecutive lanes) with DPP moves inside the group: swap neighbours,
+      // swap pairs, mirror the 8 lanes, (P = 16) mirror the 16.  Every lane ends
+      // with the same sums (each step adds two equal-shaped partial sums, and
+      // fp32 addition is commutative); lane l keeps the one of row
+      // (64 / P)(l % P) + l / P.
 #pragma unroll
-      for (int h = P / 2; h >= 1; h >>= 1) {
-        const bool up = (lane & h) != 0;  // keep the upper half of the batch's rows
-#pragma unroll
-        for (int i = 0; i < h; ++i) {
-          const float send = up ? V[i] : V[i + h], keep = up ? V[i + h] : V[i];
-          V[i] = keep + __shfl_xor(send, h);
-        }
+      for (int i = 0; i < P; ++i) {
+        V[i] += dpp_f32<0xB1>(V[i]);   // quad_perm [1, 0, 3, 2]: lane ^ 1
+        V[i] += dpp_f32<0x4E>(V[i]);   // quad_perm [2, 3, 0, 1]: lane ^ 2
+        V[i] += dpp_f32<0x141>(V[i]);  // row_half_mirror: lane i <-> 7 - i
+        if constexpr (P == 16) V[i] += dpp_f32<0x140>(V[i]);  // row_mirror: i <-> 15 - i
       }
+      float own = V[0];
+#pragma unroll
+      for (int i = 1; i < P; ++i) own = (lane & (P - 1)) == i ? V[i] : own;
       const int row = 64 * g + (64 / P) * (lane % P) + lane / P;
-      const float a = fabsf(V[0]);
+      const float a = fabsf(own);
       sc[64 * g + lane] = row < half ? a : -INFINITY;
       m = row < half ? fmaxf(m, a) : m;
     }
